@@ -1,0 +1,248 @@
+"""CPU oracle of the liveness-sparse routed-expert MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
+the CPU-baseline leg of bench.py may import this package.  The product path
+(block_diffusion_sparse_amd and its HIP library) never imports it.
+
+This module is argument marshalling around oracle.c (plain C, double sums);
+the per-step citations of the pages live there.  `OracleLayer` replays the
+per-layer state machine of one block (plan build, then forward + commit per
+refinement iteration) by calling those steps in the pages' order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+from .build import LIB, build as build_oracle
+
+_c_int = ctypes.c_int
+_ptr = ctypes.c_void_p
+_libs: dict = {}
+
+
+def load(path: str = LIB) -> ctypes.CDLL:
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        build_oracle(path, quiet=True)
+    lib = ctypes.CDLL(path)
+    lib.orc_num_threads.restype = _c_int
+    lib.orc_support_status.restype = _c_int
+    lib.orc_support_build.restype = _c_int
+    lib.orc_under_covered.restype = ctypes.c_int64
+    lib.orc_fresh_set.restype = _c_int
+    lib.orc_worklist.restype = _c_int
+    for name in ("orc_router_logits", "orc_route", "orc_expert", "orc_moe_rows", "orc_commit",
+                 "orc_dense_moe"):
+        getattr(lib, name).restype = None
+    _libs[path] = lib
+    return lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _is_bf16(a: np.ndarray) -> int:
+    return 1 if a.dtype == np.uint16 else 0
+
+
+def num_threads(lib=None) -> int:
+    return (lib or load()).orc_num_threads()
+
+
+def router_logits(x, Wg, bias=None, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(x)
+    Wg = np.ascontiguousarray(Wg, dtype=np.float32)
+    M, H = x.shape
+    E = Wg.shape[0]
+    G = np.empty((M, E), dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    lib.orc_router_logits(_c_int(M), _c_int(H), _c_int(E), _c_int(_is_bf16(x)), _p(x), _p(Wg),
+                          _p(b), _p(G))
+    return G
+
+
+def route(G, K, Kext, gate_sigmoid, norm_topk, lib=None):
+    lib = lib or load()
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    M, E = G.shape
+    ids = np.empty((M, Kext), dtype=np.int32)
+    s = np.empty((M, Kext), dtype=np.float64)
+    w = np.empty((M, K), dtype=np.float64)
+    q = np.empty((M, Kext), dtype=np.int64)
+    lib.orc_route(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _c_int(int(gate_sigmoid)),
+                  _c_int(int(norm_topk)), _p(G), _p(ids), _p(s), _p(w), _p(q))
+    return ids, s, w, q
+
+
+def support_status(ids, K, inS, support_valid, lib=None) -> int:
+    lib = lib or load()
+    M, Kext = ids.shape
+    return lib.orc_support_status(_c_int(M), _c_int(K), _c_int(Kext), _p(ids), _p(inS),
+                                  _c_int(int(support_valid)))
+
+
+def support_build(ids, q, E, K, B, c, alpha, qfrac, beta, lib=None):
+    lib = lib or load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.int64)
+    M, Kext = ids.shape
+    inS = np.zeros(E, dtype=np.uint8)
+    slot_of = np.empty(E, dtype=np.int32)
+    S_list = np.empty(E, dtype=np.int32)
+    stats = np.zeros(5, dtype=np.int64)
+    n = lib.orc_support_build(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _p(ids), _p(q),
+                              _c_int(B), _c_int(c), _c_int(alpha[0]), _c_int(alpha[1]),
+                              _c_int(qfrac[0]), _c_int(qfrac[1]), _c_int(beta[0]),
+                              _c_int(beta[1]), _p(inS), _p(slot_of), _p(S_list), _p(stats))
+    return inS, slot_of, S_list[:n].copy(), stats
+
+
+def under_covered(ids, q, K, inS, alpha, lib=None) -> int:
+    lib = lib or load()
+    M, Kext = ids.shape
+    return int(lib.orc_under_covered(_c_int(M), _c_int(K), _c_int(Kext), _p(ids), _p(q),
+                                     _p(inS), _c_int(alpha[0]), _c_int(alpha[1])))
+
+
+def fresh_set(R, it, valid, last_fresh, prev_D, D, force=None, lib=None):
+    lib = lib or load()
+    M = D.shape[0]
+    fresh = np.empty(M, dtype=np.uint8)
+    D = np.ascontiguousarray(D, dtype=np.uint8)
+    f = None if force is None else np.ascontiguousarray(force, dtype=np.uint8)
+    anomaly = lib.orc_fresh_set(_c_int(M), _c_int(R), _c_int(it), _p(valid), _p(last_fresh),
+                                _p(prev_D), _p(D), _p(f), _p(fresh))
+    return fresh, int(anomaly)
+
+
+def worklist(ids, w, K, fresh, slot_of, nS, lib=None) -> dict:
+    lib = lib or load()
+    M, Kext = ids.shape
+    P_max = M * K
+    wl_pos = np.empty(max(P_max, 1), dtype=np.int32)
+    wl_k = np.empty(max(P_max, 1), dtype=np.int32)
+    wl_w = np.empty(max(P_max, 1), dtype=np.float64)
+    offs = np.empty(nS + 1, dtype=np.int32)
+    inv = np.empty(M * K, dtype=np.int32)
+    P = lib.orc_worklist(_c_int(M), _c_int(K), _c_int(Kext), _p(ids), _p(w), _p(fresh),
+                         _p(slot_of), _c_int(nS), _p(wl_pos), _p(wl_k), _p(wl_w), _p(offs),
+                         _p(inv))
+    return dict(P=P, wl_pos=wl_pos[:P].copy(), wl_k=wl_k[:P].copy(), wl_w=wl_w[:P].copy(),
+                offs=offs, inv=inv.reshape(M, K))
+
+
+def expert(x_row, W1e, W3e, W2e, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x_row = np.ascontiguousarray(x_row)
+    I, H = W1e.shape
+    y = np.empty(H, dtype=np.float64)
+    lib.orc_expert(_c_int(H), _c_int(I), _c_int(_is_bf16(x_row)), _p(x_row),
+                   _p(np.ascontiguousarray(W1e)), _p(np.ascontiguousarray(W3e)),
+                   _p(np.ascontiguousarray(W2e)), _p(y))
+    return y
+
+
+def dense_moe(x, Wg, bias, W1, W3, W2, SW1, SW3, SW2, K, gate_sigmoid, norm_topk, lib=None):
+    lib = lib or load()
+    x = np.ascontiguousarray(x)
+    M, H = x.shape
+    E, I, _ = W1.shape
+    Is = SW1.shape[0] if SW1 is not None else 0
+    R = np.empty((M, H), dtype=np.float64)
+    Y = np.empty((M, H), dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    lib.orc_dense_moe(_c_int(M), _c_int(H), _c_int(I), _c_int(Is), _c_int(E), _c_int(K),
+                      _c_int(int(gate_sigmoid)), _c_int(int(norm_topk)), _c_int(_is_bf16(x)),
+                      _p(x), _p(np.ascontiguousarray(Wg, dtype=np.float32)), _p(b), _p(W1),
+                      _p(W3), _p(W2), _p(SW1), _p(SW3), _p(SW2), _p(R), _p(Y))
+    return R, Y
+
+
+class OracleLayer:
+    """Replays one MoE layer over one block: plan build, then forward/commit per iteration.
+
+    weights: dict with router_w [E,H] f32, router_b [E] f32 or None, w1/w3 [E,I,H],
+    w2 [E,H,I], sw1/sw3 [Is,H], sw2 [H,Is] or None (uint16 bf16 bits or f32).
+    rows: positions whose expert outputs are evaluated (None = all); the discrete
+    stages (router, top-k, support, fresh set, worklist) always cover every position.
+    """
+
+    NEG_INF_ITER = -(1 << 30)
+
+    def __init__(self, w, weights: dict, lib=None, rows=None):
+        self.lib = lib or load()
+        self.w = w
+        self.W = {k: (None if v is None else np.ascontiguousarray(v)) for k, v in weights.items()}
+        M, E, H = w.M, w.n_experts, w.hidden
+        self.rows = np.arange(M, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+        # plan build / cold path: caches cleared, support invalid, iteration 0
+        self.valid = np.zeros(M, dtype=np.uint8)
+        self.last_fresh = np.full(M, self.NEG_INF_ITER, dtype=np.int32)
+        self.prev_D = np.zeros(M, dtype=np.uint8)
+        self.cache = np.zeros((M, H), dtype=np.float64)
+        self.inS = np.zeros(E, dtype=np.uint8)
+        self.slot_of = np.full(E, -1, dtype=np.int32)
+        self.S_list = np.zeros(0, dtype=np.int32)
+        self.support_valid = False
+        self.iter = 0
+        self.counters = dict(cold=0, hot_update=0, hot_skip=0, anomalies=0, fresh_rows=0,
+                             pairs=0, coverage_unmet=0)
+        self._pending = None
+
+    def forward(self, x, D, force=None) -> dict:
+        w, lib = self.w, self.lib
+        K, Kext, E = w.top_k, w.k_ext, w.n_experts
+        W = self.W
+        G = router_logits(x, W["router_w"], W["router_b"], lib=lib)
+        ids, s, wts, q = route(G, K, Kext, w.gate == "sigmoid", w.norm_topk, lib=lib)
+        path = support_status(ids, K, self.inS, self.support_valid, lib=lib)
+        stats = None
+        if path:
+            self.inS, self.slot_of, self.S_list, stats = support_build(
+                ids, q, E, K, w.B, w.c, w.alpha, w.q, w.beta, lib=lib)
+            self.support_valid = True
+            self.counters["cold" if path == 1 else "hot_update"] += 1
+            if stats[2]:
+                self.counters["coverage_unmet"] += 1
+        else:
+            self.counters["hot_skip"] += 1
+        fresh, anomaly = fresh_set(w.staleness_R, self.iter, self.valid, self.last_fresh,
+                                   self.prev_D, D, force, lib=lib)
+        wl = worklist(ids, wts, K, fresh, self.slot_of, len(self.S_list), lib=lib)
+        H, I = w.hidden, w.inter
+        Is = w.shared_inter if W.get("sw1") is not None else 0
+        rows = self.rows
+        R = np.empty((len(rows), H), dtype=np.float64)
+        Y = np.empty((len(rows), H), dtype=np.float64)
+        x = np.ascontiguousarray(x)
+        lib.orc_moe_rows(_c_int(w.M), _c_int(H), _c_int(I), _c_int(Is), _c_int(E), _c_int(K),
+                         _c_int(Kext), _c_int(_is_bf16(x)), _p(x), _p(ids), _p(wts), _p(fresh),
+                         _p(W["w1"]), _p(W["w3"]), _p(W["w2"]), _p(W.get("sw1")),
+                         _p(W.get("sw3")), _p(W.get("sw2")), _c_int(len(rows)), _p(rows),
+                         _p(self.cache), _p(R), _p(Y))
+        self._pending = (fresh, np.ascontiguousarray(D, dtype=np.uint8).copy(), anomaly)
+        return dict(G=G, ids=ids, s=s, w=wts, q=q, path=path, support_stats=stats,
+                    inS=self.inS.copy(), slot_of=self.slot_of.copy(), S_list=self.S_list.copy(),
+                    fresh=fresh, anomaly=anomaly, worklist=wl, rows=rows, R=R, Y=Y,
+                    iter=self.iter)
+
+    def commit(self):
+        assert self._pending is not None, "commit without a forward"
+        fresh, D, anomaly = self._pending
+        self.lib.orc_commit(_c_int(self.w.M), _c_int(self.iter), _p(fresh), _p(D),
+                            _p(self.valid), _p(self.last_fresh), _p(self.prev_D))
+        self.counters["anomalies"] += anomaly
+        self.counters["fresh_rows"] += int(fresh.sum())
+        self.counters["pairs"] += int(fresh.sum()) * self.w.top_k
+        self.iter += 1
+        self._pending = None

@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each pin compares the oracle with something other than itself: a library
+routine that computes the same definition (numpy matmul, stable argsort,
+scipy softmax / expit, Python's sorted), a closed form, a special case, a
+hand-worked example, or an invariant the pages state.  `test_planted_mistakes`
+rebuilds the oracle with one mistake planted at a time and checks that some
+pin fails for each.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- independent helpers
+
+def f64(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def np_router(x, Wg, b):
+    G = f64(x) @ Wg.astype(np.float64).T
+    if b is not None:
+        G = G + b.astype(np.float64)
+    return G.astype(np.float32)
+
+
+def np_swiglu(xrow, W1, W3, W2):
+    g = f64(W1) @ xrow
+    u = f64(W3) @ xrow
+    return f64(W2) @ (g * expit(g) * u)
+
+
+def np_dense(x, W, K, sigmoid, norm):
+    xf = f64(x)
+    G = np_router(x, W["router_w"], W["router_b"])
+    order = np.argsort(-G, axis=1, kind="stable")[:, :K]
+    s = expit(G.astype(np.float64)) if sigmoid else softmax(G.astype(np.float64), axis=1)
+    M, H = xf.shape
+    R = np.zeros((M, H))
+    Y = np.zeros((M, H))
+    for t in range(M):
+        wt = s[t, order[t]]
+        if norm:
+            wt = wt / wt.sum()
+        for e, we in zip(order[t], wt):
+            R[t] += we * np_swiglu(xf[t], W["w1"][e], W["w3"][e], W["w2"][e])
+        Y[t] = R[t]
+        if W.get("sw1") is not None:
+            Y[t] += np_swiglu(xf[t], W["sw1"], W["sw3"], W["sw2"])
+    return R, Y
+
+
+def rownorm_err(a, b):
+    den = np.maximum(np.abs(b).max(axis=-1), 1e-300)
+    return float((np.abs(a - b).max(axis=-1) / den).max())
+
+
+def small_workload(**kw):
+    base = dict(name="small", hidden=64, n_experts=16, top_k=4, inter=24, n_shared=1,
+                shared_inter=20, batch=2, block=8, iters=6, staleness_R=3, n_layers=1,
+                zipf=None, sigma=0.1)
+    base.update(kw)
+    return synth.workload(3, **base)
+
+
+def rand_x(rng, M, H, bf16):
+    x = rng.standard_normal((M, H), dtype=np.float32)
+    return synth.f32_to_bf16_bits(x) if bf16 else x
+
+
+# ----------------------------------------------------------------- pins (each takes the library)
+
+def pin_router(orc, lib):
+    rng = np.random.default_rng(5)
+    for bf16 in (True, False):
+        M, H, E = 37, 96, 13
+        x = rand_x(rng, M, H, bf16)
+        Wg = rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.05)
+        b = rng.standard_normal(E).astype(np.float32)
+        G = orc.router_logits(x, Wg, b, lib=lib)
+        ref = np_router(x, Wg, b)
+        ulps = np.abs(G.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1, "router logits differ from fp32(x W^T + b) by more than 1 ulp"
+        assert (ulps == 0).mean() > 0.99
+    # one-hot rows select a column of W exactly: G[t, e] = fp32(W[e, t] + b[e])
+    H = E = 8
+    x = np.eye(H, dtype=np.float32)
+    Wg = rng.standard_normal((E, H), dtype=np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    G = orc.router_logits(x, Wg, b, lib=lib)
+    assert np.array_equal(G, (Wg.T.astype(np.float64) + b.astype(np.float64)).astype(np.float32))
+
+
+def pin_topk(orc, lib):
+    rng = np.random.default_rng(6)
+    M, E, K, Kext = 50, 24, 4, 9
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    G[:, 7] = G[:, 3]               # exact ties between experts 3 and 7 ...
+    G[::2, 3] = G[::2, 7] = 9.0     # ... that sit at the top on even rows
+    ids, s, w, q = orc.route(G, K, Kext, True, True, lib=lib)
+    ref = np.argsort(-G, axis=1, kind="stable")[:, :Kext]
+    assert np.array_equal(ids, ref), "top-k must equal a stable sort on (-G) (ties -> lower id)"
+    assert (ids[::2, 0] == 3).all() and (ids[::2, 1] == 7).all()
+
+
+def pin_weights(orc, lib):
+    rng = np.random.default_rng(7)
+    M, E, K, Kext = 40, 16, 4, 8
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    for sigmoid in (True, False):
+        for norm in (True, False):
+            ids, s, w, q = orc.route(G, K, Kext, sigmoid, norm, lib=lib)
+            full = expit(G.astype(np.float64)) if sigmoid else softmax(G.astype(np.float64), axis=1)
+            s_ref = np.take_along_axis(full, ids, axis=1)
+            np.testing.assert_allclose(s, s_ref, rtol=1e-13, atol=0)
+            w_ref = s_ref[:, :K] / s_ref[:, :K].sum(1, keepdims=True) if norm else s_ref[:, :K]
+            np.testing.assert_allclose(w, w_ref, rtol=1e-13, atol=0)
+            assert np.array_equal(q, np.floor(s * 65536.0 + 0.5).astype(np.int64))
+            if norm:
+                np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-13)
+            elif not sigmoid:
+                assert (w.sum(1) <= 1.0 + 1e-12).all()
+    ids, s, w, q = orc.route(G, E, E, False, False, lib=lib)   # K = E softmax: all mass
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-13)
+
+
+def pin_atlas_hand(orc, lib):
+    with open(os.path.join(GOLDEN, "atlas_hand_worked.json")) as f:
+        g = json.load(f)
+    inst = g["instance"]
+    ids = np.array(inst["ids"], dtype=np.int32)
+    q = np.array(inst["q"], dtype=np.int64)
+    for case in g["cases"]:
+        inS, slot_of, S, stats = orc.support_build(ids, q, inst["E"], inst["K"], inst["B"],
+                                                   case["c"], case["alpha"], case["q"],
+                                                   case["beta"], lib=lib)
+        assert list(S) == case["support"], case["name"]
+        assert int(stats[1]) == case["rounds"], case["name"]
+        assert int(stats[0]) == case["final_U"], case["name"]
+        assert int(stats[2]) == case["unmet"], case["name"]
+        assert int(stats[4]) == len(case["support_before_closure"]), case["name"]
+
+
+def pin_atlas_special(orc, lib):
+    rng = np.random.default_rng(8)
+    M, E, K, Kext = 64, 32, 4, 8
+    G = (rng.standard_normal((M, E)) + np.linspace(2, -2, E)).astype(np.float32)
+    ids, s, w, q = orc.route(G, K, Kext, True, True, lib=lib)
+    p = np.bincount(ids.ravel(), weights=q.ravel(), minlength=E).astype(np.int64)
+    closure = set(ids[:, :K].ravel().tolist())
+    # alpha = 0: nothing is under-covered; S = top-B by popularity (p desc, id asc) plus closure
+    for B in (0, 3, 10):
+        inS, slot_of, S, stats = orc.support_build(ids, q, E, K, B, 4, (0, 1), (95, 100), (1, 1), lib=lib)
+        order = sorted([e for e in range(E) if p[e] > 0], key=lambda e: (-p[e], e))[:B]
+        assert set(S.tolist()) == set(order) | closure
+        assert stats[1] == 0 and stats[0] == 0
+    # B at least the number of experts with popularity: S = every candidate expert
+    inS, slot_of, S, stats = orc.support_build(ids, q, E, K, E, 4, (9, 10), (95, 100), (1, 1), lib=lib)
+    assert set(S.tolist()) == set(np.nonzero(p > 0)[0].tolist())
+    # invariants on the real goal: closure inside S, goal met or flagged, slots are ranks
+    for B, c in ((2, 1), (4, 2), (8, 4)):
+        inS, slot_of, S, stats = orc.support_build(ids, q, E, K, B, c, (9, 10), (95, 100), (1, 1), lib=lib)
+        assert closure <= set(S.tolist())
+        assert stats[2] == 1 or 100 * stats[0] <= 5 * M
+        assert list(S) == sorted(S)
+        assert all(slot_of[e] == i for i, e in enumerate(S))
+        assert (slot_of[[e for e in range(E) if e not in set(S.tolist())]] == -1).all()
+
+
+def pin_fresh(orc, lib):
+    # tiny fp32 workload: 4 commits per iteration, R = 2 -> fresh counts 16, 16, 12, 12
+    w = synth.workload(1)
+    D = synth.decoded_masks(w)
+    M = w.M
+    valid = np.zeros(M, np.uint8)
+    last = np.full(M, -(1 << 30), np.int32)
+    prev = np.zeros(M, np.uint8)
+    counts = []
+    for i in range(w.iters):
+        fresh, an = orc.fresh_set(w.staleness_R, i, valid, last, prev, D[i], lib=lib)
+        counts.append(int(fresh.sum()))
+        lib.orc_commit(M, i, fresh.ctypes.data_as(np.ctypeslib.ctypes.c_void_p),
+                       D[i].ctypes.data_as(np.ctypeslib.ctypes.c_void_p),
+                       valid.ctypes.data_as(np.ctypeslib.ctypes.c_void_p),
+                       last.ctypes.data_as(np.ctypeslib.ctypes.c_void_p),
+                       prev.ctypes.data_as(np.ctypeslib.ctypes.c_void_p))
+    assert counts == [16, 16, 12, 12], counts
+
+
+def pin_worklist(orc, lib):
+    rng = np.random.default_rng(9)
+    M, E, K, Kext = 45, 20, 3, 5
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    ids, s, w, q = orc.route(G, K, Kext, False, False, lib=lib)
+    fresh = (rng.random(M) < 0.6).astype(np.uint8)
+    used = sorted(set(ids[:, :K].ravel().tolist()) | {0, 19})
+    slot_of = np.full(E, -1, np.int32)
+    slot_of[used] = np.arange(len(used))
+    wl = orc.worklist(ids, w, K, fresh, slot_of, len(used), lib=lib)
+    pairs = sorted((int(ids[t, k]), t, k) for t in range(M) if fresh[t] for k in range(K))
+    assert wl["P"] == len(pairs)
+    assert [(int(ids[t, k]), int(t), int(k)) for t, k in zip(wl["wl_pos"], wl["wl_k"])] == pairs
+    cnt = np.bincount([slot_of[e] for e, _, _ in pairs], minlength=len(used))
+    assert np.array_equal(wl["offs"], np.concatenate([[0], np.cumsum(cnt)]))
+    for p, (t, k) in enumerate(zip(wl["wl_pos"], wl["wl_k"])):
+        assert wl["inv"][t, k] == p and wl["wl_w"][p] == w[t, k]
+    assert (wl["inv"][fresh == 0] == -1).all()
+
+
+def pin_expert(orc, lib):
+    rng = np.random.default_rng(10)
+    for bf16 in (True, False):
+        H, I = 40, 28
+        x = rand_x(rng, 1, H, bf16)[0]
+        W1, W3 = rand_x(rng, I, H, bf16), rand_x(rng, I, H, bf16)
+        W2 = rand_x(rng, H, I, bf16)
+        y = orc.expert(x, W1, W3, W2, lib=lib)
+        np.testing.assert_allclose(y, np_swiglu(f64(x), W1, W3, W2), rtol=1e-12, atol=1e-14)
+
+
+def pin_dense(orc, lib):
+    w = small_workload()
+    W = synth.layer_weights(w, 0)
+    W["router_b"] = np.random.default_rng(11).standard_normal(w.n_experts).astype(np.float32)
+    x = synth.hidden_states(w, 0)[0]
+    for sig, norm in ((True, True), (False, False)):
+        R, Y = orc.dense_moe(x, W["router_w"], W["router_b"], W["w1"], W["w3"], W["w2"],
+                             W["sw1"], W["sw3"], W["sw2"], w.top_k, sig, norm, lib=lib)
+        Rr, Yr = np_dense(x, W, w.top_k, sig, norm)
+        assert rownorm_err(R, Rr) < 1e-12 and rownorm_err(Y, Yr) < 1e-12
+
+
+def pin_all_fresh_equals_dense(orc, lib):
+    # staleness bound R = 1: every iteration is exact and equals the dense layer
+    w = small_workload(staleness_R=1)
+    W = synth.layer_weights(w, 0)
+    D = synth.decoded_masks(w)
+    X = synth.hidden_states(w, 0, D)
+    L = orc.OracleLayer(w, W, lib=lib)
+    for i in range(w.iters):
+        out = L.forward(X[i], D[i])
+        assert out["fresh"].all()
+        Rr, Yr = np_dense(X[i], W, w.top_k, True, True)
+        assert rownorm_err(out["R"], Rr) < 1e-12 and rownorm_err(out["Y"], Yr) < 1e-12
+        L.commit()
+
+
+def pin_staleness(orc, lib):
+    # stable rows reuse the routed output of their last fresh iteration, bitwise, and
+    # that output is the dense routed output of that iteration; age <= R - 1
+    w = small_workload(staleness_R=3, iters=9)
+    W = synth.layer_weights(w, 0)
+    D = synth.decoded_masks(w)
+    X = synth.hidden_states(w, 0, D)
+    L = orc.OracleLayer(w, W, lib=lib)
+    dense_R = []
+    n_stable = 0
+    for i in range(w.iters):
+        dense_R.append(np_dense(X[i], W, w.top_k, True, True)[0])
+        last = L.last_fresh.copy()
+        cache = L.cache.copy()
+        out = L.forward(X[i], D[i])
+        fresh = out["fresh"].astype(bool)
+        newly = D[i].astype(bool) & ~L.prev_D.astype(bool)
+        assert fresh[~D[i].astype(bool)].all() and fresh[newly].all()
+        for t in np.nonzero(~fresh)[0]:
+            n_stable += 1
+            assert 0 <= i - last[t] <= w.staleness_R - 1
+            assert np.array_equal(out["R"][t], cache[t])
+            assert rownorm_err(out["R"][t:t + 1], dense_R[last[t]][t:t + 1]) < 1e-12
+        assert rownorm_err(out["R"][fresh], dense_R[i][fresh]) < 1e-12
+        L.commit()
+    assert n_stable > 0
+
+
+PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
+        pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(orc, pin):
+    pin(orc, orc.load())
+
+
+def test_anomaly_and_special_fresh_cases(orc):
+    M = 10
+    valid = np.ones(M, np.uint8)
+    last = np.full(M, 5, np.int32)
+    prev = np.ones(M, np.uint8)
+    D = np.ones(M, np.uint8)
+    fresh, an = orc.fresh_set(4, 6, valid, last, prev, D)
+    assert an == 0 and fresh.sum() == 0          # all stable, age 1 < R
+    fresh, an = orc.fresh_set(1, 6, valid, last, prev, D)
+    assert fresh.all()                             # R = 1: never stale
+    D2 = D.copy()
+    D2[3] = 0                                      # decoded -> live: anomaly, full fresh pass
+    fresh, an = orc.fresh_set(4, 6, valid, last, prev, D2)
+    assert an == 1 and fresh.all()
+    fresh, an = orc.fresh_set(4, 6, np.zeros(M, np.uint8), last, prev, D)
+    assert fresh.all()                             # cache miss
+    force = np.zeros(M, np.uint8)
+    force[[1, 7]] = 1
+    fresh, an = orc.fresh_set(4, 6, valid, last, prev, D, force)
+    assert fresh.nonzero()[0].tolist() == [1, 7]
+
+
+MUTATIONS = {1: "router bias dropped", 2: "down-projection operand indexed wrongly",
+             3: "SiLU sign flipped", 4: "ties broken toward the higher id",
+             5: "refresh-due test dropped", 6: "worklist in position order",
+             7: "H_e uses a strict inequality"}
+
+
+@pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
+def test_planted_mistakes(orc, m, tmp_path):
+    path = str(tmp_path / f"liboracle_m{m}.so")
+    orc.build_oracle(path, mutate=m, quiet=True)
+    lib = orc.load(path)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc, lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {MUTATIONS[m]}"
