@@ -1,0 +1,421 @@
+// C ABI of libepoch: descriptor validation, workspace carving, the per-iteration launch
+// sequence on the caller's stream, and the plan lifecycle.  No device allocation, no host
+// synchronisation on the forward path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "epoch_internal.h"
+
+using namespace epoch;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Layout {
+  std::vector<LayerState> layers;
+  Scratch scratch;
+  size_t bytes = 0;
+};
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t n) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += std::max<size_t>(n, 1) * sizeof(T);
+    return p;
+  }
+  void* take_bytes(size_t n) { return take<char>(n); }
+};
+
+int32_t check_desc(const epoch_desc* d) {
+  if (!d) return EPOCH_E_NULL;
+  if (d->act_dtype != EPOCH_DTYPE_BF16 && d->act_dtype != EPOCH_DTYPE_F32) return EPOCH_E_DTYPE;
+  if (d->gate != EPOCH_GATE_SOFTMAX && d->gate != EPOCH_GATE_SIGMOID) return EPOCH_E_DTYPE;
+  if (d->flags != 0) return EPOCH_E_SHAPE;
+  if (d->n_layers < 1 || d->hidden < 1 || d->hidden > 16384) return EPOCH_E_SHAPE;
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts) return EPOCH_E_SHAPE;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return EPOCH_E_SHAPE;
+  if (d->inter < 1 || d->batch < 1 || d->block < 1) return EPOCH_E_SHAPE;
+  if ((long long)d->batch * d->block > (1 << 20)) return EPOCH_E_SHAPE;
+  if (d->n_shared != 0 && d->n_shared != 1) return EPOCH_E_SHAPE;
+  if (d->n_shared && d->shared_inter < 1) return EPOCH_E_SHAPE;
+  if (d->staleness_R < 1) return EPOCH_E_SHAPE;
+  if (d->atlas_m < 0 || d->atlas_B < 0 || d->atlas_c < 1) return EPOCH_E_SHAPE;
+  if (d->alpha_num < 0 || d->alpha_den < 1 || d->q_num < 0 || d->q_den < 1 ||
+      d->q_num > d->q_den || d->beta_num < 0 || d->beta_den < 1)
+    return EPOCH_E_SHAPE;
+  const int kext = std::min(d->top_k + d->atlas_m, d->n_experts);
+  if (kext > kMaxKext) return EPOCH_E_SHAPE;
+  if (d->act_dtype == EPOCH_DTYPE_BF16) {
+    if (d->hidden % 64 || d->inter % 64) return EPOCH_E_SHAPE;
+    if (d->n_shared && d->shared_inter % 64) return EPOCH_E_SHAPE;
+  } else {
+    if (d->hidden % 16) return EPOCH_E_SHAPE;
+  }
+  return EPOCH_OK;
+}
+
+Shape make_shape(const epoch_desc* d) {
+  Shape s{};
+  s.M = d->batch * d->block;
+  s.H = d->hidden;
+  s.E = d->n_experts;
+  s.K = d->top_k;
+  s.Kext = std::min(d->top_k + d->atlas_m, d->n_experts);
+  s.I = d->inter;
+  s.n_shared = d->n_shared;
+  s.Is = d->n_shared ? d->shared_inter : 0;
+  s.R = d->staleness_R;
+  s.gate_sigmoid = d->gate == EPOCH_GATE_SIGMOID;
+  s.norm_topk = d->norm_topk != 0;
+  s.bf16 = d->act_dtype == EPOCH_DTYPE_BF16;
+  s.n_chunks = (s.M + kChunk - 1) / kChunk;
+  // split the router's k range until the grid has about 1024 waves (256 CUs x 4)
+  const int tiles = ((s.M + 31) / 32) * ((s.E + 31) / 32);
+  int splits = std::max(1, std::min(1024 / std::max(tiles, 1), s.H / 64));
+  const int kchunk = ((s.H + splits - 1) / splits + 15) / 16 * 16;
+  s.splits = (s.H + kchunk - 1) / kchunk;
+  const long long P_max = (long long)s.M * s.K;
+  s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;
+  s.T_dense = (s.M + kTileRows - 1) / kTileRows;
+  s.B = d->atlas_B;
+  s.c = d->atlas_c;
+  s.an = d->alpha_num;
+  s.ad = d->alpha_den;
+  s.qn = d->q_num;
+  s.qd = d->q_den;
+  s.bn = d->beta_num;
+  s.bd = d->beta_den;
+  return s;
+}
+
+Layout carve(const epoch_desc* d, const Shape& s, void* base) {
+  Layout lay;
+  Carver c{static_cast<char*>(base)};
+  const size_t act = s.bf16 ? 2 : 4;
+  const size_t M = s.M, H = s.H, E = s.E, K = s.K, Kext = s.Kext;
+  for (int l = 0; l < d->n_layers; ++l) {
+    LayerState L{};
+    L.cache = c.take_bytes(M * H * act);
+    L.valid = c.take<uint8_t>(M);
+    L.last_fresh = c.take<int32_t>(M);
+    L.prev_D = c.take<uint8_t>(M);
+    L.inS = c.take<uint8_t>(E);
+    L.slot_of = c.take<int32_t>(E);
+    L.S_list = c.take<int32_t>(E);
+    L.S_size = c.take<int32_t>(1);
+    L.S_valid = c.take<int32_t>(1);
+    L.counters = c.take<int64_t>(EPOCH_NUM_COUNTERS);
+    L.fresh = c.take<uint8_t>(M);
+    L.Dcur = c.take<uint8_t>(M);
+    lay.layers.push_back(L);
+  }
+  const size_t P_max = M * K;
+  Scratch& W = lay.scratch;
+  W.Gpart = c.take<double>((size_t)s.splits * M * E);
+  W.G = c.take<float>(M * E);
+  W.ids = c.take<int32_t>(M * Kext);
+  W.scores = c.take<float>(M * Kext);
+  W.q = c.take<int32_t>(M * Kext);
+  W.w = c.take<float>(M * K);
+  W.flags = c.take<int32_t>(FLAG_WORDS);
+  W.chunk_cnt = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.chunk_base = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.chunk_fresh = c.take<int32_t>(s.n_chunks);
+  W.chunk_foff = c.take<int32_t>(s.n_chunks);
+  W.offs = c.take<int32_t>(E + 1);
+  W.wl_pos = c.take<int32_t>(P_max);
+  W.wl_k = c.take<int32_t>(P_max);
+  W.wl_w = c.take<float>(P_max);
+  W.inv = c.take<int32_t>(M * K);
+  W.fresh_list = c.take<int32_t>(M);
+  W.tile_slot = c.take<int32_t>(s.T_max);
+  W.tile_row0 = c.take<int32_t>(s.T_max);
+  W.Crow = c.take<int32_t>(M);
+  W.Rrow = c.take<int32_t>(M);
+  W.h = c.take_bytes(P_max * s.I * act);
+  W.y_pair = c.take_bytes(P_max * H * act);
+  W.hs = c.take_bytes(M * std::max(s.Is, 1) * act);
+  W.S = c.take_bytes(M * H * act);
+  lay.bytes = (c.off + kAlign - 1) / kAlign * kAlign;
+  return lay;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct TimedPair {
+  int group;
+  hipEvent_t a, b;
+};
+
+struct epoch_plan {
+  epoch_desc d;
+  Shape s;
+  std::vector<epoch_layer_weights> w;
+  Layout lay;
+  std::vector<int32_t> iter;
+  std::vector<uint8_t> pending;
+  int last_layer = -1;
+  bool timing = false;
+  std::vector<TimedPair> pairs;
+  std::vector<hipEvent_t> free_events;
+  double ms[EPOCH_TIMING_GROUPS] = {};
+  int64_t launches[EPOCH_TIMING_GROUPS] = {};
+
+  hipEvent_t event() {
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+// Records an event pair around one kernel group when timing is on.
+struct GroupTimer {
+  epoch_plan* p;
+  hipStream_t st;
+  int group;
+  hipEvent_t a = nullptr;
+  GroupTimer(epoch_plan* p_, hipStream_t st_, int g) : p(p_), st(st_), group(g) {
+    if (p->timing && (a = p->event())) (void)hipEventRecord(a, st);
+  }
+  void done() {
+    if (!a) return;
+    hipEvent_t b = p->event();
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    p->pairs.push_back({group, a, b});
+    a = nullptr;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t epoch_plan_workspace_bytes(const epoch_desc* d, size_t* out_bytes) {
+  if (!out_bytes) return EPOCH_E_NULL;
+  const int32_t rc = check_desc(d);
+  if (rc) return rc;
+  const Shape s = make_shape(d);
+  *out_bytes = carve(d, s, nullptr).bytes;
+  return EPOCH_OK;
+}
+
+int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* weights,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               epoch_plan** out_plan) {
+  if (!out_plan || !weights || !workspace) return EPOCH_E_NULL;
+  *out_plan = nullptr;
+  int32_t rc = check_desc(d);
+  if (rc) return rc;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return EPOCH_E_WORKSPACE;
+  const Shape s = make_shape(d);
+  for (int l = 0; l < d->n_layers; ++l) {
+    const epoch_layer_weights& w = weights[l];
+    if (!w.router_w || !w.w1 || !w.w3 || !w.w2) return EPOCH_E_NULL;
+    if (d->n_shared && (!w.sw1 || !w.sw3 || !w.sw2)) return EPOCH_E_NULL;
+    if (!aligned16(w.router_w) || !aligned16(w.w1) || !aligned16(w.w3) || !aligned16(w.w2))
+      return EPOCH_E_ALIGN;
+    if (d->n_shared && (!aligned16(w.sw1) || !aligned16(w.sw3) || !aligned16(w.sw2)))
+      return EPOCH_E_ALIGN;
+  }
+  Layout lay = carve(d, s, workspace);
+  if (workspace_bytes < lay.bytes) return EPOCH_E_WORKSPACE;
+  epoch_plan* p = new (std::nothrow) epoch_plan();
+  if (!p) return EPOCH_E_NULL;
+  p->d = *d;
+  p->s = s;
+  p->w.assign(weights, weights + d->n_layers);
+  p->lay = std::move(lay);
+  p->iter.assign(d->n_layers, 0);
+  p->pending.assign(d->n_layers, 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < d->n_layers; ++l) {
+    if (launch_init_layer(s, p->lay.layers[l], st) != hipSuccess) {
+      delete p;
+      return EPOCH_E_HIP;
+    }
+  }
+  *out_plan = p;
+  return EPOCH_OK;
+}
+
+int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
+                                const uint8_t* decoded, const uint8_t* force_fresh, void* y,
+                                void* y_routed, void* stream) {
+  if (!p || !x || !decoded || !y) return EPOCH_E_NULL;
+  if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
+  if (!aligned16(x) || !aligned16(y) || (y_routed && !aligned16(y_routed))) return EPOCH_E_ALIGN;
+  const Shape& s = p->s;
+  const LayerState& L = p->lay.layers[layer];
+  const Scratch& W = p->lay.scratch;
+  const epoch_layer_weights& w = p->w[layer];
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    GroupTimer tm(p, st, 0);
+    e = launch_router(s, x, w.router_w, w.router_b, decoded, L, W, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  {
+    GroupTimer tm(p, st, 1);
+    e = launch_support(s, L, W, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  {
+    GroupTimer tm(p, st, 2);
+    e = launch_worklist(s, p->iter[layer], decoded, force_fresh, L, W, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  {
+    GroupTimer tm(p, st, 3);
+    e = launch_routed_gateup(s, x, w.w1, w.w3, L, W, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  {
+    GroupTimer tm(p, st, 4);
+    e = launch_routed_down(s, w.w2, L, W, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  if (s.n_shared) {
+    GroupTimer tm(p, st, 5);
+    e = launch_shared(s, x, w.sw1, w.sw3, w.sw2, W, st);
+    tm.done();
+    if (e != hipSuccess) return EPOCH_E_HIP;
+  }
+  {
+    GroupTimer tm(p, st, 6);
+    e = launch_combine(s, L, W, y, y_routed, st);
+    tm.done();
+  }
+  if (e != hipSuccess) return EPOCH_E_HIP;
+  p->pending[layer] = 1;
+  p->last_layer = layer;
+  return EPOCH_OK;
+}
+
+int32_t epoch_cache_update(epoch_plan* p, int32_t layer, void* stream) {
+  if (!p) return EPOCH_E_NULL;
+  if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
+  if (!p->pending[layer]) return EPOCH_E_STATE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_commit(p->s, p->iter[layer], p->lay.layers[layer], p->lay.scratch, st) != hipSuccess)
+    return EPOCH_E_HIP;
+  p->pending[layer] = 0;
+  p->iter[layer] += 1;
+  return EPOCH_OK;
+}
+
+int32_t epoch_plan_inspect(const epoch_plan* p, int32_t layer, epoch_inspect* out) {
+  if (!p || !out) return EPOCH_E_NULL;
+  if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
+  const Scratch& W = p->lay.scratch;
+  const LayerState& L = p->lay.layers[layer];
+  std::memset(out, 0, sizeof(*out));
+  out->logits = W.G;
+  out->ids = W.ids;
+  out->scores = W.scores;
+  out->atlas_q = W.q;
+  out->weights = W.w;
+  out->fresh = L.fresh;
+  out->fresh_list = W.fresh_list;
+  out->n_fresh = W.flags + FLAG_NFRESH;
+  out->n_pairs = W.flags + FLAG_NPAIRS;
+  out->wl_pos = W.wl_pos;
+  out->wl_k = W.wl_k;
+  out->wl_w = W.wl_w;
+  out->offs = W.offs;
+  out->inv = W.inv;
+  out->in_support = L.inS;
+  out->slot_of = L.slot_of;
+  out->support = L.S_list;
+  out->support_size = L.S_size;
+  out->cache = L.cache;
+  out->valid = L.valid;
+  out->last_fresh = L.last_fresh;
+  out->prev_decoded = L.prev_D;
+  out->counters = L.counters;
+  out->k_ext = p->s.Kext;
+  out->iteration = p->iter[layer];
+  out->last_forward_layer = p->last_layer;
+  return EPOCH_OK;
+}
+
+int32_t epoch_block_plan_destroy(epoch_plan* p) {
+  if (!p) return EPOCH_OK;
+  for (auto& tp : p->pairs) {
+    (void)hipEventDestroy(tp.a);
+    (void)hipEventDestroy(tp.b);
+  }
+  for (auto ev : p->free_events) (void)hipEventDestroy(ev);
+  delete p;
+  return EPOCH_OK;
+}
+
+const char* epoch_status_string(int32_t status) {
+  switch (status) {
+    case EPOCH_OK: return "ok";
+    case EPOCH_E_NULL: return "a required pointer is NULL";
+    case EPOCH_E_SHAPE: return "descriptor value out of the supported range";
+    case EPOCH_E_DTYPE: return "unknown dtype or gate";
+    case EPOCH_E_WORKSPACE: return "workspace too small or misaligned";
+    case EPOCH_E_LAYER: return "layer index out of range";
+    case EPOCH_E_STATE: return "commit without a preceding forward of that layer";
+    case EPOCH_E_HIP: return "a kernel launch failed";
+    case EPOCH_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t epoch_plan_set_timing(epoch_plan* p, int32_t enabled) {
+  if (!p) return EPOCH_E_NULL;
+  p->timing = enabled != 0;
+  for (int g = 0; g < EPOCH_TIMING_GROUPS; ++g) {
+    p->ms[g] = 0.0;
+    p->launches[g] = 0;
+  }
+  return EPOCH_OK;
+}
+
+int32_t epoch_plan_timing(epoch_plan* p, float* ms, int64_t* launches, int32_t n) {
+  if (!p) return EPOCH_E_NULL;
+  for (auto& tp : p->pairs) {
+    if (hipEventSynchronize(tp.b) != hipSuccess) return EPOCH_E_HIP;
+    float dt = 0.f;
+    if (hipEventElapsedTime(&dt, tp.a, tp.b) != hipSuccess) return EPOCH_E_HIP;
+    p->ms[tp.group] += dt;
+    p->launches[tp.group] += 1;
+    p->free_events.push_back(tp.a);
+    p->free_events.push_back(tp.b);
+  }
+  p->pairs.clear();
+  for (int g = 0; g < std::min<int>(n, EPOCH_TIMING_GROUPS); ++g) {
+    if (ms) ms[g] = (float)p->ms[g];
+    if (launches) launches[g] = p->launches[g];
+  }
+  return EPOCH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP translation units of libepoch (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/epoch.h"
+
+namespace epoch {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;        // positions per compaction chunk (one wave)
+constexpr int kMaxKext = 32;      // candidates per position the wave top-k keeps
+constexpr int kMaxExperts = 1024;
+constexpr int kTileRows = 32;     // rows per grouped-GEMM tile
+constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
+constexpr int kDownCols = 64;     // output columns per down workgroup
+
+// per-forward flag words (int32) in the scratch area
+enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
+       FLAG_REBUILT = 5, FLAG_WORDS = 16 };
+
+// Device-side view of one layer's persistent state.
+struct LayerState {
+  void* cache;          // [M x H] act
+  uint8_t* valid;       // [M]
+  int32_t* last_fresh;  // [M]
+  uint8_t* prev_D;      // [M]
+  uint8_t* inS;         // [E]
+  int32_t* slot_of;     // [E]
+  int32_t* S_list;      // [E]
+  int32_t* S_size;      // [1]
+  int32_t* S_valid;     // [1]
+  int64_t* counters;    // [EPOCH_NUM_COUNTERS]
+  uint8_t* fresh;       // [M] fresh flags of the layer's latest forward
+  uint8_t* Dcur;        // [M] D_i seen by the layer's latest forward
+};
+
+// Device-side view of the per-forward scratch.
+struct Scratch {
+  double* Gpart;        // [splits x M x E]
+  float* G;             // [M x E]
+  int32_t* ids;         // [M x Kext]
+  float* scores;        // [M x Kext]
+  int32_t* q;           // [M x Kext]
+  float* w;             // [M x K]
+  int32_t* flags;       // [FLAG_WORDS]
+  int32_t* chunk_cnt;   // [n_chunks x E]
+  int32_t* chunk_base;  // [n_chunks x E]
+  int32_t* chunk_fresh; // [n_chunks]
+  int32_t* chunk_foff;  // [n_chunks]
+  int32_t* offs;        // [E + 1]
+  int32_t* wl_pos;      // [P_max]
+  int32_t* wl_k;        // [P_max]
+  float* wl_w;          // [P_max]
+  int32_t* inv;         // [M x K]
+  int32_t* fresh_list;  // [M]
+  int32_t* tile_slot;   // [T_max]
+  int32_t* tile_row0;   // [T_max]
+  int32_t* Crow;        // [M] support-build coverage
+  int32_t* Rrow;        // [M]
+  void* h;              // [P_max x I] act
+  void* y_pair;         // [P_max x H] act
+  void* hs;             // [M x Is] act
+  void* S;              // [M x H] act (shared expert output)
+};
+
+struct Shape {
+  int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
+  int n_chunks, splits, T_max, T_dense;
+  int B, c, an, ad, qn, qd, bn, bd;
+};
+
+// launchers (stream-ordered, no host sync); each returns hipGetLastError()
+hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st);
+hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
+                         const uint8_t* D, const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_support(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_worklist(const Shape& s, int iter, const uint8_t* D, const uint8_t* force,
+                           const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
+                                const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
+                              const Scratch& W, hipStream_t st);
+hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const void* sw3,
+                         const void* sw2, const Scratch& W, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const LayerState& L, const Scratch& W, void* y,
+                          void* y_routed, hipStream_t st);
+hipError_t launch_commit(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                         hipStream_t st);
+
+}  // namespace epoch

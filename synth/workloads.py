@@ -312,3 +312,16 @@ def describe_recipe() -> str:
     for i, w in WORKLOADS.items():
         lines.append(f"{i}: {w.name} M={w.M} iters={w.iters} R={w.staleness_R} layers={w.n_layers}")
     return "\n".join(lines)
+
+
+def desc_fields(w: Workload, **overrides) -> dict:
+    """The C-ABI descriptor fields (include/epoch.h, epoch_desc) of a workload."""
+    f = dict(n_layers=w.n_layers, hidden=w.hidden, n_experts=w.n_experts, top_k=w.top_k,
+             inter=w.inter, n_shared=w.n_shared, shared_inter=w.shared_inter if w.n_shared else 0,
+             batch=w.batch, block=w.block, gate=1 if w.gate == "sigmoid" else 0,
+             norm_topk=int(w.norm_topk), act_dtype=1 if w.act == "bf16" else 0,
+             staleness_R=w.staleness_R, atlas_m=w.m_ext, atlas_B=w.B, atlas_c=w.c,
+             alpha_num=w.alpha[0], alpha_den=w.alpha[1], q_num=w.q[0], q_den=w.q[1],
+             beta_num=w.beta[0], beta_den=w.beta[1], flags=0)
+    f.update(overrides)
+    return f
