@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the liveness-sparse routed-expert MoE layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one block of synthetic input:
+block-plan build (cold path), then for every refinement iteration and layer the
+forward (router + top-k, support check / rebuild, fresh set, worklist, grouped
+SwiGLU experts, shared expert, combine / stale merge / dense restore) and the
+cache commit.  Inputs (weights, every iteration's hidden states and masks) are
+resident in HBM before the timed region starts.
+
+Prints one JSON line: fresh token-expert pairs/s over the timed steps, the
+per-layer-iteration time, the roofline of the dominant kernel (measured live with
+HIP events on the stream the kernels run on) and the CPU oracle timed on a
+bounded sample of the same workload as a baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--layers", type=int, default=0, help="layers to run (0 = all of the workload)")
+    ap.add_argument("--fraction", type=float, default=None, help="forced fresh fraction (workload 5)")
+    ap.add_argument("--R", type=int, default=None, help="staleness bound override")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB elementwise copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 29  # 2^29 bf16 = 1 GiB read + 1 GiB written
+    a = torch.randn(n, device="cuda", dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3}))
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("experts.hip", "epoch_internal.h", "device_common.h"):
+        with open(os.path.join(ROOT, "block_diffusion_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str, kernel: str):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it matches the source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every expert is resident on one MI355X; no collectives). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from block_diffusion_sparse_amd import binding as B
+    B.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    over = {}
+    if args.fraction is not None:
+        over["forced_fraction"] = args.fraction
+    if args.R is not None:
+        over["staleness_R"] = args.R
+    w = synth.workload(args.workload, **over)
+    n_layers = w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)
+    M, H, I, E, K = w.M, w.hidden, w.inter, w.n_experts, w.top_k
+    iters = w.iters
+
+    # ---------------------------------------------------------------- inputs resident in HBM
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    D = synth.decoded_masks(w)
+    F = synth.force_masks(w)
+    host_weights = []
+    Wdev, Xdev = [], []
+    for l in range(n_layers):
+        Wl = synth.layer_weights(w, l)
+        if l == 0:
+            host_weights.append(Wl)
+        Wdev.append({k: dev(v) for k, v in Wl.items()})
+        Xdev.append(dev(synth.hidden_states(w, l, D)))
+        if l > 0:
+            del Wl
+    Ddev = dev(D)
+    Fdev = dev(F) if F is not None else None
+    Y = torch.empty((M, H), dtype=Xdev[0].dtype, device="cuda")
+
+    desc = B.make_desc(**synth.desc_fields(w, n_layers=n_layers))
+    nbytes = B.epoch_plan_workspace_bytes(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lw = [B.layer_weights(d["router_w"], d.get("router_b"), d["w1"], d["w3"], d["w2"],
+                          d.get("sw1"), d.get("sw3"), d.get("sw2")) for d in Wdev]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def one_block(timing_groups: int):
+        plan = B.epoch_block_plan_build(desc, lw, ws, nbytes, sp)
+        if timing_groups:
+            B.epoch_plan_set_timing(plan, timing_groups)
+        for it in range(iters):
+            for l in range(n_layers):
+                B.epoch_moe_fresh_forward(plan, l, Xdev[l][it], Ddev[it],
+                                          None if Fdev is None else Fdev[it], Y, None, sp)
+                B.epoch_cache_update(plan, l, sp)
+        return plan
+
+    def block_counters(plan):
+        tot = np.zeros(B.EPOCH_NUM_COUNTERS, dtype=np.int64)
+        for l in range(n_layers):
+            ins = B.epoch_plan_inspect(plan, l)
+            off = ins.counters - ws.data_ptr()
+            tot += ws[off:off + 8 * B.EPOCH_NUM_COUNTERS].view(torch.int64).cpu().numpy()
+        return dict(zip(B.COUNTERS, tot.tolist()))
+
+    def collect(plans):
+        ms_ = {g: 0.0 for g in B.TIMING_GROUPS}
+        n_ = {g: 0 for g in B.TIMING_GROUPS}
+        for p in plans:
+            for g, (ms, n) in B.epoch_plan_timing(p).items():
+                ms_[g] += ms
+                n_[g] += n
+            B.epoch_block_plan_destroy(p)
+        return ms_, n_
+
+    # ---------------------------------------------------------------- warmup
+    for _ in range(args.warmup):
+        B.epoch_block_plan_destroy(one_block(0))
+    torch.cuda.synchronize()
+    ref_plan = one_block(0)
+    torch.cuda.synchronize()
+    per_block = block_counters(ref_plan)
+    B.epoch_block_plan_destroy(ref_plan)
+    # per-kernel breakdown (every group timed; outside the timed region).  Its events go back
+    # to the library's pool, so the timed region below creates none.
+    brk_ms, brk_n = collect([one_block(-1) for _ in range(args.steps)])
+
+    # ---------------------------------------------------------------- timed region
+    gemm_groups = (1 << B.TIMING_GROUPS.index("routed_gateup")) | \
+                  (1 << B.TIMING_GROUPS.index("routed_down"))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    plans = [one_block(gemm_groups) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    last = block_counters(plans[-1])
+    assert last["pairs"] == per_block["pairs"], "blocks are not deterministic"
+    group_ms, group_n = collect(plans)
+
+    pairs_per_block = per_block["pairs"]
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = pairs_per_block * args.steps / elapsed
+    layer_iters = iters * n_layers
+    us_per_layer_iter = 1e3 * ms_per_step / layer_iters
+
+    # ---------------------------------------------------------------- roofline of the dominant kernel
+    touched = per_block["touched"]          # sum over forwards of experts with fresh pairs
+    P = pairs_per_block
+    act = 2 if w.act == "bf16" else 4
+    algo = {
+        # W1 + W3 of every touched expert, gathered x rows, h written
+        "routed_gateup": touched * 2 * I * H * act + P * H * act + P * I * act,
+        # W2 of every touched expert, h read, y_pair written
+        "routed_down": touched * H * I * act + P * I * act + P * H * act,
+    }
+    flops = {"routed_gateup": 4.0 * P * H * I, "routed_down": 2.0 * P * H * I}
+    dom = max(("routed_gateup", "routed_down"), key=lambda g: group_ms[g])
+    launches = max(group_n[dom], 1)
+    avg_ms = group_ms[dom] / launches
+    steps = args.steps
+    bytes_per_launch = algo[dom] * steps / launches
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name, dom)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                "avg_launch_us": round(avg_ms * 1e3, 2),
+                "mfma_tflops": round(flops[dom] * steps / launches / (avg_ms * 1e-3) / 1e12, 2),
+                "mfma_frac_of_bf16_peak": round(flops[dom] * steps / launches / (avg_ms * 1e-3)
+                                                / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
+    kernels_us = {g: round(1e3 * brk_ms[g] / max(brk_n[g], 1), 2) for g in B.TIMING_GROUPS
+                  if brk_n[g]}
+    kernels_share = {g: round(brk_ms[g] / max(sum(brk_ms.values()), 1e-9), 4)
+                     for g in B.TIMING_GROUPS if brk_n[g]}
+
+    # ---------------------------------------------------------------- CPU baseline (the oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Wl = host_weights[0]
+        X0 = synth.hidden_states(w, 0, D)
+        L = oracle.OracleLayer(w, Wl)
+        t_start = time.perf_counter()
+        done_pairs, done_iters = 0, 0
+        while done_iters < iters and time.perf_counter() - t_start < args.cpu_seconds:
+            out = L.forward(X0[done_iters], D[done_iters], None if F is None else F[done_iters])
+            L.commit()
+            done_pairs += int(out["fresh"].sum()) * K
+            done_iters += 1
+        t_cpu = time.perf_counter() - t_start
+        cpu = {"value": round(done_pairs / t_cpu, 1), "unit": "pairs/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"layer 0, iterations 0..{done_iters - 1} of one block "
+                         f"({done_pairs} fresh pairs, {t_cpu:.1f} s; every position through "
+                         f"router, top-k, support, fresh set, worklist; experts for all fresh "
+                         f"rows; double precision)"}
+
+    rec = {
+        "metric": "fresh token-expert pairs/s & MoE-layer µs/iteration; MFMA % peak; HBM GB/s",
+        "value": round(value, 1),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": n_layers, "iterations_per_block": iters,
+                   "positions": M, "hidden": H, "experts": E, "top_k": K, "inter": I,
+                   "shared_expert": bool(w.n_shared), "staleness_R": w.staleness_R,
+                   "forced_fraction": w.forced_fraction, "step": "one block"},
+        "us_per_layer_iteration": round(us_per_layer_iter, 2),
+        "fresh_pairs_per_block": pairs_per_block,
+        "fresh_fraction": round(per_block["fresh_rows"] / (M * layer_iters), 4),
+        "support_paths": {"cold": per_block["cold"], "hot_update": per_block["hot_update"],
+                          "hot_skip": per_block["hot_skip"]},
+        "kernel_us_per_launch": kernels_us,
+        "kernel_time_share": kernels_share,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,8 +161,9 @@ def epoch_status_string(status: int) -> str:
     return load().epoch_status_string(status).decode()
 
 
-def epoch_plan_set_timing(plan: int, enabled: bool):
-    _check("epoch_plan_set_timing", load().epoch_plan_set_timing(plan, int(bool(enabled))))
+def epoch_plan_set_timing(plan: int, groups: int = -1):
+    """groups: bitmask of TIMING_GROUPS indices (-1 = all, 0 = off)."""
+    _check("epoch_plan_set_timing", load().epoch_plan_set_timing(plan, int(groups)))
 
 
 def epoch_plan_timing(plan: int):

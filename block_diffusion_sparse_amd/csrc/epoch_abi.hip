@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -158,6 +159,29 @@ struct TimedPair {
   hipEvent_t a, b;
 };
 
+// Process-wide pool of timing events, so that a timed region reuses events created earlier.
+std::mutex g_event_mu;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t pool_event() {
+  {
+    std::lock_guard<std::mutex> lk(g_event_mu);
+    if (!g_free_events.empty()) {
+      hipEvent_t e = g_free_events.back();
+      g_free_events.pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void pool_release(hipEvent_t e) {
+  std::lock_guard<std::mutex> lk(g_event_mu);
+  g_free_events.push_back(e);
+}
+
 struct epoch_plan {
   epoch_desc d;
   Shape s;
@@ -166,22 +190,10 @@ struct epoch_plan {
   std::vector<int32_t> iter;
   std::vector<uint8_t> pending;
   int last_layer = -1;
-  bool timing = false;
+  uint32_t timing_mask = 0;
   std::vector<TimedPair> pairs;
-  std::vector<hipEvent_t> free_events;
   double ms[EPOCH_TIMING_GROUPS] = {};
   int64_t launches[EPOCH_TIMING_GROUPS] = {};
-
-  hipEvent_t event() {
-    if (!free_events.empty()) {
-      hipEvent_t e = free_events.back();
-      free_events.pop_back();
-      return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-  }
 };
 
 namespace {
@@ -193,12 +205,15 @@ struct GroupTimer {
   int group;
   hipEvent_t a = nullptr;
   GroupTimer(epoch_plan* p_, hipStream_t st_, int g) : p(p_), st(st_), group(g) {
-    if (p->timing && (a = p->event())) (void)hipEventRecord(a, st);
+    if (((p->timing_mask >> g) & 1u) && (a = pool_event())) (void)hipEventRecord(a, st);
   }
   void done() {
     if (!a) return;
-    hipEvent_t b = p->event();
-    if (!b) return;
+    hipEvent_t b = pool_event();
+    if (!b) {
+      pool_release(a);
+      return;
+    }
     (void)hipEventRecord(b, st);
     p->pairs.push_back({group, a, b});
     a = nullptr;
@@ -366,10 +381,10 @@ int32_t epoch_plan_inspect(const epoch_plan* p, int32_t layer, epoch_inspect* ou
 int32_t epoch_block_plan_destroy(epoch_plan* p) {
   if (!p) return EPOCH_OK;
   for (auto& tp : p->pairs) {
-    (void)hipEventDestroy(tp.a);
-    (void)hipEventDestroy(tp.b);
+    (void)hipEventSynchronize(tp.b);
+    pool_release(tp.a);
+    pool_release(tp.b);
   }
-  for (auto ev : p->free_events) (void)hipEventDestroy(ev);
   delete p;
   return EPOCH_OK;
 }
@@ -391,7 +406,7 @@ const char* epoch_status_string(int32_t status) {
 
 int32_t epoch_plan_set_timing(epoch_plan* p, int32_t enabled) {
   if (!p) return EPOCH_E_NULL;
-  p->timing = enabled != 0;
+  p->timing_mask = static_cast<uint32_t>(enabled) & ((1u << EPOCH_TIMING_GROUPS) - 1u);
   for (int g = 0; g < EPOCH_TIMING_GROUPS; ++g) {
     p->ms[g] = 0.0;
     p->launches[g] = 0;
@@ -407,8 +422,8 @@ int32_t epoch_plan_timing(epoch_plan* p, float* ms, int64_t* launches, int32_t n
     if (hipEventElapsedTime(&dt, tp.a, tp.b) != hipSuccess) return EPOCH_E_HIP;
     p->ms[tp.group] += dt;
     p->launches[tp.group] += 1;
-    p->free_events.push_back(tp.a);
-    p->free_events.push_back(tp.b);
+    pool_release(tp.a);
+    pool_release(tp.b);
   }
   p->pairs.clear();
   for (int g = 0; g < std::min<int>(n, EPOCH_TIMING_GROUPS); ++g) {

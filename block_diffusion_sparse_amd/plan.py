@@ -87,8 +87,8 @@ class EpochPlan:
         c = self.inspect(layer)["counters"].cpu().tolist()
         return dict(zip(B.COUNTERS, c))
 
-    def set_timing(self, enabled: bool):
-        B.epoch_plan_set_timing(self.handle, enabled)
+    def set_timing(self, groups: int = -1):
+        B.epoch_plan_set_timing(self.handle, groups)
 
     def timing(self) -> dict:
         return B.epoch_plan_timing(self.handle)

@@ -209,15 +209,17 @@ int32_t epoch_block_plan_destroy(epoch_plan* plan);
 const char* epoch_status_string(int32_t status);
 
 /*
- * Kernel timing for measurement: when enabled, the forward records HIP events on its
- * stream around each kernel group and accumulates their durations (read after a
- * stream synchronisation).  groups: 0 router, 1 support, 2 worklist, 3 routed gate/up,
- * 4 routed down, 5 shared expert, 6 combine.  epoch_plan_timing returns the summed
- * milliseconds and launch counts per group for up to n groups and resets nothing;
- * enabling again clears the sums.
+ * Kernel timing for measurement.  `groups` is a bitmask of kernel groups (bit g = group g;
+ * -1 = all): 0 router + top-k, 1 support, 2 fresh set + worklist, 3 routed gate/up,
+ * 4 routed down, 5 shared expert, 6 combine.  While set, each forward records a pair of HIP
+ * events on its stream around every selected group (events come from a process-wide pool,
+ * so a measured region reuses events created earlier).  epoch_plan_timing synchronises the
+ * recorded events, adds their durations (ms) and counts per group into the plan's sums,
+ * writes the sums for up to n groups and returns the events to the pool.  Setting the mask
+ * clears the sums.  0 = off (the default).
  */
 enum { EPOCH_TIMING_GROUPS = 7 };
-int32_t epoch_plan_set_timing(epoch_plan* plan, int32_t enabled);
+int32_t epoch_plan_set_timing(epoch_plan* plan, int32_t groups);
 int32_t epoch_plan_timing(epoch_plan* plan, float* ms, int64_t* launches, int32_t n);
 
 #ifdef __cplusplus
