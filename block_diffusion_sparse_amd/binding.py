@@ -21,7 +21,7 @@ EPOCH_TIMING_GROUPS = 7
 COUNTERS = ["cold", "hot_update", "hot_skip", "anomaly", "fresh_rows", "pairs", "unmet",
             "forced_rows", "due_rows", "support_size", "u_final", "repair_rounds", "touched",
             "forwards", "commits", "reserved"]
-TIMING_GROUPS = ["router", "support", "worklist", "routed_gateup", "routed_down", "shared",
+TIMING_GROUPS = ["router", "plan", "place", "routed_gateup", "routed_down", "shared",
                  "combine"]
 
 _i32 = ctypes.c_int32

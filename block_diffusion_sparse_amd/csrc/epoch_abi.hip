@@ -55,11 +55,10 @@ int32_t check_desc(const epoch_desc* d) {
     return EPOCH_E_SHAPE;
   const int kext = std::min(d->top_k + d->atlas_m, d->n_experts);
   if (kext > kMaxKext) return EPOCH_E_SHAPE;
+  if (d->hidden % 64) return EPOCH_E_SHAPE;
   if (d->act_dtype == EPOCH_DTYPE_BF16) {
-    if (d->hidden % 64 || d->inter % 64) return EPOCH_E_SHAPE;
+    if (d->inter % 64) return EPOCH_E_SHAPE;
     if (d->n_shared && d->shared_inter % 64) return EPOCH_E_SHAPE;
-  } else {
-    if (d->hidden % 16) return EPOCH_E_SHAPE;
   }
   return EPOCH_OK;
 }
@@ -79,11 +78,16 @@ Shape make_shape(const epoch_desc* d) {
   s.norm_topk = d->norm_topk != 0;
   s.bf16 = d->act_dtype == EPOCH_DTYPE_BF16;
   s.n_chunks = (s.M + kChunk - 1) / kChunk;
-  // split the router's k range until the grid has about 1024 waves (256 CUs x 4)
-  const int tiles = ((s.M + 31) / 32) * ((s.E + 31) / 32);
-  int splits = std::max(1, std::min(1024 / std::max(tiles, 1), s.H / 64));
-  const int kchunk = ((s.H + splits - 1) / splits + 15) / 16 * 16;
-  s.splits = (s.H + kchunk - 1) / kchunk;
+  // router: 32 x 32 tiles when that gives at least 512 workgroups, else 16 x 16; the k range
+  // is split over the waves of a workgroup until about 2048 waves run (H / ksplit stays a
+  // multiple of 64; the LDS reduction stays within 32 KB)
+  const int tiles32 = ((s.M + 31) / 32) * ((s.E + 31) / 32);
+  s.router_bt = tiles32 >= 512 ? 32 : 16;
+  const int tiles = ((s.M + s.router_bt - 1) / s.router_bt) * ((s.E + s.router_bt - 1) / s.router_bt);
+  const int max_split = s.router_bt == 32 ? 4 : 16;
+  s.ksplit = 1;
+  while (s.ksplit < max_split && tiles * s.ksplit < 2048 && s.H % (128 * s.ksplit) == 0)
+    s.ksplit *= 2;
   const long long P_max = (long long)s.M * s.K;
   s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;
   s.T_dense = (s.M + kTileRows - 1) / kTileRows;
@@ -121,18 +125,21 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
   }
   const size_t P_max = M * K;
   Scratch& W = lay.scratch;
-  W.Gpart = c.take<double>((size_t)s.splits * M * E);
   W.G = c.take<float>(M * E);
   W.ids = c.take<int32_t>(M * Kext);
   W.scores = c.take<float>(M * Kext);
   W.q = c.take<int32_t>(M * Kext);
   W.w = c.take<float>(M * K);
   W.flags = c.take<int32_t>(FLAG_WORDS);
-  W.chunk_cnt = c.take<int32_t>((size_t)s.n_chunks * E);
-  W.chunk_base = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.fpre = c.take<uint8_t>(M);
+  // cnt_f, cnt_a, chunk_fresh: carved back to back, cleared as one range every forward
+  W.cnt_f = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.cnt_a = c.take<int32_t>((size_t)s.n_chunks * E);
   W.chunk_fresh = c.take<int32_t>(s.n_chunks);
+  W.chunk_base = c.take<int32_t>((size_t)s.n_chunks * E);
   W.chunk_foff = c.take<int32_t>(s.n_chunks);
   W.offs = c.take<int32_t>(E + 1);
+  W.eoffs = c.take<int32_t>(E + 1);
   W.wl_pos = c.take<int32_t>(P_max);
   W.wl_k = c.take<int32_t>(P_max);
   W.wl_w = c.take<float>(P_max);
@@ -286,19 +293,19 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
   hipError_t e;
   {
     GroupTimer tm(p, st, 0);
-    e = launch_router(s, x, w.router_w, w.router_b, decoded, L, W, st);
+    e = launch_router(s, x, w.router_w, w.router_b, decoded, force_fresh, p->iter[layer], L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 1);
-    e = launch_support(s, L, W, st);
+    e = launch_plan(s, L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 2);
-    e = launch_worklist(s, p->iter[layer], decoded, force_fresh, L, W, st);
+    e = launch_place(s, L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;

@@ -37,18 +37,20 @@ struct LayerState {
 
 // Device-side view of the per-forward scratch.
 struct Scratch {
-  double* Gpart;        // [splits x M x E]
   float* G;             // [M x E]
   int32_t* ids;         // [M x Kext]
   float* scores;        // [M x Kext]
   int32_t* q;           // [M x Kext]
   float* w;             // [M x K]
   int32_t* flags;       // [FLAG_WORDS]
-  int32_t* chunk_cnt;   // [n_chunks x E]
+  uint8_t* fpre;        // [M] fresh test before the anomaly override
+  int32_t* cnt_f;       // [n_chunks x E] routed pairs of fresh positions per chunk and expert
+  int32_t* cnt_a;       // [n_chunks x E] routed pairs of all positions per chunk and expert
   int32_t* chunk_base;  // [n_chunks x E]
   int32_t* chunk_fresh; // [n_chunks]
   int32_t* chunk_foff;  // [n_chunks]
-  int32_t* offs;        // [E + 1]
+  int32_t* offs;        // [E + 1] per support slot
+  int32_t* eoffs;       // [E + 1] per expert
   int32_t* wl_pos;      // [P_max]
   int32_t* wl_k;        // [P_max]
   float* wl_w;          // [P_max]
@@ -66,17 +68,17 @@ struct Scratch {
 
 struct Shape {
   int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
-  int n_chunks, splits, T_max, T_dense;
+  int n_chunks, ksplit, router_bt, T_max, T_dense;
   int B, c, an, ad, qn, qd, bn, bd;
 };
 
 // launchers (stream-ordered, no host sync); each returns hipGetLastError()
 hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st);
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
-                         const uint8_t* D, const LayerState& L, const Scratch& W, hipStream_t st);
-hipError_t launch_support(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
-hipError_t launch_worklist(const Shape& s, int iter, const uint8_t* D, const uint8_t* force,
-                           const LayerState& L, const Scratch& W, hipStream_t st);
+                         const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
+                         const Scratch& W, hipStream_t st);
+hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
                                 const LayerState& L, const Scratch& W, hipStream_t st);
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,

@@ -1,5 +1,6 @@
-// Block-clock and bookkeeping kernels: plan init, Expert Atlas support build, fresh set,
-// expert-grouped worklist compaction and the cache commit (gfx950).
+// Block-clock and bookkeeping kernels: plan init, the per-iteration plan step (Expert Atlas
+// support check / build and the worklist scans), stable worklist placement and the cache
+// commit (gfx950).
 #include "device_common.h"
 #include "epoch_internal.h"
 
@@ -17,6 +18,7 @@ __global__ void k_init_layer(int M, int E, LayerState L) {
     L.valid[i] = 0;
     L.last_fresh[i] = kNeverFresh;
     L.prev_D[i] = 0;
+    L.fresh[i] = 0;
   }
   if (i < E) {
     L.inS[i] = 0;
@@ -36,156 +38,157 @@ hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------- support build
-// Expert Atlas (teardown, Expert Atlas section, steps one and two, coverage goal
-// |U| <= (1 - q) N; "cold / hot-update / hot-skip" for when it runs).  One workgroup.
-// Planner weights are the integers q_{t,j} (units of 2^-16), alpha / q / beta are rationals,
-// so every sum is an exact integer and the result does not depend on the order of the
-// atomics.  Runs when the layer has no support yet (cold) or when the router found a routed
-// expert outside it (hot-update); otherwise counts a hot-skip and exits.
-constexpr int kSupThreads = 1024;
+// ---------------------------------------------------------------------------- plan step
+constexpr int kPlanThreads = 1024;
+
+// Inclusive scan of v[0..n) (n <= kPlanThreads) in LDS by the whole workgroup.
+__device__ __forceinline__ void block_inclusive_scan(int32_t* v, int n) {
+  const int tid = threadIdx.x;
+  for (int off = 1; off < n; off <<= 1) {
+    const int x = (tid < n && tid >= off) ? v[tid - off] : 0;
+    __syncthreads();
+    if (tid < n) v[tid] += x;
+    __syncthreads();
+  }
+}
+
+struct SupportLds {
+  unsigned long long p[kMaxExperts];
+  unsigned long long G[kMaxExperts];
+  int32_t H[kMaxExperts];
+  int32_t scan[kMaxExperts];
+  uint8_t inS[kMaxExperts];
+  uint8_t pick[kMaxExperts];
+  int nU, added;
+};
 
 __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
-                                              const int32_t* __restrict__ q,
-                                              const uint8_t* inS_sh, int M, int K, int Kext,
-                                              int an, int ad, int32_t* __restrict__ Crow,
-                                              int32_t* __restrict__ Rrow, int* nU_sh) {
+                                              const int32_t* __restrict__ q, const uint8_t* inS,
+                                              int M, int K, int Kext, int an, int ad,
+                                              int32_t* __restrict__ Crow,
+                                              int32_t* __restrict__ Rrow, int* nU) {
   int local = 0;
-  for (int t = threadIdx.x; t < M; t += kSupThreads) {
+  for (int t = threadIdx.x; t < M; t += kPlanThreads) {
     const int32_t* it = ids + (size_t)t * Kext;
     const int32_t* qt = q + (size_t)t * Kext;
     int64_t r = 0, c = 0;
     for (int j = 0; j < Kext; ++j) {
       if (j < K) r += qt[j];
-      if (inS_sh[it[j]]) c += qt[j];
+      if (inS[it[j]]) c += qt[j];
     }
     Rrow[t] = (int32_t)r;
     Crow[t] = (int32_t)c;
     local += ((int64_t)ad * c < (int64_t)an * r);
   }
-  if (local) atomicAdd(nU_sh, local);
+  if (local) atomicAdd(nU, local);
 }
 
-__global__ __launch_bounds__(kSupThreads) void k_support_build(
-    int M, int E, int K, int Kext, int B, int c, int an, int ad, int qn, int qd, int bn, int bd,
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ q, int32_t* __restrict__ Crow,
-    int32_t* __restrict__ Rrow, LayerState L, int32_t* __restrict__ flags) {
-  __shared__ unsigned long long p_sh[kMaxExperts];
-  __shared__ unsigned long long G_sh[kMaxExperts];
-  __shared__ int32_t H_sh[kMaxExperts];
-  __shared__ uint8_t inS_sh[kMaxExperts];
-  __shared__ uint8_t pick_sh[kMaxExperts];
-  __shared__ int32_t scan_sh[kMaxExperts];
-  __shared__ int nU_sh, added_sh;
+// Expert Atlas (teardown, Expert Atlas section, steps one and two, coverage goal
+// |U| <= (1 - q) N; "cold / hot-update / hot-skip" for when it runs).  Planner weights are the
+// integers q_{t,j} (units of 2^-16), alpha / q / beta are rationals, so every sum is an exact
+// integer and the result does not depend on the order of the atomics.  Runs when the layer has
+// no support yet (cold) or when the router found a routed expert outside it (hot-update);
+// otherwise counts a hot-skip.  Whole-workgroup function: every thread must call it.
+__device__ void support_phase(const Shape& s, const LayerState& L, const Scratch& W,
+                              SupportLds& sh) {
   const int tid = threadIdx.x;
+  const int M = s.M, E = s.E, K = s.K, Kext = s.Kext;
+  const long long an = s.an, ad = s.ad, qn = s.qn, qd = s.qd, bn = s.bn, bd = s.bd;
+  const int32_t* ids = W.ids;
+  const int32_t* q = W.q;
   const bool valid = *L.S_valid != 0;
-  const bool miss = flags[FLAG_MISS] != 0;
+  const bool miss = W.flags[FLAG_MISS] != 0;
   if (valid && !miss) {
-    if (tid == 0) {
-      L.counters[EPOCH_CNT_HOT_SKIP] += 1;
-      flags[FLAG_REBUILT] = 0;
-    }
+    if (tid == 0) L.counters[EPOCH_CNT_HOT_SKIP] += 1;
     return;
   }
   const long long Q = 65536;
   // (i) popularity p_e = sum_{t,j: I_{t,j} = e} W_{t,j}
-  for (int e = tid; e < E; e += kSupThreads) p_sh[e] = 0;
-  if (tid == 0) nU_sh = 0;
+  for (int e = tid; e < E; e += kPlanThreads) sh.p[e] = 0;
+  if (tid == 0) sh.nU = 0;
   __syncthreads();
-  const int n = M * Kext;
-  for (int i = tid; i < n; i += kSupThreads)
-    atomicAdd(&p_sh[ids[i]], (unsigned long long)(long long)q[i]);
+  for (int i = tid; i < M * Kext; i += kPlanThreads)
+    atomicAdd(&sh.p[ids[i]], (unsigned long long)(long long)q[i]);
   __syncthreads();
   // initial support: experts with p_e > 0 whose rank by (p desc, id asc) is below B
-  for (int e = tid; e < E; e += kSupThreads) {
-    const unsigned long long pe = p_sh[e];
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const unsigned long long pe = sh.p[e];
     int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (p_sh[f] > pe) || (p_sh[f] == pe && f < e);
-    inS_sh[e] = (pe > 0 && rank < B) ? 1 : 0;
+    for (int f = 0; f < E; ++f) rank += (sh.p[f] > pe) || (sh.p[f] == pe && f < e);
+    sh.inS[e] = (pe > 0 && rank < s.B) ? 1 : 0;
   }
   __syncthreads();
-  coverage_pass(ids, q, inS_sh, M, K, Kext, an, ad, Crow, Rrow, &nU_sh);
+  coverage_pass(ids, q, sh.inS, M, K, Kext, s.an, s.ad, W.Crow, W.Rrow, &sh.nU);
   __syncthreads();
   int rounds = 0, unmet = 0;
   // (ii) greedy repair while |U| > (1 - q) M
-  while ((long long)qd * nU_sh > (long long)(qd - qn) * M) {
-    for (int e = tid; e < E; e += kSupThreads) {
-      G_sh[e] = 0;
-      H_sh[e] = 0;
-      pick_sh[e] = 0;
+  while (qd * sh.nU > (qd - qn) * M) {
+    for (int e = tid; e < E; e += kPlanThreads) {
+      sh.G[e] = 0;
+      sh.H[e] = 0;
+      sh.pick[e] = 0;
     }
-    if (tid == 0) added_sh = 0;
+    if (tid == 0) sh.added = 0;
     __syncthreads();
-    for (int t = tid; t < M; t += kSupThreads) {
-      const long long R = Rrow[t], C = Crow[t];
-      if (!((long long)ad * C < (long long)an * R)) continue;
-      const long long gap = (long long)an * R - (long long)ad * C;
+    for (int t = tid; t < M; t += kPlanThreads) {
+      const long long R = W.Rrow[t], C = W.Crow[t];
+      if (!(ad * C < an * R)) continue;
+      const long long gap = an * R - ad * C;
       const int32_t* it = ids + (size_t)t * Kext;
       const int32_t* qt = q + (size_t)t * Kext;
       for (int j = 0; j < Kext; ++j) {
         const int e = it[j];
-        if (inS_sh[e]) continue;
-        const long long v = (long long)ad * qt[j];
-        atomicAdd(&G_sh[e], (unsigned long long)(v < gap ? v : gap));
-        if ((long long)ad * (C + qt[j]) >= (long long)an * R) atomicAdd(&H_sh[e], 1);
+        if (sh.inS[e]) continue;
+        const long long v = ad * qt[j];
+        atomicAdd(&sh.G[e], (unsigned long long)(v < gap ? v : gap));
+        if (ad * (C + qt[j]) >= an * R) atomicAdd(&sh.H[e], 1);
       }
     }
     __syncthreads();
     // score_e = H_e + beta G_e, scaled by alpha_den * Q * beta_den; add the best c positive
-    for (int e = tid; e < E; e += kSupThreads) {
-      if (inS_sh[e]) continue;
-      const long long se = (long long)bd * H_sh[e] * ad * Q + (long long)bn * (long long)G_sh[e];
+    for (int e = tid; e < E; e += kPlanThreads) {
+      if (sh.inS[e]) continue;
+      const long long se = bd * sh.H[e] * ad * Q + bn * (long long)sh.G[e];
       if (se <= 0) continue;
       int rank = 0;
       for (int f = 0; f < E; ++f) {
-        if (inS_sh[f]) continue;
-        const long long sf = (long long)bd * H_sh[f] * ad * Q + (long long)bn * (long long)G_sh[f];
+        if (sh.inS[f]) continue;
+        const long long sf = bd * sh.H[f] * ad * Q + bn * (long long)sh.G[f];
         rank += (sf > se) || (sf == se && f < e);
       }
-      if (rank < c) {
-        pick_sh[e] = 1;
-        atomicAdd(&added_sh, 1);
+      if (rank < s.c) {
+        sh.pick[e] = 1;
+        atomicAdd(&sh.added, 1);
       }
     }
     __syncthreads();
-    if (added_sh == 0) {
+    if (sh.added == 0) {
       unmet = 1;
       break;
     }
-    for (int e = tid; e < E; e += kSupThreads)
-      if (pick_sh[e]) inS_sh[e] = 1;
+    for (int e = tid; e < E; e += kPlanThreads)
+      if (sh.pick[e]) sh.inS[e] = 1;
     ++rounds;
-    if (tid == 0) nU_sh = 0;
+    if (tid == 0) sh.nU = 0;
     __syncthreads();
-    coverage_pass(ids, q, inS_sh, M, K, Kext, an, ad, Crow, Rrow, &nU_sh);
+    coverage_pass(ids, q, sh.inS, M, K, Kext, s.an, s.ad, W.Crow, W.Rrow, &sh.nU);
     __syncthreads();
   }
-  const int nU_final = nU_sh;
+  const int nU_final = sh.nU;
   // (iii) closure: every routed expert of the current iteration gets a slot
-  for (int i = tid; i < M * K; i += kSupThreads) {
+  for (int i = tid; i < M * K; i += kPlanThreads) {
     const int t = i / K, k = i - t * K;
-    inS_sh[ids[(size_t)t * Kext + k]] = 1;
+    sh.inS[ids[(size_t)t * Kext + k]] = 1;
   }
   __syncthreads();
-  // (iv) slots in expert-id order: inclusive scan of membership
-  for (int e = tid; e < kMaxExperts; e += kSupThreads) scan_sh[e] = (e < E) ? inS_sh[e] : 0;
+  // (iv) slots in expert-id order
+  for (int e = tid; e < kMaxExperts; e += kPlanThreads) sh.scan[e] = (e < E) ? sh.inS[e] : 0;
   __syncthreads();
-  for (int off = 1; off < kMaxExperts; off <<= 1) {
-    int v[kMaxExperts / kSupThreads];
-#pragma unroll
-    for (int u = 0; u < kMaxExperts / kSupThreads; ++u) {
-      const int e = tid + u * kSupThreads;
-      v[u] = (e >= off) ? scan_sh[e - off] : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kMaxExperts / kSupThreads; ++u) scan_sh[tid + u * kSupThreads] += v[u];
-    __syncthreads();
-  }
-  for (int e = tid; e < E; e += kSupThreads) {
-    const int incl = scan_sh[e];
-    L.inS[e] = inS_sh[e];
-    if (inS_sh[e]) {
+  block_inclusive_scan(sh.scan, kMaxExperts);
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int incl = sh.scan[e];
+    L.inS[e] = sh.inS[e];
+    if (sh.inS[e]) {
       L.slot_of[e] = incl - 1;
       L.S_list[incl - 1] = e;
     } else {
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kSupThreads) void k_support_build(
     }
   }
   if (tid == 0) {
-    const int size = scan_sh[E - 1];
+    const int size = sh.scan[E - 1];
     *L.S_size = size;
     *L.S_valid = 1;
     L.counters[valid ? EPOCH_CNT_HOT_UPDATE : EPOCH_CNT_COLD] += 1;
@@ -201,145 +204,129 @@ __global__ __launch_bounds__(kSupThreads) void k_support_build(
     L.counters[EPOCH_CNT_SUPPORT_SIZE] = size;
     L.counters[EPOCH_CNT_U_FINAL] = nU_final;
     L.counters[EPOCH_CNT_REPAIR_ROUNDS] += rounds;
-    flags[FLAG_REBUILT] = 1;
-  }
-}
-
-hipError_t launch_support(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
-  hipLaunchKernelGGL(k_support_build, dim3(1), dim3(kSupThreads), 0, st, s.M, s.E, s.K, s.Kext,
-                     s.B, s.c, s.an, s.ad, s.qn, s.qd, s.bn, s.bd, W.ids, W.q, W.Crow, W.Rrow, L,
-                     W.flags);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------- fresh set + counts
-// Fresh set (teardown, LSP: Z_i = D_i ∩ D_{i-1}; F_i = all on a cache miss or when refresh
-// is due, else not Z_i; refresh period: reuse only while the age is at most R - 1; a
-// liveness anomaly falls back to a full fresh pass).  One wave per chunk of 64 positions;
-// also counts the chunk's fresh pairs per support slot for the stable compaction.
-__global__ __launch_bounds__(256) void k_fresh_count(int M, int E, int K, int Kext, int R,
-                                                     int iter, int n_chunks,
-                                                     const uint8_t* __restrict__ D,
-                                                     const uint8_t* __restrict__ force,
-                                                     LayerState L, Scratch W) {
-  __shared__ int32_t hist[4][kMaxExperts];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int chunk = blockIdx.x * 4 + wave;
-  const int t = chunk * kChunk + lane;
-  const bool in = chunk < n_chunks && t < M;
-  for (int e = lane; e < E; e += 64) hist[wave][e] = 0;
-  bool fresh = false, forced = false, due = false;
-  if (in) {
-    const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
-    forced = force ? force[t] != 0 : false;
-    const bool stable = D[t] && L.prev_D[t];
-    const bool miss = !L.valid[t];
-    due = (long long)iter - (long long)L.last_fresh[t] >= (long long)R;
-    fresh = anomaly || forced || miss || !stable || due;
-    L.fresh[t] = fresh ? 1 : 0;
   }
   __syncthreads();
-  if (fresh) {
-    const int32_t* it = W.ids + (size_t)t * Kext;
-    for (int k = 0; k < K; ++k) {
-      const int sl = L.slot_of[it[k]];  // the support's closure gives every routed expert a slot
-      if (sl >= 0) atomicAdd(&hist[wave][sl], 1);
-    }
-  }
-  const uint64_t fb = ballot64(fresh);
-  const uint64_t forced_b = ballot64(in && forced);
-  const uint64_t due_b = ballot64(in && due && L.valid[t]);
-  __syncthreads();
-  if (chunk < n_chunks) {
-    for (int e = lane; e < E; e += 64) W.chunk_cnt[(size_t)chunk * E + e] = hist[wave][e];
-    if (lane == 0) {
-      W.chunk_fresh[chunk] = __popcll(fb);
-      if (forced_b) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_FORCED_ROWS],
-                              (unsigned long long)__popcll(forced_b));
-      if (due_b) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_DUE_ROWS],
-                           (unsigned long long)__popcll(due_b));
-    }
-  }
 }
 
-// Per-slot exclusive offsets of every chunk, slot offsets, chunk offsets of the fresh list and
-// the grouped-GEMM tile table (one tile = up to kTileRows consecutive pairs of one slot).
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void k_scan(int M, int E, int K, int n_chunks,
-                                                       LayerState L, Scratch W) {
+// The plan step of one forward, one workgroup: the support check / build above, then the
+// worklist bookkeeping over the router's per-chunk counts (the fresh-pair counts, or the counts
+// of every position when a liveness anomaly makes the whole layer-iteration fresh):
+//   chunk_base[c][e] = pairs of expert e in chunks before c   (stable order inside an expert)
+//   eoffs[e]         = pairs of experts before e               (expert-major worklist)
+//   offs[s]          = eoffs of the s-th support expert; tile table of up to kTileRows pairs
+//   chunk_foff[c]    = fresh positions in chunks before c      (the fresh list)
+__global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Scratch W) {
+  __shared__ SupportLds sh;
+  __shared__ int32_t part[kPlanThreads];
   __shared__ int32_t tot[kMaxExperts];
-  __shared__ int32_t tiles[kMaxExperts];
-  __shared__ int32_t scan_a[kMaxExperts];
-  __shared__ int32_t scan_b[kMaxExperts];
+  __shared__ int32_t carry;
   const int tid = threadIdx.x;
-  const int nS = *L.S_size;
-  for (int s = tid; s < kMaxExperts; s += kScanThreads) {
-    int run = 0;
-    if (s < nS) {
-      for (int c = 0; c < n_chunks; ++c) {
-        W.chunk_base[(size_t)c * E + s] = run;
-        run += W.chunk_cnt[(size_t)c * E + s];
-      }
+  support_phase(s, L, W, sh);
+  __syncthreads();
+
+  const int E = s.E, nch = s.n_chunks;
+  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
+  const int32_t* cnt = anomaly ? W.cnt_a : W.cnt_f;
+  // per-expert totals and chunk bases; Gp threads per expert, each a contiguous chunk range
+  int Epad = 1;
+  while (Epad < E) Epad <<= 1;
+  const int Gp = kPlanThreads / Epad;
+  const int e = tid / Gp, gi = tid % Gp;
+  const int seg = (nch + Gp - 1) / Gp;
+  const int c0 = min(nch, gi * seg), c1 = min(nch, c0 + seg);
+  int local = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) local += cnt[(size_t)c * E + e];
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (e < E) {
+    int base = 0, total = 0;
+    for (int j = 0; j < Gp; ++j) {
+      const int v = part[e * Gp + j];
+      if (j < gi) base += v;
+      total += v;
     }
-    tot[s] = run;
-    tiles[s] = (run + kTileRows - 1) / kTileRows;
-    scan_a[s] = run;
-    scan_b[s] = tiles[s];
+    if (gi == 0) tot[e] = total;
+    int run = base;
+    for (int c = c0; c < c1; ++c) {
+      W.chunk_base[(size_t)c * E + e] = run;
+      run += cnt[(size_t)c * E + e];
+    }
   }
   __syncthreads();
-  for (int off = 1; off < kMaxExperts; off <<= 1) {
-    int va[kMaxExperts / kScanThreads], vb[kMaxExperts / kScanThreads];
-#pragma unroll
-    for (int u = 0; u < kMaxExperts / kScanThreads; ++u) {
-      const int s = tid + u * kScanThreads;
-      va[u] = s >= off ? scan_a[s - off] : 0;
-      vb[u] = s >= off ? scan_b[s - off] : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kMaxExperts / kScanThreads; ++u) {
-      scan_a[tid + u * kScanThreads] += va[u];
-      scan_b[tid + u * kScanThreads] += vb[u];
-    }
-    __syncthreads();
+  // expert offsets: exclusive scan of the totals
+  for (int i = tid; i < kMaxExperts; i += kPlanThreads) sh.scan[i] = (i < E) ? tot[i] : 0;
+  __syncthreads();
+  block_inclusive_scan(sh.scan, kMaxExperts);
+  const int P = sh.scan[kMaxExperts - 1];
+  for (int i = tid; i < E; i += kPlanThreads) W.eoffs[i] = sh.scan[i] - tot[i];
+  if (tid == 0) W.eoffs[E] = P;
+  // slot offsets and the tile table
+  const int nS = *L.S_size;
+  int my_tiles = 0, my_off = 0;
+  if (tid < nS) {
+    const int ex = L.S_list[tid];
+    my_off = sh.scan[ex] - tot[ex];
+    my_tiles = (tot[ex] + kTileRows - 1) / kTileRows;
+    W.offs[tid] = my_off;
   }
-  // scan_* are inclusive; exclusive = inclusive - own
-  for (int s = tid; s < nS; s += kScanThreads) {
-    const int off = scan_a[s] - tot[s];
-    W.offs[s] = off;
-    const int t0 = scan_b[s] - tiles[s];
-    for (int i = 0; i < tiles[s]; ++i) {
-      W.tile_slot[t0 + i] = s;
-      W.tile_row0[t0 + i] = off + i * kTileRows;
+  if (tid == 0) W.offs[nS] = P;
+  __syncthreads();
+  part[tid] = my_tiles;
+  __syncthreads();
+  block_inclusive_scan(part, kPlanThreads);
+  const int T = part[kPlanThreads - 1];
+  if (tid < nS) {
+    const int t0 = part[tid] - my_tiles;
+    for (int i = 0; i < my_tiles; ++i) {
+      W.tile_slot[t0 + i] = tid;
+      W.tile_row0[t0 + i] = my_off + i * kTileRows;
     }
+  }
+  __syncthreads();
+  // fresh-list offsets of the chunks, in passes of kPlanThreads chunks
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nch; base += kPlanThreads) {
+    const int c = base + tid;
+    int nf = 0;
+    if (c < nch) nf = anomaly ? min(kChunk, s.M - c * kChunk) : W.chunk_fresh[c];
+    part[tid] = nf;
+    __syncthreads();
+    block_inclusive_scan(part, kPlanThreads);
+    if (c < nch) W.chunk_foff[c] = carry + part[tid] - nf;
+    __syncthreads();
+    if (tid == 0) carry += part[kPlanThreads - 1];
+    __syncthreads();
   }
   if (tid == 0) {
-    const int P = nS > 0 ? scan_a[nS - 1] : 0;
-    const int T = nS > 0 ? scan_b[nS - 1] : 0;
-    W.offs[nS] = P;
-    int run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      W.chunk_foff[c] = run;
-      run += W.chunk_fresh[c];
-    }
-    W.flags[FLAG_NFRESH] = run;
+    const int nfresh = carry;
+    W.flags[FLAG_NFRESH] = nfresh;
     W.flags[FLAG_NPAIRS] = P;
     W.flags[FLAG_NTILES] = T;
     int touched = 0;
-    for (int s = 0; s < nS; ++s) touched += tot[s] > 0;
-    L.counters[EPOCH_CNT_FRESH_ROWS] += run;
+    for (int i = 0; i < E; ++i) touched += tot[i] > 0;
+    L.counters[EPOCH_CNT_FRESH_ROWS] += nfresh;
     L.counters[EPOCH_CNT_PAIRS] += P;
     L.counters[EPOCH_CNT_TOUCHED] += touched;
     L.counters[EPOCH_CNT_FORWARDS] += 1;
-    if (W.flags[FLAG_ANOMALY]) L.counters[EPOCH_CNT_ANOMALY] += 1;
+    if (anomaly) L.counters[EPOCH_CNT_ANOMALY] += 1;
   }
 }
 
+hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- placement
 // Stable placement (teardown, FreshLane pack: fresh rows with their owner positions and
-// routing metadata in a contiguous buffer; here grouped by expert for the expert kernel).
-// Pair (t, k) of expert e lands at offs[slot] + base[chunk][slot] + rank, where rank counts
-// the chunk's earlier positions routed to the same expert (a 64-bit mask per slot).
+// routing metadata in a contiguous buffer, here grouped by expert for the expert kernel).
+// Final fresh flag = pre-anomaly test or anomaly.  Pair (t, k) of expert e lands at
+// eoffs[e] + chunk_base[chunk][e] + rank, where rank counts the chunk's earlier fresh
+// positions routed to e (a 64-bit mask per expert per chunk).  One wave per chunk.
 __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, int n_chunks,
                                                LayerState L, Scratch W) {
   __shared__ unsigned long long mask[4][kMaxExperts];
@@ -348,23 +335,20 @@ __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, in
   const int t = chunk * kChunk + lane;
   const bool in = chunk < n_chunks && t < M;
   for (int e = lane; e < E; e += 64) mask[wave][e] = 0ull;
-  const bool fresh = in && L.fresh[t];
+  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
+  const bool fresh = in && (anomaly || W.fpre[t] != 0);
+  if (in) L.fresh[t] = fresh ? 1 : 0;
   __syncthreads();
   const int32_t* it = W.ids + (size_t)(in ? t : 0) * Kext;
-  if (fresh) {
-    for (int k = 0; k < K; ++k) {
-      const int sl = L.slot_of[it[k]];
-      if (sl >= 0) atomicOr(&mask[wave][sl], 1ull << lane);
-    }
-  }
+  if (fresh)
+    for (int k = 0; k < K; ++k) atomicOr(&mask[wave][it[k]], 1ull << lane);
   __syncthreads();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (fresh) {
     for (int k = 0; k < K; ++k) {
-      const int s = L.slot_of[it[k]];
-      if (s < 0) continue;
-      const int rank = __popcll(mask[wave][s] & below);
-      const int p = W.offs[s] + W.chunk_base[(size_t)chunk * E + s] + rank;
+      const int e = it[k];
+      const int rank = __popcll(mask[wave][e] & below);
+      const int p = W.eoffs[e] + W.chunk_base[(size_t)chunk * E + e] + rank;
       W.wl_pos[p] = t;
       W.wl_k[p] = k;
       W.wl_w[p] = W.w[(size_t)t * K + k];
@@ -377,37 +361,31 @@ __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, in
   if (fresh) W.fresh_list[W.chunk_foff[chunk] + __popcll(fb & below)] = t;
 }
 
-hipError_t launch_worklist(const Shape& s, int iter, const uint8_t* D, const uint8_t* force,
-                           const LayerState& L, const Scratch& W, hipStream_t st) {
-  const int wgs = (s.n_chunks + 3) / 4;
-  hipLaunchKernelGGL(k_fresh_count, dim3(wgs), dim3(256), 0, st, s.M, s.E, s.K, s.Kext, s.R, iter,
-                     s.n_chunks, D, force, L, W);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, st, s.M, s.E, s.K, s.n_chunks, L, W);
-  hipLaunchKernelGGL(k_place, dim3(wgs), dim3(256), 0, st, s.M, s.E, s.K, s.Kext, s.n_chunks, L,
-                     W);
+hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
+  hipLaunchKernelGGL(k_place, dim3((s.n_chunks + 3) / 4), dim3(256), 0, st, s.M, s.E, s.K, s.Kext,
+                     s.n_chunks, L, W);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------- commit
 // Cache commit (teardown, LSP state machine: fresh output -> cache update; refresh period:
 // the age restarts at a fresh write; D_i becomes the D_{i-1} of the next iteration).
-__global__ void k_commit(int M, int iter, LayerState L, const uint8_t* __restrict__ fresh,
-                         const uint8_t* __restrict__ Dcopy) {
+__global__ void k_commit(int M, int iter, LayerState L) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < M) {
-    if (fresh[t]) {
+    if (L.fresh[t]) {
       L.valid[t] = 1;
       L.last_fresh[t] = iter;
     }
-    L.prev_D[t] = Dcopy[t];
+    L.prev_D[t] = L.Dcur[t];
   }
   if (t == 0) L.counters[EPOCH_CNT_COMMITS] += 1;
 }
 
 hipError_t launch_commit(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                          hipStream_t st) {
-  hipLaunchKernelGGL(k_commit, dim3((s.M + 255) / 256), dim3(256), 0, st, s.M, iter, L, L.fresh,
-                     L.Dcur);
+  (void)W;
+  hipLaunchKernelGGL(k_commit, dim3((s.M + 255) / 256), dim3(256), 0, st, s.M, iter, L);
   return hipGetLastError();
 }
 

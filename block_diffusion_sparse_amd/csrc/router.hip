@@ -1,4 +1,5 @@
-// Router: gate logits over every position and the per-position top-k (gfx950).
+// Router: gate logits over every position, per-position top-k, and the fresh-set inputs
+// of the worklist (gfx950).
 //
 // Gate logits G = x W_g^T + b are recomputed for all M positions every iteration
 // (Epoch abstract; teardown, Expert Atlas: G in R^{N x E}, top-k over sigma(G) with
@@ -11,190 +12,304 @@
 
 namespace epoch {
 
-// ---------------------------------------------------------------------------- partial logits
-// One wave computes a 32-position x 32-expert tile over one k-range with 2 x 2 blocks of
-// v_mfma_f64_16x16x4.  The contraction index is permuted so that each lane feeds four
-// consecutive k values (one 8- or 16-byte load) to four successive MFMA steps; A and B use
-// the same permutation, so every product pairs x[t,k] with W[e,k].
+// ---------------------------------------------------------------------------- gate logits
+// A workgroup of `ksplit` waves owns a BT x BT tile of (positions x experts); wave w sums the
+// k-range [w H / ksplit, (w + 1) H / ksplit) on v_mfma_f64_16x16x4 (BT / 16 blocks per side),
+// the partial tiles meet in LDS and are added in wave order, then the bias, then one rounding
+// to fp32.  The contraction index is permuted: in each 64-wide k step, lane group g = l / 16
+// owns k in [16 g, 16 g + 16) and feeds them to 16 successive MFMA steps, for the activation
+// and the weight alike, so every product pairs x[t,k] with W[e,k].  Each lane loads its
+// 16 values of each operand as whole 16-byte vectors, one step ahead of the MFMAs.
 template <typename T>
-__device__ __forceinline__ void load4_as_f64(const T* p, bool ok, double out[4]);
-
+struct RouterRaw;
 template <>
-__device__ __forceinline__ void load4_as_f64<uint16_t>(const uint16_t* p, bool ok, double out[4]) {
-  uint2 v = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
-  out[0] = (double)__uint_as_float(v.x << 16);
-  out[1] = (double)__uint_as_float(v.x & 0xffff0000u);
-  out[2] = (double)__uint_as_float(v.y << 16);
-  out[3] = (double)__uint_as_float(v.y & 0xffff0000u);
-}
-
+struct RouterRaw<uint16_t> {
+  u32x4 v[2];  // 16 bf16
+  __device__ __forceinline__ void load(const uint16_t* p, bool ok) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    v[0] = ok ? reinterpret_cast<const u32x4*>(p)[0] : z;
+    v[1] = ok ? reinterpret_cast<const u32x4*>(p)[1] : z;
+  }
+  __device__ __forceinline__ double get(int m) const {
+    const uint32_t w = v[m >> 3][(m >> 1) & 3];
+    return (double)__uint_as_float((m & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
 template <>
-__device__ __forceinline__ void load4_as_f64<float>(const float* p, bool ok, double out[4]) {
-  float4 v = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-  out[0] = v.x;
-  out[1] = v.y;
-  out[2] = v.z;
-  out[3] = v.w;
-}
-
-template <typename T>
-__global__ __launch_bounds__(64) void k_router_partial(const T* __restrict__ x,
-                                                       const float* __restrict__ Wg,
-                                                       double* __restrict__ Gpart, int M, int H,
-                                                       int E, int kchunk,
-                                                       int32_t* __restrict__ flags) {
-  const int lane = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && lane < FLAG_WORDS)
-    flags[lane] = 0;  // per-forward flags start clear; later kernels of this forward set them
-  const int e0 = blockIdx.x * 32, t0 = blockIdx.y * 32, split = blockIdx.z;
-  const int kbeg = split * kchunk;
-  const int kend = min(H, kbeg + kchunk);
-  const int r = lane & 15, g = lane >> 4;
-  const int ta = t0 + r, tb = t0 + 16 + r, ea = e0 + r, eb = e0 + 16 + r;
-  const bool vta = ta < M, vtb = tb < M, vea = ea < E, veb = eb < E;
-  const T* xa = x + (size_t)(vta ? ta : 0) * H;
-  const T* xb = x + (size_t)(vtb ? tb : 0) * H;
-  const float* wa = Wg + (size_t)(vea ? ea : 0) * H;
-  const float* wb = Wg + (size_t)(veb ? eb : 0) * H;
-  f64x4 acc00 = {0, 0, 0, 0}, acc01 = acc00, acc10 = acc00, acc11 = acc00;
-  for (int k = kbeg; k < kend; k += 16) {
-    const int kk = k + 4 * g;
-    double A0[4], A1[4], B0[4], B1[4];
-    load4_as_f64<T>(xa + kk, vta, A0);
-    load4_as_f64<T>(xb + kk, vtb, A1);
-    load4_as_f64<float>(wa + kk, vea, B0);
-    load4_as_f64<float>(wb + kk, veb, B1);
+struct RouterRaw<float> {
+  u32x4 v[4];  // 16 fp32
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc00 = __builtin_amdgcn_mfma_f64_16x16x4f64(A0[j], B0[j], acc00, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f64_16x16x4f64(A0[j], B1[j], acc01, 0, 0, 0);
-      acc10 = __builtin_amdgcn_mfma_f64_16x16x4f64(A1[j], B0[j], acc10, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f64_16x16x4f64(A1[j], B1[j], acc11, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) v[i] = ok ? reinterpret_cast<const u32x4*>(p)[i] : z;
+  }
+  __device__ __forceinline__ double get(int m) const {
+    return (double)__uint_as_float(v[m >> 2][m & 3]);
+  }
+};
+
+template <typename T, int BT>
+__global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(const T* __restrict__ x,
+                                                 const float* __restrict__ Wg,
+                                                 const float* __restrict__ bias,
+                                                 float* __restrict__ G, int M, int H, int E,
+                                                 int ksplit, int32_t* __restrict__ flags,
+                                                 int32_t* __restrict__ zero_buf, int n_zero) {
+  constexpr int NB = BT / 16;
+  extern __shared__ double red[];  // [ksplit][BT * BT]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < FLAG_WORDS)
+    flags[threadIdx.x] = 0;  // per-forward flags start clear; later kernels of this forward set them
+  {  // the next kernel accumulates per-chunk counts with atomics: clear them here
+    const size_t gid = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t nthreads = (size_t)gridDim.x * gridDim.y * blockDim.x;
+    for (size_t i = gid; i < (size_t)n_zero; i += nthreads) zero_buf[i] = 0;
+  }
+  const int e0 = blockIdx.x * BT, t0 = blockIdx.y * BT;
+  const int klen = H / ksplit, kbeg = wave * klen;
+  const int nsteps = klen / 64;
+  const int r = lane & 15, g = lane >> 4;
+  const T* xr[NB];
+  const float* wr[NB];
+  bool vx[NB], vw[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int t = t0 + 16 * b + r, e = e0 + 16 * b + r;
+    vx[b] = t < M;
+    vw[b] = e < E;
+    xr[b] = x + (size_t)(vx[b] ? t : 0) * H + kbeg + 16 * g;
+    wr[b] = Wg + (size_t)(vw[b] ? e : 0) * H + kbeg + 16 * g;
+  }
+  f64x4 acc[NB][NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
+  RouterRaw<T> xa[2][NB];
+  RouterRaw<float> wa[2][NB];
+  auto load = [&](int step, int buf) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      xa[buf][b].load(xr[b] + 64 * step, vx[b]);
+      wa[buf][b].load(wr[b] + 64 * step, vw[b]);
     }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      double A[NB], B[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        A[b] = xa[buf][b].get(m);
+        B[b] = wa[buf][b].get(m);
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[a], B[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) load(st + 1, 1);
+    mma(0);
+    if (st + 1 >= nsteps) break;
+    if (st + 2 < nsteps) load(st + 2, 0);
+    mma(1);
   }
   // f64 16x16x4 output layout: D[i][j] sits in lane (j + 16 * (i % 4)), register i / 4
-  double* out = Gpart + (size_t)split * M * E;
+  double* mine = red + (size_t)wave * BT * BT;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * i + g;
-    const int t_lo = t0 + row, t_hi = t0 + 16 + row;
-    if (t_lo < M) {
-      if (vea) out[(size_t)t_lo * E + ea] = acc00[i];
-      if (veb) out[(size_t)t_lo * E + eb] = acc01[i];
-    }
-    if (t_hi < M) {
-      if (vea) out[(size_t)t_hi * E + ea] = acc10[i];
-      if (veb) out[(size_t)t_hi * E + eb] = acc11[i];
-    }
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[(16 * a + 4 * i + g) * BT + 16 * b + r] = acc[a][b][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < BT * BT; idx += blockDim.x) {
+    const int t = t0 + idx / BT, e = e0 + idx % BT;
+    if (t >= M || e >= E) continue;
+    double s = 0.0;
+    for (int w = 0; w < ksplit; ++w) s += red[(size_t)w * BT * BT + idx];
+    if (bias) s += (double)bias[e];
+    G[(size_t)t * E + e] = (float)s;
   }
 }
 
-// ---------------------------------------------------------------------------- top-k select
-// One wave per position: sums the k-split partials and the bias, rounds to fp32, selects the
-// K_ext candidates in key order (logit desc, expert id asc), computes the gate scores in
-// double (softmax over all E or sigmoid), the routing weights of the first K, and the
-// planner weight q = floor(s * 2^16 + 1/2).  Also raises the support-miss flag (a routed
-// expert outside the current support) and the liveness-anomaly flag (decoded -> live).
-constexpr int kSelPerLane = kMaxExperts / kWave;
+// ---------------------------------------------------------------------------- top-k + fresh inputs
+// One wave per position.  Per position: the K_ext candidates in key order (logit desc, expert
+// id asc), the gate scores in double (softmax over all E, or sigmoid), the routing weights of
+// the first K, the planner weight q = floor(s * 2^16 + 1/2); the support-miss flag (a routed
+// expert outside the current support) and the liveness-anomaly flag (decoded -> live).  The
+// fresh test of the position before the anomaly override (teardown, LSP: fresh = not
+// (D_i and D_{i-1}), a cache miss, or refresh due; forced rows), and per-chunk per-expert
+// counts of the routed pairs of fresh positions and of all positions (integer atomics, so
+// their order does not matter), the inputs of the stable worklist placement.
+//
+// Selection: every (logit, expert) pair gets a unique 42-bit key, the order-preserving bits of
+// the fp32 logit above the inverted expert id, so "larger key" is exactly the key order
+// above.  A bitwise radix search with wave ballots finds the K_ext-th largest key; the K_ext
+// keys at or above it are ranked by comparing against each other (a readlane loop).
+__device__ __forceinline__ uint64_t sel_key(float g, int e) {
+  uint32_t u = __float_as_uint(g);
+  if (u == 0x80000000u) u = 0u;  // -0 and +0 compare equal as floats: one key for both
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 10) | (uint64_t)(1023 - e);
+}
 
-__global__ __launch_bounds__(256) void k_route_select(
-    const double* __restrict__ Gpart, int splits, const float* __restrict__ bias,
-    const uint8_t* __restrict__ D, const uint8_t* __restrict__ prevD,
-    const uint8_t* __restrict__ inS, const int32_t* __restrict__ S_valid, int M, int E, int K,
-    int Kext, int gate_sigmoid, int norm_topk, float* __restrict__ G, int32_t* __restrict__ ids,
-    float* __restrict__ scores, int32_t* __restrict__ qout, float* __restrict__ wout,
-    uint8_t* __restrict__ Dcopy, int32_t* __restrict__ flags) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+template <int NPER>
+__global__ __launch_bounds__(256) void k_route_rows(
+    const float* __restrict__ G, const uint8_t* __restrict__ D, const uint8_t* __restrict__ force,
+    LayerState L, Scratch W, int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, int R,
+    int iter) {
+  __shared__ double s_buf[4][kMaxKext];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= M) return;
-  const int nper = (E + 63) >> 6;
-  float gv[kSelPerLane];
+  // prologue: every global read of the position at once
+  float gv[NPER];
+  uint8_t in_s[NPER];
 #pragma unroll
-  for (int j = 0; j < kSelPerLane; ++j) {
-    gv[j] = -INFINITY;
+  for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
-    if (j < nper && e < E) {
-      double acc = 0.0;
-      for (int s = 0; s < splits; ++s) acc += Gpart[((size_t)s * M + t) * E + e];
-      if (bias) acc += (double)bias[e];
-      gv[j] = (float)acc;
-      G[(size_t)t * E + e] = gv[j];
+    gv[j] = e < E ? G[(size_t)t * E + e] : -INFINITY;
+    in_s[j] = e < E ? L.inS[e] : 0;
+  }
+  const uint8_t d = D[t], pd = L.prev_D[t];
+  const bool valid = L.valid[t] != 0;
+  const int32_t last = L.last_fresh[t];
+  const bool forced = force ? force[t] != 0 : false;
+  const bool s_valid = *L.S_valid != 0;
+
+  uint64_t key[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) key[j] = (lane + 64 * j < E) ? sel_key(gv[j], lane + 64 * j) : 0ull;
+  // largest threshold T with #{key >= T} >= K_ext: the K_ext-th largest key
+  uint64_t T = 0;
+  for (int b = 41; b >= 0; --b) {
+    const uint64_t cand = T | (1ull << b);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) cnt += __popcll(ballot64(key[j] >= cand));
+    if (cnt >= Kext) T = cand;
+  }
+  // rank of each selected key among the selected ones
+  int rank[NPER];
+  uint64_t selm[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    rank[j] = 0;
+    selm[j] = ballot64(key[j] >= T);
+  }
+#pragma unroll
+  for (int jj = 0; jj < NPER; ++jj) {
+    uint64_t m = selm[jj];
+    while (m) {
+      const int src = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const uint64_t kb = ((uint64_t)__builtin_amdgcn_readlane((int)(key[jj] >> 32), src) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[jj], src);
+#pragma unroll
+      for (int j = 0; j < NPER; ++j) rank[j] += (kb > key[j]);
     }
   }
-  uint32_t taken = 0;
-  int my_id = 0;
-  float my_g = 0.f;
-  for (int r = 0; r < Kext; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j) {
-      const int e = lane + 64 * j;
-      if (j < nper && e < E && !((taken >> j) & 1u) && (gv[j] > bv || (gv[j] == bv && e < bi))) {
-        bv = gv[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == r) {
-      my_id = bi;
-      my_g = bv;
-    }
-  }
-  double zmax = -INFINITY, z = 0.0;
+  // softmax normaliser over all E (max = the best key's logit)
+  double zmax = 0.0, z = 0.0;
   if (!gate_sigmoid) {
     double m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j)
-      if (j < nper && lane + 64 * j < E) m = fmax(m, (double)gv[j]);
+    for (int j = 0; j < NPER; ++j)
+      if (lane + 64 * j < E) m = fmax(m, (double)gv[j]);
     zmax = wave_max(m);
     double part = 0.0;
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j)
-      if (j < nper && lane + 64 * j < E) part += exp((double)gv[j] - zmax);
+    for (int j = 0; j < NPER; ++j)
+      if (lane + 64 * j < E) part += exp((double)gv[j] - zmax);
     z = wave_sum(part);
   }
-  double s = 0.0;
-  if (lane < Kext) s = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)my_g)) : exp((double)my_g - zmax) / z;
-  const double denom = wave_sum(lane < K ? s : 0.0);
-  if (lane < Kext) {
-    ids[(size_t)t * Kext + lane] = my_id;
-    scores[(size_t)t * Kext + lane] = (float)s;
-    qout[(size_t)t * Kext + lane] = (int32_t)floor(s * 65536.0 + 0.5);
+  // the fresh test before the anomaly override
+  const bool due = (long long)iter - (long long)last >= (long long)R;
+  const bool fresh = forced || !valid || !(d && pd) || due;
+  const size_t chunk = (size_t)(t / kChunk);
+  bool miss = false;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int e = lane + 64 * j;
+    if (!((selm[j] >> lane) & 1ull)) continue;
+    const int rk = rank[j];
+    const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)gv[j])) : exp((double)gv[j] - zmax) / z;
+    W.ids[(size_t)t * Kext + rk] = e;
+    W.scores[(size_t)t * Kext + rk] = (float)sc;
+    W.q[(size_t)t * Kext + rk] = (int32_t)floor(sc * 65536.0 + 0.5);
+    s_buf[wave][rk] = sc;
+    if (rk < K) {
+      miss |= s_valid && !in_s[j];
+      atomicAdd(&W.cnt_a[chunk * E + e], 1);
+      if (fresh) atomicAdd(&W.cnt_f[chunk * E + e], 1);
+    }
   }
-  if (lane < K) wout[(size_t)t * K + lane] = (float)(norm_topk ? s / denom : s);
-  const bool miss = (*S_valid != 0) && lane < K && !inS[my_id];
-  if (ballot64(miss) != 0 && lane == 0) flags[FLAG_MISS] = 1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < K) {
+    double denom = 0.0;
+    if (norm_topk)
+      for (int k = 0; k < K; ++k) denom += s_buf[wave][k];  // rank order
+    const double sk = s_buf[wave][lane];
+    W.w[(size_t)t * K + lane] = (float)(norm_topk ? sk / denom : sk);
+  }
+  if (ballot64(miss) != 0 && lane == 0) W.flags[FLAG_MISS] = 1;
   if (lane == 0) {
-    const uint8_t d = D[t];
-    Dcopy[t] = d;
-    if (prevD[t] && !d) flags[FLAG_ANOMALY] = 1;
+    L.Dcur[t] = d;
+    if (pd && !d) W.flags[FLAG_ANOMALY] = 1;
+    W.fpre[t] = fresh ? 1 : 0;
+    if (fresh) atomicAdd(&W.chunk_fresh[chunk], 1);
+    if (forced) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_FORCED_ROWS], 1ull);
+    if (due && valid) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_DUE_ROWS], 1ull);
   }
 }
 
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
-                         const uint8_t* D, const LayerState& L, const Scratch& W, hipStream_t st) {
-  const int kchunk = ((s.H + s.splits - 1) / s.splits + 15) / 16 * 16;
-  dim3 grid((s.E + 31) / 32, (s.M + 31) / 32, s.splits);
-  if (s.bf16)
-    hipLaunchKernelGGL(k_router_partial<uint16_t>, grid, dim3(64), 0, st,
-                       static_cast<const uint16_t*>(x), Wg, W.Gpart, s.M, s.H, s.E, kchunk,
-                       W.flags);
+                         const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
+                         const Scratch& W, hipStream_t st) {
+  const size_t lds = (size_t)s.ksplit * s.router_bt * s.router_bt * sizeof(double);
+  // cnt_f, cnt_a and chunk_fresh are carved back to back (one zeroing range)
+  const int nz = (int)(W.chunk_fresh + s.n_chunks - W.cnt_f);
+  dim3 grid((s.E + s.router_bt - 1) / s.router_bt, (s.M + s.router_bt - 1) / s.router_bt);
+  dim3 block(64 * s.ksplit);
+  if (s.router_bt == 32) {
+    if (s.bf16)
+      hipLaunchKernelGGL((k_router<uint16_t, 32>), grid, block, lds, st,
+                         static_cast<const uint16_t*>(x), Wg, bias, W.G, s.M, s.H, s.E, s.ksplit,
+                         W.flags, W.cnt_f, nz);
+    else
+      hipLaunchKernelGGL((k_router<float, 32>), grid, block, lds, st, static_cast<const float*>(x),
+                         Wg, bias, W.G, s.M, s.H, s.E, s.ksplit, W.flags, W.cnt_f, nz);
+  } else {
+    if (s.bf16)
+      hipLaunchKernelGGL((k_router<uint16_t, 16>), grid, block, lds, st,
+                         static_cast<const uint16_t*>(x), Wg, bias, W.G, s.M, s.H, s.E, s.ksplit,
+                         W.flags, W.cnt_f, nz);
+    else
+      hipLaunchKernelGGL((k_router<float, 16>), grid, block, lds, st, static_cast<const float*>(x),
+                         Wg, bias, W.G, s.M, s.H, s.E, s.ksplit, W.flags, W.cnt_f, nz);
+  }
+  const int nper = (s.E + 63) / 64;
+#define EPOCH_ROUTE_ROWS(NP)                                                                     \
+  hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, D, force, L, \
+                     W, s.M, s.E, s.K, s.Kext, s.gate_sigmoid, s.norm_topk, s.R, iter)
+  if (nper <= 1)
+    EPOCH_ROUTE_ROWS(1);
+  else if (nper <= 2)
+    EPOCH_ROUTE_ROWS(2);
+  else if (nper <= 4)
+    EPOCH_ROUTE_ROWS(4);
+  else if (nper <= 8)
+    EPOCH_ROUTE_ROWS(8);
   else
-    hipLaunchKernelGGL(k_router_partial<float>, grid, dim3(64), 0, st,
-                       static_cast<const float*>(x), Wg, W.Gpart, s.M, s.H, s.E, kchunk, W.flags);
-  hipLaunchKernelGGL(k_route_select, dim3((s.M + 3) / 4), dim3(256), 0, st, W.Gpart, s.splits,
-                     bias, D, L.prev_D, L.inS, L.S_valid, s.M, s.E, s.K, s.Kext, s.gate_sigmoid,
-                     s.norm_topk, W.G, W.ids, W.scores, W.q, W.w, L.Dcur, W.flags);
+    EPOCH_ROUTE_ROWS(16);
+#undef EPOCH_ROUTE_ROWS
   return hipGetLastError();
 }
 

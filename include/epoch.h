@@ -81,7 +81,7 @@ enum {
 typedef struct epoch_desc {
   /* shape */
   int32_t n_layers;     /* >= 1 */
-  int32_t hidden;       /* H: multiple of 64 for bf16, <= 16384 */
+  int32_t hidden;       /* H: multiple of 64, <= 16384 */
   int32_t n_experts;    /* E: 1..1024 */
   int32_t top_k;        /* K: 1..min(E, 16) */
   int32_t inter;        /* I: expert SwiGLU width; multiple of 64 for bf16 */
@@ -210,7 +210,8 @@ const char* epoch_status_string(int32_t status);
 
 /*
  * Kernel timing for measurement.  `groups` is a bitmask of kernel groups (bit g = group g;
- * -1 = all): 0 router + top-k, 1 support, 2 fresh set + worklist, 3 routed gate/up,
+ * -1 = all): 0 router + top-k + fresh test, 1 plan (support check / build, worklist scans),
+ * 2 worklist placement, 3 routed gate/up,
  * 4 routed down, 5 shared expert, 6 combine.  While set, each forward records a pair of HIP
  * events on its stream around every selected group (events come from a process-wide pool,
  * so a measured region reuses events created earlier).  epoch_plan_timing synchronises the
