@@ -11,7 +11,7 @@ constexpr int kWave = 64;
 constexpr int kChunk = 64;        // positions per compaction chunk (one wave)
 constexpr int kMaxKext = 32;      // candidates per position the wave top-k keeps
 constexpr int kMaxExperts = 1024;
-constexpr int kTileRows = 32;     // rows per grouped-GEMM tile
+constexpr int kTileRows = 64;     // rows per grouped-GEMM tile
 constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
 constexpr int kDownCols = 64;     // output columns per down workgroup
 

@@ -1,0 +1,195 @@
+// Grouped bf16 expert GEMM of the SwiGLU experts (gfx950, v_mfma_f32_16x16x32_bf16).
+#pragma once
+#include "device_common.h"
+#include "epoch_internal.h"
+
+namespace epoch {
+
+// A 16-byte fragment: 8 consecutive bf16 of one row.
+__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Row source of a tile: routed tiles gather activations through the worklist; dense (shared
+// expert) tiles take positions in order.
+struct TileRows {
+  int row0, row_end, slot;
+  bool active;
+};
+
+__device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_rows_max,
+                                              const int32_t* flags, const int32_t* tile_slot,
+                                              const int32_t* tile_row0, const int32_t* offs,
+                                              int M) {
+  TileRows r;
+  if (routed) {
+    r.active = tile < flags[FLAG_NTILES];
+    if (!r.active) return r;
+    r.slot = tile_slot[tile];
+    r.row0 = tile_row0[tile];
+    r.row_end = min(offs[r.slot + 1], r.row0 + tile_rows_max);
+  } else {
+    r.row0 = tile * tile_rows_max;
+    r.active = r.row0 < M;
+    r.slot = 0;
+    r.row_end = min(M, r.row0 + tile_rows_max);
+  }
+  return r;
+}
+
+// One kernel for both projections of the SwiGLU expert.
+// Workgroup = 4 waves over one tile (up to BM rows of one expert) and 4 x 32 weight rows:
+//   gate/up: wave w owns intermediate columns [16w, 16w + 16) of a 64-column block and reads
+//            those rows of W1 and of W3 (32 weight rows); epilogue h = bf16(silu(g) * u);
+//   down:    wave w owns output columns [32w, 32w + 32) of a 128-column block of W2;
+//            epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
+// The contraction runs in chunks of KC.  The tile's activation rows (gathered through the
+// worklist for routed gate/up) are staged per chunk in LDS (double-buffered) and shared by
+// the four waves; every wave streams its weight rows straight into a ring of NST register
+// stages, so NST - 1 chunks of weights are in flight while a chunk's MFMAs run.  Lane l
+// feeds A row (l % 16) and B row (l % 16) with the same 8 consecutive k values (k-group
+// l / 16), so every product pairs an activation with the weight of the same k.
+//
+// Grid: one-dimensional, n_col_blocks * (tile slots rounded up to a multiple of 8).  The
+// hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
+// (L / 8) % NB of tile 8 * ((L / 8) / NB) + L % 8, so every column block of a tile lands on
+// the same XCD and the tile's activation rows are fetched into one L2 only.
+template <int BM, int KC, int NST, bool GATEUP, bool ROUTED>
+__global__ __launch_bounds__(256) void k_expert_gemm(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
+    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
+    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+  const int n_cb = GATEUP ? Ndim / 64 : (Ndim + 127) / 128;
+  const int pos = blockIdx.x >> 3;
+  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
+  const int cb = pos % n_cb;
+  constexpr int MB = BM / 16;        // 16-row MFMA blocks per tile
+  constexpr int KS = KC / 32;        // MFMA k-steps per chunk
+  constexpr int LDA = KC + 8;        // LDS row pitch (bf16), breaks bank aliasing
+  constexpr int SEGS = BM * KC / 8;  // 16-byte segments of one activation chunk
+  constexpr int ASEG = SEGS / 256;   // per thread
+  static_assert(SEGS % 256 == 0, "activation chunk must split evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
+
+  const TileRows tr = tile_rows(ROUTED, tile, BM, flags, tile_slot, tile_row0, offs, M);
+  if (!tr.active) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t estride = (size_t)Ndim * Kdim;
+  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
+  int col0;
+  const uint16_t *bp0, *bp1;
+  if (GATEUP) {
+    col0 = cb * 64 + wave * 16;
+    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
+    bp1 = B1 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
+  } else {
+    col0 = cb * 128 + wave * 32;
+    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
+    bp1 = bp0 + (size_t)16 * Kdim;
+  }
+  // Ndim is a multiple of 64, so a wave's 16 or 32 columns are all inside or all outside;
+  // a wave outside still stages activations and meets every barrier
+  const bool wact = col0 < Ndim;
+  // activation segments this thread stages: row = seg / (KC / 8), 8 columns each
+  const uint16_t* asrc[ASEG];
+  int adst[ASEG];
+  bool aok[ASEG];
+#pragma unroll
+  for (int j = 0; j < ASEG; ++j) {
+    const int seg = tid + 256 * j;
+    const int row = seg / (KC / 8), c8 = seg % (KC / 8);
+    const int p = tr.row0 + row;
+    aok[j] = p < tr.row_end;
+    const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
+    asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
+    adst[j] = row * LDA + c8 * 8;
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int nch = Kdim / KC;
+
+  u32x4 areg[ASEG];
+  bf16x8 bx[NST][KS], by[NST][KS];
+  f32x4 c0[MB], c1[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    c0[m] = f32x4{0, 0, 0, 0};
+    c1[m] = f32x4{0, 0, 0, 0};
+  }
+
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < ASEG; ++j)
+      areg[j] = aok[j] ? *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC) : zero;
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < ASEG; ++j) *reinterpret_cast<u32x4*>(&As[buf][adst[j]]) = areg[j];
+  };
+  auto load_b = [&](int c, bf16x8* x0, bf16x8* x1) {
+    if (!wact) return;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
+      x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
+    }
+  };
+  auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
+    if (!wact) return;
+    const uint16_t* ab = &As[buf][r * LDA + 8 * g];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const bf16x8 f =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * LDA + 32 * s));
+        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, x0[s], c0[m], 0, 0, 0);
+        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, x1[s], c1[m], 0, 0, 0);
+      }
+    }
+  };
+
+  load_a(0);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < nch) load_b(st, bx[st], by[st]);
+  store_a(0);
+  __syncthreads();
+  for (int cb = 0; cb < nch; cb += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int c = cb + u;
+      if (c >= nch) break;
+      const int pre = c + NST - 1;  // weight chunk entering the ring now
+      if (pre < nch) load_b(pre, bx[(u + NST - 1) % NST], by[(u + NST - 1) % NST]);
+      if (c + 1 < nch) load_a(c + 1);
+      compute(c & 1, bx[u], by[u]);
+      if (c + 1 < nch) store_a((c + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  if (!wact) return;
+  // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = tr.row0 + 16 * m + 4 * g + q;
+      if (row >= tr.row_end) continue;
+      const float v0 = c0[m][q], v1 = c1[m][q];
+      if (GATEUP) {
+        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(v0 / (1.0f + expf(-v0)) * v1);
+      } else {
+        const float sc = ROUTED ? wl_w[row] : 1.0f;
+        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(sc * v0);
+        out[(size_t)row * Ndim + col0 + 16 + r] = f32_to_bf16(sc * v1);
+      }
+    }
+  }
+}
+
+}  // namespace epoch

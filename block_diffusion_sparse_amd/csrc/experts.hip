@@ -9,202 +9,33 @@
 // liveness split, teardown LSP section) is the same kernel over all M positions.
 #include "device_common.h"
 #include "epoch_internal.h"
+#include "expert_gemm.h"
 
 namespace epoch {
 
-// A 16-byte fragment: 8 consecutive bf16 of one row.
-__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ bf16x8 zero_frag() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, z);
-}
+// Tile shape of the bf16 path: kTileRows rows per tile, K in chunks of kGemmKC, kGemmStages
+// register stages of weights (kGemmStages - 1 chunks in flight).
+constexpr int kGemmKC = 128;
+constexpr int kGemmStages = 3;
 
-// Row source of a tile: routed tiles gather activations through the worklist; dense (shared
-// expert) tiles take positions in order.
-struct TileRows {
-  int row0, row_end, slot;
-  bool active;
-};
-
-__device__ __forceinline__ TileRows tile_rows(bool routed, int tile, const int32_t* flags,
-                                              const int32_t* tile_slot,
-                                              const int32_t* tile_row0, const int32_t* offs,
-                                              int M) {
-  TileRows r;
-  if (routed) {
-    r.active = tile < flags[FLAG_NTILES];
-    if (!r.active) return r;
-    r.slot = tile_slot[tile];
-    r.row0 = tile_row0[tile];
-    r.row_end = min(offs[r.slot + 1], r.row0 + kTileRows);
-  } else {
-    r.active = true;
-    r.slot = 0;
-    r.row0 = tile * kTileRows;
-    r.row_end = min(M, r.row0 + kTileRows);
-  }
-  return r;
-}
-
-// ---------------------------------------------------------------------------- grouped bf16 GEMM
-// One kernel for both projections of the SwiGLU expert, on v_mfma_f32_16x16x32_bf16.
-// Workgroup = 4 waves over one tile (up to 32 rows of one expert) and 4 x 32 weight rows:
-//   gate/up: wave w owns intermediate columns [16w, 16w + 16) of a 64-column block and reads
-//            those rows of W1 and of W3 (32 weight rows); epilogue h = bf16(silu(g) * u);
-//   down:    wave w owns output columns [32w, 32w + 32) of a 128-column block of W2;
-//            epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
-// The contraction runs in chunks of KC.  The tile's activation rows (gathered through the
-// worklist for routed gate/up) are staged once per chunk in LDS and shared by the 4 waves;
-// every wave streams its weight rows straight into registers, with the next chunk's loads in
-// flight while the current chunk's MFMAs run (16 KB per wave at KC = 256).  Lane l feeds A
-// row (l % 16) and B row (l % 16) with the same 8 consecutive k values (k-group l / 16), so
-// every product pairs an activation with the weight of the same k.
-template <int KC, bool GATEUP, bool ROUTED>
-__global__ __launch_bounds__(256, 2) void k_expert_gemm(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
-    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
-    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
-  constexpr int KS = KC / 32;               // MFMA k-steps per chunk
-  constexpr int LDA = KC + 8;               // LDS row pitch (bf16), breaks bank aliasing
-  constexpr int SEGS = 32 * KC / 8;         // 16-byte segments of one A chunk
-  constexpr int ASEG = (SEGS + 255) / 256;  // per thread
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTileRows * LDA];
-
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, flags, tile_slot, tile_row0, offs, M);
-  if (!tr.active) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const size_t estride = (size_t)Ndim * Kdim;
-  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  int col0;
-  const uint16_t *bp0, *bp1;
-  if (GATEUP) {
-    col0 = blockIdx.y * 64 + wave * 16;
-    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-    bp1 = B1 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-  } else {
-    col0 = blockIdx.y * 128 + wave * 32;
-    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-    bp1 = bp0 + (size_t)16 * Kdim;
-  }
-  // Ndim is a multiple of 64, so a wave's 16 or 32 columns are all inside or all outside;
-  // a wave outside still stages activations and meets every barrier
-  const bool wact = col0 < Ndim;
-  // activation segments this thread stages: row = seg / (KC / 8), 8 columns each
-  const uint16_t* asrc[ASEG];
-  int adst[ASEG];
-  bool aok[ASEG];
-#pragma unroll
-  for (int j = 0; j < ASEG; ++j) {
-    const int seg = tid + 256 * j;
-    const int row = seg / (KC / 8), c8 = seg % (KC / 8);
-    const int p = tr.row0 + row;
-    aok[j] = seg < SEGS && p < tr.row_end;
-    const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
-    asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
-    adst[j] = row * LDA + c8 * 8;
-  }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int nchunks = Kdim / KC;
-
-  u32x4 areg[ASEG];
-  bf16x8 bA[KS], bB[KS], nA[KS], nB[KS];
-  f32x4 c00 = {0, 0, 0, 0}, c01 = c00, c10 = c00, c11 = c00;
-
-  auto load_a = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < ASEG; ++j)
-      areg[j] = aok[j] ? *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC) : zero;
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < ASEG; ++j)
-      if (tid + 256 * j < SEGS) *reinterpret_cast<u32x4*>(&As[buf][adst[j]]) = areg[j];
-  };
-  auto load_b = [&](int c, bf16x8* x0, bf16x8* x1) {
-    if (!wact) return;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
-      x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
-    }
-  };
-  auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
-    if (!wact) return;
-    const uint16_t* a_lo = &As[buf][r * LDA + 8 * g];
-    const uint16_t* a_hi = a_lo + 16 * LDA;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 f0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_lo + 32 * s));
-      const bf16x8 f1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_hi + 32 * s));
-      c00 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, x0[s], c00, 0, 0, 0);
-      c10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, x0[s], c10, 0, 0, 0);
-      c01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, x1[s], c01, 0, 0, 0);
-      c11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, x1[s], c11, 0, 0, 0);
-    }
-  };
-
-  load_a(0);
-  load_b(0, bA, bB);
-  store_a(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    // chunk c from buffer 0 / registers bA,bB; chunk c+1 prefetched into nA,nB
-    if (c + 1 < nchunks) {
-      load_a(c + 1);
-      load_b(c + 1, nA, nB);
-    }
-    compute(0, bA, bB);
-    if (c + 1 < nchunks) store_a(1);
-    __syncthreads();
-    if (c + 1 >= nchunks) break;
-    if (c + 2 < nchunks) {
-      load_a(c + 2);
-      load_b(c + 2, bA, bB);
-    }
-    compute(1, nA, nB);
-    if (c + 2 < nchunks) store_a(0);
-    __syncthreads();
-  }
-
-  if (!wact) return;
-  // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int row = tr.row0 + 16 * mb + 4 * g + q;
-      if (row >= tr.row_end) continue;
-      const float v0 = mb ? c10[q] : c00[q];
-      const float v1 = mb ? c11[q] : c01[q];
-      if (GATEUP) {
-        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(v0 / (1.0f + expf(-v0)) * v1);
-      } else {
-        const float sc = ROUTED ? wl_w[row] : 1.0f;
-        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(sc * v0);
-        out[(size_t)row * Ndim + col0 + 16 + r] = f32_to_bf16(sc * v1);
-      }
-    }
-  }
+// grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
+static dim3 gemm_grid(int tiles, int Ndim, bool gateup) {
+  const int n_cb = gateup ? Ndim / 64 : (Ndim + 127) / 128;
+  return dim3(((tiles + 7) / 8) * 8 * n_cb);
 }
 
 template <bool GATEUP, bool ROUTED>
 static void launch_gemm(dim3 grid, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
                         const uint16_t* B1, const Scratch& W, const int32_t* S_list,
                         uint16_t* out, int M, int Ndim) {
-  if (Kdim % 256 == 0)
-    hipLaunchKernelGGL((k_expert_gemm<256, GATEUP, ROUTED>), grid, dim3(256), 0, st, A, B0, B1,
-                       W.flags, W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out,
-                       M, Kdim, Ndim);
+  if (Kdim % kGemmKC == 0)
+    hipLaunchKernelGGL((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED>), grid,
+                       dim3(256), 0, st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs,
+                       S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
   else
-    hipLaunchKernelGGL((k_expert_gemm<64, GATEUP, ROUTED>), grid, dim3(256), 0, st, A, B0, B1,
-                       W.flags, W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out,
-                       M, Kdim, Ndim);
+    hipLaunchKernelGGL((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED>), grid, dim3(256), 0, st,
+                       A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos,
+                       W.wl_w, out, M, Kdim, Ndim);
 }
 
 // ---------------------------------------------------------------------------- fp32 variant
@@ -217,7 +48,7 @@ __global__ __launch_bounds__(256) void k_gateup_f32(
     const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ S_list, const int32_t* __restrict__ wl_pos,
     float* __restrict__ h, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, flags, tile_slot, tile_row0, offs, M);
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, flags, tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;
   const int i0 = blockIdx.y * kGateUpCols;
@@ -245,7 +76,7 @@ __global__ __launch_bounds__(256) void k_down_f32(
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const float* __restrict__ wl_w, float* __restrict__ out, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, flags, tile_slot, tile_row0, offs, M);
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, flags, tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;
   const int j0 = blockIdx.y * kDownCols;
@@ -266,7 +97,7 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
                                 const LayerState& L, const Scratch& W, hipStream_t st) {
   dim3 grid(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols);
   if (s.bf16)
-    launch_gemm<true, true>(grid, st, s.H, static_cast<const uint16_t*>(x),
+    launch_gemm<true, true>(gemm_grid(s.T_max, s.I, true), st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
                             L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
   else
@@ -280,7 +111,7 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
                               const Scratch& W, hipStream_t st) {
   if (s.bf16)
-    launch_gemm<false, true>(dim3(s.T_max, (s.H + 127) / 128), st, s.I, static_cast<const uint16_t*>(W.h),
+    launch_gemm<false, true>(gemm_grid(s.T_max, s.H, false), st, s.I, static_cast<const uint16_t*>(W.h),
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
                              static_cast<uint16_t*>(W.y_pair), s.M, s.H);
   else
@@ -295,10 +126,10 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
   dim3 g1(s.T_dense, (s.Is + kGateUpCols - 1) / kGateUpCols);
   dim3 g2(s.T_dense, (s.H + kDownCols - 1) / kDownCols);
   if (s.bf16) {
-    launch_gemm<true, false>(g1, st, s.H, static_cast<const uint16_t*>(x),
+    launch_gemm<true, false>(gemm_grid(s.T_dense, s.Is, true), st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),
                              W, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.Is);
-    launch_gemm<false, false>(dim3(s.T_dense, (s.H + 127) / 128), st, s.Is,
+    launch_gemm<false, false>(gemm_grid(s.T_dense, s.H, false), st, s.Is,
                               static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
                               nullptr, W, nullptr, static_cast<uint16_t*>(W.S), s.M, s.H);
   } else {
