@@ -151,10 +151,15 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
 
 
 def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=None, Wdev=None,
-              bias_override=None, force_override=None, check=True, verbose=True) -> BlockReport:
-    """Replay one block of `iters` iterations over `layers` on GPU and oracle, comparing."""
+              bias_override=None, force_override=None, check=True, verbose=True,
+              D_override=None, hook=None) -> BlockReport:
+    """Replay one block of `iters` iterations over `layers` on GPU and oracle, comparing.
+
+    hook(it, plan, orcs) runs before each iteration (e.g. to rebuild the plan mid-block); it
+    may return a replacement (plan, orcs) pair.
+    """
     iters = w.iters if iters is None else iters
-    D = synth.decoded_masks(w)
+    D = synth.decoded_masks(w) if D_override is None else D_override
     F = synth.force_masks(w) if force_override is None else force_override
     rep = BlockReport()
     if weights is None:
@@ -172,6 +177,11 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
     Fdev = None if F is None else to_dev(F)
     prev_cache = [None] * len(layers)
     for it in range(iters):
+        if hook is not None:
+            repl = hook(it, plan, orcs)
+            if repl is not None:
+                plan, orcs = repl
+                prev_cache = [None] * len(layers)
         for li, l in enumerate(layers):
             x = Xdev[li][it]
             y = torch.empty_like(x)
@@ -201,6 +211,7 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
         assert c["cold"] == oc["cold"] and c["hot_update"] == oc["hot_update"]
         assert c["hot_skip"] == oc["hot_skip"] and c["anomaly"] == oc["anomalies"]
         assert c["fresh_rows"] == oc["fresh_rows"] and c["pairs"] == oc["pairs"]
-        assert c["commits"] == iters and c["forwards"] == iters
+        assert c["commits"] == c["forwards"] == orcs[li].iter
+    rep.counters = [plan.counters(li) for li in range(len(layers))]
     plan.close()
     return rep
