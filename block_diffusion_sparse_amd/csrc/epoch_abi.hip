@@ -91,6 +91,11 @@ Shape make_shape(const epoch_desc* d) {
   const long long P_max = (long long)s.M * s.K;
   s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;
   s.T_dense = (s.M + kTileRows - 1) / kTileRows;
+  // experts with at least kBigRows fresh pairs take compute-bound 128-row tiles; enabled only
+  // for shapes whose iterations can hold far more pairs than the weight-stream tiles cover
+  // well (with fewer pairs per iteration the extra launch costs more than it saves)
+  s.big_routed = s.bf16 && P_max >= 32768;
+  s.T_big_max = s.big_routed ? (int)((P_max + kBigTile - 1) / kBigTile + P_max / kBigRows + 1) : 0;
   s.B = d->atlas_B;
   s.c = d->atlas_c;
   s.an = d->alpha_num;
@@ -147,6 +152,8 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
   W.fresh_list = c.take<int32_t>(M);
   W.tile_slot = c.take<int32_t>(s.T_max);
   W.tile_row0 = c.take<int32_t>(s.T_max);
+  W.tile_slot_b = c.take<int32_t>(std::max(s.T_big_max, 1));
+  W.tile_row0_b = c.take<int32_t>(std::max(s.T_big_max, 1));
   W.Crow = c.take<int32_t>(M);
   W.Rrow = c.take<int32_t>(M);
   W.h = c.take_bytes(P_max * s.I * act);

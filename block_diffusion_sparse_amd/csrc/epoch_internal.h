@@ -12,12 +12,14 @@ constexpr int kChunk = 64;        // positions per compaction chunk (one wave)
 constexpr int kMaxKext = 32;      // candidates per position the wave top-k keeps
 constexpr int kMaxExperts = 1024;
 constexpr int kTileRows = 64;     // rows per grouped-GEMM tile
+constexpr int kBigTile = 128;     // rows per compute-bound tile
+constexpr int kBigRows = 768;     // experts with at least this many fresh rows use big tiles
 constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
 constexpr int kDownCols = 64;     // output columns per down workgroup
 
 // per-forward flag words (int32) in the scratch area
 enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
-       FLAG_REBUILT = 5, FLAG_WORDS = 16 };
+       FLAG_NTILES_BIG = 5, FLAG_WORDS = 16 };
 
 // Device-side view of one layer's persistent state.
 struct LayerState {
@@ -58,6 +60,8 @@ struct Scratch {
   int32_t* fresh_list;  // [M]
   int32_t* tile_slot;   // [T_max]
   int32_t* tile_row0;   // [T_max]
+  int32_t* tile_slot_b; // [T_big_max] tiles of kBigTile rows (experts with >= kBigRows pairs)
+  int32_t* tile_row0_b; // [T_big_max]
   int32_t* Crow;        // [M] support-build coverage
   int32_t* Rrow;        // [M]
   void* h;              // [P_max x I] act
@@ -68,7 +72,7 @@ struct Scratch {
 
 struct Shape {
   int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
-  int n_chunks, ksplit, router_bt, T_max, T_dense;
+  int n_chunks, ksplit, router_bt, T_max, T_dense, T_big_max, big_routed;
   int B, c, an, ad, qn, qd, bn, bd;
 };
 

@@ -18,12 +18,12 @@ struct TileRows {
 };
 
 __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_rows_max,
-                                              const int32_t* flags, const int32_t* tile_slot,
+                                              int ntiles, const int32_t* tile_slot,
                                               const int32_t* tile_row0, const int32_t* offs,
                                               int M) {
   TileRows r;
   if (routed) {
-    r.active = tile < flags[FLAG_NTILES];
+    r.active = tile < ntiles;
     if (!r.active) return r;
     r.slot = tile_slot[tile];
     r.row0 = tile_row0[tile];
@@ -54,15 +54,18 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
 // hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
 // (L / 8) % NB of tile 8 * ((L / 8) / NB) + L % 8, so every column block of a tile lands on
 // the same XCD and the tile's activation rows are fetched into one L2 only.
-template <int BM, int KC, int NST, bool GATEUP, bool ROUTED>
-__global__ __launch_bounds__(256) void k_expert_gemm(
+template <int BM, int KC, int NST, bool GATEUP, bool ROUTED, int WAVES = 4, bool NT = false,
+          int MINW = 1>
+__global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
-  const int n_cb = GATEUP ? Ndim / 64 : (Ndim + 127) / 128;
+  constexpr int NTH = 64 * WAVES;
+  constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // columns per workgroup
+  const int n_cb = (Ndim + CBW - 1) / CBW;
   const int pos = blockIdx.x >> 3;
   const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
   const int cb = pos % n_cb;
@@ -70,11 +73,12 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
   constexpr int KS = KC / 32;        // MFMA k-steps per chunk
   constexpr int LDA = KC + 8;        // LDS row pitch (bf16), breaks bank aliasing
   constexpr int SEGS = BM * KC / 8;  // 16-byte segments of one activation chunk
-  constexpr int ASEG = SEGS / 256;   // per thread
-  static_assert(SEGS % 256 == 0, "activation chunk must split evenly over 256 threads");
+  constexpr int ASEG = SEGS / NTH;   // per thread
+  static_assert(SEGS % NTH == 0, "activation chunk must split evenly over the threads");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
 
-  const TileRows tr = tile_rows(ROUTED, tile, BM, flags, tile_slot, tile_row0, offs, M);
+  const TileRows tr = tile_rows(ROUTED, tile, BM, ROUTED ? flags[FLAG_NTILES] : 0, tile_slot,
+                                tile_row0, offs, M);
   if (!tr.active) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -83,11 +87,11 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
   int col0;
   const uint16_t *bp0, *bp1;
   if (GATEUP) {
-    col0 = cb * 64 + wave * 16;
+    col0 = cb * CBW + wave * 16;
     bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
     bp1 = B1 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
   } else {
-    col0 = cb * 128 + wave * 32;
+    col0 = cb * CBW + wave * 32;
     bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
     bp1 = bp0 + (size_t)16 * Kdim;
   }
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
   bool aok[ASEG];
 #pragma unroll
   for (int j = 0; j < ASEG; ++j) {
-    const int seg = tid + 256 * j;
+    const int seg = tid + NTH * j;
     const int row = seg / (KC / 8), c8 = seg % (KC / 8);
     const int p = tr.row0 + row;
     aok[j] = p < tr.row_end;
@@ -133,8 +137,15 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
     if (!wact) return;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
-      x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
+      if (NT) {
+        x0[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                               reinterpret_cast<const u32x4*>(bp0 + (size_t)c * KC + 32 * s)));
+        x1[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                               reinterpret_cast<const u32x4*>(bp1 + (size_t)c * KC + 32 * s)));
+      } else {
+        x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
+        x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
+      }
     }
   };
   auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
@@ -158,10 +169,10 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
     if (st < nch) load_b(st, bx[st], by[st]);
   store_a(0);
   __syncthreads();
-  for (int cb = 0; cb < nch; cb += NST) {
+  for (int kb = 0; kb < nch; kb += NST) {
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
-      const int c = cb + u;
+      const int c = kb + u;
       if (c >= nch) break;
       const int pre = c + NST - 1;  // weight chunk entering the ring now
       if (pre < nch) load_b(pre, bx[(u + NST - 1) % NST], by[(u + NST - 1) % NST]);
@@ -187,6 +198,146 @@ __global__ __launch_bounds__(256) void k_expert_gemm(
         const float sc = ROUTED ? wl_w[row] : 1.0f;
         out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(sc * v0);
         out[(size_t)row * Ndim + col0 + 16 + r] = f32_to_bf16(sc * v1);
+      }
+    }
+  }
+}
+
+}  // namespace epoch
+
+namespace epoch {
+
+// Compute-bound variant for tiles with many rows (the shared expert over all M positions):
+// a 128-row x 128-weight-row output tile per workgroup, K in chunks of 64, the activation and
+// weight chunks both staged in LDS (double-buffered, loaded one chunk ahead through
+// registers), four waves in a 2 x 2 arrangement, each accumulating a 64 x 64 sub-tile with
+// v_mfma_f32_16x16x32_bf16 (4 x 4 blocks).  Gate/up: the 128 staged weight rows are
+// [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g and u
+// of the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of W2.
+// Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
+template <bool GATEUP, bool ROUTED>
+__global__ __launch_bounds__(256, 2) void k_gemm_big(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
+    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
+    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+  constexpr int BR = 128, KC = 64, LD = KC + 8, SEG_ROW = KC / 8;
+  constexpr int CBW = GATEUP ? 64 : 128;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BR * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BR * LD];
+  const int n_cb = (Ndim + CBW - 1) / CBW;
+  const int pos = blockIdx.x >> 3;
+  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
+  const int cb = pos % n_cb;
+  // routed big tiles come from their own table, counted in FLAG_NTILES_BIG
+  const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
+                                tile_row0, offs, M);
+  if (!tr.active) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const size_t estride = (size_t)Ndim * Kdim;
+  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
+  // staging: 4 activation and 4 weight segments of 16 bytes per thread per chunk
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
+  bool aok[4], bok[4];
+  int dst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int seg = tid + 256 * j;
+    const int row = seg / SEG_ROW, c8 = seg % SEG_ROW;
+    dst[j] = row * LD + c8 * 8;
+    const int p = tr.row0 + row;
+    aok[j] = p < tr.row_end;
+    const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
+    asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
+    int wrow;
+    const uint16_t* base;
+    if (GATEUP) {
+      const int q = row >> 5;  // quarter: W1, W3, W1, W3
+      wrow = cb * 64 + (q >> 1) * 32 + (row & 31);
+      base = (q & 1) ? B1 : B0;
+    } else {
+      wrow = cb * 128 + row;
+      base = B0;
+    }
+    bok[j] = wrow < Ndim;
+    bsrc[j] = base + e * estride + (size_t)(bok[j] ? wrow : 0) * Kdim + c8 * 8;
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 ra[4], rb[4];  // the chunk in flight from global memory to LDS
+  auto load = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = aok[j] ? *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC) : zero;
+      rb[j] = bok[j] ? *reinterpret_cast<const u32x4*>(bsrc[j] + (size_t)c * KC) : zero;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(&As[buf][dst[j]]) = ra[j];
+      *reinterpret_cast<u32x4*>(&Bs[buf][dst[j]]) = rb[j];
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+  auto compute = [&](int buf) {
+    const uint16_t* ab = &As[buf][(64 * wm + r) * LD + 8 * g];
+    const uint16_t* bb = &Bs[buf][(64 * wn + r) * LD + 8 * g];
+#pragma unroll
+    for (int s = 0; s < KC / 32; ++s) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        fa[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * LD + 32 * s));
+        fb[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bb + m * 16 * LD + 32 * s));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+    }
+  };
+  const int nch = Kdim / KC;
+  load(0);
+  store(0);
+  __syncthreads();
+  // chunk c sits in LDS buffer c & 1; chunk c + 1 is fetched while chunk c is multiplied
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) load(c + 1);
+    compute(c & 1);
+    if (c + 1 < nch) store((c + 1) & 1);
+    __syncthreads();
+  }
+  // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = tr.row0 + 64 * wm + 16 * m + 4 * g + q;
+      if (row >= tr.row_end) continue;
+      if (GATEUP) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int col = cb * 64 + 32 * wn + 16 * n + r;
+          const float gv = acc[m][n][q], uv = acc[m][n + 2][q];
+          if (col < Ndim) out[(size_t)row * Ndim + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+        }
+      } else {
+        const float sc = ROUTED ? wl_w[row] : 1.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = cb * 128 + 64 * wn + 16 * n + r;
+          if (col < Ndim) out[(size_t)row * Ndim + col] = f32_to_bf16(sc * acc[m][n][q]);
+        }
       }
     }
   }

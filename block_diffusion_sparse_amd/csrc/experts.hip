@@ -17,6 +17,9 @@ namespace epoch {
 // register stages of weights (kGemmStages - 1 chunks in flight).
 constexpr int kGemmKC = 128;
 constexpr int kGemmStages = 3;
+// dense (shared-expert) layers of at least this many positions use the compute-bound
+// 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
+constexpr int kBigTileMinRows = 2048;
 
 // grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
 static dim3 gemm_grid(int tiles, int Ndim, bool gateup) {
@@ -48,7 +51,8 @@ __global__ __launch_bounds__(256) void k_gateup_f32(
     const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ S_list, const int32_t* __restrict__ wl_pos,
     float* __restrict__ h, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, flags, tile_slot, tile_row0, offs, M);
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, ROUTED ? flags[FLAG_NTILES] : 0,
+                                tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;
   const int i0 = blockIdx.y * kGateUpCols;
@@ -76,7 +80,8 @@ __global__ __launch_bounds__(256) void k_down_f32(
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const float* __restrict__ wl_w, float* __restrict__ out, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, flags, tile_slot, tile_row0, offs, M);
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, ROUTED ? flags[FLAG_NTILES] : 0,
+                                tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;
   const int j0 = blockIdx.y * kDownCols;
@@ -96,11 +101,18 @@ __global__ __launch_bounds__(256) void k_down_f32(
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
                                 const LayerState& L, const Scratch& W, hipStream_t st) {
   dim3 grid(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols);
-  if (s.bf16)
+  if (s.bf16) {
     launch_gemm<true, true>(gemm_grid(s.T_max, s.I, true), st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
                             L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
-  else
+    if (s.big_routed)  // experts with many fresh rows: compute-bound 128 x 128 tiles
+      hipLaunchKernelGGL((k_gemm_big<true, true>),
+                         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
+                         static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
+                         W.offs, L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M,
+                         s.H, s.I);
+  } else
     hipLaunchKernelGGL(k_gateup_f32<true>, grid, dim3(256), 0, st, static_cast<const float*>(x),
                        static_cast<const float*>(w1), static_cast<const float*>(w3), W.flags,
                        W.tile_slot, W.tile_row0, W.offs, L.S_list, W.wl_pos,
@@ -110,11 +122,17 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
 
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
                               const Scratch& W, hipStream_t st) {
-  if (s.bf16)
+  if (s.bf16) {
     launch_gemm<false, true>(gemm_grid(s.T_max, s.H, false), st, s.I, static_cast<const uint16_t*>(W.h),
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
                              static_cast<uint16_t*>(W.y_pair), s.M, s.H);
-  else
+    if (s.big_routed)
+      hipLaunchKernelGGL((k_gemm_big<false, true>),
+                         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
+                         st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
+                         nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
+                         W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H);
+  } else
     hipLaunchKernelGGL(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st, static_cast<const float*>(W.h),
                        static_cast<const float*>(w2), W.flags, W.tile_slot, W.tile_row0, W.offs,
                        L.S_list, W.wl_w, static_cast<float*>(W.y_pair), s.M, s.H, s.I);
@@ -125,7 +143,19 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
                          const void* sw2, const Scratch& W, hipStream_t st) {
   dim3 g1(s.T_dense, (s.Is + kGateUpCols - 1) / kGateUpCols);
   dim3 g2(s.T_dense, (s.H + kDownCols - 1) / kDownCols);
-  if (s.bf16) {
+  if (s.bf16 && s.M >= kBigTileMinRows) {
+    // many rows: compute-bound, 128 x 128 tiles with both operands staged in LDS
+    const int tiles = (s.M + 127) / 128;
+    const dim3 gu(((tiles + 7) / 8) * 8 * (s.Is / 64)), gd(((tiles + 7) / 8) * 8 * ((s.H + 127) / 128));
+    hipLaunchKernelGGL((k_gemm_big<true, false>), gu, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(sw1),
+                       static_cast<const uint16_t*>(sw3), W.flags, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.H, s.Is);
+    hipLaunchKernelGGL((k_gemm_big<false, false>), gd, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
+                       nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       static_cast<uint16_t*>(W.S), s.M, s.Is, s.H);
+  } else if (s.bf16) {
     launch_gemm<true, false>(gemm_grid(s.T_dense, s.Is, true), st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),
                              W, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.Is);

@@ -218,6 +218,7 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Scratch W) {
   __shared__ SupportLds sh;
   __shared__ int32_t part[kPlanThreads];
+  __shared__ int32_t part_b[kPlanThreads];
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -265,24 +266,37 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
   if (tid == 0) W.eoffs[E] = P;
   // slot offsets and the tile table
   const int nS = *L.S_size;
-  int my_tiles = 0, my_off = 0;
+  // an expert with at least kBigRows pairs goes to the compute-bound table (kBigTile rows per
+  // tile) when the shape enables it, every other expert to the weight-stream table
+  int my_tiles = 0, my_big = 0, my_off = 0;
   if (tid < nS) {
     const int ex = L.S_list[tid];
     my_off = sh.scan[ex] - tot[ex];
-    my_tiles = (tot[ex] + kTileRows - 1) / kTileRows;
+    if (s.big_routed && tot[ex] >= kBigRows)
+      my_big = (tot[ex] + kBigTile - 1) / kBigTile;
+    else
+      my_tiles = (tot[ex] + kTileRows - 1) / kTileRows;
     W.offs[tid] = my_off;
   }
   if (tid == 0) W.offs[nS] = P;
   __syncthreads();
   part[tid] = my_tiles;
+  part_b[tid] = my_big;
   __syncthreads();
   block_inclusive_scan(part, kPlanThreads);
+  block_inclusive_scan(part_b, kPlanThreads);
   const int T = part[kPlanThreads - 1];
+  const int Tb = part_b[kPlanThreads - 1];
   if (tid < nS) {
     const int t0 = part[tid] - my_tiles;
     for (int i = 0; i < my_tiles; ++i) {
       W.tile_slot[t0 + i] = tid;
       W.tile_row0[t0 + i] = my_off + i * kTileRows;
+    }
+    const int b0 = part_b[tid] - my_big;
+    for (int i = 0; i < my_big; ++i) {
+      W.tile_slot_b[b0 + i] = tid;
+      W.tile_row0_b[b0 + i] = my_off + i * kBigTile;
     }
   }
   __syncthreads();
@@ -306,6 +320,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
     W.flags[FLAG_NFRESH] = nfresh;
     W.flags[FLAG_NPAIRS] = P;
     W.flags[FLAG_NTILES] = T;
+    W.flags[FLAG_NTILES_BIG] = Tb;
     int touched = 0;
     for (int i = 0; i < E; ++i) touched += tot[i] > 0;
     L.counters[EPOCH_CNT_FRESH_ROWS] += nfresh;
