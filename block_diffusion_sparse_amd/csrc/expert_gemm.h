@@ -96,9 +96,15 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     bp1 = bp0 + (size_t)16 * Kdim;
   }
   // Ndim is a multiple of 64, so a wave's 16 or 32 columns are all inside or all outside;
-  // a wave outside still stages activations and meets every barrier
+  // a wave outside streams a valid stand-in (the first columns of the expert), skips the MFMA
+  // work and the stores, and meets every barrier
   const bool wact = col0 < Ndim;
-  // activation segments this thread stages: row = seg / (KC / 8), 8 columns each
+  if (!wact) {
+    bp0 = B0 + e * estride + (size_t)r * Kdim + 8 * g;
+    bp1 = GATEUP ? B1 + e * estride + (size_t)r * Kdim + 8 * g : bp0;
+  }
+  // activation segments this thread stages: row = seg / (KC / 8), 8 columns each; a segment
+  // past the tile's last row reads row 0 (always present) and is replaced by zeros
   const uint16_t* asrc[ASEG];
   int adst[ASEG];
   bool aok[ASEG];
@@ -114,6 +120,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int nch = Kdim / KC;
+  // Workgroups start their walk over K at different chunks (rot, by column block and tile
+  // position) and wrap around, so that at any moment the weight rows being read sit at
+  // different offsets within their rows rather than all at the same one.
+  const int rot = pos % nch;
+  auto kchunk = [&](int c) { return c + rot < nch ? c + rot : c + rot - nch; };
 
   u32x4 areg[ASEG];
   bf16x8 bx[NST][KS], by[NST][KS];
@@ -124,17 +135,23 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     c1[m] = f32x4{0, 0, 0, 0};
   }
 
+  // Every global load below is issued by every lane, with no branch around it: the hardware
+  // counts outstanding loads in issue order, and a load under a lane-dependent branch makes the
+  // compiler wait for all of them at the next use.  With activations issued before the weight
+  // chunk of the same step, staging the activations waits only for themselves and the weight
+  // ring keeps NST - 1 chunks in flight across the barrier.
   auto load_a = [&](int c) {
 #pragma unroll
     for (int j = 0; j < ASEG; ++j)
-      areg[j] = aok[j] ? *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC) : zero;
+      areg[j] = *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)kchunk(c) * KC);
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < ASEG; ++j) *reinterpret_cast<u32x4*>(&As[buf][adst[j]]) = areg[j];
+    for (int j = 0; j < ASEG; ++j)
+      *reinterpret_cast<u32x4*>(&As[buf][adst[j]]) = aok[j] ? areg[j] : zero;
   };
-  auto load_b = [&](int c, bf16x8* x0, bf16x8* x1) {
-    if (!wact) return;
+  auto load_b = [&](int c_, bf16x8* x0, bf16x8* x1) {
+    const int c = kchunk(c_);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (NT) {
@@ -149,7 +166,6 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     }
   };
   auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
-    if (!wact) return;
     const uint16_t* ab = &As[buf][r * LDA + 8 * g];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -163,24 +179,32 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     }
   };
 
+  // one step: stage the activations of chunk c + 1 and fetch weight chunk c + NST - 1 into the
+  // ring slot freed by chunk c - 1, multiply chunk c, then publish chunk c + 1's activations
+  auto step = [&](int c, int u, bool next_a, bool pre_b) {
+    if (next_a) load_a(c + 1);
+    if (pre_b) load_b(c + NST - 1, bx[(u + NST - 1) % NST], by[(u + NST - 1) % NST]);
+    if (wact) compute(c & 1, bx[u], by[u]);
+    if (next_a) store_a((c + 1) & 1);
+    __syncthreads();
+  };
   load_a(0);
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < nch) load_b(st, bx[st], by[st]);
   store_a(0);
   __syncthreads();
-  for (int kb = 0; kb < nch; kb += NST) {
+  // steady state, NST steps per trip with every prefetch in range: no branch around a load
+  int kb = 0;
+  for (; kb + 2 * NST - 2 < nch; kb += NST) {
 #pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int c = kb + u;
-      if (c >= nch) break;
-      const int pre = c + NST - 1;  // weight chunk entering the ring now
-      if (pre < nch) load_b(pre, bx[(u + NST - 1) % NST], by[(u + NST - 1) % NST]);
-      if (c + 1 < nch) load_a(c + 1);
-      compute(c & 1, bx[u], by[u]);
-      if (c + 1 < nch) store_a((c + 1) & 1);
-      __syncthreads();
-    }
+    for (int u = 0; u < NST; ++u) step(kb + u, u, true, true);
+  }
+  // the last NST to 2 NST - 2 chunks (uniform conditions)
+#pragma unroll
+  for (int u = 0; u < 2 * NST - 1; ++u) {
+    const int c = kb + u;
+    if (c < nch) step(c, u % NST, c + 1 < nch, c + NST - 1 < nch);
   }
 
   if (!wact) return;

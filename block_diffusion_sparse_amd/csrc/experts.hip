@@ -13,32 +13,39 @@
 
 namespace epoch {
 
-// Tile shape of the bf16 path: kTileRows rows per tile, K in chunks of kGemmKC, kGemmStages
-// register stages of weights (kGemmStages - 1 chunks in flight).
+// Tile shape of the bf16 path: kTileRows rows per tile, K in chunks of kGemmKC, a two-stage
+// register ring of weight chunks.  Gate/up runs 4 waves (64 intermediate columns of W1 and of
+// W3 per workgroup), down 8 waves (256 output columns); both measured best for the weight
+// stream at these shapes.
 constexpr int kGemmKC = 128;
-constexpr int kGemmStages = 3;
+constexpr int kGemmStages = 2;
+constexpr int kGateUpWaves = 4;
+constexpr int kDownWaves = 8;
 // dense (shared-expert) layers of at least this many positions use the compute-bound
 // 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
 constexpr int kBigTileMinRows = 2048;
 
-// grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
+// 1-D grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
 static dim3 gemm_grid(int tiles, int Ndim, bool gateup) {
-  const int n_cb = gateup ? Ndim / 64 : (Ndim + 127) / 128;
+  const int cbw = gateup ? 16 * kGateUpWaves : 32 * kDownWaves;
+  const int n_cb = (Ndim + cbw - 1) / cbw;
   return dim3(((tiles + 7) / 8) * 8 * n_cb);
 }
 
 template <bool GATEUP, bool ROUTED>
-static void launch_gemm(dim3 grid, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
+static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
                         const uint16_t* B1, const Scratch& W, const int32_t* S_list,
                         uint16_t* out, int M, int Ndim) {
+  constexpr int WAVES = GATEUP ? kGateUpWaves : kDownWaves;
+  const dim3 grid = gemm_grid(tiles, Ndim, GATEUP), block(64 * WAVES);
   if (Kdim % kGemmKC == 0)
-    hipLaunchKernelGGL((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED>), grid,
-                       dim3(256), 0, st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs,
+    hipLaunchKernelGGL((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED, WAVES>),
+                       grid, block, 0, st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs,
                        S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
   else
-    hipLaunchKernelGGL((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED>), grid, dim3(256), 0, st,
-                       A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos,
-                       W.wl_w, out, M, Kdim, Ndim);
+    hipLaunchKernelGGL((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED, WAVES>), grid, block, 0,
+                       st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs, S_list,
+                       W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
 }
 
 // ---------------------------------------------------------------------------- fp32 variant
@@ -102,7 +109,7 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
                                 const LayerState& L, const Scratch& W, hipStream_t st) {
   dim3 grid(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols);
   if (s.bf16) {
-    launch_gemm<true, true>(gemm_grid(s.T_max, s.I, true), st, s.H, static_cast<const uint16_t*>(x),
+    launch_gemm<true, true>(s.T_max, st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
                             L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
     if (s.big_routed)  // experts with many fresh rows: compute-bound 128 x 128 tiles
@@ -123,7 +130,7 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
                               const Scratch& W, hipStream_t st) {
   if (s.bf16) {
-    launch_gemm<false, true>(gemm_grid(s.T_max, s.H, false), st, s.I, static_cast<const uint16_t*>(W.h),
+    launch_gemm<false, true>(s.T_max, st, s.I, static_cast<const uint16_t*>(W.h),
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
                              static_cast<uint16_t*>(W.y_pair), s.M, s.H);
     if (s.big_routed)
@@ -156,10 +163,10 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
                        nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                        static_cast<uint16_t*>(W.S), s.M, s.Is, s.H);
   } else if (s.bf16) {
-    launch_gemm<true, false>(gemm_grid(s.T_dense, s.Is, true), st, s.H, static_cast<const uint16_t*>(x),
+    launch_gemm<true, false>(s.T_dense, st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),
                              W, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.Is);
-    launch_gemm<false, false>(gemm_grid(s.T_dense, s.H, false), st, s.Is,
+    launch_gemm<false, false>(s.T_dense, st, s.Is,
                               static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
                               nullptr, W, nullptr, static_cast<uint16_t*>(W.S), s.M, s.H);
   } else {
