@@ -282,6 +282,10 @@ int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* w
       return EPOCH_E_HIP;
     }
   }
+  if (launch_init_scratch(s, p->lay.scratch, st) != hipSuccess) {
+    delete p;
+    return EPOCH_E_HIP;
+  }
   *out_plan = p;
   return EPOCH_OK;
 }

@@ -18,8 +18,10 @@ constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
 constexpr int kDownCols = 64;     // output columns per down workgroup
 
 // per-forward flag words (int32) in the scratch area
+// MISS and ANOMALY are raised by the router and cleared by the plan step once read (FRESH_ALL
+// keeps the anomaly decision for the placement); the rest are written by the plan step.
 enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
-       FLAG_NTILES_BIG = 5, FLAG_WORDS = 16 };
+       FLAG_NTILES_BIG = 5, FLAG_FRESH_ALL = 6, FLAG_WORDS = 16 };
 
 // Device-side view of one layer's persistent state.
 struct LayerState {
@@ -78,6 +80,7 @@ struct Shape {
 
 // launchers (stream-ordered, no host sync); each returns hipGetLastError()
 hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st);
+hipError_t launch_init_scratch(const Shape& s, const Scratch& W, hipStream_t st);
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
                          const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
                          const Scratch& W, hipStream_t st);

@@ -38,18 +38,54 @@ hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st
   return hipGetLastError();
 }
 
+// The per-forward accumulators start at zero once per plan; afterwards each forward leaves them
+// at zero for the next: the plan step clears the per-chunk counts and the router flags after
+// reading them.
+__global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_init_scratch(const Shape& s, const Scratch& W, hipStream_t st) {
+  // cnt_f, cnt_a and chunk_fresh are carved back to back
+  const int n = (int)(W.chunk_fresh + s.n_chunks - W.cnt_f);
+  hipLaunchKernelGGL(k_zero_i32, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, st, W.cnt_f, n);
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, st, W.flags, (int)FLAG_WORDS);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------- plan step
 constexpr int kPlanThreads = 1024;
 
-// Inclusive scan of v[0..n) (n <= kPlanThreads) in LDS by the whole workgroup.
-__device__ __forceinline__ void block_inclusive_scan(int32_t* v, int n) {
-  const int tid = threadIdx.x;
-  for (int off = 1; off < n; off <<= 1) {
-    const int x = (tid < n && tid >= off) ? v[tid - off] : 0;
-    __syncthreads();
-    if (tid < n) v[tid] += x;
-    __syncthreads();
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
+  return v;
+}
+
+// Inclusive scan over the workgroup, one value per thread (thread order); also returns the
+// total.  wsum is kPlanWaves ints of LDS owned by the caller; two barriers, and a third on
+// return so that wsum may be reused at once.
+__device__ __forceinline__ int block_incl_scan(int v, int32_t* wsum, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kPlanWaves ? wsum[lane] : 0;
+    w = wave_incl_scan(w);
+    if (lane < kPlanWaves) wsum[lane] = w;
+  }
+  __syncthreads();
+  const int r = inc + (wave ? wsum[wave - 1] : 0);
+  *total = wsum[kPlanWaves - 1];
+  __syncthreads();
+  return r;
 }
 
 struct SupportLds {
@@ -57,6 +93,7 @@ struct SupportLds {
   unsigned long long G[kMaxExperts];
   int32_t H[kMaxExperts];
   int32_t scan[kMaxExperts];
+  int32_t wsum[kPlanWaves];
   uint8_t inS[kMaxExperts];
   uint8_t pick[kMaxExperts];
   int nU, added;
@@ -181,22 +218,19 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
     sh.inS[ids[(size_t)t * Kext + k]] = 1;
   }
   __syncthreads();
-  // (iv) slots in expert-id order
-  for (int e = tid; e < kMaxExperts; e += kPlanThreads) sh.scan[e] = (e < E) ? sh.inS[e] : 0;
-  __syncthreads();
-  block_inclusive_scan(sh.scan, kMaxExperts);
-  for (int e = tid; e < E; e += kPlanThreads) {
-    const int incl = sh.scan[e];
-    L.inS[e] = sh.inS[e];
-    if (sh.inS[e]) {
-      L.slot_of[e] = incl - 1;
-      L.S_list[incl - 1] = e;
+  // (iv) slots in expert-id order (E <= kMaxExperts == kPlanThreads: one expert per thread)
+  int size;
+  const int incl = block_incl_scan(tid < E ? sh.inS[tid] : 0, sh.wsum, &size);
+  if (tid < E) {
+    L.inS[tid] = sh.inS[tid];
+    if (sh.inS[tid]) {
+      L.slot_of[tid] = incl - 1;
+      L.S_list[incl - 1] = tid;
     } else {
-      L.slot_of[e] = -1;
+      L.slot_of[tid] = -1;
     }
   }
   if (tid == 0) {
-    const int size = sh.scan[E - 1];
     *L.S_size = size;
     *L.S_valid = 1;
     L.counters[valid ? EPOCH_CNT_HOT_UPDATE : EPOCH_CNT_COLD] += 1;
@@ -208,19 +242,72 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
   __syncthreads();
 }
 
+// Stable placement of one chunk by one wave (teardown, FreshLane pack: fresh rows with their
+// owner positions and routing metadata in a contiguous buffer, here grouped by expert for the
+// expert kernel).  Final fresh flag = pre-anomaly test or anomaly.  Pair (t, k) of expert e
+// lands at eoffs[e] + chunk_base[chunk][e] + rank, where rank counts the chunk's earlier fresh
+// positions routed to e (a 64-bit mask per expert, in LDS, cleared by the wave beforehand).
+// Wave-level function: all 64 lanes call it; mask holds E entries owned by this wave.
+__device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int Kext,
+                                            bool anomaly, const LayerState& L, const Scratch& W,
+                                            unsigned long long* mask) {
+  const int lane = threadIdx.x & 63;
+  const int t = chunk * kChunk + lane;
+  const bool in = t < M;
+  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
+  const bool fresh = in && (anomaly || W.fpre[t] != 0);
+  if (in) L.fresh[t] = fresh ? 1 : 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int32_t* it = W.ids + (size_t)(in ? t : 0) * Kext;
+  if (fresh)
+    for (int k = 0; k < K; ++k) atomicOr(&mask[it[k]], 1ull << lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (fresh) {
+    for (int k = 0; k < K; ++k) {
+      const int e = it[k];
+      const int rank = __popcll(mask[e] & below);
+      const int p = W.eoffs[e] + W.chunk_base[(size_t)chunk * E + e] + rank;
+      W.wl_pos[p] = t;
+      W.wl_k[p] = k;
+      W.wl_w[p] = W.w[(size_t)t * K + k];
+      W.inv[(size_t)t * K + k] = p;
+    }
+  } else if (in) {
+    for (int k = 0; k < K; ++k) W.inv[(size_t)t * K + k] = -1;
+  }
+  const uint64_t fb = ballot64(fresh);
+  if (fresh) W.fresh_list[W.chunk_foff[chunk] + __popcll(fb & below)] = t;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Shapes whose placement runs inside the plan workgroup (one wave per chunk, kPlanWaves
+// chunks at a time): the per-wave masks fit in LDS and there are few chunks to walk.
+constexpr int kFusedPlaceMaxExperts = 256;
+constexpr int kFusedPlaceMaxChunks = kPlanWaves;
+
 // The plan step of one forward, one workgroup: the support check / build above, then the
 // worklist bookkeeping over the router's per-chunk counts (the fresh-pair counts, or the counts
 // of every position when a liveness anomaly makes the whole layer-iteration fresh):
 //   chunk_base[c][e] = pairs of expert e in chunks before c   (stable order inside an expert)
 //   eoffs[e]         = pairs of experts before e               (expert-major worklist)
-//   offs[s]          = eoffs of the s-th support expert; tile table of up to kTileRows pairs
+//   offs[s]          = eoffs of the s-th support expert; tile tables (kTileRows pairs per
+//                      tile, or kBigTile for experts with at least kBigRows pairs)
 //   chunk_foff[c]    = fresh positions in chunks before c      (the fresh list)
+// and, when FUSED_PLACE, the placement of every chunk.
+template <bool FUSED_PLACE>
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Scratch W) {
   __shared__ SupportLds sh;
   __shared__ int32_t part[kPlanThreads];
-  __shared__ int32_t part_b[kPlanThreads];
   __shared__ int32_t tot[kMaxExperts];
-  __shared__ int32_t carry;
+  __shared__ unsigned long long pmask[FUSED_PLACE ? kPlanWaves : 1]
+                                     [FUSED_PLACE ? kFusedPlaceMaxExperts : 1];
   const int tid = threadIdx.x;
   support_phase(s, L, W, sh);
   __syncthreads();
@@ -254,24 +341,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
     for (int c = c0; c < c1; ++c) {
       W.chunk_base[(size_t)c * E + e] = run;
       run += cnt[(size_t)c * E + e];
+      W.cnt_f[(size_t)c * E + e] = 0;  // consumed: clear for the next forward
+      W.cnt_a[(size_t)c * E + e] = 0;
     }
   }
   __syncthreads();
-  // expert offsets: exclusive scan of the totals
-  for (int i = tid; i < kMaxExperts; i += kPlanThreads) sh.scan[i] = (i < E) ? tot[i] : 0;
-  __syncthreads();
-  block_inclusive_scan(sh.scan, kMaxExperts);
-  const int P = sh.scan[kMaxExperts - 1];
-  for (int i = tid; i < E; i += kPlanThreads) W.eoffs[i] = sh.scan[i] - tot[i];
+  // expert offsets: exclusive scan of the totals (one expert per thread)
+  const int my_tot = tid < E ? tot[tid] : 0;
+  int P;
+  const int eincl = block_incl_scan(my_tot, sh.wsum, &P);
+  sh.scan[tid] = eincl - my_tot;
+  if (tid < E) W.eoffs[tid] = eincl - my_tot;
   if (tid == 0) W.eoffs[E] = P;
-  // slot offsets and the tile table
+  __syncthreads();
+  // slot offsets and the tile tables (one support slot per thread); an expert with at least
+  // kBigRows pairs goes to the compute-bound table when the shape enables it
   const int nS = *L.S_size;
-  // an expert with at least kBigRows pairs goes to the compute-bound table (kBigTile rows per
-  // tile) when the shape enables it, every other expert to the weight-stream table
   int my_tiles = 0, my_big = 0, my_off = 0;
   if (tid < nS) {
     const int ex = L.S_list[tid];
-    my_off = sh.scan[ex] - tot[ex];
+    my_off = sh.scan[ex];
     if (s.big_routed && tot[ex] >= kBigRows)
       my_big = (tot[ex] + kBigTile - 1) / kBigTile;
     else
@@ -279,41 +368,33 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
     W.offs[tid] = my_off;
   }
   if (tid == 0) W.offs[nS] = P;
-  __syncthreads();
-  part[tid] = my_tiles;
-  part_b[tid] = my_big;
-  __syncthreads();
-  block_inclusive_scan(part, kPlanThreads);
-  block_inclusive_scan(part_b, kPlanThreads);
-  const int T = part[kPlanThreads - 1];
-  const int Tb = part_b[kPlanThreads - 1];
+  int T, Tb;
+  const int tincl = block_incl_scan(my_tiles, sh.wsum, &T);
+  const int bincl = s.big_routed ? block_incl_scan(my_big, sh.wsum, &Tb) : (Tb = 0, 0);
   if (tid < nS) {
-    const int t0 = part[tid] - my_tiles;
+    const int t0 = tincl - my_tiles;
     for (int i = 0; i < my_tiles; ++i) {
       W.tile_slot[t0 + i] = tid;
       W.tile_row0[t0 + i] = my_off + i * kTileRows;
     }
-    const int b0 = part_b[tid] - my_big;
+    const int b0 = bincl - my_big;
     for (int i = 0; i < my_big; ++i) {
       W.tile_slot_b[b0 + i] = tid;
       W.tile_row0_b[b0 + i] = my_off + i * kBigTile;
     }
   }
-  __syncthreads();
-  // fresh-list offsets of the chunks, in passes of kPlanThreads chunks
-  if (tid == 0) carry = 0;
-  __syncthreads();
+  // fresh-list offsets of the chunks, kPlanThreads chunks per pass
+  int carry = 0;
   for (int base = 0; base < nch; base += kPlanThreads) {
     const int c = base + tid;
-    int nf = 0;
-    if (c < nch) nf = anomaly ? min(kChunk, s.M - c * kChunk) : W.chunk_fresh[c];
-    part[tid] = nf;
-    __syncthreads();
-    block_inclusive_scan(part, kPlanThreads);
-    if (c < nch) W.chunk_foff[c] = carry + part[tid] - nf;
-    __syncthreads();
-    if (tid == 0) carry += part[kPlanThreads - 1];
-    __syncthreads();
+    const int nf = c < nch ? (anomaly ? min(kChunk, s.M - c * kChunk) : W.chunk_fresh[c]) : 0;
+    int pass;
+    const int incl = block_incl_scan(nf, sh.wsum, &pass);
+    if (c < nch) {
+      W.chunk_foff[c] = carry + incl - nf;
+      W.chunk_fresh[c] = 0;
+    }
+    carry += pass;
   }
   if (tid == 0) {
     const int nfresh = carry;
@@ -328,57 +409,46 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
     L.counters[EPOCH_CNT_TOUCHED] += touched;
     L.counters[EPOCH_CNT_FORWARDS] += 1;
     if (anomaly) L.counters[EPOCH_CNT_ANOMALY] += 1;
+    // every thread read MISS and ANOMALY before the barriers above
+    W.flags[FLAG_FRESH_ALL] = anomaly ? 1 : 0;
+    W.flags[FLAG_MISS] = 0;
+    W.flags[FLAG_ANOMALY] = 0;
+  }
+  if (FUSED_PLACE) {
+    // chunk_base, eoffs and chunk_foff were written above by this workgroup
+    __syncthreads();
+    const int wave = tid >> 6;
+    for (int chunk = wave; chunk < nch; chunk += kPlanWaves)
+      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, L, W, pmask[wave]);
   }
 }
 
-hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------- placement
-// Stable placement (teardown, FreshLane pack: fresh rows with their owner positions and
-// routing metadata in a contiguous buffer, here grouped by expert for the expert kernel).
-// Final fresh flag = pre-anomaly test or anomaly.  Pair (t, k) of expert e lands at
-// eoffs[e] + chunk_base[chunk][e] + rank, where rank counts the chunk's earlier fresh
-// positions routed to e (a 64-bit mask per expert per chunk).  One wave per chunk.
+// Placement as its own kernel (shapes with many chunks or experts): one wave per chunk.
 __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, int n_chunks,
                                                LayerState L, Scratch W) {
   __shared__ unsigned long long mask[4][kMaxExperts];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x * 4 + wave;
-  const int t = chunk * kChunk + lane;
-  const bool in = chunk < n_chunks && t < M;
-  for (int e = lane; e < E; e += 64) mask[wave][e] = 0ull;
-  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
-  const bool fresh = in && (anomaly || W.fpre[t] != 0);
-  if (in) L.fresh[t] = fresh ? 1 : 0;
-  __syncthreads();
-  const int32_t* it = W.ids + (size_t)(in ? t : 0) * Kext;
-  if (fresh)
-    for (int k = 0; k < K; ++k) atomicOr(&mask[wave][it[k]], 1ull << lane);
-  __syncthreads();
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (fresh) {
-    for (int k = 0; k < K; ++k) {
-      const int e = it[k];
-      const int rank = __popcll(mask[wave][e] & below);
-      const int p = W.eoffs[e] + W.chunk_base[(size_t)chunk * E + e] + rank;
-      W.wl_pos[p] = t;
-      W.wl_k[p] = k;
-      W.wl_w[p] = W.w[(size_t)t * K + k];
-      W.inv[(size_t)t * K + k] = p;
-    }
-  } else if (in) {
-    for (int k = 0; k < K; ++k) W.inv[(size_t)t * K + k] = -1;
-  }
-  const uint64_t fb = ballot64(fresh);
-  if (fresh) W.fresh_list[W.chunk_foff[chunk] + __popcll(fb & below)] = t;
+  if (chunk >= n_chunks) return;
+  place_chunk(chunk, M, E, K, Kext, W.flags[FLAG_FRESH_ALL] != 0, L, W, mask[wave]);
+}
+
+static bool fused_place(const Shape& s) {
+  return s.E <= kFusedPlaceMaxExperts && s.n_chunks <= kFusedPlaceMaxChunks;
+}
+
+hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
+  if (fused_place(s))
+    hipLaunchKernelGGL(k_plan<true>, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
+  else
+    hipLaunchKernelGGL(k_plan<false>, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
+  return hipGetLastError();
 }
 
 hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
-  hipLaunchKernelGGL(k_place, dim3((s.n_chunks + 3) / 4), dim3(256), 0, st, s.M, s.E, s.K, s.Kext,
-                     s.n_chunks, L, W);
+  if (!fused_place(s))
+    hipLaunchKernelGGL(k_place, dim3((s.n_chunks + 3) / 4), dim3(256), 0, st, s.M, s.E, s.K,
+                       s.Kext, s.n_chunks, L, W);
   return hipGetLastError();
 }
 

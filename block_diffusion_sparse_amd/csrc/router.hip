@@ -48,95 +48,6 @@ struct RouterRaw<float> {
   }
 };
 
-template <typename T, int BT>
-__global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(const T* __restrict__ x,
-                                                 const float* __restrict__ Wg,
-                                                 const float* __restrict__ bias,
-                                                 float* __restrict__ G, int M, int H, int E,
-                                                 int ksplit, int32_t* __restrict__ flags,
-                                                 int32_t* __restrict__ zero_buf, int n_zero) {
-  constexpr int NB = BT / 16;
-  extern __shared__ double red[];  // [ksplit][BT * BT]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < FLAG_WORDS)
-    flags[threadIdx.x] = 0;  // per-forward flags start clear; later kernels of this forward set them
-  {  // the next kernel accumulates per-chunk counts with atomics: clear them here
-    const size_t gid = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t nthreads = (size_t)gridDim.x * gridDim.y * blockDim.x;
-    for (size_t i = gid; i < (size_t)n_zero; i += nthreads) zero_buf[i] = 0;
-  }
-  const int e0 = blockIdx.x * BT, t0 = blockIdx.y * BT;
-  const int klen = H / ksplit, kbeg = wave * klen;
-  const int nsteps = klen / 64;
-  const int r = lane & 15, g = lane >> 4;
-  const T* xr[NB];
-  const float* wr[NB];
-  bool vx[NB], vw[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int t = t0 + 16 * b + r, e = e0 + 16 * b + r;
-    vx[b] = t < M;
-    vw[b] = e < E;
-    xr[b] = x + (size_t)(vx[b] ? t : 0) * H + kbeg + 16 * g;
-    wr[b] = Wg + (size_t)(vw[b] ? e : 0) * H + kbeg + 16 * g;
-  }
-  f64x4 acc[NB][NB];
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
-  RouterRaw<T> xa[2][NB];
-  RouterRaw<float> wa[2][NB];
-  auto load = [&](int step, int buf) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      xa[buf][b].load(xr[b] + 64 * step, vx[b]);
-      wa[buf][b].load(wr[b] + 64 * step, vw[b]);
-    }
-  };
-  auto mma = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      double A[NB], B[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        A[b] = xa[buf][b].get(m);
-        B[b] = wa[buf][b].get(m);
-      }
-#pragma unroll
-      for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[a], B[b], acc[a][b], 0, 0, 0);
-    }
-  };
-  load(0, 0);
-  for (int st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) load(st + 1, 1);
-    mma(0);
-    if (st + 1 >= nsteps) break;
-    if (st + 2 < nsteps) load(st + 2, 0);
-    mma(1);
-  }
-  // f64 16x16x4 output layout: D[i][j] sits in lane (j + 16 * (i % 4)), register i / 4
-  double* mine = red + (size_t)wave * BT * BT;
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mine[(16 * a + 4 * i + g) * BT + 16 * b + r] = acc[a][b][i];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < BT * BT; idx += blockDim.x) {
-    const int t = t0 + idx / BT, e = e0 + idx % BT;
-    if (t >= M || e >= E) continue;
-    double s = 0.0;
-    for (int w = 0; w < ksplit; ++w) s += red[(size_t)w * BT * BT + idx];
-    if (bias) s += (double)bias[e];
-    G[(size_t)t * E + e] = (float)s;
-  }
-}
-
 // ---------------------------------------------------------------------------- top-k + fresh inputs
 // One wave per position.  Per position: the K_ext candidates in key order (logit desc, expert
 // id asc), the gate scores in double (softmax over all E, or sigmoid), the routing weights of
@@ -151,6 +62,15 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(const T* __res
 // the fp32 logit above the inverted expert id, so "larger key" is exactly the key order
 // above.  A bitwise radix search with wave ballots finds the K_ext-th largest key; the K_ext
 // keys at or above it are ranked by comparing against each other (a readlane loop).
+// Everything the top-k of a position reads besides the logits.
+struct RouteArgs {
+  LayerState L;
+  Scratch W;
+  const uint8_t* D;
+  const uint8_t* force;
+  int E, K, Kext, gate_sigmoid, norm_topk, R, iter;
+};
+
 __device__ __forceinline__ uint64_t sel_key(float g, int e) {
   uint32_t u = __float_as_uint(g);
   if (u == 0x80000000u) u = 0u;  // -0 and +0 compare equal as floats: one key for both
@@ -159,14 +79,15 @@ __device__ __forceinline__ uint64_t sel_key(float g, int e) {
 }
 
 template <int NPER>
-__global__ __launch_bounds__(256) void k_route_rows(
-    const float* __restrict__ G, const uint8_t* __restrict__ D, const uint8_t* __restrict__ force,
-    LayerState L, Scratch W, int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, int R,
-    int iter) {
-  __shared__ double s_buf[4][kMaxKext];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= M) return;
+__device__ __forceinline__ void route_row(int t, const float* __restrict__ G, const RouteArgs& ra,
+                                          double* s_buf) {
+  const LayerState& L = ra.L;
+  const Scratch& W = ra.W;
+  const uint8_t* __restrict__ D = ra.D;
+  const uint8_t* __restrict__ force = ra.force;
+  const int E = ra.E, K = ra.K, Kext = ra.Kext, gate_sigmoid = ra.gate_sigmoid;
+  const int norm_topk = ra.norm_topk, R = ra.R, iter = ra.iter;
+  const int lane = threadIdx.x & 63;
   // prologue: every global read of the position at once
   float gv[NPER];
   uint8_t in_s[NPER];
@@ -242,7 +163,7 @@ __global__ __launch_bounds__(256) void k_route_rows(
     W.ids[(size_t)t * Kext + rk] = e;
     W.scores[(size_t)t * Kext + rk] = (float)sc;
     W.q[(size_t)t * Kext + rk] = (int32_t)floor(sc * 65536.0 + 0.5);
-    s_buf[wave][rk] = sc;
+    s_buf[rk] = sc;
     if (rk < K) {
       miss |= s_valid && !in_s[j];
       atomicAdd(&W.cnt_a[chunk * E + e], 1);
@@ -255,8 +176,8 @@ __global__ __launch_bounds__(256) void k_route_rows(
   if (lane < K) {
     double denom = 0.0;
     if (norm_topk)
-      for (int k = 0; k < K; ++k) denom += s_buf[wave][k];  // rank order
-    const double sk = s_buf[wave][lane];
+      for (int k = 0; k < K; ++k) denom += s_buf[k];  // rank order
+    const double sk = s_buf[lane];
     W.w[(size_t)t * K + lane] = (float)(norm_topk ? sk / denom : sk);
   }
   if (ballot64(miss) != 0 && lane == 0) W.flags[FLAG_MISS] = 1;
@@ -270,35 +191,125 @@ __global__ __launch_bounds__(256) void k_route_rows(
   }
 }
 
+// The top-k as its own kernel: one wave per position.
+template <int NPER>
+__global__ __launch_bounds__(256) void k_route_rows(const float* __restrict__ G, RouteArgs ra,
+                                                    int M) {
+  __shared__ double s_buf[4][kMaxKext];
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t < M) route_row<NPER>(t, G, ra, s_buf[wave]);
+}
+
+template <typename T, int BT>
+__global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
+    const T* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bias,
+    float* __restrict__ G, int M, int H, int E, int ksplit) {
+  constexpr int NB = BT / 16;
+  extern __shared__ double red[];  // [ksplit][BT * BT]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e0 = blockIdx.x * BT, t0 = blockIdx.y * BT;
+  const int klen = H / ksplit, kbeg = wave * klen;
+  const int nsteps = klen / 64;
+  const int r = lane & 15, g = lane >> 4;
+  const T* xr[NB];
+  const float* wr[NB];
+  bool vx[NB], vw[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int t = t0 + 16 * b + r, e = e0 + 16 * b + r;
+    vx[b] = t < M;
+    vw[b] = e < E;
+    xr[b] = x + (size_t)(vx[b] ? t : 0) * H + kbeg + 16 * g;
+    wr[b] = Wg + (size_t)(vw[b] ? e : 0) * H + kbeg + 16 * g;
+  }
+  f64x4 acc[NB][NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
+  RouterRaw<T> xa[2][NB];
+  RouterRaw<float> wa[2][NB];
+  auto load = [&](int step, int buf) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      xa[buf][b].load(xr[b] + 64 * step, vx[b]);
+      wa[buf][b].load(wr[b] + 64 * step, vw[b]);
+    }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      double A[NB], B[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        A[b] = xa[buf][b].get(m);
+        B[b] = wa[buf][b].get(m);
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[a], B[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) load(st + 1, 1);
+    mma(0);
+    if (st + 1 >= nsteps) break;
+    if (st + 2 < nsteps) load(st + 2, 0);
+    mma(1);
+  }
+  // f64 16x16x4 output layout: D[i][j] sits in lane (j + 16 * (i % 4)), register i / 4
+  double* mine = red + (size_t)wave * BT * BT;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[(16 * a + 4 * i + g) * BT + 16 * b + r] = acc[a][b][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < BT * BT; idx += blockDim.x) {
+    const int t = t0 + idx / BT, e = e0 + idx % BT;
+    if (t >= M || e >= E) continue;
+    double s = 0.0;
+    for (int w = 0; w < ksplit; ++w) s += red[(size_t)w * BT * BT + idx];
+    if (bias) s += (double)bias[e];
+    G[(size_t)t * E + e] = (float)s;
+  }
+}
+
+template <typename T, int BT>
+static void launch_k_router(const Shape& s, const void* x, const float* Wg, const float* bias,
+                            const Scratch& W, hipStream_t st) {
+  const size_t lds = (size_t)s.ksplit * BT * BT * sizeof(double);
+  const dim3 grid((s.E + BT - 1) / BT, (s.M + BT - 1) / BT), block(64 * s.ksplit);
+  hipLaunchKernelGGL((k_router<T, BT>), grid, block, lds, st, static_cast<const T*>(x), Wg, bias,
+                     W.G, s.M, s.H, s.E, s.ksplit);
+}
+
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
                          const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
                          const Scratch& W, hipStream_t st) {
-  const size_t lds = (size_t)s.ksplit * s.router_bt * s.router_bt * sizeof(double);
-  // cnt_f, cnt_a and chunk_fresh are carved back to back (one zeroing range)
-  const int nz = (int)(W.chunk_fresh + s.n_chunks - W.cnt_f);
-  dim3 grid((s.E + s.router_bt - 1) / s.router_bt, (s.M + s.router_bt - 1) / s.router_bt);
-  dim3 block(64 * s.ksplit);
+  // The logits go through memory between the two kernels.  Handing a row group's logits to its
+  // last-finishing tile inside one kernel needs a device-scope release / acquire per workgroup,
+  // which on this chip writes back the XCD's L2 each time: slower than the second launch.
   if (s.router_bt == 32) {
     if (s.bf16)
-      hipLaunchKernelGGL((k_router<uint16_t, 32>), grid, block, lds, st,
-                         static_cast<const uint16_t*>(x), Wg, bias, W.G, s.M, s.H, s.E, s.ksplit,
-                         W.flags, W.cnt_f, nz);
+      launch_k_router<uint16_t, 32>(s, x, Wg, bias, W, st);
     else
-      hipLaunchKernelGGL((k_router<float, 32>), grid, block, lds, st, static_cast<const float*>(x),
-                         Wg, bias, W.G, s.M, s.H, s.E, s.ksplit, W.flags, W.cnt_f, nz);
+      launch_k_router<float, 32>(s, x, Wg, bias, W, st);
   } else {
     if (s.bf16)
-      hipLaunchKernelGGL((k_router<uint16_t, 16>), grid, block, lds, st,
-                         static_cast<const uint16_t*>(x), Wg, bias, W.G, s.M, s.H, s.E, s.ksplit,
-                         W.flags, W.cnt_f, nz);
+      launch_k_router<uint16_t, 16>(s, x, Wg, bias, W, st);
     else
-      hipLaunchKernelGGL((k_router<float, 16>), grid, block, lds, st, static_cast<const float*>(x),
-                         Wg, bias, W.G, s.M, s.H, s.E, s.ksplit, W.flags, W.cnt_f, nz);
+      launch_k_router<float, 16>(s, x, Wg, bias, W, st);
   }
+  const RouteArgs ra{L, W, D, force, s.E, s.K, s.Kext, s.gate_sigmoid, s.norm_topk, s.R, iter};
   const int nper = (s.E + 63) / 64;
-#define EPOCH_ROUTE_ROWS(NP)                                                                     \
-  hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, D, force, L, \
-                     W, s.M, s.E, s.K, s.Kext, s.gate_sigmoid, s.norm_topk, s.R, iter)
+#define EPOCH_ROUTE_ROWS(NP) \
+  hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
   if (nper <= 1)
     EPOCH_ROUTE_ROWS(1);
   else if (nper <= 2)
