@@ -107,6 +107,44 @@ def support_build(ids, q, E, K, B, c, alpha, qfrac, beta, lib=None):
     return inS, slot_of, S_list[:n].copy(), stats
 
 
+def atlas_build(ids, q, E, K, B, c, alpha, qfrac, beta, lib=None):
+    """The Atlas support without the closure over routed experts (restricted routing)."""
+    lib = lib or load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.int64)
+    M, Kext = ids.shape
+    inA = np.zeros(E, dtype=np.uint8)
+    slot_of = np.empty(E, dtype=np.int32)
+    S_list = np.empty(E, dtype=np.int32)
+    stats = np.zeros(5, dtype=np.int64)
+    n = lib.orc_atlas_build(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _p(ids), _p(q),
+                            _c_int(B), _c_int(c), _c_int(alpha[0]), _c_int(alpha[1]),
+                            _c_int(qfrac[0]), _c_int(qfrac[1]), _c_int(beta[0]),
+                            _c_int(beta[1]), _p(inA), _p(slot_of), _p(S_list), _p(stats))
+    return inA, slot_of, S_list[:n].copy(), stats
+
+
+def route_restricted(G, K, inA, gate_sigmoid, norm_topk, lib=None):
+    """Top-K inside the support mask inA: ids [M, K] int32 and weights [M, K] double."""
+    lib = lib or load()
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    M, E = G.shape
+    rids = np.empty((M, K), dtype=np.int32)
+    rw = np.empty((M, K), dtype=np.float64)
+    lib.orc_route_restricted(_c_int(M), _c_int(E), _c_int(K), _c_int(int(gate_sigmoid)),
+                             _c_int(int(norm_topk)), _p(G),
+                             _p(np.ascontiguousarray(inA, dtype=np.uint8)), _p(rids), _p(rw))
+    return rids, rw
+
+
+def slots_of(mask):
+    """Slots in expert-id order of the experts with mask = 1: (slot_of, S_list)."""
+    S_list = np.flatnonzero(np.asarray(mask)).astype(np.int32)
+    slot_of = np.full(len(mask), -1, dtype=np.int32)
+    slot_of[S_list] = np.arange(len(S_list), dtype=np.int32)
+    return slot_of, S_list
+
+
 def under_covered(ids, q, K, inS, alpha, lib=None) -> int:
     lib = lib or load()
     M, Kext = ids.shape
@@ -137,6 +175,7 @@ def worklist(ids, w, K, fresh, slot_of, nS, lib=None) -> dict:
     P = lib.orc_worklist(_c_int(M), _c_int(K), _c_int(Kext), _p(ids), _p(w), _p(fresh),
                          _p(slot_of), _c_int(nS), _p(wl_pos), _p(wl_k), _p(wl_w), _p(offs),
                          _p(inv))
+    assert P >= 0, "a routed expert of a fresh position has no slot in the support"
     return dict(P=P, wl_pos=wl_pos[:P].copy(), wl_k=wl_k[:P].copy(), wl_w=wl_w[:P].copy(),
                 offs=offs, inv=inv.reshape(M, K))
 
@@ -196,8 +235,12 @@ class OracleLayer:
         self.support_valid = False
         self.iter = 0
         self.counters = dict(cold=0, hot_update=0, hot_skip=0, anomalies=0, fresh_rows=0,
-                             pairs=0, coverage_unmet=0)
+                             pairs=0, coverage_unmet=0, restricted=0, coverage_fallback=0,
+                             period_update=0)
         self._pending = None
+        # restricted routing: the Atlas support (no closure) and the iteration it was built at
+        self.inA = np.zeros(E, dtype=np.uint8)
+        self.built_iter = 0
 
     def forward(self, x, D, force=None) -> dict:
         w, lib = self.w, self.lib
@@ -205,20 +248,24 @@ class OracleLayer:
         W = self.W
         G = router_logits(x, W["router_w"], W["router_b"], lib=lib)
         ids, s, wts, q = route(G, K, Kext, w.gate == "sigmoid", w.norm_topk, lib=lib)
-        path = support_status(ids, K, self.inS, self.support_valid, lib=lib)
         stats = None
-        if path:
-            self.inS, self.slot_of, self.S_list, stats = support_build(
-                ids, q, E, K, w.B, w.c, w.alpha, w.q, w.beta, lib=lib)
-            self.support_valid = True
-            self.counters["cold" if path == 1 else "hot_update"] += 1
-            if stats[2]:
-                self.counters["coverage_unmet"] += 1
+        if w.routing == "restricted":
+            path, stats, rids, rw = self._restricted_step(G, ids, q, wts)
         else:
-            self.counters["hot_skip"] += 1
+            path = support_status(ids, K, self.inS, self.support_valid, lib=lib)
+            if path:
+                self.inS, self.slot_of, self.S_list, stats = support_build(
+                    ids, q, E, K, w.B, w.c, w.alpha, w.q, w.beta, lib=lib)
+                self.support_valid = True
+                self.counters["cold" if path == 1 else "hot_update"] += 1
+                if stats[2]:
+                    self.counters["coverage_unmet"] += 1
+            else:
+                self.counters["hot_skip"] += 1
+            rids, rw = np.ascontiguousarray(ids[:, :K]), wts
         fresh, anomaly = fresh_set(w.staleness_R, self.iter, self.valid, self.last_fresh,
                                    self.prev_D, D, force, lib=lib)
-        wl = worklist(ids, wts, K, fresh, self.slot_of, len(self.S_list), lib=lib)
+        wl = worklist(rids, rw, K, fresh, self.slot_of, len(self.S_list), lib=lib)
         H, I = w.hidden, w.inter
         Is = w.shared_inter if W.get("sw1") is not None else 0
         rows = self.rows
@@ -226,15 +273,64 @@ class OracleLayer:
         Y = np.empty((len(rows), H), dtype=np.float64)
         x = np.ascontiguousarray(x)
         lib.orc_moe_rows(_c_int(w.M), _c_int(H), _c_int(I), _c_int(Is), _c_int(E), _c_int(K),
-                         _c_int(Kext), _c_int(_is_bf16(x)), _p(x), _p(ids), _p(wts), _p(fresh),
+                         _c_int(K), _c_int(_is_bf16(x)), _p(x), _p(rids), _p(rw), _p(fresh),
                          _p(W["w1"]), _p(W["w3"]), _p(W["w2"]), _p(W.get("sw1")),
                          _p(W.get("sw3")), _p(W.get("sw2")), _c_int(len(rows)), _p(rows),
                          _p(self.cache), _p(R), _p(Y))
         self._pending = (fresh, np.ascontiguousarray(D, dtype=np.uint8).copy(), anomaly)
         return dict(G=G, ids=ids, s=s, w=wts, q=q, path=path, support_stats=stats,
+                    routed_ids=rids, routed_w=rw, inA=self.inA.copy(),
                     inS=self.inS.copy(), slot_of=self.slot_of.copy(), S_list=self.S_list.copy(),
                     fresh=fresh, anomaly=anomaly, worklist=wl, rows=rows, R=R, Y=Y,
                     iter=self.iter)
+
+    def _restricted_step(self, G, ids, q, wts):
+        """Support lifecycle and routing of one forward under support-restricted routing.
+
+        Teardown, Expert Atlas (third step) and the block-plan lifecycle: the hot path keeps
+        the support mask and picks each position's top-K inside it (hot-skip); the support is
+        rebuilt from the current candidates (all-expert top-K_ext, recomputed every
+        iteration) at the block's first forward (cold), when its update period has run out,
+        or when the current candidates show that it no longer meets the coverage goal
+        |U| <= (1 - q) M (or holds fewer than K experts) -- hot-update.  A forward that
+        (re)builds the support routes over all experts (the full path) and gives every
+        routed expert a slot for that forward only; the stored support has no closure.
+        """
+        w, lib = self.w, self.lib
+        K, E = w.top_k, w.n_experts
+        stats = None
+        if not self.support_valid:
+            path = 1
+        elif w.atlas_period > 0 and self.iter - self.built_iter >= w.atlas_period:
+            path = 2
+            self.counters["period_update"] += 1
+        else:
+            nU = under_covered(ids, q, K, self.inA, w.alpha, lib=lib)
+            short = int(self.inA.sum()) < K
+            if short or w.q[1] * nU > (w.q[1] - w.q[0]) * w.M:
+                path = 2
+                self.counters["coverage_fallback"] += 1
+            else:
+                path = 0
+        if path:
+            self.inA, _, _, stats = atlas_build(ids, q, E, K, w.B, w.c, w.alpha, w.q, w.beta,
+                                                lib=lib)
+            self.support_valid = True
+            self.built_iter = self.iter
+            self.counters["cold" if path == 1 else "hot_update"] += 1
+            if stats[2]:
+                self.counters["coverage_unmet"] += 1
+            rids, rw = np.ascontiguousarray(ids[:, :K]), wts
+            mask = self.inA.copy()
+            mask[rids.ravel()] = 1
+        else:
+            self.counters["hot_skip"] += 1
+            self.counters["restricted"] += 1
+            rids, rw = route_restricted(G, K, self.inA, w.gate == "sigmoid", w.norm_topk, lib=lib)
+            mask = self.inA
+        self.inS = np.ascontiguousarray(mask, dtype=np.uint8).copy()
+        self.slot_of, self.S_list = slots_of(self.inS)
+        return path, stats, rids, rw
 
     def commit(self):
         assert self._pending is not None, "commit without a forward"

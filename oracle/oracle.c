@@ -193,10 +193,10 @@ int64_t orc_under_covered(int M, int K, int Kext, const int32_t* ids, const int6
  * stats: [0] final |U| (before closure), [1] repair rounds, [2] coverage unmet,
  *        [3] initial size, [4] size before closure.  Returns |S|.
  */
-int orc_support_build(int M, int E, int K, int Kext, const int32_t* ids, const int64_t* q, int B,
-                      int c, int alpha_num, int alpha_den, int q_num, int q_den, int beta_num,
-                      int beta_den, uint8_t* inS, int32_t* slot_of, int32_t* S_list,
-                      int64_t* stats) {
+static int support_build(int M, int E, int K, int Kext, const int32_t* ids, const int64_t* q,
+                         int B, int c, int alpha_num, int alpha_den, int q_num, int q_den,
+                         int beta_num, int beta_den, int closure, uint8_t* inS, int32_t* slot_of,
+                         int32_t* S_list, int64_t* stats) {
   const int64_t an = alpha_num, ad = alpha_den, qn = q_num, qd = q_den;
   const int64_t bn = beta_num, bd = beta_den;
   int64_t* p = (int64_t*)calloc((size_t)E, sizeof(int64_t));
@@ -270,8 +270,9 @@ int orc_support_build(int M, int E, int K, int Kext, const int32_t* ids, const i
   for (int e = 0; e < E; ++e) size_before += inS[e];
 
   /* (iii) closure over the current top-K selections */
-  for (int t = 0; t < M; ++t)
-    for (int k = 0; k < K; ++k) inS[ids[(size_t)t * Kext + k]] = 1;
+  if (closure)
+    for (int t = 0; t < M; ++t)
+      for (int k = 0; k < K; ++k) inS[ids[(size_t)t * Kext + k]] = 1;
 
   /* (iv) slots in expert-id order */
   int n = 0;
@@ -299,6 +300,67 @@ int orc_support_build(int M, int E, int K, int Kext, const int32_t* ids, const i
   free(R);
   free(C);
   return n;
+}
+
+/* The support with the closure (iii): routing over all experts (the exact mode). */
+int orc_support_build(int M, int E, int K, int Kext, const int32_t* ids, const int64_t* q, int B,
+                      int c, int alpha_num, int alpha_den, int q_num, int q_den, int beta_num,
+                      int beta_den, uint8_t* inS, int32_t* slot_of, int32_t* S_list,
+                      int64_t* stats) {
+  return support_build(M, E, K, Kext, ids, q, B, c, alpha_num, alpha_den, q_num, q_den, beta_num,
+                       beta_den, 1, inS, slot_of, S_list, stats);
+}
+
+/*
+ * The Atlas support alone, steps (i), (ii) and (iv) without the closure: the set of
+ * selectable experts of support-restricted routing ([T] Expert Atlas, third step: the hot
+ * path keeps the support mask and selects each position's experts inside it).
+ */
+int orc_atlas_build(int M, int E, int K, int Kext, const int32_t* ids, const int64_t* q, int B,
+                    int c, int alpha_num, int alpha_den, int q_num, int q_den, int beta_num,
+                    int beta_den, uint8_t* inA, int32_t* slot_of, int32_t* S_list,
+                    int64_t* stats) {
+  return support_build(M, E, K, Kext, ids, q, B, c, alpha_num, alpha_den, q_num, q_den, beta_num,
+                       beta_den, 0, inA, slot_of, S_list, stats);
+}
+
+/*
+ * Support-restricted top-K ([T] Expert Atlas, third step): the same selection rule as
+ * orc_route (key: logit desc, expert id asc) over the experts e with inA[e] = 1 only; the
+ * gate score of a selected expert keeps its definition over all E experts (softmax over
+ * all E, or sigmoid); the weights are the selected scores, normalised over the K selected
+ * when norm_topk.  Needs at least K experts in the support.  rids, rw: [M x K].
+ */
+void orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
+                          const uint8_t* inA, int32_t* rids, double* rw) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < M; ++t) {
+    const float* g = G + (size_t)t * E;
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    double zmax = -INFINITY, z = 0.0;
+    if (!gate_sigmoid) {
+      for (int e = 0; e < E; ++e) zmax = fmax(zmax, (double)g[e]);
+      for (int e = 0; e < E; ++e) z += exp((double)g[e] - zmax);
+    }
+    double sk[64];
+    for (int k = 0; k < K; ++k) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+#if ORC_MUTATE == 8
+        if (!taken[e] && (best < 0 || before(g[e], e, g[best], best))) best = e;
+#else
+        if (inA[e] && !taken[e] && (best < 0 || before(g[e], e, g[best], best))) best = e;
+#endif
+      taken[best] = 1;
+      rids[(size_t)t * K + k] = best;
+      const double ge = (double)g[best];
+      sk[k] = gate_sigmoid ? 1.0 / (1.0 + exp(-ge)) : exp(ge - zmax) / z;
+    }
+    free(taken);
+    double denom = 0.0;
+    for (int k = 0; k < K; ++k) denom += sk[k];
+    for (int k = 0; k < K; ++k) rw[(size_t)t * K + k] = norm_topk ? sk[k] / denom : sk[k];
+  }
 }
 
 /*
@@ -340,6 +402,14 @@ int orc_fresh_set(int M, int R, int iter, const uint8_t* valid, const int32_t* l
 int orc_worklist(int M, int K, int Kext, const int32_t* ids, const double* w,
                  const uint8_t* fresh, const int32_t* slot_of, int nS, int32_t* wl_pos,
                  int32_t* wl_k, double* wl_w, int32_t* offs, int32_t* inv) {
+  /* every routed expert of a fresh position needs a slot (the support covers every
+     selected expert); -1 reports a selection outside the slot set */
+  for (int t = 0; t < M; ++t)
+    if (fresh[t])
+      for (int k = 0; k < K; ++k) {
+        const int e = ids[(size_t)t * Kext + k];
+        if (slot_of[e] < 0 || slot_of[e] >= nS) return -1;
+      }
   int32_t* cursor = (int32_t*)calloc((size_t)(nS > 0 ? nS : 1), sizeof(int32_t));
   for (int s = 0; s <= nS; ++s) offs[s] = 0;
   for (int t = 0; t < M; ++t)

@@ -38,12 +38,21 @@ int orc_support_build(int M, int E, int K, int Kext, const int32_t* ids, const i
                       int beta_den, uint8_t* inS, int32_t* slot_of, int32_t* S_list,
                       int64_t* stats);
 
+int orc_atlas_build(int M, int E, int K, int Kext, const int32_t* ids, const int64_t* q, int B,
+                    int c, int alpha_num, int alpha_den, int q_num, int q_den, int beta_num,
+                    int beta_den, uint8_t* inA, int32_t* slot_of, int32_t* S_list,
+                    int64_t* stats);
+
+void orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
+                          const uint8_t* inA, int32_t* rids, double* rw);
+
 int64_t orc_under_covered(int M, int K, int Kext, const int32_t* ids, const int64_t* q,
                           const uint8_t* inS, int alpha_num, int alpha_den);
 
 int orc_fresh_set(int M, int R, int iter, const uint8_t* valid, const int32_t* last_fresh,
                   const uint8_t* prev_D, const uint8_t* D, const uint8_t* force, uint8_t* fresh);
 
+/* Returns the number of pairs, or -1 when a fresh position selects an expert without a slot. */
 int orc_worklist(int M, int K, int Kext, const int32_t* ids, const double* w,
                  const uint8_t* fresh, const int32_t* slot_of, int nS, int32_t* wl_pos,
                  int32_t* wl_k, double* wl_w, int32_t* offs, int32_t* inv);

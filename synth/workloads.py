@@ -78,6 +78,10 @@ class Workload:
     alpha: tuple = (9, 10)
     q: tuple = (95, 100)
     beta: tuple = (1, 1)
+    # routing over all experts ("exact") or inside the layer's Atlas support ("restricted");
+    # atlas_period > 0 rebuilds a restricted support after that many iterations
+    routing: str = "exact"
+    atlas_period: int = 0
 
     @property
     def M(self) -> int:
@@ -322,6 +326,7 @@ def desc_fields(w: Workload, **overrides) -> dict:
              norm_topk=int(w.norm_topk), act_dtype=1 if w.act == "bf16" else 0,
              staleness_R=w.staleness_R, atlas_m=w.m_ext, atlas_B=w.B, atlas_c=w.c,
              alpha_num=w.alpha[0], alpha_den=w.alpha[1], q_num=w.q[0], q_den=w.q[1],
-             beta_num=w.beta[0], beta_den=w.beta[1], flags=0)
+             beta_num=w.beta[0], beta_den=w.beta[1], flags=0,
+             routing=1 if w.routing == "restricted" else 0, atlas_period=w.atlas_period)
     f.update(overrides)
     return f

@@ -281,8 +281,122 @@ def pin_staleness(orc, lib):
     assert n_stable > 0
 
 
+def pin_restricted_topk(orc, lib):
+    """Top-K inside a support mask against a masked stable sort (brute force), with the
+    scores defined over all experts; the all-experts mask reduces to the plain top-K."""
+    rng = np.random.default_rng(11)
+    M, E, K = 45, 20, 4
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    G[:, 9] = G[:, 4]                       # exact ties inside the support
+    inA = np.zeros(E, np.uint8)
+    inA[[0, 2, 4, 5, 9, 11, 12, 17, 19]] = 1
+    for sigmoid in (True, False):
+        for norm in (True, False):
+            rids, rw = orc.route_restricted(G, K, inA, sigmoid, norm, lib=lib)
+            masked = np.where(inA.astype(bool)[None, :], -G.astype(np.float64), np.inf)
+            ref = np.argsort(masked, axis=1, kind="stable")[:, :K]
+            assert np.array_equal(rids, ref), "restricted top-K must be the masked stable sort"
+            assert inA[rids].all()
+            full = expit(G.astype(np.float64)) if sigmoid else softmax(G.astype(np.float64), axis=1)
+            sk = np.take_along_axis(full, ref, axis=1)
+            np.testing.assert_allclose(rw, sk / sk.sum(1, keepdims=True) if norm else sk,
+                                       rtol=1e-13, atol=0)
+    ids, s, w, q = orc.route(G, K, 2 * K, False, True, lib=lib)
+    rids, rw = orc.route_restricted(G, K, np.ones(E, np.uint8), False, True, lib=lib)
+    assert np.array_equal(rids, ids[:, :K]) and np.array_equal(rw, w)
+
+
+def pin_atlas_without_closure(orc, lib):
+    """The restricted-routing support is the hand-worked support before its closure step,
+    and the exact-mode support is exactly that set plus every routed expert."""
+    with open(os.path.join(GOLDEN, "atlas_hand_worked.json")) as f:
+        g = json.load(f)
+    inst = g["instance"]
+    ids = np.array(inst["ids"], dtype=np.int32)
+    q = np.array(inst["q"], dtype=np.int64)
+    for case in g["cases"]:
+        args = (ids, q, inst["E"], inst["K"], inst["B"], case["c"], case["alpha"], case["q"],
+                case["beta"])
+        inA, _, A, stats = orc.atlas_build(*args, lib=lib)
+        assert list(A) == case["support_before_closure"], case["name"]
+        inS, _, S, _ = orc.support_build(*args, lib=lib)
+        assert set(S.tolist()) == set(A.tolist()) | set(ids[:, :inst["K"]].ravel().tolist())
+    rng = np.random.default_rng(12)
+    M, E, K, Kext = 64, 32, 4, 8
+    G = (rng.standard_normal((M, E)) + np.linspace(2, -2, E)).astype(np.float32)
+    ids, s, w, q = orc.route(G, K, Kext, True, True, lib=lib)
+    for B, c in ((2, 1), (4, 2), (8, 4)):
+        inA, _, A, st = orc.atlas_build(ids, q, E, K, B, c, (9, 10), (95, 100), (1, 1), lib=lib)
+        inS, _, S, _ = orc.support_build(ids, q, E, K, B, c, (9, 10), (95, 100), (1, 1), lib=lib)
+        assert set(S.tolist()) == set(A.tolist()) | set(ids[:, :K].ravel().tolist())
+        assert int(st[4]) == len(A)
+
+
+def pin_restricted_lifecycle(orc, lib):
+    """Support-restricted routing over small blocks:
+    - the first forward (cold) and every rebuild route over all experts;
+    - hot-skip forwards route inside the support (masked stable sort of the logits);
+    - with the support holding every routed expert, restricted routing reproduces the
+      exact mode bit for bit (ids, weights, outputs, cache);
+    - an update period rebuilds on schedule; a support built on one hidden state and
+      confronted with an unrelated one fails the coverage goal and falls back."""
+    w = small_workload(routing="restricted", n_experts=16, top_k=3, iters=6,
+                       liveness="uniform", n_shared=0, shared_inter=0)
+    Wl = synth.layer_weights(w, 0)
+    D = synth.decoded_masks(w)
+    X = synth.hidden_states(w, 0, D)
+    L = orc.OracleLayer(w, Wl, lib=lib)
+    for it in range(w.iters):
+        out = L.forward(X[it], D[it])
+        K = w.top_k
+        if out["path"]:
+            assert np.array_equal(out["routed_ids"], out["ids"][:, :K])
+            assert np.array_equal(out["routed_w"], out["w"])
+        else:
+            masked = np.where(out["inA"].astype(bool)[None, :], -out["G"].astype(np.float64), np.inf)
+            assert np.array_equal(out["routed_ids"], np.argsort(masked, axis=1, kind="stable")[:, :K])
+        assert set(out["routed_ids"].ravel().tolist()) <= set(out["S_list"].tolist())
+        L.commit()
+    assert L.counters["cold"] == 1 and L.counters["restricted"] == L.counters["hot_skip"]
+    # B = E: the support holds every candidate expert, so no routed expert is ever outside it
+    wx = w.replace(routing="exact", atlas_B=w.n_experts)
+    wr = w.replace(routing="restricted", atlas_B=w.n_experts)
+    Lx = orc.OracleLayer(wx, Wl, lib=lib)
+    Lr = orc.OracleLayer(wr, Wl, lib=lib)
+    for it in range(w.iters):
+        ox = Lx.forward(X[it], D[it])
+        orr = Lr.forward(X[it], D[it])
+        if set(ox["ids"][:, :w.top_k].ravel().tolist()) <= set(np.flatnonzero(orr["inA"]).tolist()):
+            assert np.array_equal(ox["ids"][:, :w.top_k], orr["routed_ids"])
+            assert np.array_equal(ox["Y"], orr["Y"]) and np.array_equal(Lx.cache, Lr.cache)
+        Lx.commit()
+        Lr.commit()
+    assert Lr.counters["restricted"] >= 1
+    # update period 2: no forward reuses a support built two or more iterations earlier
+    Lp = orc.OracleLayer(w.replace(atlas_period=2), Wl, lib=lib)
+    last = None
+    for it in range(w.iters):
+        path = Lp.forward(X[it], D[it])["path"]
+        Lp.commit()
+        assert (path == 1) == (it == 0)
+        if path:
+            last = it
+        else:
+            assert it - last < 2
+    assert Lp.counters["period_update"] >= 1
+    # a narrow support (B = c = 1) built on one hidden state, then unrelated hidden states
+    wn = w.replace(atlas_B=1, atlas_c=1, redraw_every=1, rho_live=0.0, rho_decoded=0.0)
+    Xn = synth.hidden_states(wn, 0, D)
+    Ln = orc.OracleLayer(wn, Wl, lib=lib)
+    for it in range(w.iters):
+        out = Ln.forward(Xn[it], D[it])
+        Ln.commit()
+    assert Ln.counters["coverage_fallback"] >= 1
+
+
 PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
-        pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness]
+        pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness,
+        pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -315,7 +429,7 @@ def test_anomaly_and_special_fresh_cases(orc):
 MUTATIONS = {1: "router bias dropped", 2: "down-projection operand indexed wrongly",
              3: "SiLU sign flipped", 4: "ties broken toward the higher id",
              5: "refresh-due test dropped", 6: "worklist in position order",
-             7: "H_e uses a strict inequality"}
+             7: "H_e uses a strict inequality", 8: "restricted top-K ignores the support"}
 
 
 @pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
