@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="layers to run (0 = all of the workload)")
     ap.add_argument("--fraction", type=float, default=None, help="forced fresh fraction (workload 5)")
     ap.add_argument("--R", type=int, default=None, help="staleness bound override")
+    ap.add_argument("--routing", choices=("exact", "restricted"), default="exact",
+                    help="top-K over all experts, or inside the layer's Atlas support")
+    ap.add_argument("--atlas-period", type=int, default=0,
+                    help="restricted routing: rebuild the support after this many iterations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -106,6 +110,9 @@ def main():
         over["forced_fraction"] = args.fraction
     if args.R is not None:
         over["staleness_R"] = args.R
+    if args.routing != "exact":
+        over["routing"] = args.routing
+        over["atlas_period"] = args.atlas_period
     w = synth.workload(args.workload, **over)
     n_layers = w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)
     M, H, I, E, K = w.M, w.hidden, w.inter, w.n_experts, w.top_k
@@ -277,12 +284,16 @@ def main():
         "config": {"workload": w.name, "layers": n_layers, "iterations_per_block": iters,
                    "positions": M, "hidden": H, "experts": E, "top_k": K, "inter": I,
                    "shared_expert": bool(w.n_shared), "staleness_R": w.staleness_R,
-                   "forced_fraction": w.forced_fraction, "step": "one block"},
+                   "forced_fraction": w.forced_fraction, "routing": w.routing,
+                   "atlas_period": w.atlas_period, "step": "one block"},
         "us_per_layer_iteration": round(us_per_layer_iter, 2),
         "fresh_pairs_per_block": pairs_per_block,
         "fresh_fraction": round(per_block["fresh_rows"] / (M * layer_iters), 4),
         "support_paths": {"cold": per_block["cold"], "hot_update": per_block["hot_update"],
-                          "hot_skip": per_block["hot_skip"]},
+                          "hot_skip": per_block["hot_skip"],
+                          "restricted": per_block["restricted"],
+                          "coverage_fallback": per_block["coverage_fallback"]},
+        "touched_experts_per_forward": round(per_block["touched"] / layer_iters, 2),
         "kernel_us_per_launch": kernels_us,
         "kernel_time_share": kernels_share,
         "roofline": roofline,

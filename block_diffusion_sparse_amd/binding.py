@@ -16,11 +16,13 @@ LIB_PATH = os.path.join(PKG, "libepoch.so")
 
 EPOCH_GATE_SOFTMAX, EPOCH_GATE_SIGMOID = 0, 1
 EPOCH_DTYPE_F32, EPOCH_DTYPE_BF16 = 0, 1
-EPOCH_NUM_COUNTERS = 16
+EPOCH_ROUTING_EXACT, EPOCH_ROUTING_RESTRICTED = 0, 1
+EPOCH_NUM_COUNTERS = 20
 EPOCH_TIMING_GROUPS = 7
 COUNTERS = ["cold", "hot_update", "hot_skip", "anomaly", "fresh_rows", "pairs", "unmet",
             "forced_rows", "due_rows", "support_size", "u_final", "repair_rounds", "touched",
-            "forwards", "commits", "reserved"]
+            "forwards", "commits", "restricted", "coverage_fallback", "period_update",
+            "reserved18", "reserved19"]
 TIMING_GROUPS = ["router", "plan", "place", "routed_gateup", "routed_down", "shared",
                  "combine"]
 
@@ -32,7 +34,8 @@ class epoch_desc(ctypes.Structure):
     _fields_ = [(n, _i32) for n in (
         "n_layers", "hidden", "n_experts", "top_k", "inter", "n_shared", "shared_inter", "batch",
         "block", "gate", "norm_topk", "act_dtype", "staleness_R", "atlas_m", "atlas_B", "atlas_c",
-        "alpha_num", "alpha_den", "q_num", "q_den", "beta_num", "beta_den", "flags")]
+        "alpha_num", "alpha_den", "q_num", "q_den", "beta_num", "beta_den", "flags", "routing",
+        "atlas_period")]
 
 
 class epoch_layer_weights(ctypes.Structure):
@@ -42,8 +45,9 @@ class epoch_layer_weights(ctypes.Structure):
 class epoch_inspect(ctypes.Structure):
     _fields_ = [(n, _vp) for n in (
         "logits", "ids", "scores", "atlas_q", "weights", "fresh", "fresh_list", "n_fresh",
-        "n_pairs", "wl_pos", "wl_k", "wl_w", "offs", "inv", "in_support", "slot_of", "support",
-        "support_size", "cache", "valid", "last_fresh", "prev_decoded", "counters")] + [
+        "n_pairs", "wl_pos", "wl_k", "wl_w", "offs", "inv", "routed_ids", "routed_w",
+        "in_support", "slot_of", "support", "support_size", "atlas", "cache", "valid",
+        "last_fresh", "prev_decoded", "counters")] + [
         ("k_ext", _i32), ("iteration", _i32), ("last_forward_layer", _i32)]
 
 

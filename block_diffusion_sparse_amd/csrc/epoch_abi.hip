@@ -41,6 +41,10 @@ int32_t check_desc(const epoch_desc* d) {
   if (d->act_dtype != EPOCH_DTYPE_BF16 && d->act_dtype != EPOCH_DTYPE_F32) return EPOCH_E_DTYPE;
   if (d->gate != EPOCH_GATE_SOFTMAX && d->gate != EPOCH_GATE_SIGMOID) return EPOCH_E_DTYPE;
   if (d->flags != 0) return EPOCH_E_SHAPE;
+  if (d->routing != EPOCH_ROUTING_EXACT && d->routing != EPOCH_ROUTING_RESTRICTED)
+    return EPOCH_E_SHAPE;
+  if (d->atlas_period < 0 || (d->routing == EPOCH_ROUTING_EXACT && d->atlas_period != 0))
+    return EPOCH_E_SHAPE;
   if (d->n_layers < 1 || d->hidden < 1 || d->hidden > 16384) return EPOCH_E_SHAPE;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return EPOCH_E_SHAPE;
   if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return EPOCH_E_SHAPE;
@@ -104,6 +108,8 @@ Shape make_shape(const epoch_desc* d) {
   s.qd = d->q_den;
   s.bn = d->beta_num;
   s.bd = d->beta_den;
+  s.restricted = d->routing == EPOCH_ROUTING_RESTRICTED;
+  s.atlas_period = d->atlas_period;
   return s;
 }
 
@@ -126,6 +132,8 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
     L.counters = c.take<int64_t>(EPOCH_NUM_COUNTERS);
     L.fresh = c.take<uint8_t>(M);
     L.Dcur = c.take<uint8_t>(M);
+    L.inA = c.take<uint8_t>(E);
+    L.A_state = c.take<int32_t>(4);
     lay.layers.push_back(L);
   }
   const size_t P_max = M * K;
@@ -137,9 +145,15 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
   W.w = c.take<float>(M * K);
   W.flags = c.take<int32_t>(FLAG_WORDS);
   W.fpre = c.take<uint8_t>(M);
-  // cnt_f, cnt_a, chunk_fresh: carved back to back, cleared as one range every forward
+  W.rids = c.take<int32_t>(M * K);
+  W.rw = c.take<float>(M * K);
+  W.routed_ids = c.take<int32_t>(M * K);
+  W.routed_w = c.take<float>(M * K);
+  // cnt_f, cnt_a, cnt_fr, cnt_ar, chunk_fresh: carved back to back (cleared as one range)
   W.cnt_f = c.take<int32_t>((size_t)s.n_chunks * E);
   W.cnt_a = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.cnt_fr = c.take<int32_t>((size_t)s.n_chunks * E);
+  W.cnt_ar = c.take<int32_t>((size_t)s.n_chunks * E);
   W.chunk_fresh = c.take<int32_t>(s.n_chunks);
   W.chunk_base = c.take<int32_t>((size_t)s.n_chunks * E);
   W.chunk_foff = c.take<int32_t>(s.n_chunks);
@@ -310,7 +324,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
   if (e != hipSuccess) return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 1);
-    e = launch_plan(s, L, W, st);
+    e = launch_plan(s, p->iter[layer], L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
@@ -381,10 +395,13 @@ int32_t epoch_plan_inspect(const epoch_plan* p, int32_t layer, epoch_inspect* ou
   out->wl_w = W.wl_w;
   out->offs = W.offs;
   out->inv = W.inv;
+  out->routed_ids = W.routed_ids;
+  out->routed_w = W.routed_w;
   out->in_support = L.inS;
   out->slot_of = L.slot_of;
   out->support = L.S_list;
   out->support_size = L.S_size;
+  out->atlas = L.inA;
   out->cache = L.cache;
   out->valid = L.valid;
   out->last_fresh = L.last_fresh;

@@ -20,8 +20,12 @@ constexpr int kDownCols = 64;     // output columns per down workgroup
 // per-forward flag words (int32) in the scratch area
 // MISS and ANOMALY are raised by the router and cleared by the plan step once read (FRESH_ALL
 // keeps the anomaly decision for the placement); the rest are written by the plan step.
+// UNDER (restricted mode: positions under-covered by the Atlas support, counted by the router)
+// is cleared by the plan step too; ROUTE_R (1 = this forward routes inside the support) is
+// written by the plan step for the placement.
 enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
-       FLAG_NTILES_BIG = 5, FLAG_FRESH_ALL = 6, FLAG_WORDS = 16 };
+       FLAG_NTILES_BIG = 5, FLAG_FRESH_ALL = 6, FLAG_UNDER = 7, FLAG_ROUTE_R = 8,
+       FLAG_WORDS = 16 };
 
 // Device-side view of one layer's persistent state.
 struct LayerState {
@@ -37,6 +41,8 @@ struct LayerState {
   int64_t* counters;    // [EPOCH_NUM_COUNTERS]
   uint8_t* fresh;       // [M] fresh flags of the layer's latest forward
   uint8_t* Dcur;        // [M] D_i seen by the layer's latest forward
+  uint8_t* inA;         // [E] restricted mode: the Atlas support (no closure)
+  int32_t* A_state;     // [4] restricted mode: valid flag, iteration of the latest build, size
 };
 
 // Device-side view of the per-forward scratch.
@@ -48,10 +54,17 @@ struct Scratch {
   float* w;             // [M x K]
   int32_t* flags;       // [FLAG_WORDS]
   uint8_t* fpre;        // [M] fresh test before the anomaly override
+  int32_t* rids;        // [M x K] restricted mode: top-K inside the support
+  float* rw;            // [M x K] and its weights
+  int32_t* routed_ids;  // [M x K] the routing the worklist used
+  float* routed_w;      // [M x K]
+  // cnt_f, cnt_a, cnt_fr, cnt_ar, chunk_fresh: carved back to back (one clearing range)
   int32_t* cnt_f;       // [n_chunks x E] routed pairs of fresh positions per chunk and expert
   int32_t* cnt_a;       // [n_chunks x E] routed pairs of all positions per chunk and expert
-  int32_t* chunk_base;  // [n_chunks x E]
+  int32_t* cnt_fr;      // [n_chunks x E] the same for the in-support routing (restricted mode)
+  int32_t* cnt_ar;      // [n_chunks x E]
   int32_t* chunk_fresh; // [n_chunks]
+  int32_t* chunk_base;  // [n_chunks x E]
   int32_t* chunk_foff;  // [n_chunks]
   int32_t* offs;        // [E + 1] per support slot
   int32_t* eoffs;       // [E + 1] per expert
@@ -75,6 +88,7 @@ struct Scratch {
 struct Shape {
   int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
   int n_chunks, ksplit, router_bt, T_max, T_dense, T_big_max, big_routed;
+  int restricted, atlas_period;
   int B, c, an, ad, qn, qd, bn, bd;
 };
 
@@ -84,7 +98,8 @@ hipError_t launch_init_scratch(const Shape& s, const Scratch& W, hipStream_t st)
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
                          const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
                          const Scratch& W, hipStream_t st);
-hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_plan(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                       hipStream_t st);
 hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
                                 const LayerState& L, const Scratch& W, hipStream_t st);

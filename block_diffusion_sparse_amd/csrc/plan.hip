@@ -24,7 +24,9 @@ __global__ void k_init_layer(int M, int E, LayerState L) {
     L.inS[i] = 0;
     L.slot_of[i] = -1;
     L.S_list[i] = 0;
+    L.inA[i] = 0;
   }
+  if (i < 4) L.A_state[i] = 0;
   if (i < EPOCH_NUM_COUNTERS) L.counters[i] = 0;
   if (i == 0) {
     *L.S_size = 0;
@@ -126,19 +128,51 @@ __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
 // integer and the result does not depend on the order of the atomics.  Runs when the layer has
 // no support yet (cold) or when the router found a routed expert outside it (hot-update);
 // otherwise counts a hot-skip.  Whole-workgroup function: every thread must call it.
-__device__ void support_phase(const Shape& s, const LayerState& L, const Scratch& W,
-                              SupportLds& sh) {
+//
+// Support-restricted routing (restricted shapes) keeps the Atlas set itself (no closure) in
+// L.inA and decides here which routing the forward uses: a forward without a support (cold),
+// past the update period, or whose candidates leave more than (1 - q) M positions
+// under-covered by the support (or with fewer than K experts in it) rebuilds the support
+// and routes over all experts, its routed experts getting slots for this forward only;
+// otherwise (hot-skip) the slots are the support and the forward routes inside it.
+// Returns 1 when the forward routes inside the support.
+__device__ int support_phase(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                             SupportLds& sh) {
   const int tid = threadIdx.x;
   const int M = s.M, E = s.E, K = s.K, Kext = s.Kext;
   const long long an = s.an, ad = s.ad, qn = s.qn, qd = s.qd, bn = s.bn, bd = s.bd;
   const int32_t* ids = W.ids;
   const int32_t* q = W.q;
   const bool valid = *L.S_valid != 0;
-  const bool miss = W.flags[FLAG_MISS] != 0;
-  if (valid && !miss) {
-    if (tid == 0) L.counters[EPOCH_CNT_HOT_SKIP] += 1;
-    return;
+  int path;        // 0 hot-skip, 1 cold, 2 hot-update
+  int reason = 0;  // restricted hot-update: 1 coverage check, 2 update period
+  if (!s.restricted) {
+    path = !valid ? 1 : (W.flags[FLAG_MISS] != 0 ? 2 : 0);
+    if (path == 0) {
+      if (tid == 0) L.counters[EPOCH_CNT_HOT_SKIP] += 1;
+      return 0;
+    }
+  } else {
+    const int a_valid = L.A_state[0], built = L.A_state[1], a_size = L.A_state[2];
+    const long long nU = W.flags[FLAG_UNDER];
+    if (!a_valid) {
+      path = 1;
+    } else if (s.atlas_period > 0 && iter - built >= s.atlas_period) {
+      path = 2;
+      reason = 2;
+    } else if (a_size < K || qd * nU > (qd - qn) * (long long)M) {
+      path = 2;
+      reason = 1;
+    } else {
+      path = 0;
+    }
   }
+  int rounds = 0, unmet = 0, nU_final = 0, a_size_new = 0;
+  if (path == 0) {
+    // restricted hot-skip: the slots are the support
+    for (int e = tid; e < E; e += kPlanThreads) sh.inS[e] = L.inA[e];
+    __syncthreads();
+  } else {
   const long long Q = 65536;
   // (i) popularity p_e = sum_{t,j: I_{t,j} = e} W_{t,j}
   for (int e = tid; e < E; e += kPlanThreads) sh.p[e] = 0;
@@ -157,7 +191,6 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
   __syncthreads();
   coverage_pass(ids, q, sh.inS, M, K, Kext, s.an, s.ad, W.Crow, W.Rrow, &sh.nU);
   __syncthreads();
-  int rounds = 0, unmet = 0;
   // (ii) greedy repair while |U| > (1 - q) M
   while (qd * sh.nU > (qd - qn) * M) {
     for (int e = tid; e < E; e += kPlanThreads) {
@@ -211,13 +244,25 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
     coverage_pass(ids, q, sh.inS, M, K, Kext, s.an, s.ad, W.Crow, W.Rrow, &sh.nU);
     __syncthreads();
   }
-  const int nU_final = sh.nU;
+  nU_final = sh.nU;
+  if (s.restricted) {
+    // the Atlas support itself: kept for the next forwards, before the closure below
+    const int incl_a = block_incl_scan(tid < E ? sh.inS[tid] : 0, sh.wsum, &a_size_new);
+    (void)incl_a;
+    if (tid < E) L.inA[tid] = sh.inS[tid];
+    if (tid == 0) {
+      L.A_state[0] = 1;
+      L.A_state[1] = iter;
+      L.A_state[2] = a_size_new;
+    }
+  }
   // (iii) closure: every routed expert of the current iteration gets a slot
   for (int i = tid; i < M * K; i += kPlanThreads) {
     const int t = i / K, k = i - t * K;
     sh.inS[ids[(size_t)t * Kext + k]] = 1;
   }
   __syncthreads();
+  }
   // (iv) slots in expert-id order (E <= kMaxExperts == kPlanThreads: one expert per thread)
   int size;
   const int incl = block_incl_scan(tid < E ? sh.inS[tid] : 0, sh.wsum, &size);
@@ -233,13 +278,21 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
   if (tid == 0) {
     *L.S_size = size;
     *L.S_valid = 1;
-    L.counters[valid ? EPOCH_CNT_HOT_UPDATE : EPOCH_CNT_COLD] += 1;
-    L.counters[EPOCH_CNT_UNMET] += unmet;
-    L.counters[EPOCH_CNT_SUPPORT_SIZE] = size;
-    L.counters[EPOCH_CNT_U_FINAL] = nU_final;
-    L.counters[EPOCH_CNT_REPAIR_ROUNDS] += rounds;
+    if (path == 0) {
+      L.counters[EPOCH_CNT_HOT_SKIP] += 1;
+      L.counters[EPOCH_CNT_RESTRICTED] += 1;
+    } else {
+      L.counters[path == 1 ? EPOCH_CNT_COLD : EPOCH_CNT_HOT_UPDATE] += 1;
+      if (reason == 1) L.counters[EPOCH_CNT_COVERAGE_FALLBACK] += 1;
+      if (reason == 2) L.counters[EPOCH_CNT_PERIOD_UPDATE] += 1;
+      L.counters[EPOCH_CNT_UNMET] += unmet;
+      L.counters[EPOCH_CNT_SUPPORT_SIZE] = s.restricted ? a_size_new : size;
+      L.counters[EPOCH_CNT_U_FINAL] = nU_final;
+      L.counters[EPOCH_CNT_REPAIR_ROUNDS] += rounds;
+    }
   }
   __syncthreads();
+  return path == 0 ? 1 : 0;
 }
 
 // Stable placement of one chunk by one wave (teardown, FreshLane pack: fresh rows with their
@@ -249,8 +302,8 @@ __device__ void support_phase(const Shape& s, const LayerState& L, const Scratch
 // positions routed to e (a 64-bit mask per expert, in LDS, cleared by the wave beforehand).
 // Wave-level function: all 64 lanes call it; mask holds E entries owned by this wave.
 __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int Kext,
-                                            bool anomaly, const LayerState& L, const Scratch& W,
-                                            unsigned long long* mask) {
+                                            bool anomaly, bool route_r, const LayerState& L,
+                                            const Scratch& W, unsigned long long* mask) {
   const int lane = threadIdx.x & 63;
   const int t = chunk * kChunk + lane;
   const bool in = t < M;
@@ -260,7 +313,16 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int32_t* it = W.ids + (size_t)(in ? t : 0) * Kext;
+  // the routing this forward uses: the all-expert top-K (first K candidates) or, when it
+  // routes inside the support, the in-support top-K
+  const int32_t* it = route_r ? W.rids + (size_t)(in ? t : 0) * K
+                              : W.ids + (size_t)(in ? t : 0) * Kext;
+  const float* wt = (route_r ? W.rw : W.w) + (size_t)(in ? t : 0) * K;
+  if (in)
+    for (int k = 0; k < K; ++k) {
+      W.routed_ids[(size_t)t * K + k] = it[k];
+      W.routed_w[(size_t)t * K + k] = wt[k];
+    }
   if (fresh)
     for (int k = 0; k < K; ++k) atomicOr(&mask[it[k]], 1ull << lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -274,7 +336,7 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
       const int p = W.eoffs[e] + W.chunk_base[(size_t)chunk * E + e] + rank;
       W.wl_pos[p] = t;
       W.wl_k[p] = k;
-      W.wl_w[p] = W.w[(size_t)t * K + k];
+      W.wl_w[p] = wt[k];
       W.inv[(size_t)t * K + k] = p;
     }
   } else if (in) {
@@ -302,19 +364,20 @@ constexpr int kFusedPlaceMaxChunks = kPlanWaves;
 //   chunk_foff[c]    = fresh positions in chunks before c      (the fresh list)
 // and, when FUSED_PLACE, the placement of every chunk.
 template <bool FUSED_PLACE>
-__global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Scratch W) {
+__global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerState L,
+                                                       Scratch W) {
   __shared__ SupportLds sh;
   __shared__ int32_t part[kPlanThreads];
   __shared__ int32_t tot[kMaxExperts];
   __shared__ unsigned long long pmask[FUSED_PLACE ? kPlanWaves : 1]
                                      [FUSED_PLACE ? kFusedPlaceMaxExperts : 1];
   const int tid = threadIdx.x;
-  support_phase(s, L, W, sh);
+  const bool route_r = support_phase(s, iter, L, W, sh) != 0;
   __syncthreads();
 
   const int E = s.E, nch = s.n_chunks;
   const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
-  const int32_t* cnt = anomaly ? W.cnt_a : W.cnt_f;
+  const int32_t* cnt = route_r ? (anomaly ? W.cnt_ar : W.cnt_fr) : (anomaly ? W.cnt_a : W.cnt_f);
   // per-expert totals and chunk bases; Gp threads per expert, each a contiguous chunk range
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
@@ -343,6 +406,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
       run += cnt[(size_t)c * E + e];
       W.cnt_f[(size_t)c * E + e] = 0;  // consumed: clear for the next forward
       W.cnt_a[(size_t)c * E + e] = 0;
+      if (s.restricted) {
+        W.cnt_fr[(size_t)c * E + e] = 0;
+        W.cnt_ar[(size_t)c * E + e] = 0;
+      }
     }
   }
   __syncthreads();
@@ -411,15 +478,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, LayerState L, Sc
     if (anomaly) L.counters[EPOCH_CNT_ANOMALY] += 1;
     // every thread read MISS and ANOMALY before the barriers above
     W.flags[FLAG_FRESH_ALL] = anomaly ? 1 : 0;
+    W.flags[FLAG_ROUTE_R] = route_r ? 1 : 0;
     W.flags[FLAG_MISS] = 0;
     W.flags[FLAG_ANOMALY] = 0;
+    W.flags[FLAG_UNDER] = 0;
   }
   if (FUSED_PLACE) {
     // chunk_base, eoffs and chunk_foff were written above by this workgroup
     __syncthreads();
     const int wave = tid >> 6;
     for (int chunk = wave; chunk < nch; chunk += kPlanWaves)
-      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, L, W, pmask[wave]);
+      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, route_r, L, W, pmask[wave]);
   }
 }
 
@@ -430,18 +499,20 @@ __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, in
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x * 4 + wave;
   if (chunk >= n_chunks) return;
-  place_chunk(chunk, M, E, K, Kext, W.flags[FLAG_FRESH_ALL] != 0, L, W, mask[wave]);
+  place_chunk(chunk, M, E, K, Kext, W.flags[FLAG_FRESH_ALL] != 0, W.flags[FLAG_ROUTE_R] != 0, L,
+              W, mask[wave]);
 }
 
 static bool fused_place(const Shape& s) {
   return s.E <= kFusedPlaceMaxExperts && s.n_chunks <= kFusedPlaceMaxChunks;
 }
 
-hipError_t launch_plan(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
+hipError_t launch_plan(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                       hipStream_t st) {
   if (fused_place(s))
-    hipLaunchKernelGGL(k_plan<true>, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
+    hipLaunchKernelGGL(k_plan<true>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
   else
-    hipLaunchKernelGGL(k_plan<false>, dim3(1), dim3(kPlanThreads), 0, st, s, L, W);
+    hipLaunchKernelGGL(k_plan<false>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct RouteArgs {
   const uint8_t* D;
   const uint8_t* force;
   int E, K, Kext, gate_sigmoid, norm_topk, R, iter;
+  int restricted, an, ad;  // support-restricted routing; coverage floor alpha = an / ad
 };
 
 __device__ __forceinline__ uint64_t sel_key(float g, int e) {
@@ -88,14 +89,18 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   const int E = ra.E, K = ra.K, Kext = ra.Kext, gate_sigmoid = ra.gate_sigmoid;
   const int norm_topk = ra.norm_topk, R = ra.R, iter = ra.iter;
   const int lane = threadIdx.x & 63;
+  // restricted mode with a support in place: also route inside the support (the plan step
+  // decides which routing the forward uses)
+  const bool r_on = ra.restricted && L.A_state[0] != 0;
   // prologue: every global read of the position at once
   float gv[NPER];
-  uint8_t in_s[NPER];
+  uint8_t in_s[NPER], in_a[NPER];
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
     gv[j] = e < E ? G[(size_t)t * E + e] : -INFINITY;
     in_s[j] = e < E ? L.inS[e] : 0;
+    in_a[j] = (r_on && e < E) ? L.inA[e] : 0;
   }
   const uint8_t d = D[t], pd = L.prev_D[t];
   const bool valid = L.valid[t] != 0;
@@ -106,35 +111,39 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   uint64_t key[NPER];
 #pragma unroll
   for (int j = 0; j < NPER; ++j) key[j] = (lane + 64 * j < E) ? sel_key(gv[j], lane + 64 * j) : 0ull;
-  // largest threshold T with #{key >= T} >= K_ext: the K_ext-th largest key
-  uint64_t T = 0;
-  for (int b = 41; b >= 0; --b) {
-    const uint64_t cand = T | (1ull << b);
-    int cnt = 0;
+  // the n largest of the keys kk (0 = excluded): membership masks and ranks
+  auto select = [&](const uint64_t* kk, int n, uint64_t* selm, int* rank) {
+    // largest threshold T with #{key >= T} >= n: the n-th largest key
+    uint64_t T = 0;
+    for (int b = 41; b >= 0; --b) {
+      const uint64_t cand = T | (1ull << b);
+      int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < NPER; ++j) cnt += __popcll(ballot64(key[j] >= cand));
-    if (cnt >= Kext) T = cand;
-  }
-  // rank of each selected key among the selected ones
+      for (int j = 0; j < NPER; ++j) cnt += __popcll(ballot64(kk[j] >= cand));
+      if (cnt >= n) T = cand;
+    }
+    // rank of each selected key among the selected ones
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      rank[j] = 0;
+      selm[j] = ballot64(kk[j] >= T && kk[j] != 0ull);
+    }
+#pragma unroll
+    for (int jj = 0; jj < NPER; ++jj) {
+      uint64_t m = selm[jj];
+      while (m) {
+        const int src = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const uint64_t kb = ((uint64_t)__builtin_amdgcn_readlane((int)(kk[jj] >> 32), src) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kk[jj], src);
+#pragma unroll
+        for (int j = 0; j < NPER; ++j) rank[j] += (kb > kk[j]);
+      }
+    }
+  };
   int rank[NPER];
   uint64_t selm[NPER];
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    rank[j] = 0;
-    selm[j] = ballot64(key[j] >= T);
-  }
-#pragma unroll
-  for (int jj = 0; jj < NPER; ++jj) {
-    uint64_t m = selm[jj];
-    while (m) {
-      const int src = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const uint64_t kb = ((uint64_t)__builtin_amdgcn_readlane((int)(key[jj] >> 32), src) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[jj], src);
-#pragma unroll
-      for (int j = 0; j < NPER; ++j) rank[j] += (kb > key[j]);
-    }
-  }
+  select(key, Kext, selm, rank);
   // softmax normaliser over all E (max = the best key's logit)
   double zmax = 0.0, z = 0.0;
   if (!gate_sigmoid) {
@@ -154,20 +163,61 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   const bool fresh = forced || !valid || !(d && pd) || due;
   const size_t chunk = (size_t)(t / kChunk);
   bool miss = false;
+  int q_routed = 0, q_in_a = 0;  // R_t and C_t(A) of the Atlas coverage test, this lane's part
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
     if (!((selm[j] >> lane) & 1ull)) continue;
     const int rk = rank[j];
     const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)gv[j])) : exp((double)gv[j] - zmax) / z;
+    const int32_t qv = (int32_t)floor(sc * 65536.0 + 0.5);
     W.ids[(size_t)t * Kext + rk] = e;
     W.scores[(size_t)t * Kext + rk] = (float)sc;
-    W.q[(size_t)t * Kext + rk] = (int32_t)floor(sc * 65536.0 + 0.5);
+    W.q[(size_t)t * Kext + rk] = qv;
     s_buf[rk] = sc;
+    if (in_a[j]) q_in_a += qv;
     if (rk < K) {
+      q_routed += qv;
       miss |= s_valid && !in_s[j];
       atomicAdd(&W.cnt_a[chunk * E + e], 1);
       if (fresh) atomicAdd(&W.cnt_f[chunk * E + e], 1);
+    }
+  }
+  if (r_on) {
+    // coverage of this position by the support: under-covered when alpha_den C < alpha_num R
+    const int Rt = wave_sum(q_routed), Ct = wave_sum(q_in_a);
+    if (lane == 0 && (long long)ra.ad * Ct < (long long)ra.an * Rt)
+      atomicAdd(&W.flags[FLAG_UNDER], 1);
+    // top-K inside the support (scores keep their definition over all E)
+    uint64_t kr[NPER];
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) kr[j] = in_a[j] ? key[j] : 0ull;
+    int rrank[NPER];
+    uint64_t rsel[NPER];
+    select(kr, K, rsel, rrank);
+    double* r_buf = s_buf + kMaxKext;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int e = lane + 64 * j;
+      if (!((rsel[j] >> lane) & 1ull) || rrank[j] >= K) continue;
+      const int rk = rrank[j];
+      const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)gv[j])) : exp((double)gv[j] - zmax) / z;
+      W.rids[(size_t)t * K + rk] = e;
+      r_buf[rk] = sc;
+      atomicAdd(&W.cnt_ar[chunk * E + e], 1);
+      if (fresh) atomicAdd(&W.cnt_fr[chunk * E + e], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // fewer than K experts in the support leaves slots unset: the plan step then rebuilds
+    // and this routing is not used
+    if (lane < K) {
+      double denom = 0.0;
+      if (norm_topk)
+        for (int k = 0; k < K; ++k) denom += r_buf[k];
+      const double sk = r_buf[lane];
+      W.rw[(size_t)t * K + lane] = (float)(norm_topk ? sk / denom : sk);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -195,7 +245,7 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route_rows(const float* __restrict__ G, RouteArgs ra,
                                                     int M) {
-  __shared__ double s_buf[4][kMaxKext];
+  __shared__ double s_buf[4][2 * kMaxKext];
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t < M) route_row<NPER>(t, G, ra, s_buf[wave]);
@@ -306,7 +356,8 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
     else
       launch_k_router<float, 16>(s, x, Wg, bias, W, st);
   }
-  const RouteArgs ra{L, W, D, force, s.E, s.K, s.Kext, s.gate_sigmoid, s.norm_topk, s.R, iter};
+  const RouteArgs ra{L,         W,     D,    force, s.E,          s.K,  s.Kext, s.gate_sigmoid,
+                     s.norm_topk, s.R, iter, s.restricted, s.an, s.ad};
   const int nper = (s.E + 63) / 64;
 #define EPOCH_ROUTE_ROWS(NP) \
   hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)

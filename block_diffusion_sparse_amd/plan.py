@@ -71,10 +71,13 @@ class EpochPlan:
             wl_w=v(ins.wl_w, M * K, "f32"),
             offs=v(ins.offs, E + 1, "i32"),
             inv=v(ins.inv, M * K, "i32").view(M, K),
+            routed_ids=v(ins.routed_ids, M * K, "i32").view(M, K),
+            routed_w=v(ins.routed_w, M * K, "f32").view(M, K),
             in_support=v(ins.in_support, E, "u8"),
             slot_of=v(ins.slot_of, E, "i32"),
             support=v(ins.support, E, "i32"),
             support_size=v(ins.support_size, 1, "i32"),
+            atlas=v(ins.atlas, E, "u8"),
             cache=cache.view(torch.int16 if self.act_size == 2 else torch.float32).view(M, d.hidden),
             valid=v(ins.valid, M, "u8"),
             last_fresh=v(ins.last_fresh, M, "i32"),

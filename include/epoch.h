@@ -16,8 +16,10 @@
  *   - worklist, expert compute, combine and dense restore (teardown, LSP
  *     equations B_i = Compact(H, F_i), Y[F] = Y_F, Y[not F] = C_l[not F];
  *     FreshLane steps pack, light expert kernel, combine, scatter/merge).
- * Routing here is over all experts (the support is a compact layout and a
- * rebuild trigger); one GPU holds every expert, so no collective is involved.
+ * Routing is over all experts by default (the support is then a compact layout and
+ * a rebuild trigger); with EPOCH_ROUTING_RESTRICTED each position's top-K is taken
+ * inside the layer's support, as in the teardown's Expert Atlas step three.  One GPU
+ * holds every expert, so no collective is involved.
  *
  * Conventions for every call:
  *   - Positions: M = batch * block, position t = b * block + p.  Tensors are dense,
@@ -57,6 +59,20 @@ enum {
 
 enum { EPOCH_GATE_SOFTMAX = 0, EPOCH_GATE_SIGMOID = 1 };
 enum { EPOCH_DTYPE_F32 = 0, EPOCH_DTYPE_BF16 = 1 };
+/* Routing modes (epoch_desc.routing):
+ *   EXACT: every position's top-K over all E experts.  The support is the Atlas set plus
+ *     every routed expert (closure); it is rebuilt at the block's first forward (cold) and
+ *     whenever a routed expert falls outside it (hot-update).
+ *   RESTRICTED: the support is the Atlas set alone (no closure), and a forward that keeps it
+ *     (hot-skip) routes each position to the top-K experts inside it (teardown, Expert
+ *     Atlas, step three: ids, order and weights still change every iteration; scores keep
+ *     their definition over all E).  Every forward still ranks the K_ext candidates over
+ *     all experts; the support is rebuilt from them at the first forward (cold), after
+ *     atlas_period iterations (if > 0), or when they show it misses the coverage goal
+ *     |U| <= (1 - q) M or holds fewer than K experts (hot-update; the block-plan
+ *     lifecycle and its fallback to the full path).  A forward that rebuilds routes over
+ *     all experts, giving the routed experts outside the support slots for that forward. */
+enum { EPOCH_ROUTING_EXACT = 0, EPOCH_ROUTING_RESTRICTED = 1 };
 
 /* Per-layer counters, int64, readable through epoch_plan_inspect().counters. */
 enum {
@@ -75,7 +91,10 @@ enum {
   EPOCH_CNT_TOUCHED = 12,      /* sum over forwards of experts with at least one fresh pair */
   EPOCH_CNT_FORWARDS = 13,
   EPOCH_CNT_COMMITS = 14,
-  EPOCH_NUM_COUNTERS = 16
+  EPOCH_CNT_RESTRICTED = 15,   /* forwards routed inside the support (restricted mode) */
+  EPOCH_CNT_COVERAGE_FALLBACK = 16, /* restricted-mode rebuilds forced by the coverage check */
+  EPOCH_CNT_PERIOD_UPDATE = 17,/* restricted-mode rebuilds forced by atlas_period */
+  EPOCH_NUM_COUNTERS = 20
 };
 
 typedef struct epoch_desc {
@@ -101,6 +120,9 @@ typedef struct epoch_desc {
   int32_t atlas_m, atlas_B, atlas_c;
   int32_t alpha_num, alpha_den, q_num, q_den, beta_num, beta_den;
   int32_t flags;        /* reserved, must be 0 */
+  int32_t routing;      /* EPOCH_ROUTING_EXACT or EPOCH_ROUTING_RESTRICTED */
+  int32_t atlas_period; /* restricted mode: rebuild the support after this many iterations
+                           (0 = only on the coverage check); must be 0 in exact mode */
 } epoch_desc;
 
 /* Device pointers of one layer's weights; all row-major, contiguous, caller-owned and
@@ -133,11 +155,15 @@ typedef struct epoch_inspect {
   const float* wl_w;          /* [P] pair -> routing weight */
   const int32_t* offs;        /* [|S| + 1] exclusive pair offsets per support slot */
   const int32_t* inv;         /* [M x K] (t, k) -> pair index, -1 if t is not fresh */
+  const int32_t* routed_ids;  /* [M x K] experts the worklist used (= ids[:, :K] unless the
+                                 forward routed inside the support) */
+  const float* routed_w;      /* [M x K] their routing weights */
   /* per-layer state of the requested layer */
   const uint8_t* in_support;  /* [E] */
   const int32_t* slot_of;     /* [E] slot = rank of e in the sorted support, -1 outside */
   const int32_t* support;     /* [E] sorted support ids (first support_size valid) */
   const int32_t* support_size;/* [1] */
+  const uint8_t* atlas;       /* [E] restricted mode: the Atlas support (no closure) */
   const void* cache;          /* [M x H] act: cached routed output C_l */
   const uint8_t* valid;       /* [M] cache row written in this block */
   const int32_t* last_fresh;  /* [M] iteration of the last fresh write */

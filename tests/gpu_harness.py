@@ -114,6 +114,17 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
     assert np.array_equal(g["support"][:nS], out["S_list"]), f"{tag}: support differs"
     assert np.array_equal(g["slot_of"], out["slot_of"]), f"{tag}: slots differ"
     assert np.array_equal(g["in_support"], out["inS"]), f"{tag}: support mask differs"
+    if w.routing == "restricted":
+        assert np.array_equal(g["atlas"], out["inA"]), f"{tag}: Atlas support differs"
+    # the routing the worklist used (all-expert top-K, or top-K inside the support)
+    if not np.array_equal(g["routed_ids"], out["routed_ids"]):
+        ties, real = _near_tie_rows(out["G"], g["routed_ids"], out["routed_ids"])
+        assert not real, f"{tag}: routed ids differ on rows {real[:8]} (not near-ties)"
+        rep.near_ties += len(ties)
+        warnings.warn(f"{tag}: {len(ties)} near-tie rows in the routed ids reported")
+        return False
+    np.testing.assert_allclose(g["routed_w"], out["routed_w"], rtol=1e-6, atol=1e-12,
+                               err_msg=tag)
     fresh = out["fresh"].astype(bool)
     assert np.array_equal(g["fresh"].astype(bool), fresh), f"{tag}: fresh set differs"
     nf = int(fresh.sum())
@@ -212,6 +223,9 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
         assert c["hot_skip"] == oc["hot_skip"] and c["anomaly"] == oc["anomalies"]
         assert c["fresh_rows"] == oc["fresh_rows"] and c["pairs"] == oc["pairs"]
         assert c["commits"] == c["forwards"] == orcs[li].iter
+        assert c["restricted"] == oc["restricted"]
+        assert c["coverage_fallback"] == oc["coverage_fallback"]
+        assert c["period_update"] == oc["period_update"]
     rep.counters = [plan.counters(li) for li in range(len(layers))]
     plan.close()
     return rep
