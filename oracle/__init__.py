@@ -36,6 +36,9 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.orc_under_covered.restype = ctypes.c_int64
     lib.orc_fresh_set.restype = _c_int
     lib.orc_worklist.restype = _c_int
+    lib.orc_atlas_build.restype = _c_int
+    lib.orc_route_restricted.restype = _c_int
+    lib.orc_group_allowed.restype = None
     for name in ("orc_router_logits", "orc_route", "orc_expert", "orc_moe_rows", "orc_commit",
                  "orc_dense_moe"):
         getattr(lib, name).restype = None
@@ -71,7 +74,9 @@ def router_logits(x, Wg, bias=None, lib=None) -> np.ndarray:
     return G
 
 
-def route(G, K, Kext, gate_sigmoid, norm_topk, lib=None):
+def route(G, K, Kext, gate_sigmoid, norm_topk, allowed=None, lib=None):
+    """Top-K_ext candidates (key: logit desc, id asc) over all experts, or over the
+    selectable ones of each row when allowed [M, E] is given."""
     lib = lib or load()
     G = np.ascontiguousarray(G, dtype=np.float32)
     M, E = G.shape
@@ -79,9 +84,23 @@ def route(G, K, Kext, gate_sigmoid, norm_topk, lib=None):
     s = np.empty((M, Kext), dtype=np.float64)
     w = np.empty((M, K), dtype=np.float64)
     q = np.empty((M, Kext), dtype=np.int64)
+    al = None if allowed is None else np.ascontiguousarray(allowed, dtype=np.uint8)
     lib.orc_route(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _c_int(int(gate_sigmoid)),
-                  _c_int(int(norm_topk)), _p(G), _p(ids), _p(s), _p(w), _p(q))
+                  _c_int(int(norm_topk)), _p(G), _p(al), _p(ids), _p(s), _p(w), _p(q))
     return ids, s, w, q
+
+
+def group_allowed(G, n_group, topk_group, base=None, lib=None):
+    """[M, E] mask of the experts of each row's topk_group best groups (groups ranked by
+    their best expert among base, the [E] support mask, or all experts)."""
+    lib = lib or load()
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    M, E = G.shape
+    out = np.empty((M, E), dtype=np.uint8)
+    b = None if base is None else np.ascontiguousarray(base, dtype=np.uint8)
+    lib.orc_group_allowed(_c_int(M), _c_int(E), _c_int(n_group), _c_int(topk_group), _p(G),
+                          _p(b), _p(out))
+    return out
 
 
 def support_status(ids, K, inS, support_valid, lib=None) -> int:
@@ -125,16 +144,19 @@ def atlas_build(ids, q, E, K, B, c, alpha, qfrac, beta, lib=None):
 
 
 def route_restricted(G, K, inA, gate_sigmoid, norm_topk, lib=None):
-    """Top-K inside the support mask inA: ids [M, K] int32 and weights [M, K] double."""
+    """Top-K inside the support: inA is the [E] support mask or an [M, E] per-row mask of
+    selectable experts.  Returns ids [M, K] int32 and weights [M, K] double, or None when
+    some row has fewer than K selectable experts."""
     lib = lib or load()
     G = np.ascontiguousarray(G, dtype=np.float32)
     M, E = G.shape
+    al = np.ascontiguousarray(np.broadcast_to(np.asarray(inA, dtype=np.uint8), (M, E)))
     rids = np.empty((M, K), dtype=np.int32)
     rw = np.empty((M, K), dtype=np.float64)
-    lib.orc_route_restricted(_c_int(M), _c_int(E), _c_int(K), _c_int(int(gate_sigmoid)),
-                             _c_int(int(norm_topk)), _p(G),
-                             _p(np.ascontiguousarray(inA, dtype=np.uint8)), _p(rids), _p(rw))
-    return rids, rw
+    n_short = lib.orc_route_restricted(_c_int(M), _c_int(E), _c_int(K),
+                                       _c_int(int(gate_sigmoid)), _c_int(int(norm_topk)), _p(G),
+                                       _p(al), _p(rids), _p(rw))
+    return None if n_short else (rids, rw)
 
 
 def slots_of(mask):
@@ -247,7 +269,11 @@ class OracleLayer:
         K, Kext, E = w.top_k, w.k_ext, w.n_experts
         W = self.W
         G = router_logits(x, W["router_w"], W["router_b"], lib=lib)
-        ids, s, wts, q = route(G, K, Kext, w.gate == "sigmoid", w.norm_topk, lib=lib)
+        # group-limited rule: each row selects among the experts of its best groups
+        allowed = (group_allowed(G, w.n_group, w.topk_group, lib=lib) if w.n_group > 1
+                   else None)
+        ids, s, wts, q = route(G, K, Kext, w.gate == "sigmoid", w.norm_topk, allowed=allowed,
+                               lib=lib)
         stats = None
         if w.routing == "restricted":
             path, stats, rids, rw = self._restricted_step(G, ids, q, wts)
@@ -299,6 +325,14 @@ class OracleLayer:
         w, lib = self.w, self.lib
         K, E = w.top_k, w.n_experts
         stats = None
+        restricted = None
+        if self.support_valid:
+            # the model's rule with the selectable experts limited to the support; None when
+            # some row is left with fewer than K selectable experts
+            allowed = (group_allowed(G, w.n_group, w.topk_group, base=self.inA, lib=lib)
+                       if w.n_group > 1 else self.inA)
+            restricted = route_restricted(G, K, allowed, w.gate == "sigmoid", w.norm_topk,
+                                          lib=lib)
         if not self.support_valid:
             path = 1
         elif w.atlas_period > 0 and self.iter - self.built_iter >= w.atlas_period:
@@ -306,7 +340,7 @@ class OracleLayer:
             self.counters["period_update"] += 1
         else:
             nU = under_covered(ids, q, K, self.inA, w.alpha, lib=lib)
-            short = int(self.inA.sum()) < K
+            short = restricted is None
             if short or w.q[1] * nU > (w.q[1] - w.q[0]) * w.M:
                 path = 2
                 self.counters["coverage_fallback"] += 1
@@ -326,7 +360,7 @@ class OracleLayer:
         else:
             self.counters["hot_skip"] += 1
             self.counters["restricted"] += 1
-            rids, rw = route_restricted(G, K, self.inA, w.gate == "sigmoid", w.norm_topk, lib=lib)
+            rids, rw = restricted
             mask = self.inA
         self.inS = np.ascontiguousarray(mask, dtype=np.uint8).copy()
         self.slot_of, self.S_list = slots_of(self.inS)

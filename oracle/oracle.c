@@ -101,15 +101,16 @@ static int before(float ga, int ea, float gb, int eb) {
  * q:   the Atlas integer weight floor(s * 2^16 + 1/2) of each candidate.
  */
 void orc_route(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, const float* G,
-               int32_t* ids, double* s, double* w, int64_t* q) {
+               const uint8_t* allowed, int32_t* ids, double* s, double* w, int64_t* q) {
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < M; ++t) {
     const float* g = G + (size_t)t * E;
+    const uint8_t* al = allowed ? allowed + (size_t)t * E : NULL;
     unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
     for (int j = 0; j < Kext; ++j) {
       int best = -1;
       for (int e = 0; e < E; ++e)
-        if (!taken[e] && (best < 0 || before(g[e], e, g[best], best))) best = e;
+        if ((!al || al[e]) && !taken[e] && (best < 0 || before(g[e], e, g[best], best))) best = e;
       taken[best] = 1;
       ids[(size_t)t * Kext + j] = best;
     }
@@ -331,11 +332,19 @@ int orc_atlas_build(int M, int E, int K, int Kext, const int32_t* ids, const int
  * all E, or sigmoid); the weights are the selected scores, normalised over the K selected
  * when norm_topk.  Needs at least K experts in the support.  rids, rw: [M x K].
  */
-void orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
-                          const uint8_t* inA, int32_t* rids, double* rw) {
+int orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
+                         const uint8_t* allowed, int32_t* rids, double* rw) {
+  int n_short = 0;
+  for (int t = 0; t < M; ++t) {
+    int n = 0;
+    for (int e = 0; e < E; ++e) n += allowed[(size_t)t * E + e] != 0;
+    n_short += n < K;
+  }
+  if (n_short) return n_short;
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < M; ++t) {
     const float* g = G + (size_t)t * E;
+    const uint8_t* inA = allowed + (size_t)t * E;
     unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
     double zmax = -INFINITY, z = 0.0;
     if (!gate_sigmoid) {
@@ -360,6 +369,56 @@ void orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, 
     double denom = 0.0;
     for (int k = 0; k < K; ++k) denom += sk[k];
     for (int k = 0; k < K; ++k) rw[(size_t)t * K + k] = norm_topk ? sk[k] / denom : sk[k];
+  }
+  return 0;
+}
+
+/*
+ * Group-limited selectable set ([T] Expert Atlas, third step: the routing kernel runs the
+ * model's group-limited top-k rule, with the selectable experts limited to the support).
+ * Experts form n_group contiguous groups of E / n_group ids.  Among the experts that base
+ * allows (base = NULL: all; else a [E] support mask), a group is ranked by its best expert
+ * under the selection key (logit desc, id asc), groups without an allowed expert last; the
+ * first topk_group groups are kept.  allowed[t][e] = base[e] and e's group kept for row t.
+ */
+void orc_group_allowed(int M, int E, int n_group, int topk_group, const float* G,
+                       const uint8_t* base, uint8_t* allowed) {
+  const int gs = E / n_group;
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < M; ++t) {
+    const float* g = G + (size_t)t * E;
+    int* best = (int*)malloc(sizeof(int) * (size_t)n_group);
+    unsigned char* kept = (unsigned char*)calloc((size_t)n_group, 1);
+    for (int gr = 0; gr < n_group; ++gr) {
+      best[gr] = -1;
+      for (int e = gr * gs; e < (gr + 1) * gs; ++e)
+        if ((!base || base[e]) && (best[gr] < 0 || before(g[e], e, g[best[gr]], best[gr])))
+          best[gr] = e;
+    }
+    for (int r = 0; r < topk_group; ++r) {
+      int pick = -1;
+      for (int gr = 0; gr < n_group; ++gr) {
+        if (kept[gr] || best[gr] < 0) continue;
+#if ORC_MUTATE == 9
+        /* planted: a group ranked by its first allowed expert instead of its best */
+        int fg = -1, fp = -1;
+        for (int e = gr * gs; e < (gr + 1) * gs && fg < 0; ++e)
+          if (!base || base[e]) fg = e;
+        if (pick >= 0)
+          for (int e = pick * gs; e < (pick + 1) * gs && fp < 0; ++e)
+            if (!base || base[e]) fp = e;
+        if (pick < 0 || before(g[fg], fg, g[fp], fp)) pick = gr;
+#else
+        if (pick < 0 || before(g[best[gr]], best[gr], g[best[pick]], best[pick])) pick = gr;
+#endif
+      }
+      if (pick < 0) break;
+      kept[pick] = 1;
+    }
+    for (int e = 0; e < E; ++e)
+      allowed[(size_t)t * E + e] = (uint8_t)((!base || base[e]) && kept[e / gs]);
+    free(best);
+    free(kept);
   }
 }
 

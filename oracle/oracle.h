@@ -27,8 +27,12 @@ int orc_num_threads(void);
 void orc_router_logits(int M, int H, int E, int act_bf16, const void* x, const float* Wg,
                        const float* bias, float* G);
 
+/* allowed: [M x E] selectable experts per row, or NULL for all */
 void orc_route(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, const float* G,
-               int32_t* ids, double* s, double* w, int64_t* q);
+               const uint8_t* allowed, int32_t* ids, double* s, double* w, int64_t* q);
+
+void orc_group_allowed(int M, int E, int n_group, int topk_group, const float* G,
+                       const uint8_t* base, uint8_t* allowed);
 
 int orc_support_status(int M, int K, int Kext, const int32_t* ids, const uint8_t* inS,
                        int support_valid);
@@ -43,8 +47,10 @@ int orc_atlas_build(int M, int E, int K, int Kext, const int32_t* ids, const int
                     int beta_den, uint8_t* inA, int32_t* slot_of, int32_t* S_list,
                     int64_t* stats);
 
-void orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
-                          const uint8_t* inA, int32_t* rids, double* rw);
+/* allowed: [M x E]; returns the number of rows with fewer than K selectable experts (then
+   nothing is written) */
+int orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, const float* G,
+                         const uint8_t* allowed, int32_t* rids, double* rw);
 
 int64_t orc_under_covered(int M, int K, int Kext, const int32_t* ids, const int64_t* q,
                           const uint8_t* inS, int alpha_num, int alpha_den);

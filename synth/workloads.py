@@ -82,6 +82,10 @@ class Workload:
     # atlas_period > 0 rebuilds a restricted support after that many iterations
     routing: str = "exact"
     atlas_period: int = 0
+    # group-limited top-k: experts in n_group contiguous groups, each position selecting among
+    # the experts of its topk_group best groups (n_group <= 1: no grouping)
+    n_group: int = 0
+    topk_group: int = 0
 
     @property
     def M(self) -> int:
@@ -327,6 +331,7 @@ def desc_fields(w: Workload, **overrides) -> dict:
              staleness_R=w.staleness_R, atlas_m=w.m_ext, atlas_B=w.B, atlas_c=w.c,
              alpha_num=w.alpha[0], alpha_den=w.alpha[1], q_num=w.q[0], q_den=w.q[1],
              beta_num=w.beta[0], beta_den=w.beta[1], flags=0,
-             routing=1 if w.routing == "restricted" else 0, atlas_period=w.atlas_period)
+             routing=1 if w.routing == "restricted" else 0, atlas_period=w.atlas_period,
+             n_group=w.n_group, topk_group=w.topk_group)
     f.update(overrides)
     return f

@@ -394,9 +394,87 @@ def pin_restricted_lifecycle(orc, lib):
     assert Ln.counters["coverage_fallback"] >= 1
 
 
+def _groups_by_first_appearance(G, n_group, topk_group, base=None):
+    """Brute force of the group-limited selectable set by a second formulation: walk the
+    experts in key order (stable sort on -G, so ties -> lower id) and keep the groups in the
+    order their first (allowed) expert appears; a group's first appearance is its best expert."""
+    M, E = G.shape
+    gs = E // n_group
+    order = np.argsort(-G.astype(np.float64), axis=1, kind="stable")
+    out = np.zeros((M, E), np.uint8)
+    for t in range(M):
+        kept = []
+        for e in order[t]:
+            if base is not None and not base[e]:
+                continue
+            if e // gs not in kept:
+                kept.append(e // gs)
+            if len(kept) == topk_group:
+                break
+        for gr in kept:
+            lo = gr * gs
+            out[t, lo:lo + gs] = 1 if base is None else base[lo:lo + gs]
+    return out
+
+
+def pin_group_limited(orc, lib):
+    """Group-limited top-k: the kept groups against the first-appearance walk (with and
+    without a support mask); the candidates lie in at most topk_group groups and start with
+    the overall best expert; topk_group = n_group and single-expert groups reduce to the
+    plain top-K."""
+    rng = np.random.default_rng(13)
+    M, E, K, Kext, ng, tg = 60, 24, 3, 6, 6, 2
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    G[:, 13] = G[:, 2]                              # exact ties across groups
+    for base in (None, (rng.random(E) < 0.6).astype(np.uint8)):
+        al = orc.group_allowed(G, ng, tg, base=base, lib=lib)
+        assert np.array_equal(al, _groups_by_first_appearance(G, ng, tg, base)), \
+            "kept groups must be the first topk_group groups met in key order"
+    al = orc.group_allowed(G, ng, tg, lib=lib)
+    ids, s, w, q = orc.route(G, K, Kext, True, True, allowed=al, lib=lib)
+    plain = np.argsort(-G.astype(np.float64), axis=1, kind="stable")
+    assert (ids[:, 0] == plain[:, 0]).all()
+    assert all(len(set((ids[t] // (E // ng)).tolist())) <= tg for t in range(M))
+    masked = np.where(al.astype(bool), -G.astype(np.float64), np.inf)
+    assert np.array_equal(ids, np.argsort(masked, axis=1, kind="stable")[:, :Kext])
+    full = expit(G.astype(np.float64))
+    np.testing.assert_allclose(s, np.take_along_axis(full, ids, axis=1), rtol=1e-13, atol=0)
+    ids0, s0, w0, q0 = orc.route(G, K, Kext, True, True, lib=lib)
+    for ng2, tg2 in ((ng, ng), (E, Kext)):
+        al2 = orc.group_allowed(G, ng2, tg2, lib=lib)
+        ids2, s2, w2, q2 = orc.route(G, K, Kext, True, True, allowed=al2, lib=lib)
+        assert np.array_equal(ids2, ids0) and np.array_equal(w2, w0)
+
+
+def pin_group_limited_restricted(orc, lib):
+    """Group-limited routing inside the support over a small block: candidates and routed
+    experts stay within topk_group groups; hot-skip forwards route to the masked stable sort
+    over the experts of the groups met first among the support's experts."""
+    w = small_workload(routing="restricted", n_experts=16, top_k=3, iters=6,
+                       liveness="uniform", n_shared=0, shared_inter=0, n_group=4, topk_group=2)
+    Wl = synth.layer_weights(w, 0)
+    D = synth.decoded_masks(w)
+    X = synth.hidden_states(w, 0, D)
+    L = orc.OracleLayer(w, Wl, lib=lib)
+    gs = w.n_experts // w.n_group
+    for it in range(w.iters):
+        out = L.forward(X[it], D[it])
+        for t in range(w.M):
+            assert len(set((out["ids"][t] // gs).tolist())) <= w.topk_group
+            assert len(set((out["routed_ids"][t] // gs).tolist())) <= w.topk_group
+        if not out["path"]:
+            al = _groups_by_first_appearance(out["G"], w.n_group, w.topk_group, out["inA"])
+            masked = np.where(al.astype(bool), -out["G"].astype(np.float64), np.inf)
+            assert np.array_equal(out["routed_ids"],
+                                  np.argsort(masked, axis=1, kind="stable")[:, :w.top_k])
+        L.commit()
+    assert L.counters["restricted"] >= 1
+
+
 PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
         pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness,
-        pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle]
+        pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle,
+        pin_group_limited, pin_group_limited_restricted]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -429,7 +507,8 @@ def test_anomaly_and_special_fresh_cases(orc):
 MUTATIONS = {1: "router bias dropped", 2: "down-projection operand indexed wrongly",
              3: "SiLU sign flipped", 4: "ties broken toward the higher id",
              5: "refresh-due test dropped", 6: "worklist in position order",
-             7: "H_e uses a strict inequality", 8: "restricted top-K ignores the support"}
+             7: "H_e uses a strict inequality", 8: "restricted top-K ignores the support",
+             9: "groups ranked by their first expert, not their best"}
 
 
 @pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
