@@ -45,6 +45,10 @@ def parse():
                     help="top-K over all experts, or inside the layer's Atlas support")
     ap.add_argument("--atlas-period", type=int, default=0,
                     help="restricted routing: rebuild the support after this many iterations")
+    ap.add_argument("--n-group", type=int, default=0,
+                    help="group-limited top-k: number of contiguous expert groups (0: off)")
+    ap.add_argument("--topk-group", type=int, default=0,
+                    help="group-limited top-k: groups each position selects from")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,6 +117,9 @@ def main():
     if args.routing != "exact":
         over["routing"] = args.routing
         over["atlas_period"] = args.atlas_period
+    if args.n_group > 1:
+        over["n_group"] = args.n_group
+        over["topk_group"] = args.topk_group
     w = synth.workload(args.workload, **over)
     n_layers = w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)
     M, H, I, E, K = w.M, w.hidden, w.inter, w.n_experts, w.top_k
@@ -285,7 +292,8 @@ def main():
                    "positions": M, "hidden": H, "experts": E, "top_k": K, "inter": I,
                    "shared_expert": bool(w.n_shared), "staleness_R": w.staleness_R,
                    "forced_fraction": w.forced_fraction, "routing": w.routing,
-                   "atlas_period": w.atlas_period, "step": "one block"},
+                   "atlas_period": w.atlas_period, "n_group": w.n_group,
+                   "topk_group": w.topk_group, "step": "one block"},
         "us_per_layer_iteration": round(us_per_layer_iter, 2),
         "fresh_pairs_per_block": pairs_per_block,
         "fresh_fraction": round(per_block["fresh_rows"] / (M * layer_iters), 4),

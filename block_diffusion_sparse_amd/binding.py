@@ -35,7 +35,7 @@ class epoch_desc(ctypes.Structure):
         "n_layers", "hidden", "n_experts", "top_k", "inter", "n_shared", "shared_inter", "batch",
         "block", "gate", "norm_topk", "act_dtype", "staleness_R", "atlas_m", "atlas_B", "atlas_c",
         "alpha_num", "alpha_den", "q_num", "q_den", "beta_num", "beta_den", "flags", "routing",
-        "atlas_period")]
+        "atlas_period", "n_group", "topk_group")]
 
 
 class epoch_layer_weights(ctypes.Structure):

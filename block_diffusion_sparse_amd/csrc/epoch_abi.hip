@@ -59,6 +59,12 @@ int32_t check_desc(const epoch_desc* d) {
     return EPOCH_E_SHAPE;
   const int kext = std::min(d->top_k + d->atlas_m, d->n_experts);
   if (kext > kMaxKext) return EPOCH_E_SHAPE;
+  if (d->n_group < 0) return EPOCH_E_SHAPE;
+  if (d->n_group > 1) {
+    if (d->n_group > kMaxGroups || d->n_experts % d->n_group) return EPOCH_E_SHAPE;
+    if (d->topk_group < 1 || d->topk_group > d->n_group) return EPOCH_E_SHAPE;
+    if ((long long)d->topk_group * (d->n_experts / d->n_group) < kext) return EPOCH_E_SHAPE;
+  }
   if (d->hidden % 64) return EPOCH_E_SHAPE;
   if (d->act_dtype == EPOCH_DTYPE_BF16) {
     if (d->inter % 64) return EPOCH_E_SHAPE;
@@ -110,6 +116,8 @@ Shape make_shape(const epoch_desc* d) {
   s.bd = d->beta_den;
   s.restricted = d->routing == EPOCH_ROUTING_RESTRICTED;
   s.atlas_period = d->atlas_period;
+  s.n_group = d->n_group > 1 ? d->n_group : 0;
+  s.topk_group = d->n_group > 1 ? d->topk_group : 0;
   return s;
 }
 

@@ -25,7 +25,10 @@ constexpr int kDownCols = 64;     // output columns per down workgroup
 // written by the plan step for the placement.
 enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
        FLAG_NTILES_BIG = 5, FLAG_FRESH_ALL = 6, FLAG_UNDER = 7, FLAG_ROUTE_R = 8,
-       FLAG_WORDS = 16 };
+       FLAG_SHORT = 9, FLAG_WORDS = 16 };
+// SHORT (restricted mode): some position has fewer than K selectable support experts; set by
+// the router, cleared by the plan step.
+constexpr int kMaxGroups = 64;
 
 // Device-side view of one layer's persistent state.
 struct LayerState {
@@ -88,7 +91,7 @@ struct Scratch {
 struct Shape {
   int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
   int n_chunks, ksplit, router_bt, T_max, T_dense, T_big_max, big_routed;
-  int restricted, atlas_period;
+  int restricted, atlas_period, n_group, topk_group;  // n_group <= 1: no grouping
   int B, c, an, ad, qn, qd, bn, bd;
 };
 

@@ -160,7 +160,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     } else if (s.atlas_period > 0 && iter - built >= s.atlas_period) {
       path = 2;
       reason = 2;
-    } else if (a_size < K || qd * nU > (qd - qn) * (long long)M) {
+    } else if (a_size < K || W.flags[FLAG_SHORT] != 0 || qd * nU > (qd - qn) * (long long)M) {
       path = 2;
       reason = 1;
     } else {
@@ -482,6 +482,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     W.flags[FLAG_MISS] = 0;
     W.flags[FLAG_ANOMALY] = 0;
     W.flags[FLAG_UNDER] = 0;
+    W.flags[FLAG_SHORT] = 0;
   }
   if (FUSED_PLACE) {
     // chunk_base, eoffs and chunk_foff were written above by this workgroup

@@ -70,7 +70,12 @@ struct RouteArgs {
   const uint8_t* force;
   int E, K, Kext, gate_sigmoid, norm_topk, R, iter;
   int restricted, an, ad;  // support-restricted routing; coverage floor alpha = an / ad
+  int n_group, topk_group;  // group-limited top-k (n_group = 0: off)
 };
+
+// LDS of one wave's top-k: candidate scores (K_ext), in-support scores (K), group maxima and
+// kept-group flags, in doubles
+constexpr int kRouteLds = 2 * kMaxKext + kMaxGroups + 8;
 
 __device__ __forceinline__ uint64_t sel_key(float g, int e) {
   uint32_t u = __float_as_uint(g);
@@ -141,9 +146,48 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
       }
     }
   };
+  // group-limited rule: keep the keys of the experts of this position's topk_group best
+  // groups, a group ranking by its best key (largest key among its non-zero ones)
+  const int ng = ra.n_group, gsz = ng ? E / ng : 1;
+  auto group_keep = [&](const uint64_t* kk, uint64_t* out) {
+    unsigned long long* gmax = reinterpret_cast<unsigned long long*>(s_buf + 2 * kMaxKext);
+    uint8_t* keep = reinterpret_cast<uint8_t*>(s_buf + 2 * kMaxKext + kMaxGroups);
+    if (lane < ng) gmax[lane] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NPER; ++j)
+      if (kk[j]) atomicMax(&gmax[(lane + 64 * j) / gsz], (unsigned long long)kk[j]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t gk = lane < ng ? gmax[lane] : 0ull;
+    int grank = 0;
+    for (int g2 = 0; g2 < ng; ++g2) {
+      const uint64_t o = ((uint64_t)__builtin_amdgcn_readlane((int)(gk >> 32), g2) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gk, g2);
+      grank += o > gk;
+    }
+    if (lane < ng) keep[lane] = (gk != 0ull && grank < ra.topk_group) ? 1 : 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) out[j] = (kk[j] && keep[(lane + 64 * j) / gsz]) ? kk[j] : 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   int rank[NPER];
   uint64_t selm[NPER];
-  select(key, Kext, selm, rank);
+  if (ng) {
+    uint64_t kg[NPER];
+    group_keep(key, kg);
+    select(kg, Kext, selm, rank);
+  } else {
+    select(key, Kext, selm, rank);
+  }
   // softmax normaliser over all E (max = the best key's logit)
   double zmax = 0.0, z = 0.0;
   if (!gate_sigmoid) {
@@ -192,6 +236,11 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
     uint64_t kr[NPER];
 #pragma unroll
     for (int j = 0; j < NPER; ++j) kr[j] = in_a[j] ? key[j] : 0ull;
+    if (ng) group_keep(kr, kr);  // the model's rule with the selectable experts in the support
+    int n_sel = 0;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) n_sel += __popcll(ballot64(kr[j] != 0ull));
+    if (n_sel < K && lane == 0) W.flags[FLAG_SHORT] = 1;  // this forward takes the full path
     int rrank[NPER];
     uint64_t rsel[NPER];
     select(kr, K, rsel, rrank);
@@ -245,7 +294,7 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route_rows(const float* __restrict__ G, RouteArgs ra,
                                                     int M) {
-  __shared__ double s_buf[4][2 * kMaxKext];
+  __shared__ double s_buf[4][kRouteLds];
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t < M) route_row<NPER>(t, G, ra, s_buf[wave]);
@@ -356,8 +405,8 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
     else
       launch_k_router<float, 16>(s, x, Wg, bias, W, st);
   }
-  const RouteArgs ra{L,         W,     D,    force, s.E,          s.K,  s.Kext, s.gate_sigmoid,
-                     s.norm_topk, s.R, iter, s.restricted, s.an, s.ad};
+  const RouteArgs ra{L,         W,   D,    force,        s.E,  s.K,  s.Kext,    s.gate_sigmoid,
+                     s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group};
   const int nper = (s.E + 63) / 64;
 #define EPOCH_ROUTE_ROWS(NP) \
   hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)

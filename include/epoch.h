@@ -123,6 +123,16 @@ typedef struct epoch_desc {
   int32_t routing;      /* EPOCH_ROUTING_EXACT or EPOCH_ROUTING_RESTRICTED */
   int32_t atlas_period; /* restricted mode: rebuild the support after this many iterations
                            (0 = only on the coverage check); must be 0 in exact mode */
+  /* group-limited top-k (teardown, Expert Atlas step three: "the model's group-limited
+     top-k rule"): the experts form n_group contiguous groups of E / n_group ids; each
+     position ranks the groups by their best expert (selection key: logit desc, id asc;
+     in restricted mode among the support's experts) and selects its K_ext candidates and
+     K routed experts among the experts of its topk_group best groups.  n_group <= 1: off.
+     Otherwise 2 <= n_group <= 64, E % n_group == 0, 1 <= topk_group <= n_group and
+     topk_group * E / n_group >= K_ext.  A restricted forward in which some position's
+     groups hold fewer than K support experts routes over all experts (full path). */
+  int32_t n_group;
+  int32_t topk_group;
 } epoch_desc;
 
 /* Device pointers of one layer's weights; all row-major, contiguous, caller-owned and

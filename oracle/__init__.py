@@ -85,6 +85,8 @@ def route(G, K, Kext, gate_sigmoid, norm_topk, allowed=None, lib=None):
     w = np.empty((M, K), dtype=np.float64)
     q = np.empty((M, Kext), dtype=np.int64)
     al = None if allowed is None else np.ascontiguousarray(allowed, dtype=np.uint8)
+    if al is not None and (al.sum(axis=1) < Kext).any():
+        raise ValueError("fewer selectable experts than K_ext candidates in some row")
     lib.orc_route(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _c_int(int(gate_sigmoid)),
                   _c_int(int(norm_topk)), _p(G), _p(al), _p(ids), _p(s), _p(w), _p(q))
     return ids, s, w, q
