@@ -231,14 +231,18 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
 
 namespace epoch {
 
-// Compute-bound variant for tiles with many rows (the shared expert over all M positions):
-// a 128-row x 128-weight-row output tile per workgroup, K in chunks of 64, the activation and
-// weight chunks both staged in LDS (double-buffered, loaded one chunk ahead through
-// registers), four waves in a 2 x 2 arrangement, each accumulating a 64 x 64 sub-tile with
-// v_mfma_f32_16x16x32_bf16 (4 x 4 blocks).  Gate/up: the 128 staged weight rows are
-// [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g and u
-// of the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of W2.
-// Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
+// Compute-bound variant for tiles with many rows (the shared expert over all M positions,
+// routed experts with many fresh pairs): a 128-row x 128-weight-row output tile per
+// workgroup, four waves in a 2 x 2 arrangement, each accumulating a 64 x 64 sub-tile with
+// v_mfma_f32_16x16x32_bf16 (4 x 4 blocks).  K runs in chunks of KC = 32: both operands of a
+// chunk are staged through LDS (double-buffered), and chunk loads from global memory run NR - 1
+// steps ahead in a register ring, so that NR - 2 chunks stay in flight while a chunk is
+// multiplied (one chunk is ~256 MFMA cycles per wave, far shorter than a memory round trip).
+// Every global load is issued by every lane with no branch around it (rows past the tile read
+// a valid stand-in, replaced by zeros when stored to LDS).  Gate/up: the 128 staged weight rows
+// are [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g
+// and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of
+// W2.  Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
 template <bool GATEUP, bool ROUTED>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
@@ -247,10 +251,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
-  constexpr int BR = 128, KC = 64, LD = KC + 8, SEG_ROW = KC / 8;
+  constexpr int BR = 128, KC = 32, SEG_ROW = KC / 8;
+  constexpr int NSEG = BR * SEG_ROW / 256;  // 16-byte segments per thread per operand and chunk
+  constexpr int NR = 4;                     // register ring depth (chunks), even
+  constexpr int NB = 3;                     // LDS buffers (chunks)
   constexpr int CBW = GATEUP ? 64 : 128;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BR * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BR * LD];
+  // LDS rows of KC = 32 bf16 (64 bytes, four 16-byte segments), no padding: segment c8 of row
+  // `row` sits at slot c8 ^ ((row >> 2) & 3), so that the 16 rows of an MFMA fragment read and
+  // the four segments of the rows a wave stores both fall on distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BR * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
   const int pos = blockIdx.x >> 3;
   const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
@@ -264,16 +274,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   const int wm = wave & 1, wn = wave >> 1;
   const size_t estride = (size_t)Ndim * Kdim;
   const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  // staging: 4 activation and 4 weight segments of 16 bytes per thread per chunk
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
-  bool aok[4], bok[4];
-  int dst[4];
+  // staging: NSEG activation and NSEG weight segments of 16 bytes per thread per chunk
+  const uint16_t* asrc[NSEG];
+  const uint16_t* bsrc[NSEG];
+  bool aok[NSEG], bok[NSEG];
+  int dst[NSEG];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NSEG; ++j) {
     const int seg = tid + 256 * j;
     const int row = seg / SEG_ROW, c8 = seg % SEG_ROW;
-    dst[j] = row * LD + c8 * 8;
+    dst[j] = row * KC + ((c8 ^ ((row >> 2) & 3)) * 8);
     const int p = tr.row0 + row;
     aok[j] = p < tr.row_end;
     const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
@@ -292,19 +302,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     bsrc[j] = base + e * estride + (size_t)(bok[j] ? wrow : 0) * Kdim + c8 * 8;
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 ra[4], rb[4];  // the chunk in flight from global memory to LDS
-  auto load = [&](int c) {
+  u32x4 ra[NR][NSEG], rb[NR][NSEG];  // chunk x waits in slot x % NR from its load to its store
+  auto load = [&](int c, int slot) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = aok[j] ? *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC) : zero;
-      rb[j] = bok[j] ? *reinterpret_cast<const u32x4*>(bsrc[j] + (size_t)c * KC) : zero;
+    for (int j = 0; j < NSEG; ++j) {
+      ra[slot][j] = *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC);
+      rb[slot][j] = *reinterpret_cast<const u32x4*>(bsrc[j] + (size_t)c * KC);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int slot) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(&As[buf][dst[j]]) = ra[j];
-      *reinterpret_cast<u32x4*>(&Bs[buf][dst[j]]) = rb[j];
+    for (int j = 0; j < NSEG; ++j) {
+      *reinterpret_cast<u32x4*>(&As[buf][dst[j]]) = aok[j] ? ra[slot][j] : zero;
+      *reinterpret_cast<u32x4*>(&Bs[buf][dst[j]]) = bok[j] ? rb[slot][j] : zero;
     }
   };
   f32x4 acc[4][4];
@@ -312,34 +322,59 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
-  auto compute = [&](int buf) {
-    const uint16_t* ab = &As[buf][(64 * wm + r) * LD + 8 * g];
-    const uint16_t* bb = &Bs[buf][(64 * wn + r) * LD + 8 * g];
+  // fragments of one chunk: lane (r, g) reads segment g of rows 16 m + r, whose slot depends
+  // on r only; two register sets, so that chunk c + 1 is read from LDS while c is multiplied
+  const int swz = (g ^ ((r >> 2) & 3)) * 8;
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](int buf, int set) {
+    const uint16_t* ab = &As[buf][(64 * wm + r) * KC + swz];
+    const uint16_t* bb = &Bs[buf][(64 * wn + r) * KC + swz];
 #pragma unroll
-    for (int s = 0; s < KC / 32; ++s) {
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        fa[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * LD + 32 * s));
-        fb[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bb + m * 16 * LD + 32 * s));
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+    for (int m = 0; m < 4; ++m) {
+      fa[set][m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * KC));
+      fb[set][m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bb + m * 16 * KC));
     }
   };
-  const int nch = Kdim / KC;
-  load(0);
-  store(0);
-  __syncthreads();
-  // chunk c sits in LDS buffer c & 1; chunk c + 1 is fetched while chunk c is multiplied
-  for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) load(c + 1);
-    compute(c & 1);
-    if (c + 1 < nch) store((c + 1) & 1);
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][m], fb[set][n], acc[m][n], 0, 0, 0);
+  };
+  static_assert(KC == 32, "one MFMA k-step per chunk");
+  static_assert(NR % 2 == 0, "fragment sets alternate with the chunk parity");
+  // Chunk x: fetched from global into ring slot x % NR at step x - NR (in the prologue for
+  // x < NR), stored to LDS buffer x % NB at step x - 2, read into fragment set x & 1 at step
+  // x - 1, multiplied at step x.  A buffer is rewritten two barriers after the step that last
+  // read it; a ring slot is refilled after its chunk went to LDS.
+  auto step = [&](int c, int u, bool pre, bool rd, bool st) {
+    if (pre) load(c + NR, u % NR);
+    __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the multiply
+    if (rd) read_frags((c + 1) % NB, (u + 1) & 1);
+    mma(u & 1);
+    if (st) store((c + 2) % NB, (u + 2) % NR);
     __syncthreads();
+  };
+  const int nch = Kdim / KC;
+#pragma unroll
+  for (int x = 0; x < NR; ++x)
+    if (x < nch) load(x, x);
+  store(0, 0);
+  if (nch > 1) store(1, 1);
+  __syncthreads();
+  read_frags(0, 0);
+  // steady state: NR steps per trip (kb a multiple of NR, so slot and set follow u), every
+  // fetch, read and store in range
+  int kb = 0;
+  for (; kb + 2 * NR - 1 < nch; kb += NR) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) step(kb + u, u, true, true, true);
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * NR - 1; ++u) {
+    const int c = kb + u;
+    if (c < nch) step(c, u, c + NR < nch, c + 1 < nch, c + 2 < nch);
   }
   // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
 #pragma unroll

@@ -135,7 +135,7 @@ __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
 // under-covered by the support (or with fewer than K experts in it) rebuilds the support
 // and routes over all experts, its routed experts getting slots for this forward only;
 // otherwise (hot-skip) the slots are the support and the forward routes inside it.
-// Returns 1 when the forward routes inside the support.
+// Returns bit 0 = the forward routes inside the support, bit 1 = the slot lists were rewritten.
 __device__ int support_phase(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                              SupportLds& sh) {
   const int tid = threadIdx.x;
@@ -150,7 +150,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     path = !valid ? 1 : (W.flags[FLAG_MISS] != 0 ? 2 : 0);
     if (path == 0) {
       if (tid == 0) L.counters[EPOCH_CNT_HOT_SKIP] += 1;
-      return 0;
+      return 0;  // slots unchanged
     }
   } else {
     const int a_valid = L.A_state[0], built = L.A_state[1], a_size = L.A_state[2];
@@ -292,7 +292,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     }
   }
   __syncthreads();
-  return path == 0 ? 1 : 0;
+  return (path == 0 ? 1 : 0) | 2;  // bit 0: route inside the support; bit 1: slots rewritten
 }
 
 // Stable placement of one chunk by one wave (teardown, FreshLane pack: fresh rows with their
@@ -318,11 +318,6 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
   const int32_t* it = route_r ? W.rids + (size_t)(in ? t : 0) * K
                               : W.ids + (size_t)(in ? t : 0) * Kext;
   const float* wt = (route_r ? W.rw : W.w) + (size_t)(in ? t : 0) * K;
-  if (in)
-    for (int k = 0; k < K; ++k) {
-      W.routed_ids[(size_t)t * K + k] = it[k];
-      W.routed_w[(size_t)t * K + k] = wt[k];
-    }
   if (fresh)
     for (int k = 0; k < K; ++k) atomicOr(&mask[it[k]], 1ull << lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -344,6 +339,12 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
   }
   const uint64_t fb = ballot64(fresh);
   if (fresh) W.fresh_list[W.chunk_foff[chunk] + __popcll(fb & below)] = t;
+  // the routing the worklist used, for every position (last: nothing above waits on it)
+  if (in)
+    for (int k = 0; k < K; ++k) {
+      W.routed_ids[(size_t)t * K + k] = it[k];
+      W.routed_w[(size_t)t * K + k] = wt[k];
+    }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -372,7 +373,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   __shared__ unsigned long long pmask[FUSED_PLACE ? kPlanWaves : 1]
                                      [FUSED_PLACE ? kFusedPlaceMaxExperts : 1];
   const int tid = threadIdx.x;
-  const bool route_r = support_phase(s, iter, L, W, sh) != 0;
+  // global reads that do not depend on the support step, issued before it
+  const int nch0 = s.n_chunks;
+  const int pre_cf = tid < nch0 ? W.chunk_fresh[tid] : 0;
+  const int pre_nS = *L.S_size;
+  const int pre_ex = tid < pre_nS ? L.S_list[tid] : 0;
+  const int sp = support_phase(s, iter, L, W, sh);
+  const bool route_r = (sp & 1) != 0;
   __syncthreads();
 
   const int E = s.E, nch = s.n_chunks;
@@ -423,10 +430,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   __syncthreads();
   // slot offsets and the tile tables (one support slot per thread); an expert with at least
   // kBigRows pairs goes to the compute-bound table when the shape enables it
-  const int nS = *L.S_size;
+  const bool slots_new = (sp & 2) != 0;
+  const int nS = slots_new ? *L.S_size : pre_nS;
   int my_tiles = 0, my_big = 0, my_off = 0;
   if (tid < nS) {
-    const int ex = L.S_list[tid];
+    const int ex = slots_new ? L.S_list[tid] : pre_ex;
     my_off = sh.scan[ex];
     if (s.big_routed && tot[ex] >= kBigRows)
       my_big = (tot[ex] + kBigTile - 1) / kBigTile;
@@ -454,7 +462,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   int carry = 0;
   for (int base = 0; base < nch; base += kPlanThreads) {
     const int c = base + tid;
-    const int nf = c < nch ? (anomaly ? min(kChunk, s.M - c * kChunk) : W.chunk_fresh[c]) : 0;
+    const int nf = c < nch ? (anomaly ? min(kChunk, s.M - c * kChunk)
+                                      : (base == 0 ? pre_cf : W.chunk_fresh[c]))
+                           : 0;
     int pass;
     const int incl = block_incl_scan(nf, sh.wsum, &pass);
     if (c < nch) {
@@ -463,14 +473,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     }
     carry += pass;
   }
+  const int touched = __syncthreads_count(tid < E && tot[tid] > 0);
   if (tid == 0) {
     const int nfresh = carry;
     W.flags[FLAG_NFRESH] = nfresh;
     W.flags[FLAG_NPAIRS] = P;
     W.flags[FLAG_NTILES] = T;
     W.flags[FLAG_NTILES_BIG] = Tb;
-    int touched = 0;
-    for (int i = 0; i < E; ++i) touched += tot[i] > 0;
     L.counters[EPOCH_CNT_FRESH_ROWS] += nfresh;
     L.counters[EPOCH_CNT_PAIRS] += P;
     L.counters[EPOCH_CNT_TOUCHED] += touched;
