@@ -39,6 +39,7 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.orc_atlas_build.restype = _c_int
     lib.orc_route_restricted.restype = _c_int
     lib.orc_group_allowed.restype = None
+    lib.orc_live_decode.restype = _c_int
     for name in ("orc_router_logits", "orc_route", "orc_expert", "orc_moe_rows", "orc_commit",
                  "orc_dense_moe"):
         getattr(lib, name).restype = None
@@ -229,6 +230,25 @@ def dense_moe(x, Wg, bias, W1, W3, W2, SW1, SW3, SW2, K, gate_sigmoid, norm_topk
                       _p(x), _p(np.ascontiguousarray(Wg, dtype=np.float32)), _p(b), _p(W1),
                       _p(W3), _p(W2), _p(SW1), _p(SW3), _p(SW2), _p(R), _p(Y))
     return R, Y
+
+
+def live_decode(h, Wv, D, block, tau=0.95, token=None, lib=None) -> dict:
+    """Live-only threshold decoding of one refinement step (see orc_live_decode)."""
+    lib = lib or load()
+    h = np.ascontiguousarray(h)
+    Wv = np.ascontiguousarray(Wv)
+    M, H = h.shape
+    V = Wv.shape[0]
+    D = np.ascontiguousarray(D, dtype=np.uint8)
+    D_next = np.empty(M, np.uint8)
+    tok = np.full(M, -1, np.int32) if token is None else np.ascontiguousarray(token, np.int32).copy()
+    conf = np.empty(M, np.float64)
+    gap = np.empty(M, np.float64)
+    top = np.empty(M, np.int32)
+    n = lib.orc_live_decode(_c_int(M), _c_int(H), _c_int(V), _c_int(block), _c_int(_is_bf16(h)),
+                            _p(h), _p(Wv), _p(D), ctypes.c_double(tau), _p(D_next), _p(tok),
+                            _p(conf), _p(gap), _p(top))
+    return dict(D_next=D_next, token=tok, conf=conf, gap=gap, top=top, commits=int(n))
 
 
 class OracleLayer:

@@ -668,3 +668,74 @@ void orc_dense_moe(int M, int H, int I, int Is, int E, int K, int gate_sigmoid, 
     free(top);
   }
 }
+
+/*
+ * Live-only output decoding ([T] evaluation setup: greedy threshold decoding with commit
+ * threshold tau = 0.95, only live positions decoded; [T] LSP section: live logits z_{i,t} and
+ * their commit / no-commit decision).  For every live position t (D[t] = 0) of the block
+ * batch (t = b * block + p):
+ *   z_v = sum_h h[t,h] W[v,h]  (double)          top token v* = argmax z (lower id on ties)
+ *   conf_t = max_v softmax(z)_v = 1 / sum_v exp(z_v - z_{v*})
+ *   gap_t = z_{v*} - (second largest z)           (for reporting near ties)
+ * Commit: every live t with conf_t >= tau; a sequence b none of whose live positions reaches
+ * tau commits its single most confident live position (lower position on ties), so every
+ * refinement step decodes at least one position of a sequence that still has live ones.
+ * D_next = D with the commits set; token[t] = v* for committed t (others left unchanged).
+ * conf / gap are written for live positions (0 elsewhere).  Returns the number of commits.
+ */
+int orc_live_decode(int M, int H, int V, int block, int act_bf16, const void* h, const void* Wv,
+                    const uint8_t* D, double tau, uint8_t* D_next, int32_t* token, double* conf,
+                    double* gap, int32_t* top) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < M; ++t) {
+    conf[t] = 0.0;
+    gap[t] = 0.0;
+    top[t] = -1;
+    if (D[t]) continue;
+    double* z = (double*)malloc(sizeof(double) * (size_t)V);
+    int best = 0;
+    for (int v = 0; v < V; ++v) {
+      double acc = 0.0;
+      for (int k = 0; k < H; ++k)
+        acc += ld(h, act_bf16, (size_t)t * H + k) * ld(Wv, act_bf16, (size_t)v * H + k);
+      z[v] = acc;
+#if ORC_MUTATE == 10
+      if (acc >= z[best]) best = v; /* planted: ties toward the higher token id */
+#else
+      if (acc > z[best]) best = v;
+#endif
+    }
+    double second = -INFINITY, Z = 0.0;
+    for (int v = 0; v < V; ++v) {
+      if (v != best && z[v] > second) second = z[v];
+      Z += exp(z[v] - z[best]);
+    }
+    top[t] = best;
+    conf[t] = 1.0 / Z;
+    gap[t] = V > 1 ? z[best] - second : INFINITY;
+    free(z);
+  }
+  int commits = 0;
+  for (int t = 0; t < M; ++t) D_next[t] = D[t];
+  const int nb = M / block;
+  for (int b = 0; b < nb; ++b) {
+    int any = 0, arg = -1;
+    for (int p = 0; p < block; ++p) {
+      const int t = b * block + p;
+      if (D[t]) continue;
+      if (conf[t] >= tau) {
+        D_next[t] = 1;
+        token[t] = top[t];
+        ++commits;
+        any = 1;
+      }
+      if (arg < 0 || conf[t] > conf[arg]) arg = t;
+    }
+    if (!any && arg >= 0) {
+      D_next[arg] = 1;
+      token[arg] = top[arg];
+      ++commits;
+    }
+  }
+  return commits;
+}

@@ -80,6 +80,10 @@ void orc_dense_moe(int M, int H, int I, int Is, int E, int K, int gate_sigmoid, 
                    const void* W1, const void* W3, const void* W2, const void* SW1,
                    const void* SW3, const void* SW2, double* R_out, double* Y_out);
 
+int orc_live_decode(int M, int H, int V, int block, int act_bf16, const void* h, const void* Wv,
+                    const uint8_t* D, double tau, uint8_t* D_next, int32_t* token, double* conf,
+                    double* gap, int32_t* top);
+
 #ifdef __cplusplus
 }
 #endif

@@ -471,10 +471,56 @@ def pin_group_limited_restricted(orc, lib):
     assert L.counters["restricted"] >= 1
 
 
+def pin_live_decode(orc, lib):
+    """Live-only threshold decoding against numpy / scipy: logits as a float64 matmul of the
+    live rows, the top token as numpy argmax (first maximum, i.e. lower id on exact ties),
+    the confidence as the largest softmax probability; commits by the threshold rule, with
+    the most confident live position of an otherwise uncommitted sequence; decoded positions
+    untouched; one-token vocabularies commit every live position."""
+    rng = np.random.default_rng(14)
+    block, nb, H, V = 8, 3, 32, 50
+    M = block * nb
+    W = (rng.standard_normal((V, H)) * 0.3).astype(np.float32)
+    W[17] = W[5]                                   # exact tie between tokens 5 and 17
+    h = rng.standard_normal((M, H)).astype(np.float32) * 0.2
+    h[block + 2] = W[5] * 40.0                     # a row split between the tied tokens
+    # confident rows of sequence 1 ...
+    h[block + 6] = W[30] * 40.0
+    h[2 * block:3 * block] = W[9] * 40.0           # ... every row of sequence 2
+    D = np.zeros(M, np.uint8)
+    D[[0, 3, block + 1, 2 * block + 4]] = 1        # decoded positions
+    hb, Wb = synth.f32_to_bf16_bits(h), synth.f32_to_bf16_bits(W)
+    out = orc.live_decode(hb, Wb, D, block, 0.95, lib=lib)
+    z = synth.bf16_bits_to_f32(hb).astype(np.float64) @ synth.bf16_bits_to_f32(Wb).astype(np.float64).T
+    live = ~D.astype(bool)
+    top = np.argmax(z, axis=1)
+    conf = softmax(z, axis=1).max(axis=1)
+    assert np.array_equal(out["top"][live], top[live])
+    assert (out["top"][block + 2] == 5)                   # the tie goes to the lower id
+    np.testing.assert_allclose(out["conf"][live], conf[live], rtol=1e-12)
+    srt = np.sort(z, axis=1)
+    np.testing.assert_allclose(out["gap"][live], (srt[:, -1] - srt[:, -2])[live], rtol=1e-9, atol=1e-12)
+    expect = D.copy()
+    for b in range(nb):
+        rows = [t for t in range(b * block, (b + 1) * block) if live[t]]
+        hit = [t for t in rows if conf[t] >= 0.95]
+        for t in hit or [max(rows, key=lambda t: (conf[t], -t))]:
+            expect[t] = 1
+    assert np.array_equal(out["D_next"], expect)
+    assert not expect[block + 2]                   # the tied row holds at most half the mass
+    assert expect[block + 6] and expect[2 * block:3 * block].all()
+    assert expect[:block].sum() == D[:block].sum() + 1          # sequence 0: one fallback commit
+    new = (expect == 1) & (D == 0)
+    assert np.array_equal(out["token"][new], top[new]) and (out["token"][~new] == -1).all()
+    assert out["commits"] == int(new.sum())
+    one = orc.live_decode(hb, Wb[:1], D, block, 0.95, lib=lib)
+    assert one["D_next"].all() and np.allclose(one["conf"][live], 1.0)
+
+
 PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
         pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness,
         pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle,
-        pin_group_limited, pin_group_limited_restricted]
+        pin_group_limited, pin_group_limited_restricted, pin_live_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -508,7 +554,8 @@ MUTATIONS = {1: "router bias dropped", 2: "down-projection operand indexed wrong
              3: "SiLU sign flipped", 4: "ties broken toward the higher id",
              5: "refresh-due test dropped", 6: "worklist in position order",
              7: "H_e uses a strict inequality", 8: "restricted top-K ignores the support",
-             9: "groups ranked by their first expert, not their best"}
+             9: "groups ranked by their first expert, not their best",
+             10: "decoded token ties broken toward the higher id"}
 
 
 @pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
