@@ -51,6 +51,11 @@ class epoch_inspect(ctypes.Structure):
         ("k_ext", _i32), ("iteration", _i32), ("last_forward_layer", _i32)]
 
 
+class epoch_decode_desc(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in ("batch", "block", "hidden", "vocab", "act_dtype", "flags")] + [
+        ("tau", ctypes.c_double)]
+
+
 class EpochError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn} failed with status {status}: {text}")
@@ -80,9 +85,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.epoch_status_string.restype = ctypes.c_char_p
     lib.epoch_plan_set_timing.argtypes = [_vp, _i32]
     lib.epoch_plan_timing.argtypes = [_vp, P(ctypes.c_float), P(ctypes.c_int64), _i32]
+    lib.epoch_decode_workspace_bytes.argtypes = [P(epoch_decode_desc), P(ctypes.c_size_t)]
+    lib.epoch_live_decode.argtypes = [P(epoch_decode_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
     for fn in ("epoch_plan_workspace_bytes", "epoch_block_plan_build", "epoch_moe_fresh_forward",
                "epoch_cache_update", "epoch_plan_inspect", "epoch_block_plan_destroy",
-               "epoch_plan_set_timing", "epoch_plan_timing"):
+               "epoch_plan_set_timing", "epoch_plan_timing", "epoch_decode_workspace_bytes",
+               "epoch_live_decode"):
         getattr(lib, fn).restype = _i32
     _lib = lib
     return lib
@@ -175,3 +184,25 @@ def epoch_plan_timing(plan: int):
     n = (ctypes.c_int64 * EPOCH_TIMING_GROUPS)()
     _check("epoch_plan_timing", load().epoch_plan_timing(plan, ms, n, EPOCH_TIMING_GROUPS))
     return {g: (float(ms[i]), int(n[i])) for i, g in enumerate(TIMING_GROUPS)}
+
+
+def make_decode_desc(batch: int, block: int, hidden: int, vocab: int, tau: float = 0.95,
+                     act_dtype: int = EPOCH_DTYPE_BF16) -> epoch_decode_desc:
+    return epoch_decode_desc(batch=batch, block=block, hidden=hidden, vocab=vocab,
+                             act_dtype=act_dtype, flags=0, tau=float(tau))
+
+
+def epoch_decode_workspace_bytes(desc: epoch_decode_desc) -> int:
+    out = ctypes.c_size_t(0)
+    _check("epoch_decode_workspace_bytes",
+           load().epoch_decode_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def epoch_live_decode(desc: epoch_decode_desc, h, w_vocab, decoded, decoded_next, tokens,
+                      conf, workspace, workspace_bytes: int, stream=None):
+    _check("epoch_live_decode",
+           load().epoch_live_decode(ctypes.byref(desc), _ptr(h), _ptr(w_vocab), _ptr(decoded),
+                                    _ptr(decoded_next), _ptr(tokens), _ptr(conf),
+                                    _ptr(workspace), ctypes.c_size_t(workspace_bytes),
+                                    _stream(stream)))

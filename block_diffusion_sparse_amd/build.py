@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libepoch.so")
-SOURCES = ["epoch_abi.hip", "router.hip", "plan.hip", "experts.hip"]
+SOURCES = ["epoch_abi.hip", "router.hip", "plan.hip", "experts.hip", "decode.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -1,0 +1,230 @@
+// Live-only output decoding of one refinement step (gfx950): the LM-head logits of the live
+// positions only, their top token and confidence, and the threshold commit that produces the
+// next decoded mask (teardown, evaluation setup: greedy threshold decoding with commit
+// threshold tau = 0.95, at most 64 refinement steps per block, early exit; LSP section: only
+// live positions reach the output decoding, and a position's commit / no-commit decision
+// depends on its live logits).
+//
+// Three launches, no host synchronisation:
+//   k_live_compact  one workgroup: the live positions (D = 0) in ascending order, their count,
+//                   and each position's index in that list;
+//   k_gemm_big      LM-head mode: 128 live rows x 128 tokens per workgroup on bf16 MFMA, the
+//                   epilogue reducing each row's 64-token blocks to (max, argmax, sum exp);
+//   k_decode_final  one workgroup per sequence: the partials of each live row combined in
+//                   double (confidence = 1 / sum_v exp(z_v - z_max)), then the commits.
+#include "device_common.h"
+#include "epoch_internal.h"
+#include "expert_gemm.h"
+
+#include <new>
+
+namespace epoch {
+
+constexpr int kCompactThreads = 1024;
+
+__global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
+                                                                  const uint8_t* __restrict__ D,
+                                                                  int32_t* __restrict__ live_list,
+                                                                  int32_t* __restrict__ live_idx,
+                                                                  int32_t* __restrict__ n_live) {
+  __shared__ int32_t wcount[kCompactThreads / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int carry = 0;
+  for (int base = 0; base < M; base += kCompactThreads) {
+    const int t = base + tid;
+    const bool live = t < M && D[t] == 0;
+    const unsigned long long bal = ballot64(live);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int before = carry, total = 0;
+    for (int w = 0; w < kCompactThreads / 64; ++w) {
+      if (w < wave) before += wcount[w];
+      total += wcount[w];
+    }
+    const int idx = before + __popcll(bal & below);
+    if (t < M) live_idx[t] = live ? idx : -1;
+    if (live) live_list[idx] = t;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_live = carry;
+}
+
+// One workgroup per sequence (block positions).  Wave w combines the partials of positions
+// w, w + 4, ...; then the commit rule: every live position with confidence >= tau commits, and
+// a sequence none of whose live positions reaches tau commits its most confident one (lower
+// position on ties).
+__global__ __launch_bounds__(256) void k_decode_final(int block, int n_p, double tau,
+                                                      const uint8_t* __restrict__ D,
+                                                      const int32_t* __restrict__ live_idx,
+                                                      const float* __restrict__ pmax,
+                                                      const int32_t* __restrict__ parg,
+                                                      const float* __restrict__ psum,
+                                                      uint8_t* __restrict__ D_next,
+                                                      int32_t* __restrict__ tokens,
+                                                      float* __restrict__ conf_out) {
+  extern __shared__ double conf_s[];  // [block], then int top_s[block]
+  int32_t* top_s = reinterpret_cast<int32_t*>(conf_s + block);
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int p = wave; p < block; p += 4) {
+    const int t = b * block + p;
+    const int li = live_idx[t];
+    if (li < 0) {  // decoded: not a candidate
+      if (lane == 0) {
+        conf_s[p] = -1.0;
+        top_s[p] = -1;
+      }
+      continue;
+    }
+    const size_t row = (size_t)li * n_p;
+    float m = -INFINITY;
+    int a = 0x7fffffff;
+    for (int j = lane; j < n_p; j += 64) {
+      const float pm = pmax[row + j];
+      const int pa = parg[row + j];
+      if (pm > m || (pm == m && pa < a)) {
+        m = pm;
+        a = pa;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, 64);
+      const int oa = __shfl_xor(a, o, 64);
+      if (om > m || (om == m && oa < a)) {
+        m = om;
+        a = oa;
+      }
+    }
+    double z = 0.0;
+    for (int j = lane; j < n_p; j += 64)
+      z += (double)psum[row + j] * exp((double)pmax[row + j] - (double)m);
+    z = wave_sum(z);
+    if (lane == 0) {
+      conf_s[p] = 1.0 / z;
+      top_s[p] = a;
+    }
+  }
+  __syncthreads();
+  int hit = 0;
+  for (int p = threadIdx.x; p < block; p += blockDim.x) hit |= conf_s[p] >= tau;
+  const bool any = __syncthreads_or(hit) != 0;
+  // most confident live position (wave 0), used only when none reaches tau
+  __shared__ int fallback;
+  if (wave == 0) {
+    double bc = -1.0;
+    int bp = -1;
+    for (int p = lane; p < block; p += 64)
+      if (conf_s[p] > bc) {  // ascending p per lane: the first maximum is the lowest position
+        bc = conf_s[p];
+        bp = p;
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double oc = __shfl_xor(bc, o, 64);
+      const int op = __shfl_xor(bp, o, 64);
+      if (oc > bc || (oc == bc && op >= 0 && (bp < 0 || op < bp))) {
+        bc = oc;
+        bp = op;
+      }
+    }
+    if (lane == 0) fallback = bc >= 0.0 ? bp : -1;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < block; p += blockDim.x) {
+    const int t = b * block + p;
+    const bool live = top_s[p] >= 0;
+    const bool commit = live && (any ? conf_s[p] >= tau : p == fallback);
+    D_next[t] = (D[t] || commit) ? 1 : 0;
+    if (commit) tokens[t] = top_s[p];
+    if (conf_out) conf_out[t] = live ? (float)conf_s[p] : 0.0f;
+  }
+}
+
+namespace {
+
+struct DecodeLayout {
+  int32_t *live_list, *live_idx, *n_live, *parg;
+  float *pmax, *psum;
+  size_t bytes;
+};
+
+DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
+  const size_t M = (size_t)d->batch * d->block, n_p = (size_t)d->vocab / 64;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t n) {
+    off = (off + 255) / 256 * 256;
+    void* p = b ? b + off : nullptr;
+    off += n;
+    return p;
+  };
+  DecodeLayout L;
+  L.live_list = static_cast<int32_t*>(take(M * 4));
+  L.live_idx = static_cast<int32_t*>(take(M * 4));
+  L.n_live = static_cast<int32_t*>(take(4));
+  L.pmax = static_cast<float*>(take(M * n_p * 4));
+  L.parg = static_cast<int32_t*>(take(M * n_p * 4));
+  L.psum = static_cast<float*>(take(M * n_p * 4));
+  L.bytes = (off + 255) / 256 * 256;
+  return L;
+}
+
+int32_t check_decode_desc(const epoch_decode_desc* d) {
+  if (!d) return EPOCH_E_NULL;
+  if (d->act_dtype != EPOCH_DTYPE_BF16) return EPOCH_E_DTYPE;
+  if (d->flags != 0) return EPOCH_E_SHAPE;
+  if (d->batch < 1 || d->block < 1 || d->block > 1024) return EPOCH_E_SHAPE;
+  if ((long long)d->batch * d->block > (1 << 20)) return EPOCH_E_SHAPE;
+  if (d->hidden < 64 || d->hidden % 64 || d->hidden > 16384) return EPOCH_E_SHAPE;
+  if (d->vocab < 128 || d->vocab % 128 || d->vocab > (1 << 20)) return EPOCH_E_SHAPE;
+  if (!(d->tau > 0.0 && d->tau <= 1.0)) return EPOCH_E_SHAPE;
+  return EPOCH_OK;
+}
+
+}  // namespace
+}  // namespace epoch
+
+using namespace epoch;
+
+extern "C" {
+
+int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes) {
+  if (!out_bytes) return EPOCH_E_NULL;
+  const int32_t rc = check_decode_desc(d);
+  if (rc) return rc;
+  *out_bytes = decode_carve(d, nullptr).bytes;
+  return EPOCH_OK;
+}
+
+int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                          const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
+                          float* conf, void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t rc = check_decode_desc(d);
+  if (rc) return rc;
+  if (!h || !w_vocab || !decoded || !decoded_next || !tokens || !workspace) return EPOCH_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(w_vocab)) & 15u)
+    return EPOCH_E_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EPOCH_E_WORKSPACE;
+  const DecodeLayout L = decode_carve(d, workspace);
+  if (workspace_bytes < L.bytes) return EPOCH_E_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int M = d->batch * d->block, n_p = d->vocab / 64;
+  hipLaunchKernelGGL(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
+                     L.live_list, L.live_idx, L.n_live);
+  // grid as for every k_gemm_big launch: (row tiles rounded up to 8) x column blocks, sized
+  // for all M positions live; tiles past the live count exit at once
+  const int tiles = (M + 127) / 128, n_cb = d->vocab / 128;
+  const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
+  hipLaunchKernelGGL((k_gemm_big<false, false, true>), dim3(((tiles + 7) / 8) * 8 * n_cb),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(h),
+                     static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp);
+  const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
+  hipLaunchKernelGGL(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, n_p, d->tau,
+                     decoded, L.live_idx, L.pmax, L.parg, L.psum, decoded_next, tokens, conf);
+  return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;
+}
+
+}  // extern "C"

@@ -231,6 +231,19 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
 
 namespace epoch {
 
+// Output of the LM-head mode of k_gemm_big: the rows are live positions (gathered through
+// live_list, n_live of them), the columns vocabulary tokens, and instead of the logits each wave
+// writes, per row and per block of 64 tokens, the largest logit, its token (lower id on ties)
+// and the sum of exp(logit - largest) over the block; n_p = vocab / 64 blocks per row.
+struct LmPartials {
+  const int32_t* live_list;
+  const int32_t* n_live;
+  float* pmax;
+  int32_t* parg;
+  float* psum;
+  int n_p;
+};
+
 // Compute-bound variant for tiles with many rows (the shared expert over all M positions,
 // routed experts with many fresh pairs): a 128-row x 128-weight-row output tile per
 // workgroup, four waves in a 2 x 2 arrangement, each accumulating a 64 x 64 sub-tile with
@@ -243,14 +256,15 @@ namespace epoch {
 // are [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g
 // and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of
 // W2.  Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
-template <bool GATEUP, bool ROUTED>
+template <bool GATEUP, bool ROUTED, bool LMHEAD = false>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
+  static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
   constexpr int BR = 128, KC = 32, SEG_ROW = KC / 8;
   constexpr int NSEG = BR * SEG_ROW / 256;  // 16-byte segments per thread per operand and chunk
   constexpr int NR = 4;                     // register ring depth (chunks), even
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   const int cb = pos % n_cb;
   // routed big tiles come from their own table, counted in FLAG_NTILES_BIG
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
-                                tile_row0, offs, M);
+                                tile_row0, offs, LMHEAD ? *lp.n_live : M);
   if (!tr.active) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -286,7 +300,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     dst[j] = row * KC + ((c8 ^ ((row >> 2) & 3)) * 8);
     const int p = tr.row0 + row;
     aok[j] = p < tr.row_end;
-    const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
+    const int src_row =
+        aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p)) : 0;
     asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
     int wrow;
     const uint16_t* base;
@@ -377,6 +392,47 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     if (c < nch) step(c, u, c + NR < nch, c + 1 < nch, c + 2 < nch);
   }
   // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
+  if (LMHEAD) {
+    // per row: the 64 logits of this wave's token block sit in the 16 lanes with the same g,
+    // four per lane; reduce (max, lower token on ties) and then sum exp(logit - max)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = tr.row0 + 64 * wm + 16 * m + 4 * g + q;
+        const int col0 = cb * 128 + 64 * wn + r;
+        float mx = acc[m][0][q];
+        int arg = col0;
+#pragma unroll
+        for (int n = 1; n < 4; ++n)
+          if (acc[m][n][q] > mx) {
+            mx = acc[m][n][q];
+            arg = col0 + 16 * n;
+          }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float om = __shfl_xor(mx, o, 64);
+          const int oa = __shfl_xor(arg, o, 64);
+          if (om > mx || (om == mx && oa < arg)) {
+            mx = om;
+            arg = oa;
+          }
+        }
+        float se = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) se += expf(acc[m][n][q] - mx);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (r == 0 && row < tr.row_end) {
+          const size_t idx = (size_t)row * lp.n_p + 2 * cb + wn;
+          lp.pmax[idx] = mx;
+          lp.parg[idx] = arg;
+          lp.psum[idx] = se;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
 #pragma unroll

@@ -118,7 +118,7 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
                          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
                          W.offs, L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M,
-                         s.H, s.I);
+                         s.H, s.I, LmPartials{});
   } else
     hipLaunchKernelGGL(k_gateup_f32<true>, grid, dim3(256), 0, st, static_cast<const float*>(x),
                        static_cast<const float*>(w1), static_cast<const float*>(w3), W.flags,
@@ -138,7 +138,8 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
                          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
                          st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
                          nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
-                         W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H);
+                         W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H,
+                         LmPartials{});
   } else
     hipLaunchKernelGGL(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st, static_cast<const float*>(W.h),
                        static_cast<const float*>(w2), W.flags, W.tile_slot, W.tile_row0, W.offs,
@@ -157,11 +158,12 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
     hipLaunchKernelGGL((k_gemm_big<true, false>), gu, dim3(256), 0, st,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(sw1),
                        static_cast<const uint16_t*>(sw3), W.flags, nullptr, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.H, s.Is);
+                       nullptr, nullptr, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.H, s.Is,
+                       LmPartials{});
     hipLaunchKernelGGL((k_gemm_big<false, false>), gd, dim3(256), 0, st,
                        static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
                        nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       static_cast<uint16_t*>(W.S), s.M, s.Is, s.H);
+                       static_cast<uint16_t*>(W.S), s.M, s.Is, s.H, LmPartials{});
   } else if (s.bf16) {
     launch_gemm<true, false>(s.T_dense, st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),

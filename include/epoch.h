@@ -259,6 +259,46 @@ enum { EPOCH_TIMING_GROUPS = 7 };
 int32_t epoch_plan_set_timing(epoch_plan* plan, int32_t groups);
 int32_t epoch_plan_timing(epoch_plan* plan, float* ms, int64_t* launches, int32_t n);
 
+/* ------------------------------------------------------------------ live-only output decoding */
+
+/* One refinement step's output decoding of the block batch. */
+typedef struct epoch_decode_desc {
+  int32_t batch;     /* sequences */
+  int32_t block;     /* positions per sequence, <= 1024 */
+  int32_t hidden;    /* H: multiple of 64 */
+  int32_t vocab;     /* V: multiple of 128 */
+  int32_t act_dtype; /* EPOCH_DTYPE_BF16 (the only dtype of this call) */
+  int32_t flags;     /* reserved, must be 0 */
+  double tau;        /* commit threshold on the top softmax probability, in (0, 1] */
+} epoch_decode_desc;
+
+/* Bytes of device workspace epoch_live_decode needs for `d` (live list, per-position
+   live index, per-row partial reductions of M x V/64 entries). */
+int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes);
+
+/*
+ * Live-only output decoding (teardown, evaluation setup: greedy threshold decoding with
+ * commit threshold tau; LSP section: only live positions reach the output decoding, and each
+ * commit / no-commit decision is taken on the live logits z_{i,t}).  For every live position
+ * t (decoded[t] = 0) of the block batch:
+ *   z_v = sum_h h[t,h] w_vocab[v,h]  (bf16 products, fp32 accumulation on MFMA)
+ *   top token = argmax_v z_v (lower id on ties);  conf_t = 1 / sum_v exp(z_v - max z)
+ * Every live position with conf_t >= tau commits; a sequence none of whose live positions
+ * reaches tau commits its most confident one (lower position on ties).
+ *   h            [M x H] bf16 (device): the final hidden states of every position;
+ *   w_vocab      [V x H] bf16 (device): the LM head;
+ *   decoded      [M] u8 (device): D_i;
+ *   decoded_next [M] u8 (device, written): D_{i+1} = D_i plus the commits;
+ *   tokens       [M] i32 (device): written at the committed positions only;
+ *   conf         [M] f32 (device, written, nullable): conf_t of live positions, 0 elsewhere;
+ *   workspace    (device, 256-byte aligned, >= epoch_decode_workspace_bytes), caller-owned.
+ * Decoded positions are never decoded again: their logits are not computed.  Errors as for
+ * every call (EPOCH_E_DTYPE for a dtype other than bf16).
+ */
+int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                          const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
+                          float* conf, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

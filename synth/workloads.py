@@ -335,3 +335,29 @@ def desc_fields(w: Workload, **overrides) -> dict:
              n_group=w.n_group, topk_group=w.topk_group)
     f.update(overrides)
     return f
+
+
+def decode_inputs(seed: int, batch: int, block: int, hidden: int, vocab: int, steps: int = 1,
+                  sigma: float = 0.02, lean_fraction: float = 0.4):
+    """Seeded inputs of live-only output decoding: LM-head weights [V, H] (bf16 bits, N(0,
+    sigma)), hidden states [steps, M, H] (bf16 bits) and the starting decoded mask [M] (u8,
+    about a quarter of the positions).  A lean_fraction of the rows leans toward one token:
+    h = c w_v / (sigma^2 H) + N(0, 1/4), which puts that token's logit about c above the
+    others (c drawn from {6, 10, 14, 18, 22}); the rest are N(0, 1) rows.  With a vocabulary of
+    thousands of tokens this spreads the top-token probability on both sides of 0.95."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7001]))
+    M = batch * block
+    W = (rng.standard_normal((vocab, hidden), dtype=np.float32) * np.float32(sigma))
+    Wb = f32_to_bf16_bits(W)
+    Wf = bf16_bits_to_f32(Wb)
+    hs = np.empty((steps, M, hidden), dtype=np.uint16)
+    for s in range(steps):
+        h = rng.standard_normal((M, hidden), dtype=np.float32)
+        lean = rng.random(M) < lean_fraction
+        tok = rng.integers(0, vocab, size=M)
+        c = rng.choice(np.array([6.0, 10.0, 14.0, 18.0, 22.0], np.float32), size=M)
+        scale = (c / np.float32(sigma * sigma * hidden)).astype(np.float32)
+        h[lean] = Wf[tok[lean]] * scale[lean, None] + 0.5 * h[lean]
+        hs[s] = f32_to_bf16_bits(h)
+    D = (rng.random(M) < 0.25).astype(np.uint8)
+    return hs, Wb, D

@@ -34,6 +34,9 @@ def test_struct_layouts_match_header():
     fields = re.findall(r"int32_t\s+([A-Za-z_0-9,\s]+);", body)
     names = [n.strip() for f in fields for n in f.split(",")]
     assert names == [f for f, _ in B.epoch_desc._fields_]
+    body = src[src.index("typedef struct epoch_decode_desc"):src.index("} epoch_decode_desc;")]
+    names = re.findall(r"(?:int32_t|double)\s+([a-z_]+);", body)
+    assert names == [f for f, _ in B.epoch_decode_desc._fields_]
     body = src[src.index("typedef struct epoch_inspect"):src.index("} epoch_inspect;")]
     names = re.findall(r"\*\s*([a-z_]+);|int32_t\s+([a-z_]+);", body)
     names = [a or b for a, b in names]
@@ -52,7 +55,11 @@ def test_workspace_query_and_argument_errors():
     d2 = B.make_desc(**synth.desc_fields(synth.workload(2, batch=16)))
     assert B.epoch_plan_workspace_bytes(d2) > B.epoch_plan_workspace_bytes(d)
     bad = [dict(hidden=100), dict(top_k=0), dict(n_experts=2000), dict(staleness_R=0),
-           dict(inter=100), dict(flags=1), dict(alpha_den=0), dict(q_num=200)]
+           dict(inter=100), dict(flags=1), dict(alpha_den=0), dict(q_num=200), dict(routing=2),
+           dict(atlas_period=3),                       # a period needs restricted routing
+           dict(n_group=3, topk_group=1),              # 64 experts do not split in 3 groups
+           dict(n_group=8, topk_group=9), dict(n_group=128, topk_group=4),
+           dict(n_group=16, topk_group=3)]             # 3 groups of 4 < K_ext = 16 candidates
     for b in bad:
         with pytest.raises(B.EpochError) as ei:
             B.epoch_plan_workspace_bytes(B.make_desc(**synth.desc_fields(synth.workload(2), **b)))
@@ -71,3 +78,21 @@ def test_workspace_query_and_argument_errors():
     assert B.epoch_status_string(0) == "ok"
     assert "workspace" in B.epoch_status_string(-4)
     assert B.load().epoch_block_plan_destroy(None) == 0
+
+
+def test_decode_workspace_query_and_argument_errors():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libepoch.so not built")
+    d = B.make_decode_desc(8, 32, 2048, 32768)
+    n = B.epoch_decode_workspace_bytes(d)
+    assert n % 256 == 0 and n >= 256 * 32768 // 64 * 12
+    for kw, status in ((dict(vocab=100), -2), (dict(block=2000), -2), (dict(hidden=96), -2),
+                       (dict(tau=0.0), -2), (dict(tau=1.5), -2), (dict(act_dtype=0), -3)):
+        args = dict(batch=8, block=32, hidden=2048, vocab=32768)
+        args.update(kw)
+        with pytest.raises(B.EpochError) as ei:
+            B.epoch_decode_workspace_bytes(B.make_decode_desc(**args))
+        assert ei.value.status == status, kw
+    with pytest.raises(B.EpochError) as ei:   # NULL tensors: checked before any launch
+        B.epoch_live_decode(d, 0, 0, 0, 0, 0, None, 256, n, 0)
+    assert ei.value.status == -1
