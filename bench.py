@@ -45,6 +45,10 @@ def parse():
                     help="top-K over all experts, or inside the layer's Atlas support")
     ap.add_argument("--atlas-period", type=int, default=0,
                     help="restricted routing: rebuild the support after this many iterations")
+    ap.add_argument("--decode", action="store_true",
+                    help="measure live-only output decoding (LM head on live rows + threshold "
+                         "commit) instead of the MoE layer")
+    ap.add_argument("--vocab", type=int, default=32768, help="--decode: vocabulary size")
     ap.add_argument("--n-group", type=int, default=0,
                     help="group-limited top-k: number of contiguous expert groups (0: off)")
     ap.add_argument("--topk-group", type=int, default=0,
@@ -109,6 +113,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
+    if args.decode:
+        bench_decode(args)
+        return
     over = {}
     if args.fraction is not None:
         over["forced_fraction"] = args.fraction
@@ -308,6 +315,57 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_decode(args):
+    """Live-only output decoding of one refinement step on the workload's block batch: the
+    LM head ([V x H] bf16) over the live positions, then the threshold commit."""
+    import numpy as np
+    import torch
+
+    import synth
+    from block_diffusion_sparse_amd import binding as B
+    w = synth.workload(args.workload)
+    M, H, V = w.M, w.hidden, args.vocab
+    hs, Wb, D = synth.decode_inputs(w.seed, w.batch, w.block, H, V)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    h, Wv, Dd = dev(hs[0]), dev(Wb), dev(D)
+    d = B.make_decode_desc(w.batch, w.block, H, V)
+    n = B.epoch_decode_workspace_bytes(d)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    Dn = torch.empty(M, dtype=torch.uint8, device="cuda")
+    tok = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    conf = torch.empty(M, dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        B.epoch_live_decode(d, h, Wv, Dd, Dn, tok, conf, ws, n)
+    reps = 10 * args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        B.epoch_live_decode(d, h, Wv, Dd, Dn, tok, conf, ws, n)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    live = int((D == 0).sum())
+    row_tiles = (live + 127) // 128
+    lm_bytes = V * H * 2 * row_tiles + live * H * 2 + live * (V // 64) * 12
+    flops = 2.0 * live * V * H
+    print(json.dumps({
+        "metric": "live positions decoded per second (LM head + threshold commit)",
+        "value": round(live / dt, 1), "unit": "live positions/s", "n_gpus": 1,
+        "steps": reps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"live-decode {w.batch}x{w.block} h{H} v{V}", "live": live,
+                   "tau": 0.95},
+        "us_per_step": round(dt * 1e6, 2),
+        "lm_head_gbs": round(lm_bytes / dt / 1e9, 1),
+        "lm_head_tflops": round(flops / dt / 1e12, 2),
+    }), flush=True)
 
 
 if __name__ == "__main__":

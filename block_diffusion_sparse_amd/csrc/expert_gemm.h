@@ -276,9 +276,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BR * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
-  const int pos = blockIdx.x >> 3;
-  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
-  const int cb = pos % n_cb;
+  int pos, tile, cb;
+  if (LMHEAD) {
+    // few row tiles, many token blocks: token blocks go round the 8 XCDs and every row tile
+    // of a block runs on the block's XCD (its W_v rows enter one L2); M bounds the row tiles
+    const int T = (M + BR - 1) / BR, within = blockIdx.x >> 3;
+    cb = 8 * (within / T) + (blockIdx.x & 7);
+    tile = within % T;
+    pos = within;
+    if (cb >= n_cb) return;
+  } else {
+    pos = blockIdx.x >> 3;
+    tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
+    cb = pos % n_cb;
+  }
   // routed big tiles come from their own table, counted in FLAG_NTILES_BIG
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
                                 tile_row0, offs, LMHEAD ? *lp.n_live : M);
