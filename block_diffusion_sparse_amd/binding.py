@@ -21,7 +21,7 @@ EPOCH_NUM_COUNTERS = 20
 EPOCH_TIMING_GROUPS = 7
 COUNTERS = ["cold", "hot_update", "hot_skip", "anomaly", "fresh_rows", "pairs", "unmet",
             "forced_rows", "due_rows", "support_size", "u_final", "repair_rounds", "touched",
-            "forwards", "commits", "restricted", "coverage_fallback", "period_update",
+            "forwards", "reserved14", "restricted", "coverage_fallback", "period_update",
             "reserved18", "reserved19"]
 TIMING_GROUPS = ["router", "plan", "place", "routed_gateup", "routed_down", "shared",
                  "combine"]

@@ -132,6 +132,9 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
     L.valid = c.take<uint8_t>(M);
     L.last_fresh = c.take<int32_t>(M);
     L.prev_D = c.take<uint8_t>(M);
+    L.valid_n = c.take<uint8_t>(M);
+    L.last_fresh_n = c.take<int32_t>(M);
+    L.prev_D_n = c.take<uint8_t>(M);
     L.inS = c.take<uint8_t>(E);
     L.slot_of = c.take<int32_t>(E);
     L.S_list = c.take<int32_t>(E);
@@ -225,6 +228,7 @@ struct epoch_plan {
   Layout lay;
   std::vector<int32_t> iter;
   std::vector<uint8_t> pending;
+  std::vector<uint8_t> parity;  // which copy of the commit state is current, per layer
   int last_layer = -1;
   uint32_t timing_mask = 0;
   std::vector<TimedPair> pairs;
@@ -255,6 +259,21 @@ struct GroupTimer {
     a = nullptr;
   }
 };
+
+}  // namespace
+
+namespace {
+
+// The layer's state with the current copy of the commit state in front.
+LayerState state_now(const epoch_plan* p, int layer) {
+  LayerState L = p->lay.layers[layer];
+  if (p->parity[layer]) {
+    std::swap(L.valid, L.valid_n);
+    std::swap(L.last_fresh, L.last_fresh_n);
+    std::swap(L.prev_D, L.prev_D_n);
+  }
+  return L;
+}
 
 }  // namespace
 
@@ -297,6 +316,7 @@ int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* w
   p->lay = std::move(lay);
   p->iter.assign(d->n_layers, 0);
   p->pending.assign(d->n_layers, 0);
+  p->parity.assign(d->n_layers, 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int l = 0; l < d->n_layers; ++l) {
     if (launch_init_layer(s, p->lay.layers[l], st) != hipSuccess) {
@@ -319,7 +339,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
   if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
   if (!aligned16(x) || !aligned16(y) || (y_routed && !aligned16(y_routed))) return EPOCH_E_ALIGN;
   const Shape& s = p->s;
-  const LayerState& L = p->lay.layers[layer];
+  const LayerState L = state_now(p, layer);
   const Scratch& W = p->lay.scratch;
   const epoch_layer_weights& w = p->w[layer];
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -362,7 +382,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
   }
   {
     GroupTimer tm(p, st, 6);
-    e = launch_combine(s, L, W, y, y_routed, st);
+    e = launch_combine(s, p->iter[layer], L, W, y, y_routed, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
@@ -375,9 +395,8 @@ int32_t epoch_cache_update(epoch_plan* p, int32_t layer, void* stream) {
   if (!p) return EPOCH_E_NULL;
   if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
   if (!p->pending[layer]) return EPOCH_E_STATE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (launch_commit(p->s, p->iter[layer], p->lay.layers[layer], p->lay.scratch, st) != hipSuccess)
-    return EPOCH_E_HIP;
+  (void)stream;  // the forward already wrote the committed state into the next copy
+  p->parity[layer] ^= 1;
   p->pending[layer] = 0;
   p->iter[layer] += 1;
   return EPOCH_OK;
@@ -387,7 +406,7 @@ int32_t epoch_plan_inspect(const epoch_plan* p, int32_t layer, epoch_inspect* ou
   if (!p || !out) return EPOCH_E_NULL;
   if (layer < 0 || layer >= p->d.n_layers) return EPOCH_E_LAYER;
   const Scratch& W = p->lay.scratch;
-  const LayerState& L = p->lay.layers[layer];
+  const LayerState L = state_now(p, layer);
   std::memset(out, 0, sizeof(*out));
   out->logits = W.G;
   out->ids = W.ids;

@@ -31,11 +31,16 @@ enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_N
 constexpr int kMaxGroups = 64;
 
 // Device-side view of one layer's persistent state.
+// valid / last_fresh / prev_D exist twice: the forward reads the current copy and writes the
+// next one (combine), and a commit makes the next copy current (host side, no launch).
 struct LayerState {
   void* cache;          // [M x H] act
-  uint8_t* valid;       // [M]
-  int32_t* last_fresh;  // [M]
-  uint8_t* prev_D;      // [M]
+  uint8_t* valid;       // [M] current
+  int32_t* last_fresh;  // [M] current
+  uint8_t* prev_D;      // [M] current
+  uint8_t* valid_n;     // [M] next
+  int32_t* last_fresh_n;// [M] next
+  uint8_t* prev_D_n;    // [M] next
   uint8_t* inS;         // [E]
   int32_t* slot_of;     // [E]
   int32_t* S_list;      // [E]
@@ -110,9 +115,7 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
                               const Scratch& W, hipStream_t st);
 hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const void* sw3,
                          const void* sw2, const Scratch& W, hipStream_t st);
-hipError_t launch_combine(const Shape& s, const LayerState& L, const Scratch& W, void* y,
-                          void* y_routed, hipStream_t st);
-hipError_t launch_commit(const Shape& s, int iter, const LayerState& L, const Scratch& W,
-                         hipStream_t st);
+hipError_t launch_combine(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                          void* y, void* y_routed, hipStream_t st);
 
 }  // namespace epoch

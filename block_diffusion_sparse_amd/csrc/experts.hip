@@ -247,14 +247,22 @@ __device__ __forceinline__ void copy8(const T* src, T v[8]) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_shared,
-                                                 const uint8_t* __restrict__ fresh,
-                                                 const int32_t* __restrict__ inv,
+__global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_shared, int iter,
+                                                 LayerState L, const int32_t* __restrict__ inv,
                                                  const T* __restrict__ y_pair,
-                                                 const T* __restrict__ S, T* __restrict__ cache,
-                                                 T* __restrict__ y, T* __restrict__ y_routed) {
+                                                 const T* __restrict__ S, T* __restrict__ y,
+                                                 T* __restrict__ y_routed) {
   const int t = blockIdx.x;
-  const bool f = fresh[t] != 0;
+  const bool f = L.fresh[t] != 0;
+  T* __restrict__ cache = static_cast<T*>(L.cache);
+  if (threadIdx.x == 0) {
+    // the commit of this forward, into the next copy of the position's state (teardown, LSP
+    // state machine: a fresh output enters the cache and restarts the age; D_i becomes the
+    // D_{i-1} of the next iteration); it takes effect when the caller commits
+    L.valid_n[t] = (L.valid[t] || f) ? 1 : 0;
+    L.last_fresh_n[t] = f ? iter : L.last_fresh[t];
+    L.prev_D_n[t] = L.Dcur[t];
+  }
   for (int j = threadIdx.x * 8; j < H; j += blockDim.x * 8) {
     T rb[8];
     if (f) {
@@ -287,18 +295,18 @@ __global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_sh
   }
 }
 
-hipError_t launch_combine(const Shape& s, const LayerState& L, const Scratch& W, void* y,
-                          void* y_routed, hipStream_t st) {
+hipError_t launch_combine(const Shape& s, int iter, const LayerState& L, const Scratch& W,
+                          void* y, void* y_routed, hipStream_t st) {
   if (s.bf16)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
-                       s.n_shared, L.fresh, W.inv, static_cast<const uint16_t*>(W.y_pair),
-                       static_cast<const uint16_t*>(W.S), static_cast<uint16_t*>(L.cache),
-                       static_cast<uint16_t*>(y), static_cast<uint16_t*>(y_routed));
+                       s.n_shared, iter, L, W.inv, static_cast<const uint16_t*>(W.y_pair),
+                       static_cast<const uint16_t*>(W.S), static_cast<uint16_t*>(y),
+                       static_cast<uint16_t*>(y_routed));
   else
     hipLaunchKernelGGL(k_combine<float>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K, s.n_shared,
-                       L.fresh, W.inv, static_cast<const float*>(W.y_pair),
-                       static_cast<const float*>(W.S), static_cast<float*>(L.cache),
-                       static_cast<float*>(y), static_cast<float*>(y_routed));
+                       iter, L, W.inv, static_cast<const float*>(W.y_pair),
+                       static_cast<const float*>(W.S), static_cast<float*>(y),
+                       static_cast<float*>(y_routed));
   return hipGetLastError();
 }
 

@@ -533,26 +533,4 @@ hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, h
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------- commit
-// Cache commit (teardown, LSP state machine: fresh output -> cache update; refresh period:
-// the age restarts at a fresh write; D_i becomes the D_{i-1} of the next iteration).
-__global__ void k_commit(int M, int iter, LayerState L) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < M) {
-    if (L.fresh[t]) {
-      L.valid[t] = 1;
-      L.last_fresh[t] = iter;
-    }
-    L.prev_D[t] = L.Dcur[t];
-  }
-  if (t == 0) L.counters[EPOCH_CNT_COMMITS] += 1;
-}
-
-hipError_t launch_commit(const Shape& s, int iter, const LayerState& L, const Scratch& W,
-                         hipStream_t st) {
-  (void)W;
-  hipLaunchKernelGGL(k_commit, dim3((s.M + 255) / 256), dim3(256), 0, st, s.M, iter, L);
-  return hipGetLastError();
-}
-
 }  // namespace epoch

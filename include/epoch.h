@@ -90,7 +90,7 @@ enum {
   EPOCH_CNT_REPAIR_ROUNDS = 11,/* sum of greedy repair rounds */
   EPOCH_CNT_TOUCHED = 12,      /* sum over forwards of experts with at least one fresh pair */
   EPOCH_CNT_FORWARDS = 13,
-  EPOCH_CNT_COMMITS = 14,
+  EPOCH_CNT_RESERVED14 = 14,   /* unused: the commit count is epoch_inspect.iteration */
   EPOCH_CNT_RESTRICTED = 15,   /* forwards routed inside the support (restricted mode) */
   EPOCH_CNT_COVERAGE_FALLBACK = 16, /* restricted-mode rebuilds forced by the coverage check */
   EPOCH_CNT_PERIOD_UPDATE = 17,/* restricted-mode rebuilds forced by atlas_period */
@@ -230,7 +230,10 @@ int32_t epoch_moe_fresh_forward(epoch_plan* plan, int32_t layer, const void* x,
  * output updates the cache; refresh-period section: the age restarts at a fresh
  * write): fresh rows become valid with last_fresh = iteration, D_i becomes D_{i-1},
  * and the layer's iteration counter advances.  EPOCH_E_STATE if the layer has no
- * forward since its last commit.
+ * forward since its last commit.  The forward already wrote this state into a second
+ * copy of the per-position state (so that repeating a forward stays idempotent); the
+ * commit makes that copy current on the host and enqueues nothing on `stream`.  It is
+ * ordered after the forward by the stream the next forward runs on.
  */
 int32_t epoch_cache_update(epoch_plan* plan, int32_t layer, void* stream);
 

@@ -222,7 +222,7 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
         assert c["cold"] == oc["cold"] and c["hot_update"] == oc["hot_update"]
         assert c["hot_skip"] == oc["hot_skip"] and c["anomaly"] == oc["anomalies"]
         assert c["fresh_rows"] == oc["fresh_rows"] and c["pairs"] == oc["pairs"]
-        assert c["commits"] == c["forwards"] == orcs[li].iter
+        assert plan.inspect(li)["iteration"] == c["forwards"] == orcs[li].iter
         assert c["restricted"] == oc["restricted"]
         assert c["coverage_fallback"] == oc["coverage_fallback"]
         assert c["period_update"] == oc["period_update"]
