@@ -303,7 +303,8 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
 // Wave-level function: all 64 lanes call it; mask holds E entries owned by this wave.
 __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int Kext,
                                             bool anomaly, bool route_r, const LayerState& L,
-                                            const Scratch& W, unsigned long long* mask) {
+                                            const Scratch& W, unsigned long long* mask,
+                                            const int32_t* eoffs, const int32_t* cbase) {
   const int lane = threadIdx.x & 63;
   const int t = chunk * kChunk + lane;
   const bool in = t < M;
@@ -328,7 +329,7 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
     for (int k = 0; k < K; ++k) {
       const int e = it[k];
       const int rank = __popcll(mask[e] & below);
-      const int p = W.eoffs[e] + W.chunk_base[(size_t)chunk * E + e] + rank;
+      const int p = eoffs[e] + cbase[e] + rank;
       W.wl_pos[p] = t;
       W.wl_k[p] = k;
       W.wl_w[p] = wt[k];
@@ -372,31 +373,51 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   __shared__ int32_t tot[kMaxExperts];
   __shared__ unsigned long long pmask[FUSED_PLACE ? kPlanWaves : 1]
                                      [FUSED_PLACE ? kFusedPlaceMaxExperts : 1];
+  // chunk bases of the fused placement, kept in LDS: [chunk][expert]
+  __shared__ int32_t cbl[FUSED_PLACE ? kFusedPlaceMaxChunks * kFusedPlaceMaxExperts : 1];
   const int tid = threadIdx.x;
-  // global reads that do not depend on the support step, issued before it
-  const int nch0 = s.n_chunks;
-  const int pre_cf = tid < nch0 ? W.chunk_fresh[tid] : 0;
-  const int pre_nS = *L.S_size;
-  const int pre_ex = tid < pre_nS ? L.S_list[tid] : 0;
-  const int sp = support_phase(s, iter, L, W, sh);
-  const bool route_r = (sp & 1) != 0;
-  __syncthreads();
-
   const int E = s.E, nch = s.n_chunks;
-  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
-  const int32_t* cnt = route_r ? (anomaly ? W.cnt_ar : W.cnt_fr) : (anomaly ? W.cnt_a : W.cnt_f);
-  // per-expert totals and chunk bases; Gp threads per expert, each a contiguous chunk range
+  // per-expert totals and chunk bases: Gp threads per expert, each a contiguous chunk range
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
   const int Gp = kPlanThreads / Epad;
   const int e = tid / Gp, gi = tid % Gp;
   const int seg = (nch + Gp - 1) / Gp;
   const int c0 = min(nch, gi * seg), c1 = min(nch, c0 + seg);
-  int local = 0;
-  if (e < E) {
-#pragma unroll 8
-    for (int c = c0; c < c1; ++c) local += cnt[(size_t)c * E + e];
+  // global reads that do not depend on the support step, issued before it: the flags, the
+  // fresh-list counts, the slot list of an unchanged support, and (all-expert routing, up to
+  // kPre chunks per thread) both per-chunk pair counts
+  constexpr int kPre = 4;
+  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
+  const int pre_cf = tid < nch ? W.chunk_fresh[tid] : 0;
+  const int pre_nS = *L.S_size;
+  const int pre_ex = tid < pre_nS ? L.S_list[tid] : 0;
+  const bool pre_cnt = !s.restricted && seg <= kPre;
+  int cv_f[kPre], cv_a[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const bool in = pre_cnt && e < E && c0 + k < c1;
+    cv_f[k] = in ? W.cnt_f[(size_t)(c0 + k) * E + e] : 0;
+    cv_a[k] = in ? W.cnt_a[(size_t)(c0 + k) * E + e] : 0;
   }
+  const int sp = support_phase(s, iter, L, W, sh);
+  const bool route_r = (sp & 1) != 0;
+  __syncthreads();
+
+  const int32_t* cnt = route_r ? (anomaly ? W.cnt_ar : W.cnt_fr) : (anomaly ? W.cnt_a : W.cnt_f);
+  auto count = [&](int c) {  // pairs of expert e in chunk c (c in [c0, c1))
+    if (pre_cnt) {
+      int v = 0;
+#pragma unroll
+      for (int k = 0; k < kPre; ++k)
+        if (c == c0 + k) v = anomaly ? cv_a[k] : cv_f[k];
+      return v;
+    }
+    return cnt[(size_t)c * E + e];
+  };
+  int local = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) local += count(c);
   part[tid] = local;
   __syncthreads();
   if (e < E) {
@@ -410,7 +431,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     int run = base;
     for (int c = c0; c < c1; ++c) {
       W.chunk_base[(size_t)c * E + e] = run;
-      run += cnt[(size_t)c * E + e];
+      if (FUSED_PLACE) cbl[c * kFusedPlaceMaxExperts + e] = run;
+      run += count(c);
       W.cnt_f[(size_t)c * E + e] = 0;  // consumed: clear for the next forward
       W.cnt_a[(size_t)c * E + e] = 0;
       if (s.restricted) {
@@ -498,7 +520,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     __syncthreads();
     const int wave = tid >> 6;
     for (int chunk = wave; chunk < nch; chunk += kPlanWaves)
-      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, route_r, L, W, pmask[wave]);
+      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, route_r, L, W, pmask[wave], sh.scan,
+                  cbl + chunk * kFusedPlaceMaxExperts);
   }
 }
 
@@ -510,7 +533,7 @@ __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, in
   const int chunk = blockIdx.x * 4 + wave;
   if (chunk >= n_chunks) return;
   place_chunk(chunk, M, E, K, Kext, W.flags[FLAG_FRESH_ALL] != 0, W.flags[FLAG_ROUTE_R] != 0, L,
-              W, mask[wave]);
+              W, mask[wave], W.eoffs, W.chunk_base + (size_t)chunk * E);
 }
 
 static bool fused_place(const Shape& s) {
