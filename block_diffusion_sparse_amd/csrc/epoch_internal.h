@@ -61,7 +61,7 @@ struct Scratch {
   int32_t* q;           // [M x Kext]
   float* w;             // [M x K]
   int32_t* flags;       // [FLAG_WORDS]
-  uint8_t* fpre;        // [M] fresh test before the anomaly override
+  uint8_t* fpre;        // [M] bit 0 fresh test before the anomaly override, 1 forced, 2 due
   int32_t* rids;        // [M x K] restricted mode: top-K inside the support
   float* rw;            // [M x K] and its weights
   int32_t* routed_ids;  // [M x K] the routing the worklist used

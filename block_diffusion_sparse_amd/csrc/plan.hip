@@ -309,7 +309,16 @@ __device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int 
   const int t = chunk * kChunk + lane;
   const bool in = t < M;
   for (int e = lane; e < E; e += 64) mask[e] = 0ull;
-  const bool fresh = in && (anomaly || W.fpre[t] != 0);
+  const uint8_t fp = in ? W.fpre[t] : 0;
+  const bool fresh = in && (anomaly || (fp & 1));
+  {
+    const int n_forced = __popcll(ballot64((fp & 2) != 0));
+    const int n_due = __popcll(ballot64((fp & 4) != 0));
+    if (lane == 0 && n_forced)
+      atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_FORCED_ROWS], (unsigned long long)n_forced);
+    if (lane == 0 && n_due)
+      atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_DUE_ROWS], (unsigned long long)n_due);
+  }
   if (in) L.fresh[t] = fresh ? 1 : 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -283,10 +283,10 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   if (lane == 0) {
     L.Dcur[t] = d;
     if (pd && !d) W.flags[FLAG_ANOMALY] = 1;
-    W.fpre[t] = fresh ? 1 : 0;
+    // bit 0: fresh before the anomaly override; bits 1, 2: forced, refresh due (counted per
+    // chunk by the placement: one atomic per chunk rather than per position on one address)
+    W.fpre[t] = (fresh ? 1 : 0) | (forced ? 2 : 0) | ((due && valid) ? 4 : 0);
     if (fresh) atomicAdd(&W.chunk_fresh[chunk], 1);
-    if (forced) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_FORCED_ROWS], 1ull);
-    if (due && valid) atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_DUE_ROWS], 1ull);
   }
 }
 
