@@ -54,9 +54,8 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
 // hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
 // (L / 8) % NB of tile 8 * ((L / 8) / NB) + L % 8, so every column block of a tile lands on
 // the same XCD and the tile's activation rows are fetched into one L2 only.
-template <int BM, int KC, int NST, bool GATEUP, bool ROUTED, int WAVES = 4, bool NT = false,
-          int MINW = 1>
-__global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
+template <int BM, int KC, int NST, bool GATEUP, bool ROUTED, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES) void k_expert_gemm(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
@@ -154,15 +153,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void k_expert_gemm(
     const int c = kchunk(c_);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (NT) {
-        x0[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                               reinterpret_cast<const u32x4*>(bp0 + (size_t)c * KC + 32 * s)));
-        x1[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                               reinterpret_cast<const u32x4*>(bp1 + (size_t)c * KC + 32 * s)));
-      } else {
-        x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
-        x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
-      }
+      x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
+      x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
     }
   };
   auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
@@ -276,17 +268,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BR * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
-  int pos, tile, cb;
+  int tile, cb;
   if (LMHEAD) {
     // few row tiles, many token blocks: token blocks go round the 8 XCDs and every row tile
     // of a block runs on the block's XCD (its W_v rows enter one L2); M bounds the row tiles
     const int T = (M + BR - 1) / BR, within = blockIdx.x >> 3;
     cb = 8 * (within / T) + (blockIdx.x & 7);
     tile = within % T;
-    pos = within;
     if (cb >= n_cb) return;
   } else {
-    pos = blockIdx.x >> 3;
+    const int pos = blockIdx.x >> 3;
     tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
     cb = pos % n_cb;
   }
