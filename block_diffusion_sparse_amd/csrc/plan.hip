@@ -90,6 +90,12 @@ __device__ __forceinline__ int block_incl_scan(int v, int32_t* wsum, int* total)
   return r;
 }
 
+// Counter increments are device-scope atomics that return nothing, so the issuing wave never
+// waits for them (a read-modify-write would hold every barrier after it for a memory round trip).
+__device__ __forceinline__ void counter_add(const LayerState& L, int idx, long long v) {
+  if (v) atomicAdd((unsigned long long*)&L.counters[idx], (unsigned long long)v);
+}
+
 struct SupportLds {
   unsigned long long p[kMaxExperts];
   unsigned long long G[kMaxExperts];
@@ -149,7 +155,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
   if (!s.restricted) {
     path = !valid ? 1 : (W.flags[FLAG_MISS] != 0 ? 2 : 0);
     if (path == 0) {
-      if (tid == 0) L.counters[EPOCH_CNT_HOT_SKIP] += 1;
+      if (tid == 0) counter_add(L, EPOCH_CNT_HOT_SKIP, 1);
       return 0;  // slots unchanged
     }
   } else {
@@ -279,20 +285,61 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     *L.S_size = size;
     *L.S_valid = 1;
     if (path == 0) {
-      L.counters[EPOCH_CNT_HOT_SKIP] += 1;
-      L.counters[EPOCH_CNT_RESTRICTED] += 1;
+      counter_add(L, EPOCH_CNT_HOT_SKIP, 1);
+      counter_add(L, EPOCH_CNT_RESTRICTED, 1);
     } else {
-      L.counters[path == 1 ? EPOCH_CNT_COLD : EPOCH_CNT_HOT_UPDATE] += 1;
-      if (reason == 1) L.counters[EPOCH_CNT_COVERAGE_FALLBACK] += 1;
-      if (reason == 2) L.counters[EPOCH_CNT_PERIOD_UPDATE] += 1;
-      L.counters[EPOCH_CNT_UNMET] += unmet;
+      counter_add(L, path == 1 ? EPOCH_CNT_COLD : EPOCH_CNT_HOT_UPDATE, 1);
+      if (reason == 1) counter_add(L, EPOCH_CNT_COVERAGE_FALLBACK, 1);
+      if (reason == 2) counter_add(L, EPOCH_CNT_PERIOD_UPDATE, 1);
+      counter_add(L, EPOCH_CNT_UNMET, unmet);
       L.counters[EPOCH_CNT_SUPPORT_SIZE] = s.restricted ? a_size_new : size;
       L.counters[EPOCH_CNT_U_FINAL] = nU_final;
-      L.counters[EPOCH_CNT_REPAIR_ROUNDS] += rounds;
+      counter_add(L, EPOCH_CNT_REPAIR_ROUNDS, rounds);
     }
   }
   __syncthreads();
   return (path == 0 ? 1 : 0) | 2;  // bit 0: route inside the support; bit 1: slots rewritten
+}
+
+// One position's routing as the placement reads it: the pre-anomaly flags and the K routed
+// ids and weights, the all-expert top-K (first K candidates) or, when the forward routes inside
+// the support, the in-support top-K.  Rows past M read position 0; every guard is uniform over
+// the wave, so the loads issue back to back (16-byte loads when K and the row stride allow).
+constexpr int kMaxTopK = 16;
+struct RowRouting {
+  int id[kMaxTopK];
+  float w[kMaxTopK];
+  uint8_t fp;
+  bool inside;  // which routing the ids are
+};
+
+__device__ __forceinline__ void load_row_routing(int t, int M, int K, int Kext, bool inside,
+                                                 const Scratch& W, RowRouting& r) {
+  const size_t tt = t < M ? (size_t)t : 0;
+  const int stride = inside ? K : Kext;
+  const int32_t* it = (inside ? W.rids : W.ids) + tt * stride;
+  const float* wt = (inside ? W.rw : W.w) + tt * K;
+  if ((K & 3) == 0 && (stride & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK / 4; ++j) {
+      if (4 * j < K) {
+        const int4 a = *reinterpret_cast<const int4*>(it + 4 * j);
+        const float4 b = *reinterpret_cast<const float4*>(wt + 4 * j);
+        r.id[4 * j] = a.x, r.id[4 * j + 1] = a.y, r.id[4 * j + 2] = a.z, r.id[4 * j + 3] = a.w;
+        r.w[4 * j] = b.x, r.w[4 * j + 1] = b.y, r.w[4 * j + 2] = b.z, r.w[4 * j + 3] = b.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k < K) {
+        r.id[k] = it[k];
+        r.w[k] = wt[k];
+      }
+    }
+  }
+  r.fp = W.fpre[tt];
+  r.inside = inside;
 }
 
 // Stable placement of one chunk by one wave (teardown, FreshLane pack: fresh rows with their
@@ -300,61 +347,81 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
 // expert kernel).  Final fresh flag = pre-anomaly test or anomaly.  Pair (t, k) of expert e
 // lands at eoffs[e] + chunk_base[chunk][e] + rank, where rank counts the chunk's earlier fresh
 // positions routed to e (a 64-bit mask per expert, in LDS, cleared by the wave beforehand).
-// Wave-level function: all 64 lanes call it; mask holds E entries owned by this wave.
-__device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, int Kext,
-                                            bool anomaly, bool route_r, const LayerState& L,
-                                            const Scratch& W, unsigned long long* mask,
-                                            const int32_t* eoffs, const int32_t* cbase) {
+// foff = fresh positions in chunks before this one.  r holds this lane's row (loaded by the
+// caller, possibly long before).  Wave-level function: all 64 lanes call it; mask holds E
+// entries owned by this wave.  Issues no global load; the per-position rows (inv and the
+// routing used) go out as 16-byte stores when K allows.
+__device__ __forceinline__ void place_chunk(int chunk, int M, int E, int K, bool anomaly,
+                                            const LayerState& L, const Scratch& W,
+                                            unsigned long long* mask, const int32_t* eoffs,
+                                            const int32_t* cbase, int foff, const RowRouting& r) {
   const int lane = threadIdx.x & 63;
   const int t = chunk * kChunk + lane;
   const bool in = t < M;
   for (int e = lane; e < E; e += 64) mask[e] = 0ull;
-  const uint8_t fp = in ? W.fpre[t] : 0;
+  const uint8_t fp = in ? r.fp : 0;
   const bool fresh = in && (anomaly || (fp & 1));
-  {
-    const int n_forced = __popcll(ballot64((fp & 2) != 0));
-    const int n_due = __popcll(ballot64((fp & 4) != 0));
-    if (lane == 0 && n_forced)
-      atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_FORCED_ROWS], (unsigned long long)n_forced);
-    if (lane == 0 && n_due)
-      atomicAdd((unsigned long long*)&L.counters[EPOCH_CNT_DUE_ROWS], (unsigned long long)n_due);
-  }
-  if (in) L.fresh[t] = fresh ? 1 : 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // the routing this forward uses: the all-expert top-K (first K candidates) or, when it
-  // routes inside the support, the in-support top-K
-  const int32_t* it = route_r ? W.rids + (size_t)(in ? t : 0) * K
-                              : W.ids + (size_t)(in ? t : 0) * Kext;
-  const float* wt = (route_r ? W.rw : W.w) + (size_t)(in ? t : 0) * K;
   if (fresh)
-    for (int k = 0; k < K; ++k) atomicOr(&mask[it[k]], 1ull << lane);
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+      if (k < K) atomicOr(&mask[r.id[k]], 1ull << lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (fresh) {
-    for (int k = 0; k < K; ++k) {
-      const int e = it[k];
-      const int rank = __popcll(mask[e] & below);
-      const int p = eoffs[e] + cbase[e] + rank;
+  int pk[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    pk[k] = -1;
+    if (k < K && fresh) {
+      const int e = r.id[k];
+      const int p = eoffs[e] + cbase[e] + __popcll(mask[e] & below);
       W.wl_pos[p] = t;
       W.wl_k[p] = k;
-      W.wl_w[p] = wt[k];
-      W.inv[(size_t)t * K + k] = p;
+      W.wl_w[p] = r.w[k];
+      pk[k] = p;
     }
-  } else if (in) {
-    for (int k = 0; k < K; ++k) W.inv[(size_t)t * K + k] = -1;
+  }
+  if (in) {
+    // the slot of every pair (-1: not fresh) and the routing the worklist used
+    int32_t* iv = W.inv + (size_t)t * K;
+    int32_t* ri = W.routed_ids + (size_t)t * K;
+    float* rw = W.routed_w + (size_t)t * K;
+    if ((K & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK / 4; ++j) {
+        if (4 * j < K) {
+          const int k = 4 * j;
+          *reinterpret_cast<int4*>(iv + k) = make_int4(pk[k], pk[k + 1], pk[k + 2], pk[k + 3]);
+          *reinterpret_cast<int4*>(ri + k) =
+              make_int4(r.id[k], r.id[k + 1], r.id[k + 2], r.id[k + 3]);
+          *reinterpret_cast<float4*>(rw + k) =
+              make_float4(r.w[k], r.w[k + 1], r.w[k + 2], r.w[k + 3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < K) {
+          iv[k] = pk[k];
+          ri[k] = r.id[k];
+          rw[k] = r.w[k];
+        }
+      }
+    }
+    L.fresh[t] = fresh ? 1 : 0;
   }
   const uint64_t fb = ballot64(fresh);
-  if (fresh) W.fresh_list[W.chunk_foff[chunk] + __popcll(fb & below)] = t;
-  // the routing the worklist used, for every position (last: nothing above waits on it)
-  if (in)
-    for (int k = 0; k < K; ++k) {
-      W.routed_ids[(size_t)t * K + k] = it[k];
-      W.routed_w[(size_t)t * K + k] = wt[k];
-    }
+  if (fresh) W.fresh_list[foff + __popcll(fb & below)] = t;
+  const int n_forced = __popcll(ballot64((fp & 2) != 0));
+  const int n_due = __popcll(ballot64((fp & 4) != 0));
+  if (lane == 0) {
+    counter_add(L, EPOCH_CNT_FORCED_ROWS, n_forced);
+    counter_add(L, EPOCH_CNT_DUE_ROWS, n_due);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -382,15 +449,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   __shared__ int32_t tot[kMaxExperts];
   __shared__ unsigned long long pmask[FUSED_PLACE ? kPlanWaves : 1]
                                      [FUSED_PLACE ? kFusedPlaceMaxExperts : 1];
-  // chunk bases of the fused placement, kept in LDS: [chunk][expert]
+  // chunk bases and fresh-list offsets of the fused placement, kept in LDS: [chunk][expert]
   __shared__ int32_t cbl[FUSED_PLACE ? kFusedPlaceMaxChunks * kFusedPlaceMaxExperts : 1];
+  __shared__ int32_t foffl[FUSED_PLACE ? kFusedPlaceMaxChunks : 1];
   const int tid = threadIdx.x;
   const int E = s.E, nch = s.n_chunks;
-  // per-expert totals and chunk bases: Gp threads per expert, each a contiguous chunk range
+  // per-expert totals and chunk bases: Gp groups of Epad threads, adjacent threads on adjacent
+  // experts (coalesced rows of the [chunk][expert] tables), each group a contiguous chunk range
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
   const int Gp = kPlanThreads / Epad;
-  const int e = tid / Gp, gi = tid % Gp;
+  const int e = tid & (Epad - 1), gi = tid / Epad;
   const int seg = (nch + Gp - 1) / Gp;
   const int c0 = min(nch, gi * seg), c1 = min(nch, c0 + seg);
   // global reads that do not depend on the support step, issued before it: the flags, the
@@ -400,7 +469,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
   const int pre_cf = tid < nch ? W.chunk_fresh[tid] : 0;
   const int pre_nS = *L.S_size;
-  const int pre_ex = tid < pre_nS ? L.S_list[tid] : 0;
+  const int pre_ex = tid < E ? L.S_list[tid] : 0;  // entries at and past S_size unused
   const bool pre_cnt = !s.restricted && seg <= kPre;
   int cv_f[kPre], cv_a[kPre];
 #pragma unroll
@@ -409,8 +478,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     cv_f[k] = in ? W.cnt_f[(size_t)(c0 + k) * E + e] : 0;
     cv_a[k] = in ? W.cnt_a[(size_t)(c0 + k) * E + e] : 0;
   }
+  // the fused placement's rows (one chunk per wave: position t = tid), read with the routing
+  // a restricted shape usually takes (inside the support) and read again if it takes the other
+  RowRouting row;
+  const bool placer = FUSED_PLACE && (tid >> 6) < nch;
+  if (placer) load_row_routing(tid, s.M, s.K, s.Kext, s.restricted, W, row);
   const int sp = support_phase(s, iter, L, W, sh);
   const bool route_r = (sp & 1) != 0;
+  if (placer && route_r != row.inside) load_row_routing(tid, s.M, s.K, s.Kext, route_r, W, row);
   __syncthreads();
 
   const int32_t* cnt = route_r ? (anomaly ? W.cnt_ar : W.cnt_fr) : (anomaly ? W.cnt_a : W.cnt_f);
@@ -424,29 +499,52 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     }
     return cnt[(size_t)c * E + e];
   };
+  // longer chunk ranges: kBatch loads in flight, then the batch's stores (a load issued after
+  // a store waits for it, so loads and stores alternate by batch, not by chunk)
+  constexpr int kBatch = 8;
   int local = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) local += count(c);
+  if (e < E) {
+    if (pre_cnt) {
+      for (int c = c0; c < c1; ++c) local += count(c);
+    } else {
+      for (int cb = c0; cb < c1; cb += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = cb + j < c1 ? cnt[(size_t)(cb + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) local += v[j];
+      }
+    }
+  }
   part[tid] = local;
   __syncthreads();
   if (e < E) {
     int base = 0, total = 0;
     for (int j = 0; j < Gp; ++j) {
-      const int v = part[e * Gp + j];
+      const int v = part[j * Epad + e];
       if (j < gi) base += v;
       total += v;
     }
     if (gi == 0) tot[e] = total;
     int run = base;
-    for (int c = c0; c < c1; ++c) {
-      W.chunk_base[(size_t)c * E + e] = run;
-      if (FUSED_PLACE) cbl[c * kFusedPlaceMaxExperts + e] = run;
-      run += count(c);
-      W.cnt_f[(size_t)c * E + e] = 0;  // consumed: clear for the next forward
-      W.cnt_a[(size_t)c * E + e] = 0;
-      if (s.restricted) {
-        W.cnt_fr[(size_t)c * E + e] = 0;
-        W.cnt_ar[(size_t)c * E + e] = 0;
+    for (int cb = c0; cb < c1; cb += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = cb + j < c1 ? count(cb + j) : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = cb + j;
+        if (c < c1) {
+          W.chunk_base[(size_t)c * E + e] = run;
+          if (FUSED_PLACE) cbl[c * kFusedPlaceMaxExperts + e] = run;
+          run += v[j];
+          W.cnt_f[(size_t)c * E + e] = 0;  // consumed: clear for the next forward
+          W.cnt_a[(size_t)c * E + e] = 0;
+          if (s.restricted) {
+            W.cnt_fr[(size_t)c * E + e] = 0;
+            W.cnt_ar[(size_t)c * E + e] = 0;
+          }
+        }
       }
     }
   }
@@ -500,6 +598,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     const int incl = block_incl_scan(nf, sh.wsum, &pass);
     if (c < nch) {
       W.chunk_foff[c] = carry + incl - nf;
+      if (FUSED_PLACE) foffl[c] = carry + incl - nf;
       W.chunk_fresh[c] = 0;
     }
     carry += pass;
@@ -511,11 +610,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     W.flags[FLAG_NPAIRS] = P;
     W.flags[FLAG_NTILES] = T;
     W.flags[FLAG_NTILES_BIG] = Tb;
-    L.counters[EPOCH_CNT_FRESH_ROWS] += nfresh;
-    L.counters[EPOCH_CNT_PAIRS] += P;
-    L.counters[EPOCH_CNT_TOUCHED] += touched;
-    L.counters[EPOCH_CNT_FORWARDS] += 1;
-    if (anomaly) L.counters[EPOCH_CNT_ANOMALY] += 1;
+    counter_add(L, EPOCH_CNT_FRESH_ROWS, nfresh);
+    counter_add(L, EPOCH_CNT_PAIRS, P);
+    counter_add(L, EPOCH_CNT_TOUCHED, touched);
+    counter_add(L, EPOCH_CNT_FORWARDS, 1);
+    if (anomaly) counter_add(L, EPOCH_CNT_ANOMALY, 1);
     // every thread read MISS and ANOMALY before the barriers above
     W.flags[FLAG_FRESH_ALL] = anomaly ? 1 : 0;
     W.flags[FLAG_ROUTE_R] = route_r ? 1 : 0;
@@ -525,12 +624,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     W.flags[FLAG_SHORT] = 0;
   }
   if (FUSED_PLACE) {
-    // chunk_base, eoffs and chunk_foff were written above by this workgroup
+    // the expert offsets, chunk bases and fresh-list offsets are in LDS (written above)
     __syncthreads();
     const int wave = tid >> 6;
-    for (int chunk = wave; chunk < nch; chunk += kPlanWaves)
-      place_chunk(chunk, s.M, E, s.K, s.Kext, anomaly, route_r, L, W, pmask[wave], sh.scan,
-                  cbl + chunk * kFusedPlaceMaxExperts);
+    if (wave < nch)
+      place_chunk(wave, s.M, E, s.K, anomaly, L, W, pmask[wave], sh.scan,
+                  cbl + wave * kFusedPlaceMaxExperts, foffl[wave], row);
   }
 }
 
@@ -541,8 +640,11 @@ __global__ __launch_bounds__(256) void k_place(int M, int E, int K, int Kext, in
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x * 4 + wave;
   if (chunk >= n_chunks) return;
-  place_chunk(chunk, M, E, K, Kext, W.flags[FLAG_FRESH_ALL] != 0, W.flags[FLAG_ROUTE_R] != 0, L,
-              W, mask[wave], W.eoffs, W.chunk_base + (size_t)chunk * E);
+  RowRouting row;
+  load_row_routing(chunk * kChunk + (threadIdx.x & 63), M, K, Kext, W.flags[FLAG_ROUTE_R] != 0, W,
+                   row);
+  place_chunk(chunk, M, E, K, W.flags[FLAG_FRESH_ALL] != 0, L, W, mask[wave], W.eoffs,
+              W.chunk_base + (size_t)chunk * E, W.chunk_foff[chunk], row);
 }
 
 static bool fused_place(const Shape& s) {
