@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+TIMED_EVERY = 4            # the timed region times the dominant kernel on every 4th forward
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -164,24 +165,49 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def one_block(timing_groups: int):
+    def one_block(timing_groups: int, every: int = 1):
+        # timing_groups on every `every`-th forward (a timed dispatch costs a few us of gap on
+        # each side, so the timed region samples its launches instead of timing them all)
         plan = B.epoch_block_plan_build(desc, lw, ws, nbytes, sp)
-        if timing_groups:
-            B.epoch_plan_set_timing(plan, timing_groups)
+        n_fwd = 0
         for it in range(iters):
             for l in range(n_layers):
+                if timing_groups and (every == 1 or n_fwd % every in (0, 1)):
+                    B.epoch_plan_set_timing(plan, timing_groups if n_fwd % every == 0 else 0)
+                n_fwd += 1
                 B.epoch_moe_fresh_forward(plan, l, Xdev[l][it], Ddev[it],
                                           None if Fdev is None else Fdev[it], Y, None, sp)
                 B.epoch_cache_update(plan, l, sp)
         return plan
 
+    def layer_counters(plan, l):
+        ins = B.epoch_plan_inspect(plan, l)
+        off = ins.counters - ws.data_ptr()
+        return ws[off:off + 8 * B.EPOCH_NUM_COUNTERS].view(torch.int64).cpu().numpy()
+
     def block_counters(plan):
-        tot = np.zeros(B.EPOCH_NUM_COUNTERS, dtype=np.int64)
-        for l in range(n_layers):
-            ins = B.epoch_plan_inspect(plan, l)
-            off = ins.counters - ws.data_ptr()
-            tot += ws[off:off + 8 * B.EPOCH_NUM_COUNTERS].view(torch.int64).cpu().numpy()
+        tot = sum(layer_counters(plan, l) for l in range(n_layers))
         return dict(zip(B.COUNTERS, tot.tolist()))
+
+    def reference_block():
+        """An untimed block, read after every forward: the block's counters and each forward's
+        touched experts and fresh pairs (blocks are deterministic, so they hold for every
+        block)."""
+        plan = B.epoch_block_plan_build(desc, lw, ws, nbytes, sp)
+        prev = [layer_counters(plan, l) for l in range(n_layers)]
+        i_t, i_p = B.COUNTERS.index("touched"), B.COUNTERS.index("pairs")
+        fwd = []
+        for it in range(iters):
+            for l in range(n_layers):
+                B.epoch_moe_fresh_forward(plan, l, Xdev[l][it], Ddev[it],
+                                          None if Fdev is None else Fdev[it], Y, None, sp)
+                B.epoch_cache_update(plan, l, sp)
+                c = layer_counters(plan, l)
+                fwd.append((int(c[i_t] - prev[l][i_t]), int(c[i_p] - prev[l][i_p])))
+                prev[l] = c
+        counters = block_counters(plan)
+        B.epoch_block_plan_destroy(plan)
+        return counters, fwd
 
     def collect(plans):
         ms_ = {g: 0.0 for g in B.TIMING_GROUPS}
@@ -197,20 +223,17 @@ def main():
     for _ in range(args.warmup):
         B.epoch_block_plan_destroy(one_block(0))
     torch.cuda.synchronize()
-    ref_plan = one_block(0)
-    torch.cuda.synchronize()
-    per_block = block_counters(ref_plan)
-    B.epoch_block_plan_destroy(ref_plan)
+    per_block, per_fwd = reference_block()
     # per-kernel breakdown (every group timed; outside the timed region).  Its events go back
     # to the library's pool, so the timed region below creates none.
     brk_ms, brk_n = collect([one_block(-1) for _ in range(args.steps)])
 
     # ---------------------------------------------------------------- timed region
-    gemm_groups = (1 << B.TIMING_GROUPS.index("routed_gateup")) | \
-                  (1 << B.TIMING_GROUPS.index("routed_down"))
+    # the dominant expert kernel (by the breakdown) is the one timed live, two events a forward
+    dom = max(("routed_gateup", "routed_down"), key=lambda g: brk_ms[g] / max(brk_n[g], 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    plans = [one_block(gemm_groups) for _ in range(args.steps)]
+    plans = [one_block(1 << B.TIMING_GROUPS.index(dom), TIMED_EVERY) for _ in range(args.steps)]
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     last = block_counters(plans[-1])
@@ -224,8 +247,11 @@ def main():
     us_per_layer_iter = 1e3 * ms_per_step / layer_iters
 
     # ---------------------------------------------------------------- roofline of the dominant kernel
-    touched = per_block["touched"]          # sum over forwards of experts with fresh pairs
-    P = pairs_per_block
+    # the forwards the timed region timed (every TIMED_EVERY-th of each block), their touched
+    # experts and fresh pairs from the reference block
+    sampled = per_fwd[::TIMED_EVERY]
+    touched = sum(t for t, _ in sampled)     # experts with fresh pairs, summed over forwards
+    P = sum(p for _, p in sampled)
     act = 2 if w.act == "bf16" else 4
     algo = {
         # W1 + W3 of every touched expert, gathered x rows, h written
@@ -234,8 +260,8 @@ def main():
         "routed_down": touched * H * I * act + P * I * act + P * H * act,
     }
     flops = {"routed_gateup": 4.0 * P * H * I, "routed_down": 2.0 * P * H * I}
-    dom = max(("routed_gateup", "routed_down"), key=lambda g: group_ms[g])
     launches = max(group_n[dom], 1)
+    assert launches == len(sampled) * args.steps, (launches, len(sampled), args.steps)
     avg_ms = group_ms[dom] / launches
     steps = args.steps
     bytes_per_launch = algo[dom] * steps / launches
@@ -245,7 +271,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": dom,
                 "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                "avg_launch_us": round(avg_ms * 1e3, 2),
+                "avg_launch_us": round(avg_ms * 1e3, 2), "timed_launches": launches,
+                "timed_every": TIMED_EVERY,
                 "mfma_tflops": round(flops[dom] * steps / launches / (avg_ms * 1e-3) / 1e12, 2),
                 "mfma_frac_of_bf16_peak": round(flops[dom] * steps / launches / (avg_ms * 1e-3)
                                                 / 1e12 / MFMA_BF16_PEAK_TFS, 4)}

@@ -211,18 +211,18 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   if (workspace_bytes < L.bytes) return EPOCH_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int M = d->batch * d->block, n_p = d->vocab / 64;
-  hipLaunchKernelGGL(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
+  launch(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
                      L.live_list, L.live_idx, L.n_live);
   // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
   // at once) x token blocks per XCD
   const int tiles = (M + 127) / 128, n_cb = d->vocab / 128;
   const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
-  hipLaunchKernelGGL((k_gemm_big<false, false, true>), dim3(8 * tiles * ((n_cb + 7) / 8)),
+  launch((k_gemm_big<false, false, true>), dim3(8 * tiles * ((n_cb + 7) / 8)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
-  hipLaunchKernelGGL(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, n_p, d->tau,
+  launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, n_p, d->tau,
                      decoded, L.live_idx, L.pmax, L.parg, L.psum, decoded_next, tokens, conf);
   return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;
 }

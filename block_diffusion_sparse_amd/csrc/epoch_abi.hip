@@ -193,6 +193,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+namespace epoch {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace epoch
+
 struct TimedPair {
   int group;
   hipEvent_t a, b;
@@ -211,8 +218,10 @@ hipEvent_t pool_event() {
       return e;
     }
   }
+  // timing only: no system-scope fence (cache writeback and invalidate) at each record, which
+  // would otherwise stall the work after it; elapsed times are still exact
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -238,26 +247,35 @@ struct epoch_plan {
 
 namespace {
 
-// Records an event pair around one kernel group when timing is on.
+// Times one kernel group when timing is on: the group's launches carry an event pair (see
+// launch()), kept for epoch_plan_timing if some kernel of the group ran.
 struct GroupTimer {
   epoch_plan* p;
-  hipStream_t st;
   int group;
-  hipEvent_t a = nullptr;
-  GroupTimer(epoch_plan* p_, hipStream_t st_, int g) : p(p_), st(st_), group(g) {
-    if (((p->timing_mask >> g) & 1u) && (a = pool_event())) (void)hipEventRecord(a, st);
-  }
-  void done() {
-    if (!a) return;
-    hipEvent_t b = pool_event();
+  hipEvent_t a = nullptr, b = nullptr;
+  GroupTimer(epoch_plan* p_, hipStream_t, int g) : p(p_), group(g) {
+    if (!((p->timing_mask >> g) & 1u)) return;
+    a = pool_event();
+    b = a ? pool_event() : nullptr;
     if (!b) {
-      pool_release(a);
+      if (a) pool_release(a);
+      a = nullptr;
       return;
     }
-    (void)hipEventRecord(b, st);
-    p->pairs.push_back({group, a, b});
-    a = nullptr;
+    launch_events() = LaunchEvents{a, b, false};
   }
+  void done() {
+    if (!b) return;
+    if (launch_events().used) {
+      p->pairs.push_back({group, a, b});
+    } else {
+      pool_release(a);
+      pool_release(b);
+    }
+    launch_events() = LaunchEvents{};
+    a = b = nullptr;
+  }
+  ~GroupTimer() { done(); }
 };
 
 }  // namespace

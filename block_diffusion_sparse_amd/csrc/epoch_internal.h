@@ -1,11 +1,31 @@
 // Internal declarations shared by the HIP translation units of libepoch (gfx950 only).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/epoch.h"
 
 namespace epoch {
+
+// Timing events of the kernel group being launched on this host thread (none: not timed).
+// The group's first launch carries `start`, every launch carries `stop`, so the pair spans the
+// group from its first kernel's start to its last kernel's end, stamped by the dispatches
+// themselves: timing adds no packets between kernels.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;  // a launch has taken `start`
+};
+LaunchEvents& launch_events();
+
+// Every kernel launch of the library goes through here.
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  LaunchEvents& ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.used ? nullptr : ev.start, ev.stop, 0u,
+                        args...);
+  if (ev.stop) ev.used = true;
+}
 
 constexpr int kWave = 64;
 constexpr int kChunk = 64;        // positions per compaction chunk (one wave)

@@ -39,11 +39,11 @@ static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, 
   constexpr int WAVES = GATEUP ? kGateUpWaves : kDownWaves;
   const dim3 grid = gemm_grid(tiles, Ndim, GATEUP), block(64 * WAVES);
   if (Kdim % kGemmKC == 0)
-    hipLaunchKernelGGL((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED, WAVES>),
+    launch((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED, WAVES>),
                        grid, block, 0, st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs,
                        S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
   else
-    hipLaunchKernelGGL((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED, WAVES>), grid, block, 0,
+    launch((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED, WAVES>), grid, block, 0,
                        st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs, S_list,
                        W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
 }
@@ -113,14 +113,14 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
                             L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
     if (s.big_routed)  // experts with many fresh rows: compute-bound 128 x 128 tiles
-      hipLaunchKernelGGL((k_gemm_big<true, true>),
+      launch((k_gemm_big<true, true>),
                          dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
                          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
                          W.offs, L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M,
                          s.H, s.I, LmPartials{});
   } else
-    hipLaunchKernelGGL(k_gateup_f32<true>, grid, dim3(256), 0, st, static_cast<const float*>(x),
+    launch(k_gateup_f32<true>, grid, dim3(256), 0, st, static_cast<const float*>(x),
                        static_cast<const float*>(w1), static_cast<const float*>(w3), W.flags,
                        W.tile_slot, W.tile_row0, W.offs, L.S_list, W.wl_pos,
                        static_cast<float*>(W.h), s.M, s.H, s.I);
@@ -134,14 +134,14 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
                              static_cast<uint16_t*>(W.y_pair), s.M, s.H);
     if (s.big_routed)
-      hipLaunchKernelGGL((k_gemm_big<false, true>),
+      launch((k_gemm_big<false, true>),
                          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
                          st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
                          nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
                          W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H,
                          LmPartials{});
   } else
-    hipLaunchKernelGGL(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st, static_cast<const float*>(W.h),
+    launch(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st, static_cast<const float*>(W.h),
                        static_cast<const float*>(w2), W.flags, W.tile_slot, W.tile_row0, W.offs,
                        L.S_list, W.wl_w, static_cast<float*>(W.y_pair), s.M, s.H, s.I);
   return hipGetLastError();
@@ -155,12 +155,12 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
     // many rows: compute-bound, 128 x 128 tiles with both operands staged in LDS
     const int tiles = (s.M + 127) / 128;
     const dim3 gu(((tiles + 7) / 8) * 8 * (s.Is / 64)), gd(((tiles + 7) / 8) * 8 * ((s.H + 127) / 128));
-    hipLaunchKernelGGL((k_gemm_big<true, false>), gu, dim3(256), 0, st,
+    launch((k_gemm_big<true, false>), gu, dim3(256), 0, st,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(sw1),
                        static_cast<const uint16_t*>(sw3), W.flags, nullptr, nullptr, nullptr,
                        nullptr, nullptr, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.H, s.Is,
                        LmPartials{});
-    hipLaunchKernelGGL((k_gemm_big<false, false>), gd, dim3(256), 0, st,
+    launch((k_gemm_big<false, false>), gd, dim3(256), 0, st,
                        static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
                        nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                        static_cast<uint16_t*>(W.S), s.M, s.Is, s.H, LmPartials{});
@@ -172,11 +172,11 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
                               static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
                               nullptr, W, nullptr, static_cast<uint16_t*>(W.S), s.M, s.H);
   } else {
-    hipLaunchKernelGGL(k_gateup_f32<false>, g1, dim3(256), 0, st, static_cast<const float*>(x),
+    launch(k_gateup_f32<false>, g1, dim3(256), 0, st, static_cast<const float*>(x),
                        static_cast<const float*>(sw1), static_cast<const float*>(sw3), W.flags,
                        nullptr, nullptr, nullptr, nullptr, nullptr, static_cast<float*>(W.hs),
                        s.M, s.H, s.Is);
-    hipLaunchKernelGGL(k_down_f32<false>, g2, dim3(256), 0, st, static_cast<const float*>(W.hs),
+    launch(k_down_f32<false>, g2, dim3(256), 0, st, static_cast<const float*>(W.hs),
                        static_cast<const float*>(sw2), W.flags, nullptr, nullptr, nullptr, nullptr,
                        nullptr, static_cast<float*>(W.S), s.M, s.H, s.Is);
   }
@@ -298,12 +298,12 @@ __global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_sh
 hipError_t launch_combine(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                           void* y, void* y_routed, hipStream_t st) {
   if (s.bf16)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
+    launch(k_combine<uint16_t>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
                        s.n_shared, iter, L, W.inv, static_cast<const uint16_t*>(W.y_pair),
                        static_cast<const uint16_t*>(W.S), static_cast<uint16_t*>(y),
                        static_cast<uint16_t*>(y_routed));
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K, s.n_shared,
+    launch(k_combine<float>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K, s.n_shared,
                        iter, L, W.inv, static_cast<const float*>(W.y_pair),
                        static_cast<const float*>(W.S), static_cast<float*>(y),
                        static_cast<float*>(y_routed));

@@ -36,7 +36,7 @@ __global__ void k_init_layer(int M, int E, LayerState L) {
 
 hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st) {
   const int n = max(max(s.M, s.E), (int)EPOCH_NUM_COUNTERS);
-  hipLaunchKernelGGL(k_init_layer, dim3((n + 255) / 256), dim3(256), 0, st, s.M, s.E, L);
+  launch(k_init_layer, dim3((n + 255) / 256), dim3(256), 0, st, s.M, s.E, L);
   return hipGetLastError();
 }
 
@@ -50,8 +50,8 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 hipError_t launch_init_scratch(const Shape& s, const Scratch& W, hipStream_t st) {
   // cnt_f, cnt_a and chunk_fresh are carved back to back
   const int n = (int)(W.chunk_fresh + s.n_chunks - W.cnt_f);
-  hipLaunchKernelGGL(k_zero_i32, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, st, W.cnt_f, n);
-  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, st, W.flags, (int)FLAG_WORDS);
+  launch(k_zero_i32, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, st, W.cnt_f, n);
+  launch(k_zero_i32, dim3(1), dim3(64), 0, st, W.flags, (int)FLAG_WORDS);
   return hipGetLastError();
 }
 
@@ -96,15 +96,64 @@ __device__ __forceinline__ void counter_add(const LayerState& L, int idx, long l
   if (v) atomicAdd((unsigned long long*)&L.counters[idx], (unsigned long long)v);
 }
 
+// Inclusive scans of N values per thread over the workgroup at once (two barriers); msum is
+// N x kPlanWaves ints of LDS owned by the caller, free again after the caller's next barrier.
+template <int N>
+__device__ __forceinline__ void block_multi_scan(int (&v)[N], int32_t (*msum)[kPlanWaves],
+                                                 int (&total)[N]) {
+  static_assert(N <= kPlanWaves, "one wave scans each column of wave sums");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int n = 0; n < N; ++n) v[n] = wave_incl_scan(v[n]);
+  if (lane == 63)
+#pragma unroll
+    for (int n = 0; n < N; ++n) msum[n][wave] = v[n];
+  __syncthreads();
+  if (wave < N) {
+    int w = lane < kPlanWaves ? msum[wave][lane] : 0;
+    w = wave_incl_scan(w);
+    if (lane < kPlanWaves) msum[wave][lane] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    v[n] += wave ? msum[n][wave - 1] : 0;
+    total[n] = msum[n][kPlanWaves - 1];
+  }
+}
+
+// The uniform state the plan step starts from, read in one batch after the per-thread
+// prefetches so that a single wait covers all of them.
+struct PlanState {
+  int anomaly, miss, under, short_rows;  // router flags of this forward
+  int s_valid, s_size;                   // the slot lists
+  int a_valid, a_built, a_size;          // the Atlas set (restricted routing)
+};
+
+__device__ __forceinline__ PlanState load_plan_state(const LayerState& L, const Scratch& W) {
+  PlanState ps;
+  ps.anomaly = W.flags[FLAG_ANOMALY];
+  ps.miss = W.flags[FLAG_MISS];
+  ps.under = W.flags[FLAG_UNDER];
+  ps.short_rows = W.flags[FLAG_SHORT];
+  ps.s_valid = *L.S_valid;
+  ps.s_size = *L.S_size;
+  ps.a_valid = L.A_state[0];
+  ps.a_built = L.A_state[1];
+  ps.a_size = L.A_state[2];
+  return ps;
+}
+
 struct SupportLds {
   unsigned long long p[kMaxExperts];
   unsigned long long G[kMaxExperts];
   int32_t H[kMaxExperts];
   int32_t scan[kMaxExperts];
   int32_t wsum[kPlanWaves];
+  int32_t slist[kMaxExperts];  // the slot list as last written (bit 1 of support_phase)
   uint8_t inS[kMaxExperts];
   uint8_t pick[kMaxExperts];
-  int nU, added;
+  int nU, added, size;
 };
 
 __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
@@ -143,30 +192,30 @@ __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
 // otherwise (hot-skip) the slots are the support and the forward routes inside it.
 // Returns bit 0 = the forward routes inside the support, bit 1 = the slot lists were rewritten.
 __device__ int support_phase(const Shape& s, int iter, const LayerState& L, const Scratch& W,
-                             SupportLds& sh) {
+                             const PlanState& ps, SupportLds& sh) {
   const int tid = threadIdx.x;
   const int M = s.M, E = s.E, K = s.K, Kext = s.Kext;
   const long long an = s.an, ad = s.ad, qn = s.qn, qd = s.qd, bn = s.bn, bd = s.bd;
   const int32_t* ids = W.ids;
   const int32_t* q = W.q;
-  const bool valid = *L.S_valid != 0;
+  const bool valid = ps.s_valid != 0;
   int path;        // 0 hot-skip, 1 cold, 2 hot-update
   int reason = 0;  // restricted hot-update: 1 coverage check, 2 update period
   if (!s.restricted) {
-    path = !valid ? 1 : (W.flags[FLAG_MISS] != 0 ? 2 : 0);
+    path = !valid ? 1 : (ps.miss != 0 ? 2 : 0);
     if (path == 0) {
       if (tid == 0) counter_add(L, EPOCH_CNT_HOT_SKIP, 1);
       return 0;  // slots unchanged
     }
   } else {
-    const int a_valid = L.A_state[0], built = L.A_state[1], a_size = L.A_state[2];
-    const long long nU = W.flags[FLAG_UNDER];
+    const int a_valid = ps.a_valid, built = ps.a_built, a_size = ps.a_size;
+    const long long nU = ps.under;
     if (!a_valid) {
       path = 1;
     } else if (s.atlas_period > 0 && iter - built >= s.atlas_period) {
       path = 2;
       reason = 2;
-    } else if (a_size < K || W.flags[FLAG_SHORT] != 0 || qd * nU > (qd - qn) * (long long)M) {
+    } else if (a_size < K || ps.short_rows != 0 || qd * nU > (qd - qn) * (long long)M) {
       path = 2;
       reason = 1;
     } else {
@@ -277,6 +326,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     if (sh.inS[tid]) {
       L.slot_of[tid] = incl - 1;
       L.S_list[incl - 1] = tid;
+      sh.slist[incl - 1] = tid;
     } else {
       L.slot_of[tid] = -1;
     }
@@ -284,6 +334,7 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
   if (tid == 0) {
     *L.S_size = size;
     *L.S_valid = 1;
+    sh.size = size;
     if (path == 0) {
       counter_add(L, EPOCH_CNT_HOT_SKIP, 1);
       counter_add(L, EPOCH_CNT_RESTRICTED, 1);
@@ -452,6 +503,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   // chunk bases and fresh-list offsets of the fused placement, kept in LDS: [chunk][expert]
   __shared__ int32_t cbl[FUSED_PLACE ? kFusedPlaceMaxChunks * kFusedPlaceMaxExperts : 1];
   __shared__ int32_t foffl[FUSED_PLACE ? kFusedPlaceMaxChunks : 1];
+  __shared__ int32_t msum[6][kPlanWaves];
   const int tid = threadIdx.x;
   const int E = s.E, nch = s.n_chunks;
   // per-expert totals and chunk bases: Gp groups of Epad threads, adjacent threads on adjacent
@@ -466,9 +518,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   // fresh-list counts, the slot list of an unchanged support, and (all-expert routing, up to
   // kPre chunks per thread) both per-chunk pair counts
   constexpr int kPre = 4;
-  const bool anomaly = W.flags[FLAG_ANOMALY] != 0;
   const int pre_cf = tid < nch ? W.chunk_fresh[tid] : 0;
-  const int pre_nS = *L.S_size;
   const int pre_ex = tid < E ? L.S_list[tid] : 0;  // entries at and past S_size unused
   const bool pre_cnt = !s.restricted && seg <= kPre;
   int cv_f[kPre], cv_a[kPre];
@@ -483,7 +533,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   RowRouting row;
   const bool placer = FUSED_PLACE && (tid >> 6) < nch;
   if (placer) load_row_routing(tid, s.M, s.K, s.Kext, s.restricted, W, row);
-  const int sp = support_phase(s, iter, L, W, sh);
+  const PlanState ps = load_plan_state(L, W);
+  const bool anomaly = ps.anomaly != 0;
+  const int pre_nS = ps.s_size;
+  const int sp = support_phase(s, iter, L, W, ps, sh);
   const bool route_r = (sp & 1) != 0;
   if (placer && route_r != row.inside) load_row_routing(tid, s.M, s.K, s.Kext, route_r, W, row);
   __syncthreads();
@@ -549,61 +602,71 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     }
   }
   __syncthreads();
-  // expert offsets: exclusive scan of the totals (one expert per thread)
-  const int my_tot = tid < E ? tot[tid] : 0;
-  int P;
-  const int eincl = block_incl_scan(my_tot, sh.wsum, &P);
-  sh.scan[tid] = eincl - my_tot;
-  if (tid < E) W.eoffs[tid] = eincl - my_tot;
-  if (tid == 0) W.eoffs[E] = P;
-  __syncthreads();
-  // slot offsets and the tile tables (one support slot per thread); an expert with at least
-  // kBigRows pairs goes to the compute-bound table when the shape enables it
+  // The prefix sums of the step in one workgroup scan:
+  //   [0] pair totals by expert (one expert per thread)      -> eoffs, P
+  //   [1] pair totals by support slot (one slot per thread)   -> offs
+  //   [2], [3] small and big tile counts by slot              -> tile tables, T, Tb
+  //   [4] fresh positions by chunk (first kPlanThreads chunks) -> chunk_foff
+  //   [5] touched experts (a count only)
+  // offs[j] equals eoffs[S_list[j]]: every expert with pairs has a slot (the router flags a
+  // routed expert outside the support, and such a forward rebuilds the slots), so the experts
+  // between two slots contribute nothing.  An expert with at least kBigRows pairs goes to the
+  // compute-bound table when the shape enables it.
   const bool slots_new = (sp & 2) != 0;
-  const int nS = slots_new ? *L.S_size : pre_nS;
-  int my_tiles = 0, my_big = 0, my_off = 0;
+  const int nS = slots_new ? sh.size : pre_nS;
+  const int my_tot = tid < E ? tot[tid] : 0;
+  int slot_tot = 0, my_tiles = 0, my_big = 0;
   if (tid < nS) {
-    const int ex = slots_new ? L.S_list[tid] : pre_ex;
-    my_off = sh.scan[ex];
-    if (s.big_routed && tot[ex] >= kBigRows)
-      my_big = (tot[ex] + kBigTile - 1) / kBigTile;
+    slot_tot = tot[slots_new ? sh.slist[tid] : pre_ex];
+    if (s.big_routed && slot_tot >= kBigRows)
+      my_big = (slot_tot + kBigTile - 1) / kBigTile;
     else
-      my_tiles = (tot[ex] + kTileRows - 1) / kTileRows;
-    W.offs[tid] = my_off;
+      my_tiles = (slot_tot + kTileRows - 1) / kTileRows;
   }
-  if (tid == 0) W.offs[nS] = P;
-  int T, Tb;
-  const int tincl = block_incl_scan(my_tiles, sh.wsum, &T);
-  const int bincl = s.big_routed ? block_incl_scan(my_big, sh.wsum, &Tb) : (Tb = 0, 0);
+  const int nf0 = tid < nch ? (anomaly ? min(kChunk, s.M - tid * kChunk) : pre_cf) : 0;
+  int sc[6] = {my_tot, slot_tot, my_tiles, my_big, nf0, my_tot > 0 ? 1 : 0};
+  int stot[6];
+  block_multi_scan(sc, msum, stot);
+  const int P = stot[0], T = stot[2], Tb = stot[3], touched = stot[5];
+  sh.scan[tid] = sc[0] - my_tot;  // read by the fused placement after the barrier below
+  if (tid < E) W.eoffs[tid] = sc[0] - my_tot;
+  if (tid == 0) {
+    W.eoffs[E] = P;
+    W.offs[nS] = P;
+  }
   if (tid < nS) {
-    const int t0 = tincl - my_tiles;
+    const int my_off = sc[1] - slot_tot;
+    W.offs[tid] = my_off;
+    const int t0 = sc[2] - my_tiles;
     for (int i = 0; i < my_tiles; ++i) {
       W.tile_slot[t0 + i] = tid;
       W.tile_row0[t0 + i] = my_off + i * kTileRows;
     }
-    const int b0 = bincl - my_big;
+    const int b0 = sc[3] - my_big;
     for (int i = 0; i < my_big; ++i) {
       W.tile_slot_b[b0 + i] = tid;
       W.tile_row0_b[b0 + i] = my_off + i * kBigTile;
     }
   }
-  // fresh-list offsets of the chunks, kPlanThreads chunks per pass
-  int carry = 0;
-  for (int base = 0; base < nch; base += kPlanThreads) {
+  // fresh-list offsets of the chunks: the first kPlanThreads from the scan above, the rest
+  // (more than kPlanThreads * kChunk positions) kPlanThreads chunks per pass
+  if (tid < nch) {
+    W.chunk_foff[tid] = sc[4] - nf0;
+    if (FUSED_PLACE) foffl[tid] = sc[4] - nf0;
+    W.chunk_fresh[tid] = 0;
+  }
+  int carry = stot[4];
+  for (int base = kPlanThreads; base < nch; base += kPlanThreads) {
     const int c = base + tid;
-    const int nf = c < nch ? (anomaly ? min(kChunk, s.M - c * kChunk)
-                                      : (base == 0 ? pre_cf : W.chunk_fresh[c]))
-                           : 0;
+    const int nf = c < nch ? (anomaly ? min(kChunk, s.M - c * kChunk) : W.chunk_fresh[c]) : 0;
     int pass;
     const int incl = block_incl_scan(nf, sh.wsum, &pass);
     if (c < nch) {
       W.chunk_foff[c] = carry + incl - nf;
-      if (FUSED_PLACE) foffl[c] = carry + incl - nf;
       W.chunk_fresh[c] = 0;
     }
     carry += pass;
   }
-  const int touched = __syncthreads_count(tid < E && tot[tid] > 0);
   if (tid == 0) {
     const int nfresh = carry;
     W.flags[FLAG_NFRESH] = nfresh;
@@ -654,15 +717,15 @@ static bool fused_place(const Shape& s) {
 hipError_t launch_plan(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                        hipStream_t st) {
   if (fused_place(s))
-    hipLaunchKernelGGL(k_plan<true>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
+    launch(k_plan<true>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
   else
-    hipLaunchKernelGGL(k_plan<false>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
+    launch(k_plan<false>, dim3(1), dim3(kPlanThreads), 0, st, s, iter, L, W);
   return hipGetLastError();
 }
 
 hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st) {
   if (!fused_place(s))
-    hipLaunchKernelGGL(k_place, dim3((s.n_chunks + 3) / 4), dim3(256), 0, st, s.M, s.E, s.K,
+    launch(k_place, dim3((s.n_chunks + 3) / 4), dim3(256), 0, st, s.M, s.E, s.K,
                        s.Kext, s.n_chunks, L, W);
   return hipGetLastError();
 }

@@ -384,7 +384,7 @@ static void launch_k_router(const Shape& s, const void* x, const float* Wg, cons
                             const Scratch& W, hipStream_t st) {
   const size_t lds = (size_t)s.ksplit * BT * BT * sizeof(double);
   const dim3 grid((s.E + BT - 1) / BT, (s.M + BT - 1) / BT), block(64 * s.ksplit);
-  hipLaunchKernelGGL((k_router<T, BT>), grid, block, lds, st, static_cast<const T*>(x), Wg, bias,
+  launch((k_router<T, BT>), grid, block, lds, st, static_cast<const T*>(x), Wg, bias,
                      W.G, s.M, s.H, s.E, s.ksplit);
 }
 
@@ -409,7 +409,7 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
                      s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group};
   const int nper = (s.E + 63) / 64;
 #define EPOCH_ROUTE_ROWS(NP) \
-  hipLaunchKernelGGL(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
+  launch(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
   if (nper <= 1)
     EPOCH_ROUTE_ROWS(1);
   else if (nper <= 2)

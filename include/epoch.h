@@ -251,9 +251,12 @@ const char* epoch_status_string(int32_t status);
  * Kernel timing for measurement.  `groups` is a bitmask of kernel groups (bit g = group g;
  * -1 = all): 0 router + top-k + fresh test, 1 plan (support check / build, worklist scans),
  * 2 worklist placement, 3 routed gate/up,
- * 4 routed down, 5 shared expert, 6 combine.  While set, each forward records a pair of HIP
- * events on its stream around every selected group (events come from a process-wide pool,
- * so a measured region reuses events created earlier).  epoch_plan_timing synchronises the
+ * 4 routed down, 5 shared expert, 6 combine.  While set, the kernels of every selected group
+ * of each forward carry a pair of HIP events on the forward's stream, stamped by the dispatches
+ * themselves: the start of the group's first kernel and the end of its last (events come from
+ * a process-wide pool, so a measured region reuses events created earlier; a timed dispatch
+ * still waits a few microseconds longer for its neighbours, so a measurement that must not
+ * disturb the work can set the mask on some forwards only).  epoch_plan_timing synchronises the
  * recorded events, adds their durations (ms) and counts per group into the plan's sums,
  * writes the sums for up to n groups and returns the events to the pool.  Setting the mask
  * clears the sums.  0 = off (the default).
