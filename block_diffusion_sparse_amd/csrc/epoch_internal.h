@@ -32,7 +32,7 @@ constexpr int kChunk = 64;        // positions per compaction chunk (one wave)
 constexpr int kMaxKext = 32;      // candidates per position the wave top-k keeps
 constexpr int kMaxExperts = 1024;
 constexpr int kTileRows = 64;     // rows per grouped-GEMM tile
-constexpr int kBigTile = 128;     // rows per compute-bound tile
+constexpr int kBigTile = 256;     // rows per compute-bound routed tile
 constexpr int kBigRows = 768;     // experts with at least this many fresh rows use big tiles
 constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
 constexpr int kDownCols = 64;     // output columns per down workgroup

@@ -236,19 +236,39 @@ struct LmPartials {
   int n_p;
 };
 
+// Wait until at most N of this wave's vector-memory operations are outstanding and all of its
+// LDS operations have completed (s_waitcnt: vmcnt N, lgkmcnt 0, expcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// One 16-byte copy per lane from global memory into LDS (global_load_lds_dwordx4): lane l's
+// bytes land at lds_dst + 16 l, where lds_dst is the same for the whole wave.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
 // Compute-bound variant for tiles with many rows (the shared expert over all M positions,
-// routed experts with many fresh pairs): a 128-row x 128-weight-row output tile per
-// workgroup, four waves in a 2 x 2 arrangement, each accumulating a 64 x 64 sub-tile with
-// v_mfma_f32_16x16x32_bf16 (4 x 4 blocks).  K runs in chunks of KC = 32: both operands of a
-// chunk are staged through LDS (double-buffered), and chunk loads from global memory run NR - 1
-// steps ahead in a register ring, so that NR - 2 chunks stay in flight while a chunk is
-// multiplied (one chunk is ~256 MFMA cycles per wave, far shorter than a memory round trip).
-// Every global load is issued by every lane with no branch around it (rows past the tile read
-// a valid stand-in, replaced by zeros when stored to LDS).  Gate/up: the 128 staged weight rows
-// are [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g
-// and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of
-// W2.  Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
-template <bool GATEUP, bool ROUTED, bool LMHEAD = false>
+// routed experts with many fresh pairs, the LM head over the live positions): a BR-row x
+// 128-weight-row output tile per workgroup, four waves in a 2 x 2 arrangement, each
+// accumulating a (BR / 2) x 64 sub-tile with v_mfma_f32_16x16x32_bf16 (BR / 32 x 4 blocks).
+// K runs in chunks of KC = 32.  Both operands of a chunk go from global memory straight into
+// LDS (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 x lane),
+// NB chunk buffers deep, NB - 2 chunks in flight while a chunk is multiplied.  LDS rows of
+// KC = 32 bf16 (64 bytes, four 16-byte slots) hold k-segment slot ^ ((row >> 2) & 3) in slot
+// `slot`: a lane fetches the segment its slot must hold, so the 16 rows of an MFMA fragment
+// fall on distinct banks.  Rows past the tile (and weight rows past N) load a stand-in row of
+// the same operand: they only feed outputs that are never stored.
+// Synchronisation is explicit: before each barrier a wave waits for its own copies of the next
+// chunk (vmcnt) and for its LDS reads (lgkmcnt); the fragment reads are inline ds_read_b128,
+// because the compiler, which cannot tell chunk buffers apart, would otherwise wait for every
+// copy in flight before any LDS read.  Gate/up: the 128 staged weight rows are
+// [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g and u of
+// the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of W2.
+// Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
+template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
@@ -257,16 +277,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
   static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
-  constexpr int BR = 128, KC = 32, SEG_ROW = KC / 8;
-  constexpr int NSEG = BR * SEG_ROW / 256;  // 16-byte segments per thread per operand and chunk
-  constexpr int NR = 4;                     // register ring depth (chunks), even
-  constexpr int NB = 3;                     // LDS buffers (chunks)
+  static_assert(BR == 128 || BR == 256, "row tiles of 128 or 256");
+  constexpr int KC = 32, BC = 128;
+  constexpr int MB = BR / 32;                // 16-row blocks per wave
+  constexpr int NB = BR == 256 ? 3 : 4;      // LDS chunk buffers (2 workgroups per CU)
+  constexpr int NA = BR / 64, NBI = BC / 64; // copies per wave and chunk: A rows, B rows
   constexpr int CBW = GATEUP ? 64 : 128;
-  // LDS rows of KC = 32 bf16 (64 bytes, four 16-byte segments), no padding: segment c8 of row
-  // `row` sits at slot c8 ^ ((row >> 2) & 3), so that the 16 rows of an MFMA fragment read and
-  // the four segments of the rows a wave stores both fall on distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BR * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BC * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
   int tile, cb;
   if (LMHEAD) {
@@ -285,26 +303,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
                                 tile_row0, offs, LMHEAD ? *lp.n_live : M);
   if (!tr.active) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
   const size_t estride = (size_t)Ndim * Kdim;
   const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  // staging: NSEG activation and NSEG weight segments of 16 bytes per thread per chunk
-  const uint16_t* asrc[NSEG];
-  const uint16_t* bsrc[NSEG];
-  bool aok[NSEG], bok[NSEG];
-  int dst[NSEG];
+  // copy sources: copy j of wave w fills LDS rows [64 j + 16 w, +16) of a chunk buffer, lane l
+  // slot l % 4 of row 64 j + 16 w + l / 4
+  const uint16_t* asrc[NA];
+  const uint16_t* bsrc[NBI];
 #pragma unroll
-  for (int j = 0; j < NSEG; ++j) {
-    const int seg = tid + 256 * j;
-    const int row = seg / SEG_ROW, c8 = seg % SEG_ROW;
-    dst[j] = row * KC + ((c8 ^ ((row >> 2) & 3)) * 8);
-    const int p = tr.row0 + row;
-    aok[j] = p < tr.row_end;
-    const int src_row =
-        aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p)) : 0;
+  for (int j = 0; j < NA; ++j) {
+    const int row = 64 * j + 16 * wave + (lane >> 2);
+    const int c8 = (lane & 3) ^ ((row >> 2) & 3);
+    const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
+    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p);
     asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NBI; ++j) {
+    const int row = 64 * j + 16 * wave + (lane >> 2);
+    const int c8 = (lane & 3) ^ ((row >> 2) & 3);
     int wrow;
     const uint16_t* base;
     if (GATEUP) {
@@ -315,93 +335,111 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
       wrow = cb * 128 + row;
       base = B0;
     }
-    bok[j] = wrow < Ndim;
-    bsrc[j] = base + e * estride + (size_t)(bok[j] ? wrow : 0) * Kdim + c8 * 8;
+    bsrc[j] = base + e * estride + (size_t)(wrow < Ndim ? wrow : 0) * Kdim + c8 * 8;
   }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 ra[NR][NSEG], rb[NR][NSEG];  // chunk x waits in slot x % NR from its load to its store
-  auto load = [&](int c, int slot) {
+  auto issue = [&](int c, int buf) {
 #pragma unroll
-    for (int j = 0; j < NSEG; ++j) {
-      ra[slot][j] = *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)c * KC);
-      rb[slot][j] = *reinterpret_cast<const u32x4*>(bsrc[j] + (size_t)c * KC);
-    }
+    for (int j = 0; j < NA; ++j)
+      copy16_to_lds(asrc[j] + (size_t)c * KC, &As[buf][(64 * j + 16 * wave) * KC]);
+#pragma unroll
+    for (int j = 0; j < NBI; ++j)
+      copy16_to_lds(bsrc[j] + (size_t)c * KC, &Bs[buf][(64 * j + 16 * wave) * KC]);
   };
-  auto store = [&](int buf, int slot) {
+  f32x4 acc[MB][4];
 #pragma unroll
-    for (int j = 0; j < NSEG; ++j) {
-      *reinterpret_cast<u32x4*>(&As[buf][dst[j]]) = aok[j] ? ra[slot][j] : zero;
-      *reinterpret_cast<u32x4*>(&Bs[buf][dst[j]]) = bok[j] ? rb[slot][j] : zero;
-    }
-  };
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
-  // fragments of one chunk: lane (r, g) reads segment g of rows 16 m + r, whose slot depends
-  // on r only; two register sets, so that chunk c + 1 is read from LDS while c is multiplied
+  // fragments of one chunk: lane (r, g) reads slot g ^ ((r >> 2) & 3) of rows 16 m + r; two
+  // register sets, so that chunk c + 1 is read from LDS while c is multiplied
   const int swz = (g ^ ((r >> 2) & 3)) * 8;
-  bf16x8 fa[2][4], fb[2][4];
+  u32x4 fa[2][MB], fb[2][4];
   auto read_frags = [&](int buf, int set) {
-    const uint16_t* ab = &As[buf][(64 * wm + r) * KC + swz];
-    const uint16_t* bb = &Bs[buf][(64 * wn + r) * KC + swz];
+    const uint32_t ab = (uint32_t)(uintptr_t)&As[buf][(BR / 2 * wm + r) * KC + swz];
+    const uint32_t bb = (uint32_t)(uintptr_t)&Bs[buf][(64 * wn + r) * KC + swz];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      fa[set][m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * KC));
-      fb[set][m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bb + m * 16 * KC));
-    }
+    for (int m = 0; m < MB; ++m)
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[set][m]) : "v"(ab), "i"(m * 16 * KC * 2));
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[set][n]) : "v"(bb), "i"(n * 16 * KC * 2));
+  };
+  // a set's fragments are complete once this wave's LDS reads are: the wait names them as
+  // operands, so no use of them can be scheduled before it (it adds no wait of its own when
+  // the wait before the barrier already covered the reads)
+  auto frags_ready = [&](int set) {
+    if constexpr (MB == 8)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
+                     "+v"(fa[set][4]), "+v"(fa[set][5]), "+v"(fa[set][6]), "+v"(fa[set][7]),
+                     "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
+                     "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]));
   };
   auto mma = [&](int set) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][m], fb[set][n], acc[m][n], 0, 0, 0);
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, fa[set][m]), __builtin_bit_cast(bf16x8, fb[set][n]),
+            acc[m][n], 0, 0, 0);
   };
-  static_assert(KC == 32, "one MFMA k-step per chunk");
-  static_assert(NR % 2 == 0, "fragment sets alternate with the chunk parity");
-  // Chunk x: fetched from global into ring slot x % NR at step x - NR (in the prologue for
-  // x < NR), stored to LDS buffer x % NB at step x - 2, read into fragment set x & 1 at step
-  // x - 1, multiplied at step x.  A buffer is rewritten two barriers after the step that last
-  // read it; a ring slot is refilled after its chunk went to LDS.
-  auto step = [&](int c, int u, bool pre, bool rd, bool st) {
-    if (pre) load(c + NR, u % NR);
-    __builtin_amdgcn_sched_barrier(0);  // keep the fetch ahead of the multiply
-    if (rd) read_frags((c + 1) % NB, (u + 1) & 1);
-    mma(u & 1);
-    if (st) store((c + 2) % NB, (u + 2) % NR);
-    __syncthreads();
-  };
+  constexpr int kInFlight = (NA + NBI) * (NB - 2);  // copies after chunk c + 1's
   const int nch = Kdim / KC;
+  // prologue: chunks 0 .. NB - 2 in flight, chunk 0 landed, its fragments read
 #pragma unroll
-  for (int x = 0; x < NR; ++x)
-    if (x < nch) load(x, x);
-  store(0, 0);
-  if (nch > 1) store(1, 1);
-  __syncthreads();
+  for (int x = 0; x < NB - 1; ++x)
+    if (x < nch) issue(x, x);
+  if (nch >= NB - 1)
+    wait_vm_lds<(NA + NBI) * (NB - 2)>();
+  else
+    wait_vm_lds<0>();
+  __builtin_amdgcn_s_barrier();
   read_frags(0, 0);
-  // steady state: NR steps per trip (kb a multiple of NR, so slot and set follow u), every
-  // fetch, read and store in range
-  int kb = 0;
-  for (; kb + 2 * NR - 1 < nch; kb += NR) {
+  // step c: copy chunk c + NB - 1 into the buffer of chunk c - 1 (every wave read it before
+  // the previous barrier), wait for chunk c + 1, barrier, read its fragments, multiply chunk c
+  int c = 0;
+  for (; c + NB - 1 < nch; c += 2) {
 #pragma unroll
-    for (int u = 0; u < NR; ++u) step(kb + u, u, true, true, true);
+    for (int u = 0; u < 2; ++u) {
+      const int cc = c + u;
+      if (cc + NB - 1 < nch) {
+        issue(cc + NB - 1, (cc + NB - 1) % NB);
+        wait_vm_lds<kInFlight>();
+      } else {
+        wait_vm_lds<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      frags_ready(u & 1);
+      read_frags((cc + 1) % NB, (u + 1) & 1);
+      mma(u & 1);
+    }
   }
+  for (; c < nch; c += 2) {  // the last chunks: nothing more to copy
 #pragma unroll
-  for (int u = 0; u < 2 * NR - 1; ++u) {
-    const int c = kb + u;
-    if (c < nch) step(c, u, c + NR < nch, c + 1 < nch, c + 2 < nch);
+    for (int u = 0; u < 2; ++u) {
+      const int cc = c + u;
+      if (cc < nch) {
+        wait_vm_lds<0>();
+        __builtin_amdgcn_s_barrier();
+        frags_ready(u & 1);
+        if (cc + 1 < nch) read_frags((cc + 1) % NB, (u + 1) & 1);
+        mma(u & 1);
+      }
+    }
   }
   // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
   if (LMHEAD) {
     // per row: the 64 logits of this wave's token block sit in the 16 lanes with the same g,
     // four per lane; reduce (max, lower token on ties) and then sum exp(logit - max)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MB; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = tr.row0 + 64 * wm + 16 * m + 4 * g + q;
+        const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
         const int col0 = cb * 128 + 64 * wn + r;
         float mx = acc[m][0][q];
         int arg = col0;
@@ -436,10 +474,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     return;
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MB; ++m) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = tr.row0 + 64 * wm + 16 * m + 4 * g + q;
+      const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
       if (row >= tr.row_end) continue;
       if (GATEUP) {
 #pragma unroll

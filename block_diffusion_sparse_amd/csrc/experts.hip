@@ -24,6 +24,7 @@ constexpr int kDownWaves = 8;
 // dense (shared-expert) layers of at least this many positions use the compute-bound
 // 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
 constexpr int kBigTileMinRows = 2048;
+constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups per CU remain
 
 // 1-D grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
 static dim3 gemm_grid(int tiles, int Ndim, bool gateup) {
@@ -112,8 +113,8 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
     launch_gemm<true, true>(s.T_max, st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
                             L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
-    if (s.big_routed)  // experts with many fresh rows: compute-bound 128 x 128 tiles
-      launch((k_gemm_big<true, true>),
+    if (s.big_routed)  // experts with many fresh rows: compute-bound kBigTile x 128 tiles
+      launch((k_gemm_big<true, true, false, kBigTile>),
                          dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
                          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
@@ -134,7 +135,7 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
                              static_cast<uint16_t*>(W.y_pair), s.M, s.H);
     if (s.big_routed)
-      launch((k_gemm_big<false, true>),
+      launch((k_gemm_big<false, true, false, kBigTile>),
                          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
                          st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
                          nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
@@ -152,18 +153,34 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
   dim3 g1(s.T_dense, (s.Is + kGateUpCols - 1) / kGateUpCols);
   dim3 g2(s.T_dense, (s.H + kDownCols - 1) / kDownCols);
   if (s.bf16 && s.M >= kBigTileMinRows) {
-    // many rows: compute-bound, 128 x 128 tiles with both operands staged in LDS
-    const int tiles = (s.M + 127) / 128;
-    const dim3 gu(((tiles + 7) / 8) * 8 * (s.Is / 64)), gd(((tiles + 7) / 8) * 8 * ((s.H + 127) / 128));
-    launch((k_gemm_big<true, false>), gu, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(sw1),
-                       static_cast<const uint16_t*>(sw3), W.flags, nullptr, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, static_cast<uint16_t*>(W.hs), s.M, s.H, s.Is,
-                       LmPartials{});
-    launch((k_gemm_big<false, false>), gd, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(W.hs), static_cast<const uint16_t*>(sw2),
-                       nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       static_cast<uint16_t*>(W.S), s.M, s.Is, s.H, LmPartials{});
+    // many rows: compute-bound tiles with both operands copied into LDS; 256-row tiles when
+    // they still give every CU two workgroups, else 128-row tiles
+    const int t128 = (s.M + 127) / 128, t256 = (s.M + 255) / 256;
+    const int ncu = s.Is / 64, ncd = (s.H + 127) / 128;
+    auto grid = [](int tiles, int n_cb) { return dim3(((tiles + 7) / 8) * 8 * n_cb); };
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* hs = static_cast<const uint16_t*>(W.hs);
+    uint16_t* hs_out = static_cast<uint16_t*>(W.hs);
+    uint16_t* S_out = static_cast<uint16_t*>(W.S);
+    const uint16_t* w1b = static_cast<const uint16_t*>(sw1);
+    const uint16_t* w3b = static_cast<const uint16_t*>(sw3);
+    const uint16_t* w2b = static_cast<const uint16_t*>(sw2);
+    if (t256 * ncu >= kBig256MinBlocks)
+      launch((k_gemm_big<true, false, false, 256>), grid(t256, ncu), dim3(256), 0, st, xb, w1b,
+             w3b, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H,
+             s.Is, LmPartials{});
+    else
+      launch((k_gemm_big<true, false>), grid(t128, ncu), dim3(256), 0, st, xb, w1b, w3b, W.flags,
+             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H, s.Is,
+             LmPartials{});
+    if (t256 * ncd >= kBig256MinBlocks)
+      launch((k_gemm_big<false, false, false, 256>), grid(t256, ncd), dim3(256), 0, st, hs, w2b,
+             nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M,
+             s.Is, s.H, LmPartials{});
+    else
+      launch((k_gemm_big<false, false>), grid(t128, ncd), dim3(256), 0, st, hs, w2b, nullptr,
+             W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M, s.Is, s.H,
+             LmPartials{});
   } else if (s.bf16) {
     launch_gemm<true, false>(s.T_dense, st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),
