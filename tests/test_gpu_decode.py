@@ -87,6 +87,21 @@ def test_small_decode_step(shape):
     assert out["commits"] > 0 and (Dn >= D).all()
 
 
+@pytest.mark.parametrize("shape", [(8, 32, 128, 384), (9, 32, 128, 384)],
+                         ids=["b8x32-two-row-tiles-v384", "b9x32-three-row-tiles-v384"])
+def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
+    """256 and 288 positions (two and three 128-row LM-head tiles, the last one ragged) with a
+    vocabulary that is not a multiple of 256."""
+    batch, block, H, V = shape
+    hs, Wb, D = synth.decode_inputs(70 + batch, batch, block, H, V)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
+    assert reported <= int((D == 0).sum()) // 4
+
+
 def test_all_decoded_and_all_live():
     batch, block, H, V = 2, 32, 128, 256
     hs, Wb, _ = synth.decode_inputs(77, batch, block, H, V)
