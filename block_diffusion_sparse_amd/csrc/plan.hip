@@ -156,6 +156,45 @@ struct SupportLds {
   int nU, added, size;
 };
 
+// Entries [j0, min(j0 + kRowGroup, n)) of one position's candidates (ids, and the planner
+// weights when WITH_Q), rows of `stride` entries: all loads of a group issue together (uniform
+// guards; 16-byte loads when the stride allows), one memory round trip per group instead of one
+// per candidate.
+constexpr int kRowGroup = 8;
+struct RowGroup {
+  int32_t id[kRowGroup];
+  int32_t q[kRowGroup];
+};
+
+template <bool WITH_Q>
+__device__ __forceinline__ void load_row_group(const int32_t* __restrict__ ids,
+                                               const int32_t* __restrict__ q, int t, int stride,
+                                               int j0, int n, RowGroup& g) {
+  const int32_t* it = ids + (size_t)t * stride + j0;
+  const int32_t* qt = q + (size_t)t * stride + j0;
+  if ((stride & 3) == 0 && (n & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < kRowGroup / 4; ++v) {
+      if (j0 + 4 * v < n) {
+        const int4 a = *reinterpret_cast<const int4*>(it + 4 * v);
+        g.id[4 * v] = a.x, g.id[4 * v + 1] = a.y, g.id[4 * v + 2] = a.z, g.id[4 * v + 3] = a.w;
+        if (WITH_Q) {
+          const int4 b = *reinterpret_cast<const int4*>(qt + 4 * v);
+          g.q[4 * v] = b.x, g.q[4 * v + 1] = b.y, g.q[4 * v + 2] = b.z, g.q[4 * v + 3] = b.w;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRowGroup; ++j) {
+      if (j0 + j < n) {
+        g.id[j] = it[j];
+        if (WITH_Q) g.q[j] = qt[j];
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
                                               const int32_t* __restrict__ q, const uint8_t* inS,
                                               int M, int K, int Kext, int an, int ad,
@@ -163,12 +202,17 @@ __device__ __forceinline__ void coverage_pass(const int32_t* __restrict__ ids,
                                               int32_t* __restrict__ Rrow, int* nU) {
   int local = 0;
   for (int t = threadIdx.x; t < M; t += kPlanThreads) {
-    const int32_t* it = ids + (size_t)t * Kext;
-    const int32_t* qt = q + (size_t)t * Kext;
     int64_t r = 0, c = 0;
-    for (int j = 0; j < Kext; ++j) {
-      if (j < K) r += qt[j];
-      if (inS[it[j]]) c += qt[j];
+    for (int j0 = 0; j0 < Kext; j0 += kRowGroup) {
+      RowGroup g;
+      load_row_group<true>(ids, q, t, Kext, j0, Kext, g);
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j) {
+        if (j0 + j < Kext) {
+          if (j0 + j < K) r += g.q[j];
+          if (inS[g.id[j]]) c += g.q[j];
+        }
+      }
     }
     Rrow[t] = (int32_t)r;
     Crow[t] = (int32_t)c;
@@ -233,16 +277,34 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
   for (int e = tid; e < E; e += kPlanThreads) sh.p[e] = 0;
   if (tid == 0) sh.nU = 0;
   __syncthreads();
-  for (int i = tid; i < M * Kext; i += kPlanThreads)
-    atomicAdd(&sh.p[ids[i]], (unsigned long long)(long long)q[i]);
+  for (int e = tid; e < E; e += kPlanThreads) sh.H[e] = 0;
+  for (int t = tid; t < M; t += kPlanThreads)
+    for (int j0 = 0; j0 < Kext; j0 += kRowGroup) {
+      RowGroup g;
+      load_row_group<true>(ids, q, t, Kext, j0, Kext, g);
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (j0 + j < Kext) atomicAdd(&sh.p[g.id[j]], (unsigned long long)(long long)g.q[j]);
+    }
   __syncthreads();
-  // initial support: experts with p_e > 0 whose rank by (p desc, id asc) is below B
-  for (int e = tid; e < E; e += kPlanThreads) {
-    const unsigned long long pe = sh.p[e];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (sh.p[f] > pe) || (sh.p[f] == pe && f < e);
-    sh.inS[e] = (pe > 0 && rank < s.B) ? 1 : 0;
+  // initial support: experts with p_e > 0 whose rank by (p desc, id asc) is below B; the
+  // E x E comparisons go to every thread (adjacent threads on adjacent experts, each group of
+  // Epad threads a range of the others), the partial ranks summed in sh.H
+  {
+    int Epad = 1;
+    while (Epad < E) Epad <<= 1;
+    const int groups = kPlanThreads / Epad, e = tid & (Epad - 1), grp = tid / Epad;
+    const int seg = (E + groups - 1) / groups, f0 = min(E, grp * seg), f1 = min(E, f0 + seg);
+    if (e < E) {
+      const unsigned long long pe = sh.p[e];
+      int rank = 0;
+#pragma unroll 8
+      for (int f = f0; f < f1; ++f) rank += (sh.p[f] > pe) || (sh.p[f] == pe && f < e);
+      if (rank) atomicAdd(&sh.H[e], rank);
+    }
   }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) sh.inS[e] = (sh.p[e] > 0 && sh.H[e] < s.B) ? 1 : 0;
   __syncthreads();
   coverage_pass(ids, q, sh.inS, M, K, Kext, s.an, s.ad, W.Crow, W.Rrow, &sh.nU);
   __syncthreads();
@@ -259,14 +321,18 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
       const long long R = W.Rrow[t], C = W.Crow[t];
       if (!(ad * C < an * R)) continue;
       const long long gap = an * R - ad * C;
-      const int32_t* it = ids + (size_t)t * Kext;
-      const int32_t* qt = q + (size_t)t * Kext;
-      for (int j = 0; j < Kext; ++j) {
-        const int e = it[j];
-        if (sh.inS[e]) continue;
-        const long long v = ad * qt[j];
-        atomicAdd(&sh.G[e], (unsigned long long)(v < gap ? v : gap));
-        if (ad * (C + qt[j]) >= an * R) atomicAdd(&sh.H[e], 1);
+      for (int j0 = 0; j0 < Kext; j0 += kRowGroup) {
+        RowGroup g;
+        load_row_group<true>(ids, q, t, Kext, j0, Kext, g);
+#pragma unroll
+        for (int j = 0; j < kRowGroup; ++j) {
+          if (j0 + j >= Kext) continue;
+          const int e = g.id[j];
+          if (sh.inS[e]) continue;
+          const long long v = ad * g.q[j];
+          atomicAdd(&sh.G[e], (unsigned long long)(v < gap ? v : gap));
+          if (ad * (C + g.q[j]) >= an * R) atomicAdd(&sh.H[e], 1);
+        }
       }
     }
     __syncthreads();
@@ -312,10 +378,14 @@ __device__ int support_phase(const Shape& s, int iter, const LayerState& L, cons
     }
   }
   // (iii) closure: every routed expert of the current iteration gets a slot
-  for (int i = tid; i < M * K; i += kPlanThreads) {
-    const int t = i / K, k = i - t * K;
-    sh.inS[ids[(size_t)t * Kext + k]] = 1;
-  }
+  for (int t = tid; t < M; t += kPlanThreads)
+    for (int j0 = 0; j0 < K; j0 += kRowGroup) {
+      RowGroup g;
+      load_row_group<false>(ids, q, t, Kext, j0, K, g);
+#pragma unroll
+      for (int j = 0; j < kRowGroup; ++j)
+        if (j0 + j < K) sh.inS[g.id[j]] = 1;
+    }
   __syncthreads();
   }
   // (iv) slots in expert-id order (E <= kMaxExperts == kPlanThreads: one expert per thread)
