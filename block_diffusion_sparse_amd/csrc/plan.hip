@@ -60,13 +60,17 @@ constexpr int kPlanThreads = 1024;
 
 constexpr int kPlanWaves = kPlanThreads / 64;
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS traffic): shifts
+// by 1, 2, 4, 8 inside each row of 16 lanes, then each row's total carried into the rows
+// after it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).  Lanes whose
+// source falls outside the row, or whose row the mask leaves out, add 0.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
