@@ -98,6 +98,12 @@ Shape make_shape(const epoch_desc* d) {
   s.ksplit = 1;
   while (s.ksplit < max_split && tiles * s.ksplit < 2048 && s.H % (128 * s.ksplit) == 0)
     s.ksplit *= 2;
+  // few logit tiles: part of that split goes to workgroups instead of waves (router_kw of them
+  // per tile, their fp64 partial sums added in order by the top-k kernel) so that about 256
+  // workgroups share the fp64 MFMA work
+  s.router_kw = 1;
+  while (s.router_kw < s.ksplit && tiles * s.router_kw < 256) s.router_kw *= 2;
+  s.ksplit /= s.router_kw;  // waves per workgroup
   const long long P_max = (long long)s.M * s.K;
   s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;
   s.T_dense = (s.M + kTileRows - 1) / kTileRows;
@@ -150,6 +156,7 @@ Layout carve(const epoch_desc* d, const Shape& s, void* base) {
   const size_t P_max = M * K;
   Scratch& W = lay.scratch;
   W.G = c.take<float>(M * E);
+  W.Gp = c.take<double>(s.router_kw > 1 ? (size_t)s.router_kw * M * E : 1);
   W.ids = c.take<int32_t>(M * Kext);
   W.scores = c.take<float>(M * Kext);
   W.q = c.take<int32_t>(M * Kext);

@@ -76,6 +76,7 @@ struct LayerState {
 // Device-side view of the per-forward scratch.
 struct Scratch {
   float* G;             // [M x E]
+  double* Gp;           // [router_kw x M x E] per-workgroup partial logits (router_kw > 1)
   int32_t* ids;         // [M x Kext]
   float* scores;        // [M x Kext]
   int32_t* q;           // [M x Kext]
@@ -115,7 +116,7 @@ struct Scratch {
 
 struct Shape {
   int M, H, E, K, Kext, I, Is, n_shared, R, gate_sigmoid, norm_topk, bf16;
-  int n_chunks, ksplit, router_bt, T_max, T_dense, T_big_max, big_routed;
+  int n_chunks, ksplit, router_bt, router_kw, T_max, T_dense, T_big_max, big_routed;
   int restricted, atlas_period, n_group, topk_group;  // n_group <= 1: no grouping
   int B, c, an, ad, qn, qd, bn, bd;
 };

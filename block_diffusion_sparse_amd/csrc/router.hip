@@ -71,6 +71,11 @@ struct RouteArgs {
   int E, K, Kext, gate_sigmoid, norm_topk, R, iter;
   int restricted, an, ad;  // support-restricted routing; coverage floor alpha = an / ad
   int n_group, topk_group;  // group-limited top-k (n_group = 0: off)
+  // logits split over kw workgroups (kw > 1): the fp64 partials [kw][M][E], summed here in
+  // order, plus the bias, then one rounding to fp32 (also stored to G)
+  const double* Gp;
+  const float* bias;
+  int kw, M;
 };
 
 // LDS of one wave's top-k: candidate scores (K_ext), in-support scores (K), group maxima and
@@ -103,7 +108,16 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
     const int e = lane + 64 * j;
-    gv[j] = e < E ? G[(size_t)t * E + e] : -INFINITY;
+    if (ra.kw > 1) {
+      double sum = 0.0;
+      for (int z = 0; z < ra.kw; ++z)
+        sum += e < E ? ra.Gp[((size_t)z * ra.M + t) * E + e] : 0.0;
+      if (ra.bias && e < E) sum += (double)ra.bias[e];
+      gv[j] = e < E ? (float)sum : -INFINITY;
+      if (e < E) W.G[(size_t)t * E + e] = gv[j];
+    } else {
+      gv[j] = e < E ? G[(size_t)t * E + e] : -INFINITY;
+    }
     in_s[j] = e < E ? L.inS[e] : 0;
     in_a[j] = (r_on && e < E) ? L.inA[e] : 0;
   }
@@ -303,12 +317,13 @@ __global__ __launch_bounds__(256) void k_route_rows(const float* __restrict__ G,
 template <typename T, int BT>
 __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
     const T* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bias,
-    float* __restrict__ G, int M, int H, int E, int ksplit) {
+    float* __restrict__ G, double* __restrict__ Gp, int M, int H, int E, int ksplit, int kw) {
   constexpr int NB = BT / 16;
   extern __shared__ double red[];  // [ksplit][BT * BT]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e0 = blockIdx.x * BT, t0 = blockIdx.y * BT;
-  const int klen = H / ksplit, kbeg = wave * klen;
+  // workgroup blockIdx.z of kw sums its k range; its waves split it further
+  const int klen = H / (ksplit * kw), kbeg = (blockIdx.z * ksplit + wave) * klen;
   const int nsteps = klen / 64;
   const int r = lane & 15, g = lane >> 4;
   const T* xr[NB];
@@ -374,8 +389,12 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
     if (t >= M || e >= E) continue;
     double s = 0.0;
     for (int w = 0; w < ksplit; ++w) s += red[(size_t)w * BT * BT + idx];
-    if (bias) s += (double)bias[e];
-    G[(size_t)t * E + e] = (float)s;
+    if (kw > 1) {
+      Gp[((size_t)blockIdx.z * M + t) * E + e] = s;  // the top-k kernel adds the parts and bias
+    } else {
+      if (bias) s += (double)bias[e];
+      G[(size_t)t * E + e] = (float)s;
+    }
   }
 }
 
@@ -383,9 +402,9 @@ template <typename T, int BT>
 static void launch_k_router(const Shape& s, const void* x, const float* Wg, const float* bias,
                             const Scratch& W, hipStream_t st) {
   const size_t lds = (size_t)s.ksplit * BT * BT * sizeof(double);
-  const dim3 grid((s.E + BT - 1) / BT, (s.M + BT - 1) / BT), block(64 * s.ksplit);
+  const dim3 grid((s.E + BT - 1) / BT, (s.M + BT - 1) / BT, s.router_kw), block(64 * s.ksplit);
   launch((k_router<T, BT>), grid, block, lds, st, static_cast<const T*>(x), Wg, bias,
-                     W.G, s.M, s.H, s.E, s.ksplit);
+                     W.G, W.Gp, s.M, s.H, s.E, s.ksplit, s.router_kw);
 }
 
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
@@ -406,7 +425,8 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
       launch_k_router<float, 16>(s, x, Wg, bias, W, st);
   }
   const RouteArgs ra{L,         W,   D,    force,        s.E,  s.K,  s.Kext,    s.gate_sigmoid,
-                     s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group};
+                     s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group,
+                     W.Gp,        bias, s.router_kw, s.M};
   const int nper = (s.E + 63) / 64;
 #define EPOCH_ROUTE_ROWS(NP) \
   launch(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
