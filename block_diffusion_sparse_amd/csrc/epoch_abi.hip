@@ -102,7 +102,8 @@ Shape make_shape(const epoch_desc* d) {
   // per tile, their fp64 partial sums added in order by the top-k kernel) so that about 256
   // workgroups share the fp64 MFMA work
   s.router_kw = 1;
-  while (s.router_kw < s.ksplit && tiles * s.router_kw < 256) s.router_kw *= 2;
+  while (s.E <= 64 && s.router_kw < 4 && s.router_kw < s.ksplit && tiles * s.router_kw < 256)
+    s.router_kw *= 2;  // (the top-k kernel holds up to 4 parts per lane, one expert per lane)
   s.ksplit /= s.router_kw;  // waves per workgroup
   const long long P_max = (long long)s.M * s.K;
   s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;

@@ -71,12 +71,15 @@ struct RouteArgs {
   int E, K, Kext, gate_sigmoid, norm_topk, R, iter;
   int restricted, an, ad;  // support-restricted routing; coverage floor alpha = an / ad
   int n_group, topk_group;  // group-limited top-k (n_group = 0: off)
-  // logits split over kw workgroups (kw > 1): the fp64 partials [kw][M][E], summed here in
-  // order, plus the bias, then one rounding to fp32 (also stored to G)
+  // logits split over kw workgroups (kw > 1): the fp64 partials [kw][M][E] (the first with
+  // the bias added), summed here in order, then one rounding to fp32 (also stored to G)
   const double* Gp;
-  const float* bias;
   int kw, M;
 };
+
+// The router's k split over workgroups (partial logits summed by the top-k) is used only with
+// at most 64 experts (one per lane) and at most this many parts.
+constexpr int kRouterMaxKw = 4;
 
 // LDS of one wave's top-k: candidate scores (K_ext), in-support scores (K), group maxima and
 // kept-group flags, in doubles
@@ -102,31 +105,45 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   // restricted mode with a support in place: also route inside the support (the plan step
   // decides which routing the forward uses)
   const bool r_on = ra.restricted && L.A_state[0] != 0;
-  // prologue: every global read of the position at once
+  // prologue: every global read of the position at once.  No load sits under a lane mask
+  // (lanes past E read expert E - 1 and drop it afterwards): a masked load makes the compiler
+  // wait for it before the next one is issued.
+  // workgroups per logit (router k split): up to 4, and only with one expert per lane
+  constexpr int kMaxKw = NPER == 1 ? kRouterMaxKw : 1;
   float gv[NPER];
   uint8_t in_s[NPER], in_a[NPER];
+  double part[NPER][kMaxKw];
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
-    const int e = lane + 64 * j;
-    if (ra.kw > 1) {
-      double sum = 0.0;
-      for (int z = 0; z < ra.kw; ++z)
-        sum += e < E ? ra.Gp[((size_t)z * ra.M + t) * E + e] : 0.0;
-      if (ra.bias && e < E) sum += (double)ra.bias[e];
-      gv[j] = e < E ? (float)sum : -INFINITY;
-      if (e < E) W.G[(size_t)t * E + e] = gv[j];
-    } else {
-      gv[j] = e < E ? G[(size_t)t * E + e] : -INFINITY;
-    }
-    in_s[j] = e < E ? L.inS[e] : 0;
-    in_a[j] = (r_on && e < E) ? L.inA[e] : 0;
+    const int e = lane + 64 * j, ec = e < E ? e : E - 1;
+    gv[j] = G[(size_t)t * E + ec];  // not yet written when kw > 1 (replaced below)
+#pragma unroll
+    for (int z = 0; z < kMaxKw; ++z)  // (a one-element buffer when kw = 1)
+      part[j][z] = ra.Gp[z < ra.kw && ra.kw > 1 ? ((size_t)z * ra.M + t) * E + ec : 0];
+    in_s[j] = L.inS[ec];
+    in_a[j] = L.inA[ec];
   }
   const uint8_t d = D[t], pd = L.prev_D[t];
   const bool valid = L.valid[t] != 0;
   const int32_t last = L.last_fresh[t];
   const bool forced = force ? force[t] != 0 : false;
   const bool s_valid = *L.S_valid != 0;
-
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int e = lane + 64 * j;
+    if (ra.kw > 1) {
+      // the parts in workgroup order (the first one carries the bias), then one rounding
+      double sum = 0.0;
+#pragma unroll
+      for (int z = 0; z < kMaxKw; ++z)
+        if (z < ra.kw) sum += part[j][z];
+      gv[j] = (float)sum;
+      if (e < E) W.G[(size_t)t * E + e] = gv[j];
+    }
+    if (e >= E) gv[j] = -INFINITY;
+    in_s[j] = e < E ? in_s[j] : 0;
+    in_a[j] = (r_on && e < E) ? in_a[j] : 0;
+  }
   uint64_t key[NPER];
 #pragma unroll
   for (int j = 0; j < NPER; ++j) key[j] = (lane + 64 * j < E) ? sel_key(gv[j], lane + 64 * j) : 0ull;
@@ -390,7 +407,8 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
     double s = 0.0;
     for (int w = 0; w < ksplit; ++w) s += red[(size_t)w * BT * BT + idx];
     if (kw > 1) {
-      Gp[((size_t)blockIdx.z * M + t) * E + e] = s;  // the top-k kernel adds the parts and bias
+      if (bias && blockIdx.z == 0) s += (double)bias[e];
+      Gp[((size_t)blockIdx.z * M + t) * E + e] = s;  // the top-k kernel adds the parts
     } else {
       if (bias) s += (double)bias[e];
       G[(size_t)t * E + e] = (float)s;
@@ -426,7 +444,7 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
   }
   const RouteArgs ra{L,         W,   D,    force,        s.E,  s.K,  s.Kext,    s.gate_sigmoid,
                      s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group,
-                     W.Gp,        bias, s.router_kw, s.M};
+                     W.Gp,        s.router_kw, s.M};
   const int nper = (s.E + 63) / 64;
 #define EPOCH_ROUTE_ROWS(NP) \
   launch(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
