@@ -92,9 +92,13 @@ __device__ __forceinline__ uint64_t sel_key(float g, int e) {
   return ((uint64_t)u << 10) | (uint64_t)(1023 - e);
 }
 
+// lc: the workgroup's LDS counters of the position's chunk ([E] routed pairs of all positions,
+// [E] of fresh positions, the same two for the in-support routing, then the fresh positions and
+// the under-covered positions), flushed to global memory by the caller: a position updates
+// them with LDS atomics only.
 template <int NPER>
 __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, const RouteArgs& ra,
-                                          double* s_buf) {
+                                          double* s_buf, int32_t* lc) {
   const LayerState& L = ra.L;
   const Scratch& W = ra.W;
   const uint8_t* __restrict__ D = ra.D;
@@ -236,7 +240,6 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   // the fresh test before the anomaly override
   const bool due = (long long)iter - (long long)last >= (long long)R;
   const bool fresh = forced || !valid || !(d && pd) || due;
-  const size_t chunk = (size_t)(t / kChunk);
   bool miss = false;
   int q_routed = 0, q_in_a = 0;  // R_t and C_t(A) of the Atlas coverage test, this lane's part
 #pragma unroll
@@ -254,15 +257,15 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
     if (rk < K) {
       q_routed += qv;
       miss |= s_valid && !in_s[j];
-      atomicAdd(&W.cnt_a[chunk * E + e], 1);
-      if (fresh) atomicAdd(&W.cnt_f[chunk * E + e], 1);
+      atomicAdd(&lc[e], 1);
+      if (fresh) atomicAdd(&lc[E + e], 1);
     }
   }
   if (r_on) {
     // coverage of this position by the support: under-covered when alpha_den C < alpha_num R
     const int Rt = wave_sum(q_routed), Ct = wave_sum(q_in_a);
     if (lane == 0 && (long long)ra.ad * Ct < (long long)ra.an * Rt)
-      atomicAdd(&W.flags[FLAG_UNDER], 1);
+      atomicAdd(&lc[4 * E + 1], 1);
     // top-K inside the support (scores keep their definition over all E)
     uint64_t kr[NPER];
 #pragma unroll
@@ -284,8 +287,8 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
       const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)gv[j])) : exp((double)gv[j] - zmax) / z;
       W.rids[(size_t)t * K + rk] = e;
       r_buf[rk] = sc;
-      atomicAdd(&W.cnt_ar[chunk * E + e], 1);
-      if (fresh) atomicAdd(&W.cnt_fr[chunk * E + e], 1);
+      atomicAdd(&lc[2 * E + e], 1);
+      if (fresh) atomicAdd(&lc[3 * E + e], 1);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -317,18 +320,45 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
     // bit 0: fresh before the anomaly override; bits 1, 2: forced, refresh due (counted per
     // chunk by the placement: one atomic per chunk rather than per position on one address)
     W.fpre[t] = (fresh ? 1 : 0) | (forced ? 2 : 0) | ((due && valid) ? 4 : 0);
-    if (fresh) atomicAdd(&W.chunk_fresh[chunk], 1);
+    if (fresh) atomicAdd(&lc[4 * E], 1);
   }
 }
 
-// The top-k as its own kernel: one wave per position.
-template <int NPER>
-__global__ __launch_bounds__(256) void k_route_rows(const float* __restrict__ G, RouteArgs ra,
-                                                    int M) {
-  __shared__ double s_buf[4][kRouteLds];
+// The top-k as its own kernel: one wave per position, WAVES positions per workgroup, all of
+// one chunk (kChunk is a multiple of WAVES).  The per-chunk pair counts and the fresh /
+// under-covered counts are summed in LDS and added to global memory once per workgroup: with
+// popular experts, one global atomic per position and expert piles up dozens of same-address
+// atomics per chunk in the L2.  Many positions take 16-wave workgroups (16 times fewer global
+// atomics); few take 4-wave ones (more workgroups to spread over the CUs).
+constexpr int kRouteRowsBigM = 4096;
+
+template <int NPER, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_route_rows(const float* __restrict__ G,
+                                                           RouteArgs ra, int M) {
+  constexpr int kWaves = WAVES;
+  static_assert(kChunk % kWaves == 0, "a workgroup's positions lie in one chunk");
+  __shared__ double s_buf[kWaves][kRouteLds];
+  __shared__ int32_t lc[4 * kMaxExperts + 2];
+  const int E = ra.E;
+  for (int i = threadIdx.x; i < 4 * E + 2; i += blockDim.x) lc[i] = 0;
+  __syncthreads();
   const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t < M) route_row<NPER>(t, G, ra, s_buf[wave]);
+  const int t = blockIdx.x * kWaves + wave;
+  if (t < M) route_row<NPER>(t, G, ra, s_buf[wave], lc);
+  __syncthreads();
+  const Scratch& W = ra.W;
+  const size_t chunk = (size_t)blockIdx.x * kWaves / kChunk;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const size_t i = chunk * E + e;
+    if (lc[e]) atomicAdd(&W.cnt_a[i], lc[e]);
+    if (lc[E + e]) atomicAdd(&W.cnt_f[i], lc[E + e]);
+    if (lc[2 * E + e]) atomicAdd(&W.cnt_ar[i], lc[2 * E + e]);
+    if (lc[3 * E + e]) atomicAdd(&W.cnt_fr[i], lc[3 * E + e]);
+  }
+  if (threadIdx.x == 0) {
+    if (lc[4 * E]) atomicAdd(&W.chunk_fresh[chunk], lc[4 * E]);
+    if (lc[4 * E + 1]) atomicAdd(&W.flags[FLAG_UNDER], lc[4 * E + 1]);
+  }
 }
 
 template <typename T, int BT>
@@ -425,6 +455,18 @@ static void launch_k_router(const Shape& s, const void* x, const float* Wg, cons
                      W.G, W.Gp, s.M, s.H, s.E, s.ksplit, s.router_kw);
 }
 
+template <int NP>
+static void launch_route_rows(const Shape& s, const Scratch& W, const RouteArgs& ra,
+                              hipStream_t st) {
+  if constexpr (NP <= 8) {
+    if (s.M >= kRouteRowsBigM) {
+      launch(k_route_rows<NP, 16>, dim3((s.M + 15) / 16), dim3(1024), 0, st, W.G, ra, s.M);
+      return;
+    }
+  }
+  launch(k_route_rows<NP, 4>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M);
+}
+
 hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const float* bias,
                          const uint8_t* D, const uint8_t* force, int iter, const LayerState& L,
                          const Scratch& W, hipStream_t st) {
@@ -446,19 +488,16 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
                      s.norm_topk, s.R, iter, s.restricted, s.an, s.ad, s.n_group, s.topk_group,
                      W.Gp,        s.router_kw, s.M};
   const int nper = (s.E + 63) / 64;
-#define EPOCH_ROUTE_ROWS(NP) \
-  launch(k_route_rows<NP>, dim3((s.M + 3) / 4), dim3(256), 0, st, W.G, ra, s.M)
   if (nper <= 1)
-    EPOCH_ROUTE_ROWS(1);
+    launch_route_rows<1>(s, W, ra, st);
   else if (nper <= 2)
-    EPOCH_ROUTE_ROWS(2);
+    launch_route_rows<2>(s, W, ra, st);
   else if (nper <= 4)
-    EPOCH_ROUTE_ROWS(4);
+    launch_route_rows<4>(s, W, ra, st);
   else if (nper <= 8)
-    EPOCH_ROUTE_ROWS(8);
+    launch_route_rows<8>(s, W, ra, st);
   else
-    EPOCH_ROUTE_ROWS(16);
-#undef EPOCH_ROUTE_ROWS
+    launch_route_rows<16>(s, W, ra, st);
   return hipGetLastError();
 }
 
