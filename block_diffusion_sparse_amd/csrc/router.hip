@@ -223,8 +223,10 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   } else {
     select(key, Kext, selm, rank);
   }
-  // softmax normaliser over all E (max = the best key's logit)
+  // softmax normaliser over all E (max = the best key's logit); the exponentials are kept for
+  // the scores of the candidates
   double zmax = 0.0, z = 0.0;
+  double ex[NPER];
   if (!gate_sigmoid) {
     double m = -INFINITY;
 #pragma unroll
@@ -233,30 +235,45 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
     zmax = wave_max(m);
     double part = 0.0;
 #pragma unroll
-    for (int j = 0; j < NPER; ++j)
-      if (lane + 64 * j < E) part += exp((double)gv[j] - zmax);
+    for (int j = 0; j < NPER; ++j) {
+      ex[j] = exp((double)gv[j] - zmax);
+      if (lane + 64 * j < E) part += ex[j];
+    }
     z = wave_sum(part);
   }
   // the fresh test before the anomaly override
   const bool due = (long long)iter - (long long)last >= (long long)R;
   const bool fresh = forced || !valid || !(d && pd) || due;
-  bool miss = false;
-  int q_routed = 0, q_in_a = 0;  // R_t and C_t(A) of the Atlas coverage test, this lane's part
+  // the candidates in rank order, candidate r on lane r (through the group-maxima LDS, free
+  // after the selection): the scores, planner weights, stores and counts then take one pass
+  // over K_ext lanes instead of one per expert slot of a lane
+  double* cval = s_buf + 2 * kMaxKext;                                      // [K_ext]
+  int32_t* cmeta = reinterpret_cast<int32_t*>(s_buf + 2 * kMaxKext + kMaxKext);  // [K_ext]
 #pragma unroll
   for (int j = 0; j < NPER; ++j) {
-    const int e = lane + 64 * j;
     if (!((selm[j] >> lane) & 1ull)) continue;
     const int rk = rank[j];
-    const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-(double)gv[j])) : exp((double)gv[j] - zmax) / z;
+    cval[rk] = gate_sigmoid ? (double)gv[j] : ex[j];
+    cmeta[rk] = (lane + 64 * j) | (in_s[j] ? 1 << 16 : 0) | (in_a[j] ? 1 << 17 : 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bool miss = false;
+  int q_routed = 0, q_in_a = 0;  // R_t and C_t(A) of the Atlas coverage test, this lane's part
+  if (lane < Kext) {
+    const double v = cval[lane];
+    const int meta = cmeta[lane], e = meta & 0xffff;
+    const double sc = gate_sigmoid ? 1.0 / (1.0 + exp(-v)) : v / z;
     const int32_t qv = (int32_t)floor(sc * 65536.0 + 0.5);
-    W.ids[(size_t)t * Kext + rk] = e;
-    W.scores[(size_t)t * Kext + rk] = (float)sc;
-    W.q[(size_t)t * Kext + rk] = qv;
-    s_buf[rk] = sc;
-    if (in_a[j]) q_in_a += qv;
-    if (rk < K) {
+    W.ids[(size_t)t * Kext + lane] = e;
+    W.scores[(size_t)t * Kext + lane] = (float)sc;
+    W.q[(size_t)t * Kext + lane] = qv;
+    s_buf[lane] = sc;
+    if (meta & (1 << 17)) q_in_a += qv;
+    if (lane < K) {
       q_routed += qv;
-      miss |= s_valid && !in_s[j];
+      miss |= s_valid && !(meta & (1 << 16));
       atomicAdd(&lc[e], 1);
       if (fresh) atomicAdd(&lc[E + e], 1);
     }
