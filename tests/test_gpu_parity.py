@@ -41,15 +41,21 @@ def test_tiny_fp32_full_block():
     assert rep.max_err_y <= 1e-5
 
 
-@pytest.mark.parametrize("variant", ["softmax-unnorm", "sigmoid-norm-shared"])
+@pytest.mark.parametrize("variant", ["softmax-unnorm", "sigmoid-norm-shared", "softmax-bias-ksplit"])
 def test_small_bf16_ragged(variant):
-    """Ragged in positions (M = 63 / 65), experts (E = 20 / 40: partial 32-expert router
-    tiles), pairs per expert (partial 32-row GEMM tiles), with several k tiles."""
+    """Ragged in positions (M = 63 / 65), experts (E = 20 / 40 / 48: partial router tiles),
+    pairs per expert (partial GEMM tiles), with several k tiles.  softmax-bias-ksplit: the
+    router's contraction split over 4 workgroups (fp64 partials added by the top-k, the bias
+    carried by the first) with a router bias."""
     h = H()
     if variant == "softmax-unnorm":
         w = synth.workload(2, hidden=256, n_experts=20, top_k=4, inter=128, batch=3, block=21,
                            iters=8, staleness_R=3)
         bias = None
+    elif variant == "softmax-bias-ksplit":
+        w = synth.workload(2, hidden=512, n_experts=48, top_k=4, inter=128, batch=3, block=21,
+                           iters=6, staleness_R=2)
+        bias = (np.random.default_rng(78).standard_normal(w.n_experts) * 0.3).astype(np.float32)
     else:
         w = synth.workload(3, hidden=192, n_experts=40, top_k=6, inter=192, shared_inter=128,
                            batch=5, block=13, iters=8, staleness_R=2, n_layers=1, zipf=None)
@@ -64,6 +70,16 @@ def test_workload2_full_size():
     w = synth.workload(2)
     h.log(f"[full] {w.name}")
     rep = h.run_block(w, rows=sample_rows(w.M, 24, 2))
+    assert rep.iters == w.iters and rep.stable_rows_checked > 0
+
+
+def test_many_positions_one_expert_per_lane():
+    """4096 positions of the single-layer expert shape: the top-k's 16-wave workgroups with one
+    expert per lane (per-chunk counts summed in LDS over 16 positions), one k part."""
+    h = H()
+    w = synth.workload(2, batch=128, block=32, iters=4)
+    h.log(f"[many positions] M={w.M} E={w.n_experts}")
+    rep = h.run_block(w, rows=sample_rows(w.M, 24, 5))
     assert rep.iters == w.iters and rep.stable_rows_checked > 0
 
 
