@@ -378,14 +378,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
                    : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
                      "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]));
   };
+  // Expert tiles multiply with the operands swapped (weights as the 16 x 32 left operand), so
+  // that a block holds its outputs transposed: lane (r, g) gets four consecutive columns
+  // 4 g .. 4 g + 3 of row r, one 8-byte store.  The LM head keeps rows x tokens, whose
+  // epilogue reduces along a row across lanes.
   auto mma = [&](int set) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, fa[set][m]), __builtin_bit_cast(bf16x8, fb[set][n]),
-            acc[m][n], 0, 0, 0);
+        acc[m][n] = LMHEAD ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                 __builtin_bit_cast(bf16x8, fa[set][m]),
+                                 __builtin_bit_cast(bf16x8, fb[set][n]), acc[m][n], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                 __builtin_bit_cast(bf16x8, fb[set][n]),
+                                 __builtin_bit_cast(bf16x8, fa[set][m]), acc[m][n], 0, 0, 0);
   };
   constexpr int kInFlight = (NA + NBI) * (NB - 2);  // copies after chunk c + 1's
   const int nch = Kdim / KC;
@@ -473,26 +480,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     }
     return;
   }
+  // transposed blocks: lane (r, g) holds row 16 m + r, columns 16 n + 4 g .. + 3
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
+    const int row = tr.row0 + BR / 2 * wm + 16 * m + r;
+    if (row >= tr.row_end) continue;
+    if (GATEUP) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
-      if (row >= tr.row_end) continue;
-      if (GATEUP) {
+      for (int n = 0; n < 2; ++n) {
+        const int col = cb * 64 + 32 * wn + 16 * n + 4 * g;
+        if (col >= Ndim) continue;
+        uint16_t hv[4];
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const int col = cb * 64 + 32 * wn + 16 * n + r;
-          const float gv = acc[m][n][q], uv = acc[m][n + 2][q];
-          if (col < Ndim) out[(size_t)row * Ndim + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+        for (int i = 0; i < 4; ++i) {
+          const float gv = acc[m][n][i], uv = acc[m][n + 2][i];
+          hv[i] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
         }
-      } else {
-        const float sc = ROUTED ? wl_w[row] : 1.0f;
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
+            make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+      }
+    } else {
+      const float sc = ROUTED ? wl_w[row] : 1.0f;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = cb * 128 + 64 * wn + 16 * n + r;
-          if (col < Ndim) out[(size_t)row * Ndim + col] = f32_to_bf16(sc * acc[m][n][q]);
-        }
+      for (int n = 0; n < 4; ++n) {
+        const int col = cb * 128 + 64 * wn + 16 * n + 4 * g;
+        if (col >= Ndim) continue;
+        uint16_t yv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yv[i] = f32_to_bf16(sc * acc[m][n][i]);
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
+            make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
       }
     }
   }
