@@ -165,8 +165,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_gemm(
       for (int m = 0; m < MB; ++m) {
         const bf16x8 f =
             __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * LDA + 32 * s));
-        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, x0[s], c0[m], 0, 0, 0);
-        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, x1[s], c1[m], 0, 0, 0);
+        // weights as the left operand: the block is held transposed, lane (r, g) with four
+        // consecutive columns 4 g .. 4 g + 3 of row r (one 8-byte store in the epilogue)
+        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0[s], f, c0[m], 0, 0, 0);
+        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1[s], f, c1[m], 0, 0, 0);
       }
     }
   };
@@ -200,21 +202,29 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_gemm(
   }
 
   if (!wact) return;
-  // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
+  // transposed blocks: lane (r, g) holds row 16 m + r, columns col0 + 4 g .. + 3 (c0) and
+  // col0 + 16 + 4 g .. + 3 (c1, down)
+  auto pack4 = [](const float* v) {
+    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+  };
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
+    const int row = tr.row0 + 16 * m + r;
+    if (row >= tr.row_end) continue;
+    float v[4];
+    if (GATEUP) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = tr.row0 + 16 * m + 4 * g + q;
-      if (row >= tr.row_end) continue;
-      const float v0 = c0[m][q], v1 = c1[m][q];
-      if (GATEUP) {
-        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(v0 / (1.0f + expf(-v0)) * v1);
-      } else {
-        const float sc = ROUTED ? wl_w[row] : 1.0f;
-        out[(size_t)row * Ndim + col0 + r] = f32_to_bf16(sc * v0);
-        out[(size_t)row * Ndim + col0 + 16 + r] = f32_to_bf16(sc * v1);
-      }
+      for (int i = 0; i < 4; ++i) v[i] = c0[m][i] / (1.0f + expf(-c0[m][i])) * c1[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
+    } else {
+      const float sc = ROUTED ? wl_w[row] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sc * c0[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sc * c1[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 16 + 4 * g) = pack4(v);
     }
   }
 }
