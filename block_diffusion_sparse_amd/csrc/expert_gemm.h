@@ -5,11 +5,6 @@
 
 namespace epoch {
 
-// A 16-byte fragment: 8 consecutive bf16 of one row.
-__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
 // Row source of a tile: routed tiles gather activations through the worklist; dense (shared
 // expert) tiles take positions in order.
 struct TileRows {
@@ -36,202 +31,6 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
   }
   return r;
 }
-
-// One kernel for both projections of the SwiGLU expert.
-// Workgroup = 4 waves over one tile (up to BM rows of one expert) and 4 x 32 weight rows:
-//   gate/up: wave w owns intermediate columns [16w, 16w + 16) of a 64-column block and reads
-//            those rows of W1 and of W3 (32 weight rows); epilogue h = bf16(silu(g) * u);
-//   down:    wave w owns output columns [32w, 32w + 32) of a 128-column block of W2;
-//            epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
-// The contraction runs in chunks of KC.  The tile's activation rows (gathered through the
-// worklist for routed gate/up) are staged per chunk in LDS (double-buffered) and shared by
-// the four waves; every wave streams its weight rows straight into a ring of NST register
-// stages, so NST - 1 chunks of weights are in flight while a chunk's MFMAs run.  Lane l
-// feeds A row (l % 16) and B row (l % 16) with the same 8 consecutive k values (k-group
-// l / 16), so every product pairs an activation with the weight of the same k.
-//
-// Grid: one-dimensional, n_col_blocks * (tile slots rounded up to a multiple of 8).  The
-// hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
-// (L / 8) % NB of tile 8 * ((L / 8) / NB) + L % 8, so every column block of a tile lands on
-// the same XCD and the tile's activation rows are fetched into one L2 only.
-template <int BM, int KC, int NST, bool GATEUP, bool ROUTED, int WAVES = 4>
-__global__ __launch_bounds__(64 * WAVES) void k_expert_gemm(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
-    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
-    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
-    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
-  constexpr int NTH = 64 * WAVES;
-  constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // columns per workgroup
-  const int n_cb = (Ndim + CBW - 1) / CBW;
-  const int pos = blockIdx.x >> 3;
-  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
-  const int cb = pos % n_cb;
-  constexpr int MB = BM / 16;        // 16-row MFMA blocks per tile
-  constexpr int KS = KC / 32;        // MFMA k-steps per chunk
-  constexpr int LDA = KC + 8;        // LDS row pitch (bf16), breaks bank aliasing
-  constexpr int SEGS = BM * KC / 8;  // 16-byte segments of one activation chunk
-  constexpr int ASEG = SEGS / NTH;   // per thread
-  static_assert(SEGS % NTH == 0, "activation chunk must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
-
-  const TileRows tr = tile_rows(ROUTED, tile, BM, ROUTED ? flags[FLAG_NTILES] : 0, tile_slot,
-                                tile_row0, offs, M);
-  if (!tr.active) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const size_t estride = (size_t)Ndim * Kdim;
-  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  int col0;
-  const uint16_t *bp0, *bp1;
-  if (GATEUP) {
-    col0 = cb * CBW + wave * 16;
-    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-    bp1 = B1 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-  } else {
-    col0 = cb * CBW + wave * 32;
-    bp0 = B0 + e * estride + (size_t)(col0 + r) * Kdim + 8 * g;
-    bp1 = bp0 + (size_t)16 * Kdim;
-  }
-  // Ndim is a multiple of 64, so a wave's 16 or 32 columns are all inside or all outside;
-  // a wave outside streams a valid stand-in (the first columns of the expert), skips the MFMA
-  // work and the stores, and meets every barrier
-  const bool wact = col0 < Ndim;
-  if (!wact) {
-    bp0 = B0 + e * estride + (size_t)r * Kdim + 8 * g;
-    bp1 = GATEUP ? B1 + e * estride + (size_t)r * Kdim + 8 * g : bp0;
-  }
-  // activation segments this thread stages: row = seg / (KC / 8), 8 columns each; a segment
-  // past the tile's last row reads row 0 (always present) and is replaced by zeros
-  const uint16_t* asrc[ASEG];
-  int adst[ASEG];
-  bool aok[ASEG];
-#pragma unroll
-  for (int j = 0; j < ASEG; ++j) {
-    const int seg = tid + NTH * j;
-    const int row = seg / (KC / 8), c8 = seg % (KC / 8);
-    const int p = tr.row0 + row;
-    aok[j] = p < tr.row_end;
-    const int src_row = aok[j] ? ((ROUTED && GATEUP) ? wl_pos[p] : p) : 0;
-    asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
-    adst[j] = row * LDA + c8 * 8;
-  }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int nch = Kdim / KC;
-  // Workgroups start their walk over K at different chunks (rot, by column block and tile
-  // position) and wrap around, so that at any moment the weight rows being read sit at
-  // different offsets within their rows rather than all at the same one.
-  const int rot = pos % nch;
-  auto kchunk = [&](int c) { return c + rot < nch ? c + rot : c + rot - nch; };
-
-  u32x4 areg[ASEG];
-  bf16x8 bx[NST][KS], by[NST][KS];
-  f32x4 c0[MB], c1[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    c0[m] = f32x4{0, 0, 0, 0};
-    c1[m] = f32x4{0, 0, 0, 0};
-  }
-
-  // Every global load below is issued by every lane, with no branch around it: the hardware
-  // counts outstanding loads in issue order, and a load under a lane-dependent branch makes the
-  // compiler wait for all of them at the next use.  With activations issued before the weight
-  // chunk of the same step, staging the activations waits only for themselves and the weight
-  // ring keeps NST - 1 chunks in flight across the barrier.
-  auto load_a = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < ASEG; ++j)
-      areg[j] = *reinterpret_cast<const u32x4*>(asrc[j] + (size_t)kchunk(c) * KC);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < ASEG; ++j)
-      *reinterpret_cast<u32x4*>(&As[buf][adst[j]]) = aok[j] ? areg[j] : zero;
-  };
-  auto load_b = [&](int c_, bf16x8* x0, bf16x8* x1) {
-    const int c = kchunk(c_);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      x0[s] = ld_frag(bp0 + (size_t)c * KC + 32 * s);
-      x1[s] = ld_frag(bp1 + (size_t)c * KC + 32 * s);
-    }
-  };
-  auto compute = [&](int buf, const bf16x8* x0, const bf16x8* x1) {
-    const uint16_t* ab = &As[buf][r * LDA + 8 * g];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const bf16x8 f =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ab + m * 16 * LDA + 32 * s));
-        // weights as the left operand: the block is held transposed, lane (r, g) with four
-        // consecutive columns 4 g .. 4 g + 3 of row r (one 8-byte store in the epilogue)
-        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0[s], f, c0[m], 0, 0, 0);
-        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1[s], f, c1[m], 0, 0, 0);
-      }
-    }
-  };
-
-  // one step: stage the activations of chunk c + 1 and fetch weight chunk c + NST - 1 into the
-  // ring slot freed by chunk c - 1, multiply chunk c, then publish chunk c + 1's activations
-  auto step = [&](int c, int u, bool next_a, bool pre_b) {
-    if (next_a) load_a(c + 1);
-    if (pre_b) load_b(c + NST - 1, bx[(u + NST - 1) % NST], by[(u + NST - 1) % NST]);
-    if (wact) compute(c & 1, bx[u], by[u]);
-    if (next_a) store_a((c + 1) & 1);
-    __syncthreads();
-  };
-  load_a(0);
-#pragma unroll
-  for (int st = 0; st < NST - 1; ++st)
-    if (st < nch) load_b(st, bx[st], by[st]);
-  store_a(0);
-  __syncthreads();
-  // steady state, NST steps per trip with every prefetch in range: no branch around a load
-  int kb = 0;
-  for (; kb + 2 * NST - 2 < nch; kb += NST) {
-#pragma unroll
-    for (int u = 0; u < NST; ++u) step(kb + u, u, true, true);
-  }
-  // the last NST to 2 NST - 2 chunks (uniform conditions)
-#pragma unroll
-  for (int u = 0; u < 2 * NST - 1; ++u) {
-    const int c = kb + u;
-    if (c < nch) step(c, u % NST, c + 1 < nch, c + NST - 1 < nch);
-  }
-
-  if (!wact) return;
-  // transposed blocks: lane (r, g) holds row 16 m + r, columns col0 + 4 g .. + 3 (c0) and
-  // col0 + 16 + 4 g .. + 3 (c1, down)
-  auto pack4 = [](const float* v) {
-    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
-  };
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int row = tr.row0 + 16 * m + r;
-    if (row >= tr.row_end) continue;
-    float v[4];
-    if (GATEUP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = c0[m][i] / (1.0f + expf(-c0[m][i])) * c1[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
-    } else {
-      const float sc = ROUTED ? wl_w[row] : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = sc * c0[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = sc * c1[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 16 + 4 * g) = pack4(v);
-    }
-  }
-}
-
-}  // namespace epoch
-
-namespace epoch {
 
 // Output of the LM-head mode of k_gemm_big: the rows are live positions (gathered through
 // live_list, n_live of them), the columns vocabulary tokens, and instead of the logits each wave
@@ -260,6 +59,234 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
+// The same copy with the non-temporal policy (nt), for operands streamed once per launch (the
+// expert weights): whole 128-byte lines read this way sustain a higher HBM rate on gfx950.
+__device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 2);
+}
+
+// Weight-stream grouped GEMM of both projections of the SwiGLU expert (v_mfma_f32_16x16x32_bf16,
+// fp32 accumulation), for tiles of up to 64 rows of one expert: the rows (fresh pairs, gathered
+// through the worklist for routed gate/up; positions in order for the shared expert) are few,
+// so the expert's weights, read once per tile, dominate the traffic.  A workgroup of WAVES
+// waves multiplies the tile by 32 WAVES weight rows:
+//   gate/up: wave w owns intermediate columns 16 w .. 16 w + 15 of the workgroup's 16 WAVES
+//            and holds those rows of W1 and of W3; epilogue h = bf16(silu(g) * u);
+//   down:    wave w owns output columns 32 w .. 32 w + 31 of the workgroup's 32 WAVES rows of
+//            W2; epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
+// K runs in chunks of 64 bf16, so a row of a chunk is one 128-byte line and one copy
+// instruction (global_load_lds_dwordx4, lane l's 16 bytes landing at the wave's LDS base +
+// 16 l) moves eight whole lines.  Every wave copies its own 32 weight rows with the
+// non-temporal policy (whole lines streamed that way sustain a higher HBM rate) and its share
+// of the activation rows with the cached one (the tile's other column blocks read them again).
+// LDS rows of 128 bytes hold k-segment slot ^ ((row >> 1) & 7) in 16-byte slot `slot`, so the
+// 16 rows of an MFMA fragment read fall on distinct banks.  NB chunk buffers, NB - 2 chunks in
+// flight while a chunk is multiplied, fragments double-buffered in registers; the
+// synchronisation is that of k_gemm_big below (explicit vmcnt / lgkmcnt waits, raw barriers,
+// inline fragment reads).
+//
+// Grid: one-dimensional, n_col_blocks * (tile slots rounded up to a multiple of 8).  The
+// hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
+// (L / 8) % n_col_blocks of tile 8 * ((L / 8) / n_col_blocks) + L % 8, so every column block of
+// a tile lands on the same XCD and the tile's activation rows are fetched into one L2 only.
+template <bool GATEUP, bool ROUTED, int NB, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
+    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
+    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+  static_assert(NB >= 3, "a chunk buffer is refilled two steps after its fragments were read");
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
+  constexpr int BM = 64, KC = 64, WR = 32 * WAVES;
+  constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // output columns per workgroup
+  constexpr int MB = BM / 16;
+  constexpr int NAW = BM / 8 / WAVES;     // activation copies per wave and chunk (8 rows each)
+  constexpr int NBW = 4;                  // weight copies per wave and chunk (its 32 rows)
+  constexpr int CPW = NAW + NBW;
+  __shared__ __attribute__((aligned(16))) uint16_t As[NB][BM * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][WR * KC];
+  const int n_cb = (Ndim + CBW - 1) / CBW;
+  const int pos = blockIdx.x >> 3;
+  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
+  const int cb = pos % n_cb;
+  const TileRows tr = tile_rows(ROUTED, tile, BM, ROUTED ? flags[FLAG_NTILES] : 0, tile_slot,
+                                tile_row0, offs, M);
+  if (!tr.active) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const size_t estride = (size_t)Ndim * Kdim;
+  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
+  const int col0 = cb * CBW + (GATEUP ? 16 : 32) * wave;
+  // Ndim is a multiple of 64, so a wave's columns are all inside or all outside; a wave outside
+  // copies stand-in rows (the first 32 of the expert), skips its MFMAs and stores, and still
+  // copies its share of the activations and meets every barrier
+  const bool wact = col0 < Ndim;
+  // copy sources: lane l moves 16-byte slot l % 8 of row l / 8 of an 8-row group
+  const int lrow = lane >> 3, pslot = lane & 7;
+  const uint16_t* asrc[NAW];
+  const uint16_t* bsrc[NBW];
+#pragma unroll
+  for (int j = 0; j < NAW; ++j) {
+    const int row = 8 * (NAW * wave + j) + lrow;
+    const int lslot = pslot ^ ((row >> 1) & 7);
+    const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
+    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : p;
+    asrc[j] = A + (size_t)src_row * Kdim + lslot * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int row = 8 * j + lrow;  // within the wave's 32 rows; (32 w + row) >> 1 & 7 == row >> 1 & 7
+    const int lslot = pslot ^ ((row >> 1) & 7);
+    int wrow;
+    const uint16_t* base;
+    if (GATEUP) {
+      wrow = col0 + (row & 15);
+      base = row < 16 ? B0 : B1;
+    } else {
+      wrow = col0 + row;
+      base = B0;
+    }
+    if (!wact) wrow = row;
+    bsrc[j] = base + e * estride + (size_t)wrow * Kdim + lslot * 8;
+  }
+  const int nch = Kdim / KC;
+  // Workgroups start their walk over K at different chunks (rot, by column block and tile
+  // position) and wrap around, so that at any moment the weight rows being read sit at
+  // different offsets within their rows rather than all at the same one.
+  const int rot = pos % nch;
+  auto issue = [&](int c, int buf) {
+    const int cc = c + rot < nch ? c + rot : c + rot - nch;
+#pragma unroll
+    for (int j = 0; j < NAW; ++j)
+      copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf][8 * (NAW * wave + j) * KC]);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+      copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf][(32 * wave + 8 * j) * KC]);
+  };
+  f32x4 c0[MB], c1[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    c0[m] = f32x4{0, 0, 0, 0};
+    c1[m] = f32x4{0, 0, 0, 0};
+  }
+  // fragments: k-step s of a chunk is k-segment 4 s + g for lane (r, g), held in slot
+  // (4 s + g) ^ ((r >> 1) & 7) of LDS rows 16 m + r (activations) and 32 w + r, 32 w + 16 + r
+  // (weights)
+  const int key = (r >> 1) & 7;
+  const int off0 = (g ^ key) * 8, off1 = ((4 + g) ^ key) * 8;
+  u32x4 fa[2][2][MB], fb[2][2][2];
+  auto read_frags = [&](int buf, int set) {
+    const uint32_t a0 = (uint32_t)(uintptr_t)&As[buf][r * KC + off0];
+    const uint32_t a1 = (uint32_t)(uintptr_t)&As[buf][r * KC + off1];
+    const uint32_t b0 = (uint32_t)(uintptr_t)&Bs[buf][(32 * wave + r) * KC + off0];
+    const uint32_t b1 = (uint32_t)(uintptr_t)&Bs[buf][(32 * wave + r) * KC + off1];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[set][0][m]) : "v"(a0), "i"(m * 16 * KC * 2));
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[set][1][m]) : "v"(a1), "i"(m * 16 * KC * 2));
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[set][0][n]) : "v"(b0), "i"(n * 16 * KC * 2));
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[set][1][n]) : "v"(b1), "i"(n * 16 * KC * 2));
+    }
+  };
+  auto frags_ready = [&](int set) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fa[set][0][0]), "+v"(fa[set][0][1]), "+v"(fa[set][0][2]), "+v"(fa[set][0][3]),
+                   "+v"(fa[set][1][0]), "+v"(fa[set][1][1]), "+v"(fa[set][1][2]), "+v"(fa[set][1][3]),
+                   "+v"(fb[set][0][0]), "+v"(fb[set][0][1]), "+v"(fb[set][1][0]), "+v"(fb[set][1][1]));
+  };
+  // weights as the left operand: lane (r, g) of block m ends up with row 16 m + r and the four
+  // consecutive columns 4 g .. 4 g + 3 (one 8-byte store in the epilogue)
+  auto mma = [&](int set) {
+    if (!wact) return;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const bf16x8 f = __builtin_bit_cast(bf16x8, fa[set][s][m]);
+        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[set][s][0]), f,
+                                                         c0[m], 0, 0, 0);
+        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[set][s][1]), f,
+                                                         c1[m], 0, 0, 0);
+      }
+  };
+  static_assert(CPW * (NB - 2) < 64, "vmcnt range");
+  constexpr int kInFlight = CPW * (NB - 2);  // copies after chunk c + 1's
+  // prologue: chunks 0 .. NB - 2 in flight, chunk 0 landed, its fragments read
+#pragma unroll
+  for (int x = 0; x < NB - 1; ++x)
+    if (x < nch) issue(x, x);
+  if (nch >= NB - 1)
+    wait_vm_lds<kInFlight>();
+  else
+    wait_vm_lds<0>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0);
+  // step c: copy chunk c + NB - 1 into the buffer of chunk c - 1 (every wave finished reading
+  // it before the previous barrier), wait for chunk c + 1, barrier, read its fragments,
+  // multiply chunk c
+  int c = 0;
+  for (; c + NB - 1 < nch; c += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cc = c + u;
+      if (cc + NB - 1 < nch) {
+        issue(cc + NB - 1, (cc + NB - 1) % NB);
+        wait_vm_lds<kInFlight>();
+      } else {
+        wait_vm_lds<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      frags_ready(u & 1);
+      read_frags((cc + 1) % NB, (u + 1) & 1);
+      mma(u & 1);
+    }
+  }
+  for (; c < nch; c += 2) {  // the last chunks: nothing more to copy
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cc = c + u;
+      if (cc < nch) {
+        wait_vm_lds<0>();
+        __builtin_amdgcn_s_barrier();
+        frags_ready(u & 1);
+        if (cc + 1 < nch) read_frags((cc + 1) % NB, (u + 1) & 1);
+        mma(u & 1);
+      }
+    }
+  }
+
+  if (!wact) return;
+  auto pack4 = [](const float* v) {
+    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+  };
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = tr.row0 + 16 * m + r;
+    if (row >= tr.row_end) continue;
+    float v[4];
+    if (GATEUP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = c0[m][i] / (1.0f + expf(-c0[m][i])) * c1[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
+    } else {
+      const float sc = ROUTED ? wl_w[row] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sc * c0[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = sc * c1[m][i];
+      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 16 + 4 * g) = pack4(v);
+    }
+  }
+}
+
 // Compute-bound variant for tiles with many rows (the shared expert over all M positions,
 // routed experts with many fresh pairs, the LM head over the live positions): a BR-row x
 // 128-weight-row output tile per workgroup, four waves in a 2 x 2 arrangement, each
@@ -277,7 +304,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
 // copy in flight before any LDS read.  Gate/up: the 128 staged weight rows are
 // [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g and u of
 // the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of W2.
-// Grid as k_expert_gemm (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
+// Grid as k_expert_stream (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
 template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,

@@ -13,40 +13,28 @@
 
 namespace epoch {
 
-// Tile shape of the bf16 path: kTileRows rows per tile, K in chunks of kGemmKC, a two-stage
-// register ring of weight chunks.  Gate/up runs 4 waves (64 intermediate columns of W1 and of
-// W3 per workgroup), down 8 waves (256 output columns); both measured best for the weight
-// stream at these shapes.
-constexpr int kGemmKC = 128;
-constexpr int kGemmStages = 2;
-constexpr int kGateUpWaves = 4;
-constexpr int kDownWaves = 8;
+// Weight-stream tiles (k_expert_stream, kTileRows = 64 rows): three chunk buffers, so two
+// workgroups of four waves or one of eight fit a CU's LDS.  Routed experts run eight waves
+// (128 gate/up or 256 down columns share each staged activation chunk); the shared expert,
+// only used here below kBigTileMinRows positions, runs four, which doubles its workgroup
+// count.  Both measured best at the benchmark shapes.
+constexpr int kStreamBuffers = 3;
 // dense (shared-expert) layers of at least this many positions use the compute-bound
 // 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
 constexpr int kBigTileMinRows = 2048;
 constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups per CU remain
 
-// 1-D grid of k_expert_gemm: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
-static dim3 gemm_grid(int tiles, int Ndim, bool gateup) {
-  const int cbw = gateup ? 16 * kGateUpWaves : 32 * kDownWaves;
-  const int n_cb = (Ndim + cbw - 1) / cbw;
-  return dim3(((tiles + 7) / 8) * 8 * n_cb);
-}
-
 template <bool GATEUP, bool ROUTED>
 static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
                         const uint16_t* B1, const Scratch& W, const int32_t* S_list,
                         uint16_t* out, int M, int Ndim) {
-  constexpr int WAVES = GATEUP ? kGateUpWaves : kDownWaves;
-  const dim3 grid = gemm_grid(tiles, Ndim, GATEUP), block(64 * WAVES);
-  if (Kdim % kGemmKC == 0)
-    launch((k_expert_gemm<kTileRows, kGemmKC, kGemmStages, GATEUP, ROUTED, WAVES>),
-                       grid, block, 0, st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs,
-                       S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
-  else
-    launch((k_expert_gemm<kTileRows, 64, 2, GATEUP, ROUTED, WAVES>), grid, block, 0,
-                       st, A, B0, B1, W.flags, W.tile_slot, W.tile_row0, W.offs, S_list,
-                       W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
+  constexpr int WAVES = ROUTED ? 8 : 4;
+  constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per workgroup
+  const int n_cb = (Ndim + cbw - 1) / cbw;
+  // 1-D grid: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
+  launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES>),
+         dim3(((tiles + 7) / 8) * 8 * n_cb), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
+         W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
 }
 
 // ---------------------------------------------------------------------------- fp32 variant
