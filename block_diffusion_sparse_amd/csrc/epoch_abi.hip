@@ -248,6 +248,11 @@ struct epoch_plan {
   std::vector<uint8_t> parity;  // which copy of the commit state is current, per layer
   int last_layer = -1;
   uint32_t timing_mask = 0;
+  // the shared expert depends only on x, so it runs on a stream of its own, concurrently with
+  // the router, plan and routed experts: forked after the caller's earlier work and joined
+  // before the combine (null when there is no shared expert)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   std::vector<TimedPair> pairs;
   double ms[EPOCH_TIMING_GROUPS] = {};
   int64_t launches[EPOCH_TIMING_GROUPS] = {};
@@ -344,14 +349,22 @@ int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* w
   p->pending.assign(d->n_layers, 0);
   p->parity.assign(d->n_layers, 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d->n_shared) {
+    if (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess) {
+      epoch_block_plan_destroy(p);
+      return EPOCH_E_HIP;
+    }
+  }
   for (int l = 0; l < d->n_layers; ++l) {
     if (launch_init_layer(s, p->lay.layers[l], st) != hipSuccess) {
-      delete p;
+      epoch_block_plan_destroy(p);
       return EPOCH_E_HIP;
     }
   }
   if (launch_init_scratch(s, p->lay.scratch, st) != hipSuccess) {
-    delete p;
+    epoch_block_plan_destroy(p);
     return EPOCH_E_HIP;
   }
   *out_plan = p;
@@ -370,6 +383,15 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
   const epoch_layer_weights& w = p->w[layer];
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (s.n_shared) {
+    if (hipEventRecord(p->fork, st) != hipSuccess ||
+        hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess)
+      return EPOCH_E_HIP;
+    GroupTimer tm(p, p->side, 5);
+    e = launch_shared(s, x, w.sw1, w.sw3, w.sw2, W, p->side);
+    tm.done();
+    if (e != hipSuccess || hipEventRecord(p->join, p->side) != hipSuccess) return EPOCH_E_HIP;
+  }
   {
     GroupTimer tm(p, st, 0);
     e = launch_router(s, x, w.router_w, w.router_b, decoded, force_fresh, p->iter[layer], L, W, st);
@@ -400,12 +422,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
-  if (s.n_shared) {
-    GroupTimer tm(p, st, 5);
-    e = launch_shared(s, x, w.sw1, w.sw3, w.sw2, W, st);
-    tm.done();
-    if (e != hipSuccess) return EPOCH_E_HIP;
-  }
+  if (s.n_shared && hipStreamWaitEvent(st, p->join, 0) != hipSuccess) return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 6);
     e = launch_combine(s, p->iter[layer], L, W, y, y_routed, st);
@@ -473,6 +490,12 @@ int32_t epoch_block_plan_destroy(epoch_plan* p) {
     pool_release(tp.a);
     pool_release(tp.b);
   }
+  if (p->side) {
+    (void)hipStreamSynchronize(p->side);
+    (void)hipStreamDestroy(p->side);
+  }
+  if (p->fork) (void)hipEventDestroy(p->fork);
+  if (p->join) (void)hipEventDestroy(p->join);
   delete p;
   return EPOCH_OK;
 }

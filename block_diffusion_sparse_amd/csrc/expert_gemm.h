@@ -68,12 +68,12 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // Weight-stream grouped GEMM of both projections of the SwiGLU expert (v_mfma_f32_16x16x32_bf16,
 // fp32 accumulation), for tiles of up to 64 rows of one expert: the rows (fresh pairs, gathered
 // through the worklist for routed gate/up; positions in order for the shared expert) are few,
-// so the expert's weights, read once per tile, dominate the traffic.  A workgroup of WAVES
-// waves multiplies the tile by 32 WAVES weight rows:
-//   gate/up: wave w owns intermediate columns 16 w .. 16 w + 15 of the workgroup's 16 WAVES
-//            and holds those rows of W1 and of W3; epilogue h = bf16(silu(g) * u);
-//   down:    wave w owns output columns 32 w .. 32 w + 31 of the workgroup's 32 WAVES rows of
-//            W2; epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
+// so the expert's weights, read once per tile, dominate the traffic.  A work item is one tile
+// against 32 WAVES weight rows (a column block):
+//   gate/up: wave w owns intermediate columns 16 w .. 16 w + 15 of the block's 16 WAVES and
+//            holds those rows of W1 and of W3; epilogue h = bf16(silu(g) * u);
+//   down:    wave w owns output columns 32 w .. 32 w + 31 of the block's 32 WAVES rows of W2;
+//            epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
 // K runs in chunks of 64 bf16, so a row of a chunk is one 128-byte line and one copy
 // instruction (global_load_lds_dwordx4, lane l's 16 bytes landing at the wave's LDS base +
 // 16 l) moves eight whole lines.  Every wave copies its own 32 weight rows with the
@@ -85,10 +85,16 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // synchronisation is that of k_gemm_big below (explicit vmcnt / lgkmcnt waits, raw barriers,
 // inline fragment reads).
 //
-// Grid: one-dimensional, n_col_blocks * (tile slots rounded up to a multiple of 8).  The
-// hardware hands consecutive workgroups to the 8 XCDs in turn; workgroup L runs column block
-// (L / 8) % n_col_blocks of tile 8 * ((L / 8) / n_col_blocks) + L % 8, so every column block of
-// a tile lands on the same XCD and the tile's activation rows are fetched into one L2 only.
+// Persistent workgroups: the grid (a multiple of 8, about one workgroup per CU slot) walks the
+// work items i = blockIdx.x + k gridDim.x, and the chunks of consecutive items form one
+// stream, so the next item's first chunks are already in flight while the current one is
+// multiplied and stored (no pipeline fill or drain per item).  Item i is column block
+// (i / 8) % n_col_blocks of tile 8 ((i / 8) / n_col_blocks) + i % 8: the hardware hands
+// workgroups to the 8 XCDs in turn, so every column block of a tile runs on one XCD and the
+// tile's activation rows are fetched into one L2 only.  Everything an item needs that lives in
+// memory (tile table, offsets, expert id, gathered row ids, routing weights) is read with
+// uniform addresses, i.e. scalar loads, and spread to the lanes by selects: a vector load here
+// would make the wait for it also wait for every copy in flight.
 template <bool GATEUP, bool ROUTED, int NB, int WAVES = 4>
 __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   static_assert(NB >= 3, "a chunk buffer is refilled two steps after its fragments were read");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
   constexpr int BM = 64, KC = 64, WR = 32 * WAVES;
-  constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // output columns per workgroup
+  constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // output columns per item
   constexpr int MB = BM / 16;
   constexpr int NAW = BM / 8 / WAVES;     // activation copies per wave and chunk (8 rows each)
   constexpr int NBW = 4;                  // weight copies per wave and chunk (its 32 rows)
@@ -108,70 +114,110 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BM * KC];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][WR * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
-  const int pos = blockIdx.x >> 3;
-  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
-  const int cb = pos % n_cb;
-  const TileRows tr = tile_rows(ROUTED, tile, BM, ROUTED ? flags[FLAG_NTILES] : 0, tile_slot,
-                                tile_row0, offs, M);
-  if (!tr.active) return;
+  const int ntiles = ROUTED ? flags[FLAG_NTILES] : (M + BM - 1) / BM;
+  // this workgroup's items: position (blockIdx.x / 8) + k G8 along the tile-major order of
+  // its XCD lane, active while the tile 8 (position / n_cb) + lane8 exists
+  const int lane8 = blockIdx.x & 7, pos0 = blockIdx.x >> 3, G8 = gridDim.x >> 3;
+  const int T8 = ntiles > lane8 ? (ntiles - lane8 + 7) >> 3 : 0;
+  const int span = T8 * n_cb - pos0;
+  const int nitems = span > 0 ? (span + G8 - 1) / G8 : 0;
+  if (nitems == 0) return;
+  const int nch = Kdim / KC;
+  const int Q = nitems * nch;  // chunks in this workgroup's stream
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const size_t estride = (size_t)Ndim * Kdim;
-  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  const int col0 = cb * CBW + (GATEUP ? 16 : 32) * wave;
-  // Ndim is a multiple of 64, so a wave's columns are all inside or all outside; a wave outside
-  // copies stand-in rows (the first 32 of the expert), skips its MFMAs and stores, and still
-  // copies its share of the activations and meets every barrier
-  const bool wact = col0 < Ndim;
-  // copy sources: lane l moves 16-byte slot l % 8 of row l / 8 of an 8-row group
-  const int lrow = lane >> 3, pslot = lane & 7;
+  const int lrow = lane >> 3, pslot = lane & 7;  // copies: lane l moves slot l % 8 of row l / 8
+
+  struct Item {
+    int row0, row_end, col0, rot;
+    size_t e;
+    bool wact;
+  };
+  auto item = [&](int k) {
+    const int pos = pos0 + k * G8;
+    const int cb = pos % n_cb;
+    const TileRows tr = tile_rows(ROUTED, 8 * (pos / n_cb) + lane8, BM, ntiles, tile_slot,
+                                  tile_row0, offs, M);
+    Item it;
+    it.row0 = tr.row0;
+    it.row_end = tr.row_end;
+    it.e = ROUTED ? (size_t)S_list[tr.slot] : 0;
+    it.col0 = cb * CBW + (GATEUP ? 16 : 32) * wave;
+    // Ndim is a multiple of 64, so a wave's columns are all inside or all outside; a wave
+    // outside copies stand-in rows (the first 32 of the expert), skips its MFMAs and stores,
+    // and still copies its share of the activations and meets every barrier
+    it.wact = it.col0 < Ndim;
+    // items start their walk over K at different chunks and wrap around, so that at any
+    // moment the weight rows being read sit at different offsets within their rows
+    it.rot = pos % nch;
+    return it;
+  };
+
+  auto item_wact = [&](int k) { return ((pos0 + k * G8) % n_cb) * CBW + (GATEUP ? 16 : 32) * wave < Ndim; };
+
+  // issue side: the item whose chunks are being copied, its copy sources, the next chunk
   const uint16_t* asrc[NAW];
   const uint16_t* bsrc[NBW];
+  int ik = 0, ic = 0, irot = 0;
+  auto sources = [&](const Item& it) {
 #pragma unroll
-  for (int j = 0; j < NAW; ++j) {
-    const int row = 8 * (NAW * wave + j) + lrow;
-    const int lslot = pslot ^ ((row >> 1) & 7);
-    const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
-    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : p;
-    asrc[j] = A + (size_t)src_row * Kdim + lslot * 8;
-  }
+    for (int j = 0; j < NAW; ++j) {
+      const int row0 = 8 * (NAW * wave + j);
+      const int row = row0 + lrow;
+      const int lslot = pslot ^ ((row >> 1) & 7);
+      int src_row;
+      if (ROUTED && GATEUP) {
+        // the eight gathered rows of this copy (rows past the tile repeat its last row)
+        src_row = 0;
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    const int row = 8 * j + lrow;  // within the wave's 32 rows; (32 w + row) >> 1 & 7 == row >> 1 & 7
-    const int lslot = pslot ^ ((row >> 1) & 7);
-    int wrow;
-    const uint16_t* base;
-    if (GATEUP) {
-      wrow = col0 + (row & 15);
-      base = row < 16 ? B0 : B1;
-    } else {
-      wrow = col0 + row;
-      base = B0;
+        for (int t = 0; t < 8; ++t) {
+          const int v = wl_pos[min(it.row0 + row0 + t, it.row_end - 1)];
+          src_row = lrow == t ? v : src_row;
+        }
+      } else {
+        src_row = min(it.row0 + row, it.row_end - 1);
+      }
+      asrc[j] = A + (size_t)src_row * Kdim + lslot * 8;
     }
-    if (!wact) wrow = row;
-    bsrc[j] = base + e * estride + (size_t)wrow * Kdim + lslot * 8;
-  }
-  const int nch = Kdim / KC;
-  // Workgroups start their walk over K at different chunks (rot, by column block and tile
-  // position) and wrap around, so that at any moment the weight rows being read sit at
-  // different offsets within their rows rather than all at the same one.
-  const int rot = pos % nch;
-  auto issue = [&](int c, int buf) {
-    const int cc = c + rot < nch ? c + rot : c + rot - nch;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int row = 8 * j + lrow;  // within the wave's 32 rows; (32 w + row) >> 1 & 7 == row >> 1 & 7
+      const int lslot = pslot ^ ((row >> 1) & 7);
+      int wrow;
+      const uint16_t* base;
+      if (GATEUP) {
+        wrow = it.col0 + (row & 15);
+        base = row < 16 ? B0 : B1;
+      } else {
+        wrow = it.col0 + row;
+        base = B0;
+      }
+      if (!it.wact) wrow = row;
+      bsrc[j] = base + it.e * estride + (size_t)wrow * Kdim + lslot * 8;
+    }
+    irot = it.rot;
+  };
+  // copy the next chunk of the stream into chunk buffer buf (moving to the next item when the
+  // current one is done; the caller keeps the stream within its Q chunks)
+  auto issue_next = [&](int buf) {
+    if (ic == nch) {
+      ++ik;
+      ic = 0;
+      sources(item(ik));
+    }
+    const int cc = ic + irot < nch ? ic + irot : ic + irot - nch;
 #pragma unroll
     for (int j = 0; j < NAW; ++j)
       copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf][8 * (NAW * wave + j) * KC]);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
       copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf][(32 * wave + 8 * j) * KC]);
+    ++ic;
   };
+
   f32x4 c0[MB], c1[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    c0[m] = f32x4{0, 0, 0, 0};
-    c1[m] = f32x4{0, 0, 0, 0};
-  }
   // fragments: k-step s of a chunk is k-segment 4 s + g for lane (r, g), held in slot
   // (4 s + g) ^ ((r >> 1) & 7) of LDS rows 16 m + r (activations) and 32 w + r, 32 w + 16 + r
   // (weights)
@@ -203,7 +249,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   // weights as the left operand: lane (r, g) of block m ends up with row 16 m + r and the four
   // consecutive columns 4 g .. 4 g + 3 (one 8-byte store in the epilogue)
   auto mma = [&](int set) {
-    if (!wact) return;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -215,74 +260,87 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
                                                          c1[m], 0, 0, 0);
       }
   };
+  auto pack4 = [](const float* v) {
+    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+  };
+  auto epilogue = [&](const Item& it) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float sc = 1.0f;
+      if (ROUTED && !GATEUP) {  // routing weights of rows 16 m .. 16 m + 15
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float v = wl_w[min(it.row0 + 16 * m + t, it.row_end - 1)];
+          sc = r == t ? v : sc;
+        }
+      }
+      const int row = it.row0 + 16 * m + r;
+      if (row >= it.row_end) continue;
+      float v[4];
+      if (GATEUP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = c0[m][i] / (1.0f + expf(-c0[m][i])) * c1[m][i];
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + it.col0 + 4 * g) = pack4(v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = sc * c0[m][i];
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + it.col0 + 4 * g) = pack4(v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = sc * c1[m][i];
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + it.col0 + 16 + 4 * g) = pack4(v);
+      }
+    }
+  };
+
   static_assert(CPW * (NB - 2) < 64, "vmcnt range");
-  constexpr int kInFlight = CPW * (NB - 2);  // copies after chunk c + 1's
-  // prologue: chunks 0 .. NB - 2 in flight, chunk 0 landed, its fragments read
+  constexpr int kInFlight = CPW * (NB - 2);  // copies after chunk q + 1's
+  sources(item(0));
+  // prologue: chunks 0 .. NB - 2 of the stream in flight, chunk 0 landed, its fragments read
 #pragma unroll
   for (int x = 0; x < NB - 1; ++x)
-    if (x < nch) issue(x, x);
-  if (nch >= NB - 1)
+    if (x < Q) issue_next(x);
+  if (Q >= NB - 1)
     wait_vm_lds<kInFlight>();
   else
     wait_vm_lds<0>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0);
-  // step c: copy chunk c + NB - 1 into the buffer of chunk c - 1 (every wave finished reading
-  // it before the previous barrier), wait for chunk c + 1, barrier, read its fragments,
-  // multiply chunk c
-  int c = 0;
-  for (; c + NB - 1 < nch; c += 2) {
+  // step q: copy chunk q + NB - 1 into the buffer of chunk q - 1 (every wave finished reading
+  // it before the previous barrier), wait for chunk q + 1, barrier, read its fragments,
+  // multiply chunk q; after an item's last chunk, store its outputs
+  int ck = 0, cc = 0;  // item and chunk of the chunk being multiplied
+  bool cwact = item_wact(0);
+  for (int q = 0; q < Q; q += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int cc = c + u;
-      if (cc + NB - 1 < nch) {
-        issue(cc + NB - 1, (cc + NB - 1) % NB);
-        wait_vm_lds<kInFlight>();
-      } else {
-        wait_vm_lds<0>();
-      }
-      __builtin_amdgcn_s_barrier();
-      frags_ready(u & 1);
-      read_frags((cc + 1) % NB, (u + 1) & 1);
-      mma(u & 1);
-    }
-  }
-  for (; c < nch; c += 2) {  // the last chunks: nothing more to copy
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int cc = c + u;
-      if (cc < nch) {
-        wait_vm_lds<0>();
+      const int qq = q + u;
+      if (qq < Q) {
+        if (qq + NB - 1 < Q) {
+          issue_next((qq + NB - 1) % NB);
+          wait_vm_lds<kInFlight>();
+        } else {
+          wait_vm_lds<0>();
+        }
         __builtin_amdgcn_s_barrier();
         frags_ready(u & 1);
-        if (cc + 1 < nch) read_frags((cc + 1) % NB, (u + 1) & 1);
-        mma(u & 1);
+        if (qq + 1 < Q) read_frags((qq + 1) % NB, (u + 1) & 1);
+        if (cc == 0) {
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            c0[m] = f32x4{0, 0, 0, 0};
+            c1[m] = f32x4{0, 0, 0, 0};
+          }
+        }
+        if (cwact) mma(u & 1);
+        if (++cc == nch) {
+          const Item it = item(ck);
+          if (it.wact) epilogue(it);
+          ++ck;
+          cc = 0;
+          cwact = item_wact(ck);
+        }
       }
-    }
-  }
-
-  if (!wact) return;
-  auto pack4 = [](const float* v) {
-    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
-  };
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int row = tr.row0 + 16 * m + r;
-    if (row >= tr.row_end) continue;
-    float v[4];
-    if (GATEUP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = c0[m][i] / (1.0f + expf(-c0[m][i])) * c1[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
-    } else {
-      const float sc = ROUTED ? wl_w[row] : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = sc * c0[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 4 * g) = pack4(v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = sc * c1[m][i];
-      *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col0 + 16 + 4 * g) = pack4(v);
     }
   }
 }

@@ -16,9 +16,10 @@ namespace epoch {
 // Weight-stream tiles (k_expert_stream, kTileRows = 64 rows): three chunk buffers, so two
 // workgroups of four waves or one of eight fit a CU's LDS.  Routed experts run eight waves
 // (128 gate/up or 256 down columns share each staged activation chunk); the shared expert,
-// only used here below kBigTileMinRows positions, runs four, which doubles its workgroup
-// count.  Both measured best at the benchmark shapes.
+// only used here below kBigTileMinRows positions, runs four, which doubles its work items.
+// Both measured best at the benchmark shapes.
 constexpr int kStreamBuffers = 3;
+constexpr int kLdsPerCu = 160 * 1024;
 // dense (shared-expert) layers of at least this many positions use the compute-bound
 // 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
 constexpr int kBigTileMinRows = 2048;
@@ -28,12 +29,25 @@ template <bool GATEUP, bool ROUTED>
 static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
                         const uint16_t* B1, const Scratch& W, const int32_t* S_list,
                         uint16_t* out, int M, int Ndim) {
-  constexpr int WAVES = ROUTED ? 8 : 4;
-  constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per workgroup
+#ifndef EPOCH_RW
+#define EPOCH_RW 8
+#endif
+  constexpr int WAVES = ROUTED ? EPOCH_RW : 4;
+  constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per work item
+  constexpr int lds = kStreamBuffers * (64 * 64 + 32 * WAVES * 64) * 2;
   const int n_cb = (Ndim + cbw - 1) / cbw;
-  // 1-D grid: column blocks x tile slots rounded up to a multiple of 8 (XCDs)
+  // persistent grid: as many workgroups as fit on the device at once (a multiple of 8, one
+  // per XCD lane), never more than the work items (tile slots rounded up to a multiple of 8,
+  // times the column blocks)
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    n_cu = 256;
+  const int slots = ((n_cu * (kLdsPerCu / lds)) / 8) * 8;
+  const int items = ((tiles + 7) / 8) * 8 * n_cb;
   launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES>),
-         dim3(((tiles + 7) / 8) * 8 * n_cb), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
+         dim3(items < slots ? items : slots), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
          W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
 }
 

@@ -27,9 +27,16 @@
  *     the descriptor: bf16 (raw 16-bit bfloat16) or fp32.
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (weights, inputs, outputs, workspace); the library never allocates
- *     device memory.  The only allocation is the small host-side plan object.
+ *     device memory.  The only allocations are host-side: the plan object and, for
+ *     layers with a shared expert, one HIP stream and two events that the plan owns
+ *     (created by epoch_block_plan_build on the current device, default priority,
+ *     released by epoch_block_plan_destroy).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     only enqueue work on it: no host synchronisation, no host<->device copies.
+ *     A forward with a shared expert forks that expert onto the plan's own stream
+ *     (an event recorded on `stream`) and joins it back before the combine, so all
+ *     of its work is still ordered after earlier work on `stream` and before later
+ *     work on it (graph capture of `stream` captures both branches).
  *   - Return value: EPOCH_OK (0) or a negative EPOCH_E_* code; nothing is enqueued
  *     when a call fails its argument checks.  A kernel fault surfaces at the
  *     caller's next synchronisation of the stream.
@@ -241,7 +248,8 @@ int32_t epoch_cache_update(epoch_plan* plan, int32_t layer, void* stream);
    Enqueues nothing; read the buffers after synchronising the stream. */
 int32_t epoch_plan_inspect(const epoch_plan* plan, int32_t layer, epoch_inspect* out);
 
-/* Frees the host-side plan object (the workspace stays the caller's). NULL is a no-op. */
+/* Frees the host-side plan object and its stream and events (the workspace stays the
+ * caller's).  Waits for the plan's own stream first.  NULL is a no-op. */
 int32_t epoch_block_plan_destroy(epoch_plan* plan);
 
 /* Static text for a status code. */
