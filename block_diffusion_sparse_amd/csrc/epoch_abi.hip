@@ -248,11 +248,13 @@ struct epoch_plan {
   std::vector<uint8_t> parity;  // which copy of the commit state is current, per layer
   int last_layer = -1;
   uint32_t timing_mask = 0;
-  // the shared expert depends only on x, so it runs on a stream of its own, concurrently with
-  // the router, plan and routed experts: forked after the caller's earlier work and joined
-  // before the combine (null when there is no shared expert)
+  // Work that does not depend on the rest of the forward runs on a stream of its own, forked
+  // after the caller's earlier work and joined before the combine: the shared expert (it
+  // depends only on x) from the start of the forward, and the compute-bound big-tile routed
+  // experts (they depend on the plan step) beside the light tiles' weight stream.  Null when
+  // the layer has neither.
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, fork_big = nullptr, join = nullptr;
   std::vector<TimedPair> pairs;
   double ms[EPOCH_TIMING_GROUPS] = {};
   int64_t launches[EPOCH_TIMING_GROUPS] = {};
@@ -349,9 +351,10 @@ int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* w
   p->pending.assign(d->n_layers, 0);
   p->parity.assign(d->n_layers, 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d->n_shared) {
+  if (d->n_shared || s.big_routed) {
     if (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&p->fork_big, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess) {
       epoch_block_plan_destroy(p);
       return EPOCH_E_HIP;
@@ -390,7 +393,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     GroupTimer tm(p, p->side, 5);
     e = launch_shared(s, x, w.sw1, w.sw3, w.sw2, W, p->side);
     tm.done();
-    if (e != hipSuccess || hipEventRecord(p->join, p->side) != hipSuccess) return EPOCH_E_HIP;
+    if (e != hipSuccess) return EPOCH_E_HIP;
   }
   {
     GroupTimer tm(p, st, 0);
@@ -410,19 +413,28 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
+  hipStream_t big_st = st;
+  if (s.big_routed) {
+    if (hipEventRecord(p->fork_big, st) != hipSuccess ||
+        hipStreamWaitEvent(p->side, p->fork_big, 0) != hipSuccess)
+      return EPOCH_E_HIP;
+    big_st = p->side;
+  }
   {
     GroupTimer tm(p, st, 3);
-    e = launch_routed_gateup(s, x, w.w1, w.w3, L, W, st);
+    e = launch_routed_gateup(s, x, w.w1, w.w3, L, W, st, big_st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 4);
-    e = launch_routed_down(s, w.w2, L, W, st);
+    e = launch_routed_down(s, w.w2, L, W, st, big_st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
-  if (s.n_shared && hipStreamWaitEvent(st, p->join, 0) != hipSuccess) return EPOCH_E_HIP;
+  if (p->side && (hipEventRecord(p->join, p->side) != hipSuccess ||
+                  hipStreamWaitEvent(st, p->join, 0) != hipSuccess))
+    return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 6);
     e = launch_combine(s, p->iter[layer], L, W, y, y_routed, st);
@@ -495,6 +507,7 @@ int32_t epoch_block_plan_destroy(epoch_plan* p) {
     (void)hipStreamDestroy(p->side);
   }
   if (p->fork) (void)hipEventDestroy(p->fork);
+  if (p->fork_big) (void)hipEventDestroy(p->fork_big);
   if (p->join) (void)hipEventDestroy(p->join);
   delete p;
   return EPOCH_OK;

@@ -25,30 +25,48 @@ constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kBigTileMinRows = 2048;
 constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups per CU remain
 
-template <bool GATEUP, bool ROUTED>
-static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
-                        const uint16_t* B1, const Scratch& W, const int32_t* S_list,
-                        uint16_t* out, int M, int Ndim) {
-#ifndef EPOCH_RW
-#define EPOCH_RW 8
-#endif
-  constexpr int WAVES = ROUTED ? EPOCH_RW : 4;
-  constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per work item
-  constexpr int lds = kStreamBuffers * (64 * 64 + 32 * WAVES * 64) * 2;
-  const int n_cb = (Ndim + cbw - 1) / cbw;
-  // persistent grid: as many workgroups as fit on the device at once (a multiple of 8, one
-  // per XCD lane), never more than the work items (tile slots rounded up to a multiple of 8,
-  // times the column blocks)
+// Workgroups of k_expert_stream with lds bytes each that fit on the device at once, at most
+// per_cu per CU, as a multiple of 8 (one per XCD lane).
+static int stream_slots(int lds, int per_cu) {
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n_cu <= 0)
     n_cu = 256;
-  const int slots = ((n_cu * (kLdsPerCu / lds)) / 8) * 8;
+  const int fit = kLdsPerCu / lds;
+  return ((n_cu * (fit < per_cu ? fit : per_cu)) / 8) * 8;
+}
+
+template <bool GATEUP, bool ROUTED, int WAVES>
+static void launch_gemm_w(int tiles, int per_cu, hipStream_t st, int Kdim, const uint16_t* A,
+                          const uint16_t* B0, const uint16_t* B1, const Scratch& W,
+                          const int32_t* S_list, uint16_t* out, int M, int Ndim) {
+  constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per work item
+  constexpr int lds = kStreamBuffers * (64 * 64 + 32 * WAVES * 64) * 2;
+  const int n_cb = (Ndim + cbw - 1) / cbw;
+  // persistent grid: as many workgroups as fit at once, never more than the work items (tile
+  // slots rounded up to a multiple of 8, times the column blocks)
+  const int slots = stream_slots(lds, per_cu);
   const int items = ((tiles + 7) / 8) * 8 * n_cb;
   launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES>),
          dim3(items < slots ? items : slots), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
          W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
+}
+
+// Routed experts run eight waves per workgroup, the shared expert four.  When the compute-bound
+// big tiles run concurrently on another stream, the routed stream kernel takes four waves and
+// one workgroup per CU, leaving LDS for one big-tile workgroup beside it (measured: the two
+// kernels slow each other down, but less than they take one after the other).
+template <bool GATEUP, bool ROUTED>
+static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
+                        const uint16_t* B1, const Scratch& W, const int32_t* S_list,
+                        uint16_t* out, int M, int Ndim, bool beside_big = false) {
+  if (!ROUTED)
+    launch_gemm_w<GATEUP, ROUTED, 4>(tiles, 2, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
+  else if (beside_big)
+    launch_gemm_w<GATEUP, ROUTED, 4>(tiles, 1, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
+  else
+    launch_gemm_w<GATEUP, ROUTED, 8>(tiles, 1, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
 }
 
 // ---------------------------------------------------------------------------- fp32 variant
@@ -109,15 +127,16 @@ __global__ __launch_bounds__(256) void k_down_f32(
 }
 
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
-                                const LayerState& L, const Scratch& W, hipStream_t st) {
+                                const LayerState& L, const Scratch& W, hipStream_t st,
+                                hipStream_t big_st) {
   dim3 grid(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols);
   if (s.bf16) {
     launch_gemm<true, true>(s.T_max, st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
-                            L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I);
+                            L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I, big_st != st);
     if (s.big_routed)  // experts with many fresh rows: compute-bound kBigTile x 128 tiles
       launch((k_gemm_big<true, true, false, kBigTile>),
-                         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
+                         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, big_st,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
                          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
                          W.offs, L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M,
@@ -131,15 +150,15 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
 }
 
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
-                              const Scratch& W, hipStream_t st) {
+                              const Scratch& W, hipStream_t st, hipStream_t big_st) {
   if (s.bf16) {
     launch_gemm<false, true>(s.T_max, st, s.I, static_cast<const uint16_t*>(W.h),
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
-                             static_cast<uint16_t*>(W.y_pair), s.M, s.H);
+                             static_cast<uint16_t*>(W.y_pair), s.M, s.H, big_st != st);
     if (s.big_routed)
       launch((k_gemm_big<false, true, false, kBigTile>),
                          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
-                         st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
+                         big_st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
                          nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
                          W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H,
                          LmPartials{});
