@@ -195,7 +195,7 @@ def main():
         block)."""
         plan = B.epoch_block_plan_build(desc, lw, ws, nbytes, sp)
         prev = [layer_counters(plan, l) for l in range(n_layers)]
-        i_t, i_p = B.COUNTERS.index("touched"), B.COUNTERS.index("pairs")
+        idx = [B.COUNTERS.index(n) for n in ("touched", "pairs", "big_experts", "big_pairs")]
         fwd = []
         for it in range(iters):
             for l in range(n_layers):
@@ -203,7 +203,7 @@ def main():
                                           None if Fdev is None else Fdev[it], Y, None, sp)
                 B.epoch_cache_update(plan, l, sp)
                 c = layer_counters(plan, l)
-                fwd.append((int(c[i_t] - prev[l][i_t]), int(c[i_p] - prev[l][i_p])))
+                fwd.append(tuple(int(c[i] - prev[l][i]) for i in idx))
                 prev[l] = c
         counters = block_counters(plan)
         B.epoch_block_plan_destroy(plan)
@@ -229,8 +229,11 @@ def main():
     brk_ms, brk_n = collect([one_block(-1) for _ in range(args.steps)])
 
     # ---------------------------------------------------------------- timed region
-    # the dominant expert kernel (by the breakdown) is the one timed live, two events a forward
-    dom = max(("routed_gateup", "routed_down"), key=lambda g: brk_ms[g] / max(brk_n[g], 1))
+    # the dominant expert kernel group (by the breakdown) is the one timed live, two events a
+    # forward: the weight-stream tiles, or (shapes with them) the 256-row compute-bound tiles
+    routed = [g for g in ("routed_gateup", "routed_down", "routed_gateup_big", "routed_down_big")
+              if brk_n[g]]
+    dom = max(routed, key=lambda g: brk_ms[g] / max(brk_n[g], 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     plans = [one_block(1 << B.TIMING_GROUPS.index(dom), TIMED_EVERY) for _ in range(args.steps)]
@@ -247,35 +250,48 @@ def main():
     us_per_layer_iter = 1e3 * ms_per_step / layer_iters
 
     # ---------------------------------------------------------------- roofline of the dominant kernel
-    # the forwards the timed region timed (every TIMED_EVERY-th of each block), their touched
-    # experts and fresh pairs from the reference block
+    # the forwards the timed region timed (every TIMED_EVERY-th of each block): their touched
+    # experts and fresh pairs, and how many of each the big tiles took, from the reference block
     sampled = per_fwd[::TIMED_EVERY]
-    touched = sum(t for t, _ in sampled)     # experts with fresh pairs, summed over forwards
-    P = sum(p for _, p in sampled)
+    touched = sum(f[0] for f in sampled)     # experts with fresh pairs, summed over forwards
+    P = sum(f[1] for f in sampled)
+    Eb = sum(f[2] for f in sampled)          # of which on big tiles, and their pairs
+    Pb = sum(f[3] for f in sampled)
+    El, Pl = touched - Eb, P - Pb            # on the weight-stream tiles
     act = 2 if w.act == "bf16" else 4
-    algo = {
-        # W1 + W3 of every touched expert, gathered x rows, h written
-        "routed_gateup": touched * 2 * I * H * act + P * H * act + P * I * act,
-        # W2 of every touched expert, h read, y_pair written
-        "routed_down": touched * H * I * act + P * I * act + P * H * act,
+    # (bound, algorithmic bytes, flops) per group over the sampled forwards
+    work = {
+        # W1 + W3 of every expert of the group, gathered x rows, h written
+        "routed_gateup": ("hbm", El * 2 * I * H * act + Pl * H * act + Pl * I * act, 4.0 * Pl * H * I),
+        # W2 of every expert of the group, h read, y_pair written
+        "routed_down": ("hbm", El * H * I * act + Pl * I * act + Pl * H * act, 2.0 * Pl * H * I),
+        "routed_gateup_big": ("mfma", Eb * 2 * I * H * act + Pb * (H + I) * act, 4.0 * Pb * H * I),
+        "routed_down_big": ("mfma", Eb * H * I * act + Pb * (I + H) * act, 2.0 * Pb * H * I),
     }
-    flops = {"routed_gateup": 4.0 * P * H * I, "routed_down": 2.0 * P * H * I}
+    bound, nbytes, nflop = work[dom]
     launches = max(group_n[dom], 1)
     assert launches == len(sampled) * args.steps, (launches, len(sampled), args.steps)
     avg_ms = group_ms[dom] / launches
     steps = args.steps
-    bytes_per_launch = algo[dom] * steps / launches
-    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    bytes_per_launch = nbytes * steps / launches
+    flop_per_launch = nflop * steps / launches
+    gbs = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    tfs = flop_per_launch / (avg_ms * 1e-3) / 1e12
     traffic = load_traffic(w.name, dom)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": dom,
-                "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                "avg_launch_us": round(avg_ms * 1e3, 2), "timed_launches": launches,
-                "timed_every": TIMED_EVERY,
-                "mfma_tflops": round(flops[dom] * steps / launches / (avg_ms * 1e-3) / 1e12, 2),
-                "mfma_frac_of_bf16_peak": round(flops[dom] * steps / launches / (avg_ms * 1e-3)
-                                                / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
+    common = {"traffic": traffic, "kernel": dom,
+              "algorithmic_bytes_per_launch": int(bytes_per_launch),
+              "algorithmic_flop_per_launch": int(flop_per_launch),
+              "avg_launch_us": round(avg_ms * 1e3, 2), "timed_launches": launches,
+              "timed_every": TIMED_EVERY}
+    if bound == "hbm":
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), **common,
+                    "mfma_tflops": round(tfs, 2),
+                    "mfma_frac_of_bf16_peak": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), **common,
+                    "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     kernels_us = {g: round(1e3 * brk_ms[g] / max(brk_n[g], 1), 2) for g in B.TIMING_GROUPS
                   if brk_n[g]}
     kernels_share = {g: round(brk_ms[g] / max(sum(brk_ms.values()), 1e-9), 4)

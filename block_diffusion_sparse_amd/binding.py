@@ -18,13 +18,13 @@ EPOCH_GATE_SOFTMAX, EPOCH_GATE_SIGMOID = 0, 1
 EPOCH_DTYPE_F32, EPOCH_DTYPE_BF16 = 0, 1
 EPOCH_ROUTING_EXACT, EPOCH_ROUTING_RESTRICTED = 0, 1
 EPOCH_NUM_COUNTERS = 20
-EPOCH_TIMING_GROUPS = 7
+EPOCH_TIMING_GROUPS = 9
 COUNTERS = ["cold", "hot_update", "hot_skip", "anomaly", "fresh_rows", "pairs", "unmet",
             "forced_rows", "due_rows", "support_size", "u_final", "repair_rounds", "touched",
             "forwards", "reserved14", "restricted", "coverage_fallback", "period_update",
-            "reserved18", "reserved19"]
+            "big_experts", "big_pairs"]
 TIMING_GROUPS = ["router", "plan", "place", "routed_gateup", "routed_down", "shared",
-                 "combine"]
+                 "combine", "routed_gateup_big", "routed_down_big"]
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p

@@ -413,25 +413,34 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
-  hipStream_t big_st = st;
-  if (s.big_routed) {
-    if (hipEventRecord(p->fork_big, st) != hipSuccess ||
-        hipStreamWaitEvent(p->side, p->fork_big, 0) != hipSuccess)
-      return EPOCH_E_HIP;
-    big_st = p->side;
-  }
+  // the big tiles depend on the plan step: forked onto the plan's stream from here
+  if (s.big_routed && (hipEventRecord(p->fork_big, st) != hipSuccess ||
+                       hipStreamWaitEvent(p->side, p->fork_big, 0) != hipSuccess))
+    return EPOCH_E_HIP;
   {
     GroupTimer tm(p, st, 3);
-    e = launch_routed_gateup(s, x, w.w1, w.w3, L, W, st, big_st);
+    e = launch_routed_gateup(s, x, w.w1, w.w3, L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
+  if (s.big_routed) {
+    GroupTimer tm(p, p->side, 7);
+    e = launch_routed_gateup_big(s, x, w.w1, w.w3, L, W, p->side);
+    tm.done();
+    if (e != hipSuccess) return EPOCH_E_HIP;
+  }
   {
     GroupTimer tm(p, st, 4);
-    e = launch_routed_down(s, w.w2, L, W, st, big_st);
+    e = launch_routed_down(s, w.w2, L, W, st);
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
+  if (s.big_routed) {
+    GroupTimer tm(p, p->side, 8);
+    e = launch_routed_down_big(s, w.w2, L, W, p->side);
+    tm.done();
+    if (e != hipSuccess) return EPOCH_E_HIP;
+  }
   if (p->side && (hipEventRecord(p->join, p->side) != hipSuccess ||
                   hipStreamWaitEvent(st, p->join, 0) != hipSuccess))
     return EPOCH_E_HIP;

@@ -130,12 +130,17 @@ hipError_t launch_router(const Shape& s, const void* x, const float* Wg, const f
 hipError_t launch_plan(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                        hipStream_t st);
 hipError_t launch_place(const Shape& s, const LayerState& L, const Scratch& W, hipStream_t st);
-// routed experts: light tiles on st, the compute-bound big tiles (if any) on big_st
+// routed experts: the weight-stream tiles, and (shapes with big_routed) the compute-bound
+// 256-row tiles of experts with many fresh pairs, which the forward runs on another stream
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
-                                const LayerState& L, const Scratch& W, hipStream_t st,
-                                hipStream_t big_st);
+                                const LayerState& L, const Scratch& W, hipStream_t st);
+hipError_t launch_routed_gateup_big(const Shape& s, const void* x, const void* w1,
+                                    const void* w3, const LayerState& L, const Scratch& W,
+                                    hipStream_t st);
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
-                              const Scratch& W, hipStream_t st, hipStream_t big_st);
+                              const Scratch& W, hipStream_t st);
+hipError_t launch_routed_down_big(const Shape& s, const void* w2, const LayerState& L,
+                                  const Scratch& W, hipStream_t st);
 hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const void* sw3,
                          const void* sw2, const Scratch& W, hipStream_t st);
 hipError_t launch_combine(const Shape& s, int iter, const LayerState& L, const Scratch& W,

@@ -127,45 +127,51 @@ __global__ __launch_bounds__(256) void k_down_f32(
 }
 
 hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, const void* w3,
-                                const LayerState& L, const Scratch& W, hipStream_t st,
-                                hipStream_t big_st) {
-  dim3 grid(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols);
-  if (s.bf16) {
+                                const LayerState& L, const Scratch& W, hipStream_t st) {
+  if (s.bf16)
     launch_gemm<true, true>(s.T_max, st, s.H, static_cast<const uint16_t*>(x),
                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), W,
-                            L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I, big_st != st);
-    if (s.big_routed)  // experts with many fresh rows: compute-bound kBigTile x 128 tiles
-      launch((k_gemm_big<true, true, false, kBigTile>),
-                         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, big_st,
-                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
-                         static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b,
-                         W.offs, L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M,
-                         s.H, s.I, LmPartials{});
-  } else
-    launch(k_gateup_f32<true>, grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       static_cast<const float*>(w1), static_cast<const float*>(w3), W.flags,
-                       W.tile_slot, W.tile_row0, W.offs, L.S_list, W.wl_pos,
-                       static_cast<float*>(W.h), s.M, s.H, s.I);
+                            L.S_list, static_cast<uint16_t*>(W.h), s.M, s.I, s.big_routed);
+  else
+    launch(k_gateup_f32<true>, dim3(s.T_max, (s.I + kGateUpCols - 1) / kGateUpCols), dim3(256),
+           0, st, static_cast<const float*>(x), static_cast<const float*>(w1),
+           static_cast<const float*>(w3), W.flags, W.tile_slot, W.tile_row0, W.offs, L.S_list,
+           W.wl_pos, static_cast<float*>(W.h), s.M, s.H, s.I);
+  return hipGetLastError();
+}
+
+hipError_t launch_routed_gateup_big(const Shape& s, const void* x, const void* w1,
+                                    const void* w3, const LayerState& L, const Scratch& W,
+                                    hipStream_t st) {
+  // experts with many fresh rows: compute-bound kBigTile x 128 tiles
+  launch((k_gemm_big<true, true, false, kBigTile>),
+         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
+         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
+         static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b, W.offs,
+         L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M, s.H, s.I, LmPartials{});
   return hipGetLastError();
 }
 
 hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& L,
-                              const Scratch& W, hipStream_t st, hipStream_t big_st) {
-  if (s.bf16) {
+                              const Scratch& W, hipStream_t st) {
+  if (s.bf16)
     launch_gemm<false, true>(s.T_max, st, s.I, static_cast<const uint16_t*>(W.h),
                              static_cast<const uint16_t*>(w2), nullptr, W, L.S_list,
-                             static_cast<uint16_t*>(W.y_pair), s.M, s.H, big_st != st);
-    if (s.big_routed)
-      launch((k_gemm_big<false, true, false, kBigTile>),
-                         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0,
-                         big_st, static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2),
-                         nullptr, W.flags, W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list,
-                         W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H,
-                         LmPartials{});
-  } else
-    launch(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st, static_cast<const float*>(W.h),
-                       static_cast<const float*>(w2), W.flags, W.tile_slot, W.tile_row0, W.offs,
-                       L.S_list, W.wl_w, static_cast<float*>(W.y_pair), s.M, s.H, s.I);
+                             static_cast<uint16_t*>(W.y_pair), s.M, s.H, s.big_routed);
+  else
+    launch(k_down_f32<true>, dim3(s.T_max, (s.H + kDownCols - 1) / kDownCols), dim3(256), 0, st,
+           static_cast<const float*>(W.h), static_cast<const float*>(w2), W.flags, W.tile_slot,
+           W.tile_row0, W.offs, L.S_list, W.wl_w, static_cast<float*>(W.y_pair), s.M, s.H, s.I);
+  return hipGetLastError();
+}
+
+hipError_t launch_routed_down_big(const Shape& s, const void* w2, const LayerState& L,
+                                  const Scratch& W, hipStream_t st) {
+  launch((k_gemm_big<false, true, false, kBigTile>),
+         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0, st,
+         static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2), nullptr, W.flags,
+         W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list, W.wl_pos, W.wl_w,
+         static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H, LmPartials{});
   return hipGetLastError();
 }
 

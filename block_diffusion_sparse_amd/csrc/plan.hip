@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   // chunk bases and fresh-list offsets of the fused placement, kept in LDS: [chunk][expert]
   __shared__ int32_t cbl[FUSED_PLACE ? kFusedPlaceMaxChunks * kFusedPlaceMaxExperts : 1];
   __shared__ int32_t foffl[FUSED_PLACE ? kFusedPlaceMaxChunks : 1];
-  __shared__ int32_t msum[6][kPlanWaves];
+  __shared__ int32_t msum[8][kPlanWaves];
   const int tid = threadIdx.x;
   const int E = s.E, nch = s.n_chunks;
   // per-expert totals and chunk bases: Gp groups of Epad threads, adjacent threads on adjacent
@@ -682,6 +682,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   //   [2], [3] small and big tile counts by slot              -> tile tables, T, Tb
   //   [4] fresh positions by chunk (first kPlanThreads chunks) -> chunk_foff
   //   [5] touched experts (a count only)
+  //   [6], [7] experts on big tiles and their pairs (counts only)
   // offs[j] equals eoffs[S_list[j]]: every expert with pairs has a slot (the router flags a
   // routed expert outside the support, and such a forward rebuilds the slots), so the experts
   // between two slots contribute nothing.  An expert with at least kBigRows pairs goes to the
@@ -698,8 +699,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
       my_tiles = (slot_tot + kTileRows - 1) / kTileRows;
   }
   const int nf0 = tid < nch ? (anomaly ? min(kChunk, s.M - tid * kChunk) : pre_cf) : 0;
-  int sc[6] = {my_tot, slot_tot, my_tiles, my_big, nf0, my_tot > 0 ? 1 : 0};
-  int stot[6];
+  int sc[8] = {my_tot, slot_tot, my_tiles, my_big, nf0, my_tot > 0 ? 1 : 0, my_big > 0 ? 1 : 0,
+               my_big > 0 ? slot_tot : 0};
+  int stot[8];
   block_multi_scan(sc, msum, stot);
   const int P = stot[0], T = stot[2], Tb = stot[3], touched = stot[5];
   sh.scan[tid] = sc[0] - my_tot;  // read by the fused placement after the barrier below
@@ -750,6 +752,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     counter_add(L, EPOCH_CNT_FRESH_ROWS, nfresh);
     counter_add(L, EPOCH_CNT_PAIRS, P);
     counter_add(L, EPOCH_CNT_TOUCHED, touched);
+    counter_add(L, EPOCH_CNT_BIG_EXPERTS, stot[6]);
+    counter_add(L, EPOCH_CNT_BIG_PAIRS, stot[7]);
     counter_add(L, EPOCH_CNT_FORWARDS, 1);
     if (anomaly) counter_add(L, EPOCH_CNT_ANOMALY, 1);
     // every thread read MISS and ANOMALY before the barriers above

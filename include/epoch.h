@@ -101,6 +101,8 @@ enum {
   EPOCH_CNT_RESTRICTED = 15,   /* forwards routed inside the support (restricted mode) */
   EPOCH_CNT_COVERAGE_FALLBACK = 16, /* restricted-mode rebuilds forced by the coverage check */
   EPOCH_CNT_PERIOD_UPDATE = 17,/* restricted-mode rebuilds forced by atlas_period */
+  EPOCH_CNT_BIG_EXPERTS = 18,  /* sum over forwards of experts run on 256-row compute-bound tiles */
+  EPOCH_CNT_BIG_PAIRS = 19,    /* sum over forwards of those experts' fresh pairs */
   EPOCH_NUM_COUNTERS = 20
 };
 
@@ -258,9 +260,11 @@ const char* epoch_status_string(int32_t status);
 /*
  * Kernel timing for measurement.  `groups` is a bitmask of kernel groups (bit g = group g;
  * -1 = all): 0 router + top-k + fresh test, 1 plan (support check / build, worklist scans),
- * 2 worklist placement, 3 routed gate/up,
- * 4 routed down, 5 shared expert, 6 combine.  While set, the kernels of every selected group
- * of each forward carry a pair of HIP events on the forward's stream, stamped by the dispatches
+ * 2 worklist placement, 3 routed gate/up (weight-stream tiles), 4 routed down (weight-stream
+ * tiles), 5 shared expert, 6 combine, 7 routed gate/up on 256-row compute-bound tiles, 8 routed
+ * down on those tiles (7 and 8 only for shapes with big tiles).  While set, the kernels of every
+ * selected group of each forward carry a pair of HIP events on the stream the group runs on
+ * (the forward's stream, or the plan's own stream for 5, 7 and 8), stamped by the dispatches
  * themselves: the start of the group's first kernel and the end of its last (events come from
  * a process-wide pool, so a measured region reuses events created earlier; a timed dispatch
  * still waits a few microseconds longer for its neighbours, so a measurement that must not
@@ -269,7 +273,7 @@ const char* epoch_status_string(int32_t status);
  * writes the sums for up to n groups and returns the events to the pool.  Setting the mask
  * clears the sums.  0 = off (the default).
  */
-enum { EPOCH_TIMING_GROUPS = 7 };
+enum { EPOCH_TIMING_GROUPS = 9 };
 int32_t epoch_plan_set_timing(epoch_plan* plan, int32_t groups);
 int32_t epoch_plan_timing(epoch_plan* plan, float* ms, int64_t* launches, int32_t n);
 

@@ -70,6 +70,8 @@ class BlockReport:
     paths: list = field(default_factory=list)
     stable_rows_checked: int = 0
     rows_checked: int = 0
+    big_experts: int = 0  # experts the worklist sends to 256-row compute-bound tiles, summed
+    big_pairs: int = 0    # and their fresh pairs
 
 
 def make_plan(w: synth.Workload, Wdev: list, n_layers: int) -> EpochPlan:
@@ -137,6 +139,12 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
     assert np.array_equal(g["wl_k"][:P], wl["wl_k"]), f"{tag}: worklist k differ"
     np.testing.assert_allclose(g["wl_w"][:P], wl["wl_w"], rtol=1e-6, atol=1e-12, err_msg=tag)
     assert np.array_equal(g["offs"][:nS + 1], wl["offs"]), f"{tag}: offsets differ"
+    # bf16 shapes whose iterations can hold >= 32768 pairs run experts with >= 768 fresh pairs
+    # on the compute-bound tiles
+    if w.act == "bf16" and w.M * w.top_k >= 32768:
+        per_slot = np.diff(wl["offs"])
+        rep.big_experts += int((per_slot >= 768).sum())
+        rep.big_pairs += int(per_slot[per_slot >= 768].sum())
     assert np.array_equal(g["inv"], wl["inv"]), f"{tag}: inverse map differs"
     # outputs on the oracle's evaluated rows
     tol = TOL[w.act]
@@ -226,6 +234,10 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
         assert c["restricted"] == oc["restricted"]
         assert c["coverage_fallback"] == oc["coverage_fallback"]
         assert c["period_update"] == oc["period_update"]
+    if check and len(layers) == 1:
+        c = plan.counters(0)
+        assert c["big_experts"] == rep.big_experts and c["big_pairs"] == rep.big_pairs, (
+            c["big_experts"], rep.big_experts, c["big_pairs"], rep.big_pairs)
     rep.counters = [plan.counters(li) for li in range(len(layers))]
     plan.close()
     return rep

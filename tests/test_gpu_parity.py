@@ -133,3 +133,33 @@ def test_big_tiles_every_row(frac, R):
     h.log(f"[big tiles] M={w.M} f={frac} R={R} load={load.tolist()}")
     rep = h.run_block(w, weights=[W0], bias_override=bias)
     assert rep.iters == w.iters
+
+
+def test_kernel_timing_on_both_streams():
+    """Kernel timing with every group on, at a shape with big tiles and a shared expert: the
+    shared expert and the big tiles run on the plan's own stream and are timed there, and
+    every group reads back one duration per forward."""
+    h = H()
+    w = synth.workload(5, hidden=192, n_experts=12, top_k=2, inter=128, shared_inter=192,
+                       batch=400, block=41, iters=3, staleness_R=1, forced_fraction=1.0,
+                       zipf=None, redraw_every=0)
+    W0 = synth.layer_weights(w, 0)
+    W0["router_b"] = (-0.3 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
+    plan = h.make_plan(w, [h.upload_weights(W0)], 1)
+    D = synth.decoded_masks(w)
+    X = h.to_dev(synth.hidden_states(w, 0, D, iters=w.iters))
+    Dd = h.to_dev(D)
+    plan.set_timing(-1)
+    for it in range(w.iters):
+        y = torch.empty_like(X[it])
+        plan.forward(0, X[it], Dd[it], None, y, None)
+        plan.commit(0)
+    torch.cuda.synchronize()
+    t = plan.timing()
+    c = plan.counters(0)
+    plan.close()
+    from block_diffusion_sparse_amd import binding as B
+    assert list(t) == B.TIMING_GROUPS
+    for g, (ms, n) in t.items():
+        assert n == w.iters and ms > 0.0, (g, ms, n)
+    assert c["big_experts"] > 0 and c["big_pairs"] >= 768 * c["big_experts"]
