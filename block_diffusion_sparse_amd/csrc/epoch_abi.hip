@@ -107,7 +107,7 @@ Shape make_shape(const epoch_desc* d) {
   s.ksplit /= s.router_kw;  // waves per workgroup
   const long long P_max = (long long)s.M * s.K;
   s.T_max = (int)((P_max + kTileRows - 1) / kTileRows) + s.E;
-  s.T_dense = (s.M + kTileRows - 1) / kTileRows;
+  s.T_dense = (s.M + kDenseTileRows - 1) / kDenseTileRows;
   // experts with at least kBigRows fresh pairs take compute-bound 128-row tiles; enabled only
   // for shapes whose iterations can hold far more pairs than the weight-stream tiles cover
   // well (with fewer pairs per iteration the extra launch costs more than it saves)

@@ -31,7 +31,12 @@ constexpr int kWave = 64;
 constexpr int kChunk = 64;        // positions per compaction chunk (one wave)
 constexpr int kMaxKext = 32;      // candidates per position the wave top-k keeps
 constexpr int kMaxExperts = 1024;
-constexpr int kTileRows = 64;     // rows per grouped-GEMM tile
+// Routed weight-stream tiles: kTileRows rows, or kTileRowsTall when the plan step finds that
+// taller tiles need fewer of them (experts with more than kTileRows fresh pairs stream their
+// weights once per tile); FLAG_TILE_TALL tells the expert kernel which.
+constexpr int kTileRows = 64;
+constexpr int kTileRowsTall = 128;
+constexpr int kDenseTileRows = 64;  // rows per shared-expert weight-stream tile
 constexpr int kBigTile = 256;     // rows per compute-bound routed tile
 constexpr int kBigRows = 768;     // experts with at least this many fresh rows use big tiles
 constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
@@ -45,9 +50,10 @@ constexpr int kDownCols = 64;     // output columns per down workgroup
 // written by the plan step for the placement.
 enum { FLAG_MISS = 0, FLAG_ANOMALY = 1, FLAG_NFRESH = 2, FLAG_NPAIRS = 3, FLAG_NTILES = 4,
        FLAG_NTILES_BIG = 5, FLAG_FRESH_ALL = 6, FLAG_UNDER = 7, FLAG_ROUTE_R = 8,
-       FLAG_SHORT = 9, FLAG_WORDS = 16 };
+       FLAG_SHORT = 9, FLAG_TILE_TALL = 10, FLAG_WORDS = 16 };
 // SHORT (restricted mode): some position has fewer than K selectable support experts; set by
 // the router, cleared by the plan step.
+// TILE_TALL (written by the plan step): the routed tile table holds kTileRowsTall-row tiles.
 constexpr int kMaxGroups = 64;
 
 // Device-side view of one layer's persistent state.

@@ -66,7 +66,7 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 }
 
 // Weight-stream grouped GEMM of both projections of the SwiGLU expert (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation), for tiles of up to 64 rows of one expert: the rows (fresh pairs, gathered
+// fp32 accumulation), for tiles of up to BM rows of one expert: the rows (fresh pairs, gathered
 // through the worklist for routed gate/up; positions in order for the shared expert) are few,
 // so the expert's weights, read once per tile, dominate the traffic.  A work item is one tile
 // against 32 WAVES weight rows (a column block):
@@ -74,16 +74,23 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 //            holds those rows of W1 and of W3; epilogue h = bf16(silu(g) * u);
 //   down:    wave w owns output columns 32 w .. 32 w + 31 of the block's 32 WAVES rows of W2;
 //            epilogue y = bf16(w_p * acc) (routed) or bf16(acc) (shared expert).
+// Every wave multiplies all rows of the tile; 16-row blocks past the tile's last row are
+// skipped (no fragment reads, no MFMAs), so a short tile costs only its weight stream.
 // K runs in chunks of 64 bf16, so a row of a chunk is one 128-byte line and one copy
 // instruction (global_load_lds_dwordx4, lane l's 16 bytes landing at the wave's LDS base +
 // 16 l) moves eight whole lines.  Every wave copies its own 32 weight rows with the
 // non-temporal policy (whole lines streamed that way sustain a higher HBM rate) and its share
 // of the activation rows with the cached one (the tile's other column blocks read them again).
 // LDS rows of 128 bytes hold k-segment slot ^ ((row >> 1) & 7) in 16-byte slot `slot`, so the
-// 16 rows of an MFMA fragment read fall on distinct banks.  NB chunk buffers, NB - 2 chunks in
-// flight while a chunk is multiplied, fragments double-buffered in registers; the
-// synchronisation is that of k_gemm_big below (explicit vmcnt / lgkmcnt waits, raw barriers,
-// inline fragment reads).
+// 16 rows of an MFMA fragment read fall on distinct banks.
+//
+// Synchronisation (NB chunk buffers): step q waits for its own copies of chunk q (vmcnt; the
+// NB - 2 chunks after it may stay in flight), meets the barrier (every wave's copies of chunk q
+// have landed, every wave has finished reading chunk q - 1), copies chunk q + NB - 1 into the
+// buffer of chunk q - 1, then reads chunk q's fragments (inline ds_read_b128, with an explicit
+// lgkmcnt wait that names them, since the compiler cannot tell chunk buffers apart and would
+// otherwise wait for every copy in flight) and multiplies.  NB - 1 chunks are in flight during
+// the MFMAs.
 //
 // Persistent workgroups: the grid (a multiple of 8, about one workgroup per CU slot) walks the
 // work items i = blockIdx.x + k gridDim.x, and the chunks of consecutive items form one
@@ -95,24 +102,26 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // memory (tile table, offsets, expert id, gathered row ids, routing weights) is read with
 // uniform addresses, i.e. scalar loads, and spread to the lanes by selects: a vector load here
 // would make the wait for it also wait for every copy in flight.
-template <bool GATEUP, bool ROUTED, int NB, int WAVES = 4>
-__global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+// The kernel body for tiles of BM rows; As / Bs: NB chunk buffers of BM x 64 and 32 WAVES x 64
+// bf16 in LDS.
+template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BM>
+__device__ __forceinline__ void expert_stream_body(
+    uint16_t* As, uint16_t* Bs, const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
-  static_assert(NB >= 3, "a chunk buffer is refilled two steps after its fragments were read");
+  static_assert(NB >= 3, "a chunk buffer is refilled one step after its fragments were read");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
-  constexpr int BM = 64, KC = 64, WR = 32 * WAVES;
+  static_assert(BM == 64 || BM == 128, "tiles of 64 or 128 rows");
+  constexpr int KC = 64, WR = 32 * WAVES;
   constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // output columns per item
   constexpr int MB = BM / 16;
   constexpr int NAW = BM / 8 / WAVES;     // activation copies per wave and chunk (8 rows each)
   constexpr int NBW = 4;                  // weight copies per wave and chunk (its 32 rows)
   constexpr int CPW = NAW + NBW;
-  __shared__ __attribute__((aligned(16))) uint16_t As[NB][BM * KC];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][WR * KC];
+  constexpr int ABUF = BM * KC, BBUF = WR * KC;  // elements per chunk buffer
   const int n_cb = (Ndim + CBW - 1) / CBW;
   const int ntiles = ROUTED ? flags[FLAG_NTILES] : (M + BM - 1) / BM;
   // this workgroup's items: position (blockIdx.x / 8) + k G8 along the tile-major order of
@@ -154,8 +163,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
     it.rot = pos % nch;
     return it;
   };
-
-  auto item_wact = [&](int k) { return ((pos0 + k * G8) % n_cb) * CBW + (GATEUP ? 16 : 32) * wave < Ndim; };
 
   // issue side: the item whose chunks are being copied, its copy sources, the next chunk
   const uint16_t* asrc[NAW];
@@ -210,10 +217,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
     const int cc = ic + irot < nch ? ic + irot : ic + irot - nch;
 #pragma unroll
     for (int j = 0; j < NAW; ++j)
-      copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf][8 * (NAW * wave + j) * KC]);
+      copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf * ABUF + 8 * (NAW * wave + j) * KC]);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
-      copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf][(32 * wave + 8 * j) * KC]);
+      copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
     ++ic;
   };
 
@@ -223,41 +230,52 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   // (weights)
   const int key = (r >> 1) & 7;
   const int off0 = (g ^ key) * 8, off1 = ((4 + g) ^ key) * 8;
-  u32x4 fa[2][2][MB], fb[2][2][2];
-  auto read_frags = [&](int buf, int set) {
-    const uint32_t a0 = (uint32_t)(uintptr_t)&As[buf][r * KC + off0];
-    const uint32_t a1 = (uint32_t)(uintptr_t)&As[buf][r * KC + off1];
-    const uint32_t b0 = (uint32_t)(uintptr_t)&Bs[buf][(32 * wave + r) * KC + off0];
-    const uint32_t b1 = (uint32_t)(uintptr_t)&Bs[buf][(32 * wave + r) * KC + off1];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[set][0][m]) : "v"(a0), "i"(m * 16 * KC * 2));
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[set][1][m]) : "v"(a1), "i"(m * 16 * KC * 2));
-    }
+  u32x4 fa[2][MB], fb[2][2];
+  // the fragments of chunk buffer buf for the first mlive row blocks, complete on return
+  auto read_frags = [&](int buf, int mlive) {
+    const uint32_t a0 = (uint32_t)(uintptr_t)&As[buf * ABUF + r * KC + off0];
+    const uint32_t a1 = (uint32_t)(uintptr_t)&As[buf * ABUF + r * KC + off1];
+    const uint32_t b0 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off0];
+    const uint32_t b1 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off1];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[set][0][n]) : "v"(b0), "i"(n * 16 * KC * 2));
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[set][1][n]) : "v"(b1), "i"(n * 16 * KC * 2));
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[0][n]) : "v"(b0), "i"(n * 16 * KC * 2));
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[1][n]) : "v"(b1), "i"(n * 16 * KC * 2));
     }
-  };
-  auto frags_ready = [&](int set) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(fa[set][0][0]), "+v"(fa[set][0][1]), "+v"(fa[set][0][2]), "+v"(fa[set][0][3]),
-                   "+v"(fa[set][1][0]), "+v"(fa[set][1][1]), "+v"(fa[set][1][2]), "+v"(fa[set][1][3]),
-                   "+v"(fb[set][0][0]), "+v"(fb[set][0][1]), "+v"(fb[set][1][0]), "+v"(fb[set][1][1]));
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m < mlive) {
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[0][m]) : "v"(a0), "i"(m * 16 * KC * 2));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[1][m]) : "v"(a1), "i"(m * 16 * KC * 2));
+      }
+    }
+    if constexpr (MB == 8)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]),
+                     "+v"(fa[0][4]), "+v"(fa[0][5]), "+v"(fa[0][6]), "+v"(fa[0][7]),
+                     "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]),
+                     "+v"(fa[1][4]), "+v"(fa[1][5]), "+v"(fa[1][6]), "+v"(fa[1][7]),
+                     "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[1][0]), "+v"(fb[1][1]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]),
+                     "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]),
+                     "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[1][0]), "+v"(fb[1][1]));
   };
   // weights as the left operand: lane (r, g) of block m ends up with row 16 m + r and the four
   // consecutive columns 4 g .. 4 g + 3 (one 8-byte store in the epilogue)
-  auto mma = [&](int set) {
+  auto mma = [&](int mlive) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const bf16x8 f = __builtin_bit_cast(bf16x8, fa[set][s][m]);
-        c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[set][s][0]), f,
-                                                         c0[m], 0, 0, 0);
-        c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[set][s][1]), f,
-                                                         c1[m], 0, 0, 0);
+        if (m < mlive) {
+          const bf16x8 f = __builtin_bit_cast(bf16x8, fa[s][m]);
+          c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[s][0]),
+                                                           f, c0[m], 0, 0, 0);
+          c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[s][1]),
+                                                           f, c1[m], 0, 0, 0);
+        }
       }
   };
   auto pack4 = [](const float* v) {
@@ -267,6 +285,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   auto epilogue = [&](const Item& it) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
+      if (it.row0 + 16 * m >= it.row_end) continue;  // uniform: a block past the tile's rows
       float sc = 1.0f;
       if (ROUTED && !GATEUP) {  // routing weights of rows 16 m .. 16 m + 15
 #pragma unroll
@@ -294,54 +313,74 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   };
 
   static_assert(CPW * (NB - 2) < 64, "vmcnt range");
-  constexpr int kInFlight = CPW * (NB - 2);  // copies after chunk q + 1's
+  constexpr int kAfter = CPW * (NB - 2);  // copies of the chunks after chunk q
+  // prologue: chunks 0 .. NB - 2 of the stream in flight
   sources(item(0));
-  // prologue: chunks 0 .. NB - 2 of the stream in flight, chunk 0 landed, its fragments read
 #pragma unroll
   for (int x = 0; x < NB - 1; ++x)
     if (x < Q) issue_next(x);
-  if (Q >= NB - 1)
-    wait_vm_lds<kInFlight>();
-  else
-    wait_vm_lds<0>();
-  __builtin_amdgcn_s_barrier();
-  read_frags(0, 0);
-  // step q: copy chunk q + NB - 1 into the buffer of chunk q - 1 (every wave finished reading
-  // it before the previous barrier), wait for chunk q + 1, barrier, read its fragments,
-  // multiply chunk q; after an item's last chunk, store its outputs
   int ck = 0, cc = 0;  // item and chunk of the chunk being multiplied
-  bool cwact = item_wact(0);
-  for (int q = 0; q < Q; q += 2) {
+  Item cur = item(0);
+  int mlive = (cur.row_end - cur.row0 + 15) >> 4;
+  for (int q = 0; q < Q; ++q) {
+    // every chunk up to q + NB - 2 has been issued: while all NB - 2 after q exist, they may
+    // stay in flight, else wait for everything
+    if (q + NB - 2 < Q)
+      wait_vm_lds<kAfter>();
+    else
+      wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
+    if (q + NB - 1 < Q) issue_next((q + NB - 1) % NB);
+    if (cc == 0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int qq = q + u;
-      if (qq < Q) {
-        if (qq + NB - 1 < Q) {
-          issue_next((qq + NB - 1) % NB);
-          wait_vm_lds<kInFlight>();
-        } else {
-          wait_vm_lds<0>();
-        }
-        __builtin_amdgcn_s_barrier();
-        frags_ready(u & 1);
-        if (qq + 1 < Q) read_frags((qq + 1) % NB, (u + 1) & 1);
-        if (cc == 0) {
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            c0[m] = f32x4{0, 0, 0, 0};
-            c1[m] = f32x4{0, 0, 0, 0};
-          }
-        }
-        if (cwact) mma(u & 1);
-        if (++cc == nch) {
-          const Item it = item(ck);
-          if (it.wact) epilogue(it);
-          ++ck;
-          cc = 0;
-          cwact = item_wact(ck);
-        }
+      for (int m = 0; m < MB; ++m) {
+        c0[m] = f32x4{0, 0, 0, 0};
+        c1[m] = f32x4{0, 0, 0, 0};
       }
     }
+    if (cur.wact) {
+      read_frags(q % NB, mlive);
+      mma(mlive);
+    }
+    if (++cc == nch) {
+      if (cur.wact) epilogue(cur);
+      ++ck;
+      cc = 0;
+      if (ck < nitems) {
+        cur = item(ck);
+        mlive = (cur.row_end - cur.row0 + 15) >> 4;
+      }
+    }
+  }
+}
+
+// Routed tiles: the plan step's tile table holds kTileRows- or kTileRowsTall-row tiles
+// (FLAG_TILE_TALL; never tall for shapes with big tiles); shared-expert tiles: kDenseTileRows
+// rows.  BMAX = the tallest tile the instance handles, which sizes its LDS.
+template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BMAX>
+__global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
+    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
+    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[NB * BMAX * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NB * 32 * WAVES * 64];
+  if constexpr (ROUTED && BMAX == kTileRowsTall) {
+    if (flags[FLAG_TILE_TALL]) {
+      expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRowsTall>(
+          As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M,
+          Kdim, Ndim);
+      return;
+    }
+    expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRows>(
+        As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M, Kdim,
+        Ndim);
+  } else {
+    expert_stream_body<GATEUP, ROUTED, NB, WAVES, BMAX>(
+        As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M, Kdim,
+        Ndim);
   }
 }
 

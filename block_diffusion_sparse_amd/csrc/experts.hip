@@ -13,11 +13,12 @@
 
 namespace epoch {
 
-// Weight-stream tiles (k_expert_stream, kTileRows = 64 rows): three chunk buffers, so two
-// workgroups of four waves or one of eight fit a CU's LDS.  Routed experts run eight waves
-// (128 gate/up or 256 down columns share each staged activation chunk); the shared expert,
-// only used here below kBigTileMinRows positions, runs four, which doubles its work items.
-// Both measured best at the benchmark shapes.
+// Weight-stream tiles (k_expert_stream), three chunk buffers.  Routed experts: tiles of 64 rows
+// or, when the plan step finds them fewer, 128 (an expert with 65..128 fresh pairs then streams
+// its weights once, not twice), eight waves (128 gate/up or 256 down columns share each staged
+// activation chunk), one workgroup per CU.  The shared expert, only used here below
+// kBigTileMinRows positions: 64-row tiles and four waves, two workgroups per CU, which gives it
+// four times the work items.  Both measured best at the benchmark shapes.
 constexpr int kStreamBuffers = 3;
 constexpr int kLdsPerCu = 160 * 1024;
 // dense (shared-expert) layers of at least this many positions use the compute-bound
@@ -37,18 +38,18 @@ static int stream_slots(int lds, int per_cu) {
   return ((n_cu * (fit < per_cu ? fit : per_cu)) / 8) * 8;
 }
 
-template <bool GATEUP, bool ROUTED, int WAVES>
+template <bool GATEUP, bool ROUTED, int WAVES, int BMAX>
 static void launch_gemm_w(int tiles, int per_cu, hipStream_t st, int Kdim, const uint16_t* A,
                           const uint16_t* B0, const uint16_t* B1, const Scratch& W,
                           const int32_t* S_list, uint16_t* out, int M, int Ndim) {
   constexpr int cbw = (GATEUP ? 16 : 32) * WAVES;  // output columns per work item
-  constexpr int lds = kStreamBuffers * (64 * 64 + 32 * WAVES * 64) * 2;
+  constexpr int lds = kStreamBuffers * (BMAX * 64 + 32 * WAVES * 64) * 2;
   const int n_cb = (Ndim + cbw - 1) / cbw;
   // persistent grid: as many workgroups as fit at once, never more than the work items (tile
   // slots rounded up to a multiple of 8, times the column blocks)
   const int slots = stream_slots(lds, per_cu);
   const int items = ((tiles + 7) / 8) * 8 * n_cb;
-  launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES>),
+  launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES, BMAX>),
          dim3(items < slots ? items : slots), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
          W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
 }
@@ -61,12 +62,15 @@ template <bool GATEUP, bool ROUTED>
 static void launch_gemm(int tiles, hipStream_t st, int Kdim, const uint16_t* A, const uint16_t* B0,
                         const uint16_t* B1, const Scratch& W, const int32_t* S_list,
                         uint16_t* out, int M, int Ndim, bool beside_big = false) {
-  if (!ROUTED)
-    launch_gemm_w<GATEUP, ROUTED, 4>(tiles, 2, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
-  else if (beside_big)
-    launch_gemm_w<GATEUP, ROUTED, 4>(tiles, 1, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
+  if constexpr (!ROUTED)
+    launch_gemm_w<GATEUP, ROUTED, 4, kDenseTileRows>(tiles, 2, st, Kdim, A, B0, B1, W, S_list,
+                                                     out, M, Ndim);
+  else if (beside_big)  // short tiles only (the plan step never makes tall ones here)
+    launch_gemm_w<GATEUP, ROUTED, 4, kTileRows>(tiles, 1, st, Kdim, A, B0, B1, W, S_list, out,
+                                                M, Ndim);
   else
-    launch_gemm_w<GATEUP, ROUTED, 8>(tiles, 1, st, Kdim, A, B0, B1, W, S_list, out, M, Ndim);
+    launch_gemm_w<GATEUP, ROUTED, 8, kTileRowsTall>(tiles, 1, st, Kdim, A, B0, B1, W, S_list,
+                                                    out, M, Ndim);
 }
 
 // ---------------------------------------------------------------------------- fp32 variant
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(256) void k_gateup_f32(
     const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ S_list, const int32_t* __restrict__ wl_pos,
     float* __restrict__ h, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, ROUTED ? flags[FLAG_NTILES] : 0,
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, ROUTED ? kTileRows : kDenseTileRows,
+                                ROUTED ? flags[FLAG_NTILES] : 0,
                                 tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;
@@ -108,7 +113,8 @@ __global__ __launch_bounds__(256) void k_down_f32(
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const float* __restrict__ wl_w, float* __restrict__ out, int M, int H, int I) {
-  const TileRows tr = tile_rows(ROUTED, blockIdx.x, kTileRows, ROUTED ? flags[FLAG_NTILES] : 0,
+  const TileRows tr = tile_rows(ROUTED, blockIdx.x, ROUTED ? kTileRows : kDenseTileRows,
+                                ROUTED ? flags[FLAG_NTILES] : 0,
                                 tile_slot, tile_row0, offs, M);
   if (!tr.active) return;
   const int e = ROUTED ? S_list[tr.slot] : 0;

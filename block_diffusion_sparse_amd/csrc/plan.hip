@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   // chunk bases and fresh-list offsets of the fused placement, kept in LDS: [chunk][expert]
   __shared__ int32_t cbl[FUSED_PLACE ? kFusedPlaceMaxChunks * kFusedPlaceMaxExperts : 1];
   __shared__ int32_t foffl[FUSED_PLACE ? kFusedPlaceMaxChunks : 1];
-  __shared__ int32_t msum[8][kPlanWaves];
+  __shared__ int32_t msum[9][kPlanWaves];
   const int tid = threadIdx.x;
   const int E = s.E, nch = s.n_chunks;
   // per-expert totals and chunk bases: Gp groups of Epad threads, adjacent threads on adjacent
@@ -683,6 +683,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   //   [4] fresh positions by chunk (first kPlanThreads chunks) -> chunk_foff
   //   [5] touched experts (a count only)
   //   [6], [7] experts on big tiles and their pairs (counts only)
+  //   [8] tall tile counts by slot                             -> the tall tile table
   // offs[j] equals eoffs[S_list[j]]: every expert with pairs has a slot (the router flags a
   // routed expert outside the support, and such a forward rebuilds the slots), so the experts
   // between two slots contribute nothing.  An expert with at least kBigRows pairs goes to the
@@ -690,20 +691,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
   const bool slots_new = (sp & 2) != 0;
   const int nS = slots_new ? sh.size : pre_nS;
   const int my_tot = tid < E ? tot[tid] : 0;
-  int slot_tot = 0, my_tiles = 0, my_big = 0;
+  int slot_tot = 0, my_tiles = 0, my_tall = 0, my_big = 0;
   if (tid < nS) {
     slot_tot = tot[slots_new ? sh.slist[tid] : pre_ex];
-    if (s.big_routed && slot_tot >= kBigRows)
+    if (s.big_routed && slot_tot >= kBigRows) {
       my_big = (slot_tot + kBigTile - 1) / kBigTile;
-    else
+    } else {
       my_tiles = (slot_tot + kTileRows - 1) / kTileRows;
+      my_tall = (slot_tot + kTileRowsTall - 1) / kTileRowsTall;
+    }
   }
   const int nf0 = tid < nch ? (anomaly ? min(kChunk, s.M - tid * kChunk) : pre_cf) : 0;
-  int sc[8] = {my_tot, slot_tot, my_tiles, my_big, nf0, my_tot > 0 ? 1 : 0, my_big > 0 ? 1 : 0,
-               my_big > 0 ? slot_tot : 0};
-  int stot[8];
+  int sc[9] = {my_tot, slot_tot, my_tiles, my_big, nf0, my_tot > 0 ? 1 : 0, my_big > 0 ? 1 : 0,
+               my_big > 0 ? slot_tot : 0, my_tall};
+  int stot[9];
   block_multi_scan(sc, msum, stot);
-  const int P = stot[0], T = stot[2], Tb = stot[3], touched = stot[5];
+  // tall tiles when they are fewer: bf16 shapes without big tiles (the weight-stream kernel
+  // beside the big tiles keeps short tiles, so that its workgroups fit beside theirs)
+  const bool tall = s.bf16 && !s.big_routed && stot[8] < stot[2];
+  const int P = stot[0], T = tall ? stot[8] : stot[2], Tb = stot[3], touched = stot[5];
+  const int tile_rows_now = tall ? kTileRowsTall : kTileRows;
+  if (tall) {
+    sc[2] = sc[8];
+    my_tiles = my_tall;
+  }
   sh.scan[tid] = sc[0] - my_tot;  // read by the fused placement after the barrier below
   if (tid < E) W.eoffs[tid] = sc[0] - my_tot;
   if (tid == 0) {
@@ -716,7 +727,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     const int t0 = sc[2] - my_tiles;
     for (int i = 0; i < my_tiles; ++i) {
       W.tile_slot[t0 + i] = tid;
-      W.tile_row0[t0 + i] = my_off + i * kTileRows;
+      W.tile_row0[t0 + i] = my_off + i * tile_rows_now;
     }
     const int b0 = sc[3] - my_big;
     for (int i = 0; i < my_big; ++i) {
@@ -749,6 +760,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Shape s, int iter, LayerS
     W.flags[FLAG_NPAIRS] = P;
     W.flags[FLAG_NTILES] = T;
     W.flags[FLAG_NTILES_BIG] = Tb;
+    W.flags[FLAG_TILE_TALL] = tall ? 1 : 0;
     counter_add(L, EPOCH_CNT_FRESH_ROWS, nfresh);
     counter_add(L, EPOCH_CNT_PAIRS, P);
     counter_add(L, EPOCH_CNT_TOUCHED, touched);

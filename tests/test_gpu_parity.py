@@ -163,3 +163,29 @@ def test_kernel_timing_on_both_streams():
     for g, (ms, n) in t.items():
         assert n == w.iters and ms > 0.0, (g, ms, n)
     assert c["big_experts"] > 0 and c["big_pairs"] >= 768 * c["big_experts"]
+
+
+@pytest.mark.parametrize("frac,R", [(1.0, 1), (0.5, 3)])
+def test_tall_tiles_every_row(frac, R):
+    """bf16 shapes without big tiles take 128-row routed tiles when that needs fewer tiles than
+    64-row ones (an expert with more than 64 fresh pairs): the skewed bias gives experts with
+    several tall tiles (ragged last tile), experts with one short tile, and iterations where
+    the fresh fraction leaves every expert at 64 pairs or fewer (short tiles again); H = 192
+    leaves waves without columns in the down projection.  Every row is compared."""
+    h = H()
+    w = synth.workload(5, hidden=192, n_experts=12, top_k=2, inter=128, shared_inter=128,
+                       batch=20, block=33, iters=4, staleness_R=R, forced_fraction=frac,
+                       zipf=None, redraw_every=0)
+    assert w.M * w.top_k < 32768
+    bias = (-0.3 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
+    W0 = synth.layer_weights(w, 0)
+    x0 = synth.bf16_bits_to_f32(synth.hidden_states(w, 0, synth.decoded_masks(w), iters=1)[0])
+    G = x0.astype(np.float64) @ W0["router_w"].astype(np.float64).T + bias
+    top = np.argsort(-G, axis=1, kind="stable")[:, : w.top_k]
+    load = np.bincount(top.ravel(), minlength=w.n_experts)
+    tiles64 = int(np.sum((load + 63) // 64))
+    tiles128 = int(np.sum((load + 127) // 128))
+    assert load.max() > 128 and tiles128 < tiles64, load
+    h.log(f"[tall tiles] M={w.M} f={frac} R={R} load={load.tolist()}")
+    rep = h.run_block(w, weights=[W0], bias_override=bias)
+    assert rep.iters == w.iters
