@@ -5,13 +5,20 @@
 // live positions reach the output decoding, and a position's commit / no-commit decision
 // depends on its live logits).
 //
-// Three launches, no host synchronisation:
+// Five launches, no host synchronisation:
 //   k_live_compact  one workgroup: the live positions (D = 0) in ascending order, their count,
 //                   and each position's index in that list;
-//   k_gemm_big      LM-head mode: 128 live rows x 128 tokens per workgroup on bf16 MFMA, the
-//                   epilogue reducing each row's 64-token blocks to (max, argmax, sum exp);
-//   k_decode_final  one workgroup per sequence: the partials of each live row combined in
-//                   double (confidence = 1 / sum_v exp(z_v - z_max)), then the commits.
+//   k_expert_stream LM-head mode, when at most kLmStreamMaxRows positions are live: the
+//                   vocabulary streamed through LDS once per 128 live rows (the slab's further
+//                   passes in L2), 128 tokens per work item, the epilogue reducing each row's
+//                   32-token blocks to (max, argmax, sum exp);
+//   k_gemm_big      LM-head mode, when more are live: 128 live rows x 128 tokens per
+//                   workgroup on the compute-bound tiles, the same partials;
+//   k_decode_rows   one workgroup per position: the partials of each live row combined in double
+//                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
+//   k_decode_final  one workgroup per sequence: the commits.
+// The live count is known on the device only, so both LM-head kernels are launched and the one
+// that does not own it exits at once.
 #include "device_common.h"
 #include "epoch_internal.h"
 #include "expert_gemm.h"
@@ -21,6 +28,8 @@
 namespace epoch {
 
 constexpr int kCompactThreads = 1024;
+constexpr int kLmStreamBuffers = 3;
+constexpr int kLmStreamTileRows = 128;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
                                                                   const uint8_t* __restrict__ D,
@@ -51,60 +60,89 @@ __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
   if (tid == 0) *n_live = carry;
 }
 
-// One workgroup per sequence (block positions).  Wave w combines the partials of positions
-// w, w + 4, ...; then the commit rule: every live position with confidence >= tau commits, and
-// a sequence none of whose live positions reaches tau commits its most confident one (lower
-// position on ties).
-__global__ __launch_bounds__(256) void k_decode_final(int block, int n_p, double tau,
+// One workgroup per position: a live position's partials combined in double, the confidence
+// of its top token 1 / sum_v exp(z_v - z_max) and that token (the lowest id among equal
+// maxima); a decoded position gets confidence -1 and token -1.
+__global__ __launch_bounds__(256) void k_decode_rows(int n_p, const int32_t* __restrict__ live_idx,
+                                                     const float* __restrict__ pmax,
+                                                     const int32_t* __restrict__ parg,
+                                                     const float* __restrict__ psum,
+                                                     double* __restrict__ conf_pos,
+                                                     int32_t* __restrict__ top_pos) {
+  __shared__ float sm[4];
+  __shared__ int sa[4];
+  __shared__ double sz[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x;
+  const int li = live_idx[t];
+  if (li < 0) {
+    if (threadIdx.x == 0) {
+      conf_pos[t] = -1.0;
+      top_pos[t] = -1;
+    }
+    return;
+  }
+  const size_t row = (size_t)li * n_p;
+  float m = -INFINITY;
+  int a = 0x7fffffff;
+  for (int j = threadIdx.x; j < n_p; j += 256) {
+    const float pm = pmax[row + j];
+    const int pa = parg[row + j];
+    if (pm > m || (pm == m && pa < a)) {
+      m = pm;
+      a = pa;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const int oa = __shfl_xor(a, o, 64);
+    if (om > m || (om == m && oa < a)) {
+      m = om;
+      a = oa;
+    }
+  }
+  if (lane == 0) {
+    sm[wave] = m;
+    sa[wave] = a;
+  }
+  __syncthreads();
+  m = sm[0];
+  a = sa[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (sm[w] > m || (sm[w] == m && sa[w] < a)) {
+      m = sm[w];
+      a = sa[w];
+    }
+  double z = 0.0;
+  for (int j = threadIdx.x; j < n_p; j += 256)
+    z += (double)psum[row + j] * exp((double)pmax[row + j] - (double)m);
+  z = wave_sum(z);
+  if (lane == 0) sz[wave] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    conf_pos[t] = 1.0 / (((sz[0] + sz[1]) + sz[2]) + sz[3]);
+    top_pos[t] = a;
+  }
+}
+
+// One workgroup per sequence (block positions): the commit rule.  Every live position with
+// confidence >= tau commits, and a sequence none of whose live positions reaches tau commits
+// its most confident one (lower position on ties).
+__global__ __launch_bounds__(256) void k_decode_final(int block, double tau,
                                                       const uint8_t* __restrict__ D,
-                                                      const int32_t* __restrict__ live_idx,
-                                                      const float* __restrict__ pmax,
-                                                      const int32_t* __restrict__ parg,
-                                                      const float* __restrict__ psum,
+                                                      const double* __restrict__ conf_pos,
+                                                      const int32_t* __restrict__ top_pos,
                                                       uint8_t* __restrict__ D_next,
                                                       int32_t* __restrict__ tokens,
                                                       float* __restrict__ conf_out) {
   extern __shared__ double conf_s[];  // [block], then int top_s[block]
   int32_t* top_s = reinterpret_cast<int32_t*>(conf_s + block);
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int p = wave; p < block; p += 4) {
-    const int t = b * block + p;
-    const int li = live_idx[t];
-    if (li < 0) {  // decoded: not a candidate
-      if (lane == 0) {
-        conf_s[p] = -1.0;
-        top_s[p] = -1;
-      }
-      continue;
-    }
-    const size_t row = (size_t)li * n_p;
-    float m = -INFINITY;
-    int a = 0x7fffffff;
-    for (int j = lane; j < n_p; j += 64) {
-      const float pm = pmax[row + j];
-      const int pa = parg[row + j];
-      if (pm > m || (pm == m && pa < a)) {
-        m = pm;
-        a = pa;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float om = __shfl_xor(m, o, 64);
-      const int oa = __shfl_xor(a, o, 64);
-      if (om > m || (om == m && oa < a)) {
-        m = om;
-        a = oa;
-      }
-    }
-    double z = 0.0;
-    for (int j = lane; j < n_p; j += 64)
-      z += (double)psum[row + j] * exp((double)pmax[row + j] - (double)m);
-    z = wave_sum(z);
-    if (lane == 0) {
-      conf_s[p] = 1.0 / z;
-      top_s[p] = a;
-    }
+  for (int p = threadIdx.x; p < block; p += blockDim.x) {
+    conf_s[p] = conf_pos[(size_t)b * block + p];
+    top_s[p] = top_pos[(size_t)b * block + p];
   }
   __syncthreads();
   int hit = 0;
@@ -145,13 +183,14 @@ __global__ __launch_bounds__(256) void k_decode_final(int block, int n_p, double
 namespace {
 
 struct DecodeLayout {
-  int32_t *live_list, *live_idx, *n_live, *parg;
+  int32_t *live_list, *live_idx, *n_live, *parg, *top_pos;
   float *pmax, *psum;
+  double* conf_pos;
   size_t bytes;
 };
 
 DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
-  const size_t M = (size_t)d->batch * d->block, n_p = (size_t)d->vocab / 64;
+  const size_t M = (size_t)d->batch * d->block, n_p = (size_t)d->vocab / 32;
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t n) {
@@ -167,6 +206,8 @@ DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
   L.pmax = static_cast<float*>(take(M * n_p * 4));
   L.parg = static_cast<int32_t*>(take(M * n_p * 4));
   L.psum = static_cast<float*>(take(M * n_p * 4));
+  L.conf_pos = static_cast<double*>(take(M * 8));
+  L.top_pos = static_cast<int32_t*>(take(M * 4));
   L.bytes = (off + 255) / 256 * 256;
   return L;
 }
@@ -210,20 +251,45 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   const DecodeLayout L = decode_carve(d, workspace);
   if (workspace_bytes < L.bytes) return EPOCH_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int M = d->batch * d->block, n_p = d->vocab / 64;
+  const int M = d->batch * d->block, n_p = d->vocab / 32;
   launch(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
                      L.live_list, L.live_idx, L.n_live);
+  const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
+  // few live rows: the streamed LM head, one workgroup per CU walking token blocks
+  // blockIdx.x + j gridDim.x: eight waves (256 tokens a block) when that still gives every CU
+  // a block, else four (128 tokens)
+  {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu <= 0)
+      n_cu = 256;
+    const uint16_t* hb = static_cast<const uint16_t*>(h);
+    const uint16_t* wv = static_cast<const uint16_t*>(w_vocab);
+    if (d->vocab / 256 >= n_cu) {
+      const int n_cb = d->vocab / 256;
+      launch((k_expert_stream<false, false, kLmStreamBuffers, 8, kLmStreamTileRows, true>),
+             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(512), 0, st, hb, wv, nullptr, nullptr, nullptr,
+             nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
+    } else {
+      const int n_cb = d->vocab / 128;
+      launch((k_expert_stream<false, false, kLmStreamBuffers, 4, kLmStreamTileRows, true>),
+             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(256), 0, st, hb, wv, nullptr, nullptr, nullptr,
+             nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
+    }
+  }
   // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
   // at once) x token blocks per XCD
   const int tiles = (M + 127) / 128, n_cb = d->vocab / 128;
-  const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
   launch((k_gemm_big<false, false, true>), dim3(8 * tiles * ((n_cb + 7) / 8)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
-  launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, n_p, d->tau,
-                     decoded, L.live_idx, L.pmax, L.parg, L.psum, decoded_next, tokens, conf);
+  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, L.live_idx, L.pmax, L.parg, L.psum,
+         L.conf_pos, L.top_pos);
+  launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, d->tau, decoded,
+         L.conf_pos, L.top_pos, decoded_next, tokens, conf);
   return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;
 }
 

@@ -32,10 +32,12 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
   return r;
 }
 
-// Output of the LM-head mode of k_gemm_big: the rows are live positions (gathered through
-// live_list, n_live of them), the columns vocabulary tokens, and instead of the logits each wave
-// writes, per row and per block of 64 tokens, the largest logit, its token (lower id on ties)
-// and the sum of exp(logit - largest) over the block; n_p = vocab / 64 blocks per row.
+
+// Output of the LM-head modes (k_gemm_big, k_expert_stream): the rows are live positions
+// (gathered through live_list, n_live of them), the columns vocabulary tokens, and instead of
+// the logits the kernels write, per row and per block of 32 tokens, the largest logit, its
+// token (lower id on ties) and the sum of exp(logit - largest) over the block; n_p = vocab / 32
+// blocks per row.
 struct LmPartials {
   const int32_t* live_list;
   const int32_t* n_live;
@@ -104,15 +106,16 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // would make the wait for it also wait for every copy in flight.
 // The kernel body for tiles of BM rows; As / Bs: NB chunk buffers of BM x 64 and 32 WAVES x 64
 // bf16 in LDS.
-template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BM>
+template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BM, bool LMHEAD>
 __device__ __forceinline__ void expert_stream_body(
     uint16_t* As, uint16_t* Bs, const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, const LmPartials& lp) {
   static_assert(NB >= 3, "a chunk buffer is refilled one step after its fragments were read");
+  static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered product");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
   static_assert(BM == 64 || BM == 128, "tiles of 64 or 128 rows");
   constexpr int KC = 64, WR = 32 * WAVES;
@@ -123,13 +126,25 @@ __device__ __forceinline__ void expert_stream_body(
   constexpr int CPW = NAW + NBW;
   constexpr int ABUF = BM * KC, BBUF = WR * KC;  // elements per chunk buffer
   const int n_cb = (Ndim + CBW - 1) / CBW;
-  const int ntiles = ROUTED ? flags[FLAG_NTILES] : (M + BM - 1) / BM;
+  // LM head: the live rows, this kernel's only when there are at most kLmStreamMaxRows
+  const int rows = LMHEAD ? *lp.n_live : M;
+  const int ntiles = ROUTED   ? flags[FLAG_NTILES]
+                     : LMHEAD ? (rows <= kLmStreamMaxRows ? (rows + BM - 1) / BM : 0)
+                              : (M + BM - 1) / BM;
   // this workgroup's items: position (blockIdx.x / 8) + k G8 along the tile-major order of
-  // its XCD lane, active while the tile 8 (position / n_cb) + lane8 exists
+  // its XCD lane, active while the tile 8 (position / n_cb) + lane8 exists.  LM head: the
+  // column blocks blockIdx.x + j gridDim.x, each with all its row tiles back to back (the
+  // vocabulary slab is read from memory once and its next passes find it in L2).
   const int lane8 = blockIdx.x & 7, pos0 = blockIdx.x >> 3, G8 = gridDim.x >> 3;
-  const int T8 = ntiles > lane8 ? (ntiles - lane8 + 7) >> 3 : 0;
-  const int span = T8 * n_cb - pos0;
-  const int nitems = span > 0 ? (span + G8 - 1) / G8 : 0;
+  int nitems;
+  if (LMHEAD) {
+    const int ncb_w = (int)blockIdx.x < n_cb ? (n_cb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    nitems = ncb_w * ntiles;
+  } else {
+    const int T8 = ntiles > lane8 ? (ntiles - lane8 + 7) >> 3 : 0;
+    const int span = T8 * n_cb - pos0;
+    nitems = span > 0 ? (span + G8 - 1) / G8 : 0;
+  }
   if (nitems == 0) return;
   const int nch = Kdim / KC;
   const int Q = nitems * nch;  // chunks in this workgroup's stream
@@ -145,10 +160,18 @@ __device__ __forceinline__ void expert_stream_body(
     bool wact;
   };
   auto item = [&](int k) {
-    const int pos = pos0 + k * G8;
-    const int cb = pos % n_cb;
-    const TileRows tr = tile_rows(ROUTED, 8 * (pos / n_cb) + lane8, BM, ntiles, tile_slot,
-                                  tile_row0, offs, M);
+    int pos, cb, tile;
+    if (LMHEAD) {
+      const int j = k / ntiles;
+      tile = k - j * ntiles;
+      cb = blockIdx.x + j * gridDim.x;
+      pos = cb;
+    } else {
+      pos = pos0 + k * G8;
+      cb = pos % n_cb;
+      tile = 8 * (pos / n_cb) + lane8;
+    }
+    const TileRows tr = tile_rows(ROUTED, tile, BM, ntiles, tile_slot, tile_row0, offs, rows);
     Item it;
     it.row0 = tr.row0;
     it.row_end = tr.row_end;
@@ -175,7 +198,7 @@ __device__ __forceinline__ void expert_stream_body(
       const int row = row0 + lrow;
       const int lslot = pslot ^ ((row >> 1) & 7);
       int src_row;
-      if (ROUTED && GATEUP) {
+      if ((ROUTED && GATEUP) || LMHEAD) {
         // the eight gathered rows of this copy (rows past the tile repeat its last row)
         src_row = 0;
 #pragma unroll
@@ -219,8 +242,12 @@ __device__ __forceinline__ void expert_stream_body(
     for (int j = 0; j < NAW; ++j)
       copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf * ABUF + 8 * (NAW * wave + j) * KC]);
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
-      copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
+    for (int j = 0; j < NBW; ++j) {
+      if (LMHEAD)  // the slab's next row tile reads it again: keep it in L2
+        copy16_to_lds(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
+      else
+        copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
+    }
     ++ic;
   };
 
@@ -283,6 +310,51 @@ __device__ __forceinline__ void expert_stream_body(
                       f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
   };
   auto epilogue = [&](const Item& it) {
+    if constexpr (LMHEAD) {
+      // per row: the 32 logits of this wave's token block sit in the 4 lanes with the same r
+      // (tokens 4 g .. 4 g + 3 and 16 + 4 g .. + 3); reduce (max, lower token on ties), then
+      // the sum of exp(logit - max)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (it.row0 + 16 * m >= it.row_end) continue;
+        float mx = c0[m][0];
+        int arg = it.col0 + 4 * g;
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+          if (c0[m][i] > mx) {
+            mx = c0[m][i];
+            arg = it.col0 + 4 * g + i;
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c1[m][i] > mx) {
+            mx = c1[m][i];
+            arg = it.col0 + 16 + 4 * g + i;
+          }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+          const float om = __shfl_xor(mx, o, 64);
+          const int oa = __shfl_xor(arg, o, 64);
+          if (om > mx || (om == mx && oa < arg)) {
+            mx = om;
+            arg = oa;
+          }
+        }
+        float se = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) se += expf(c0[m][i] - mx) + expf(c1[m][i] - mx);
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
+        const int li = it.row0 + 16 * m + r;
+        if (g == 0 && li < it.row_end) {
+          const size_t idx = (size_t)li * lp.n_p + it.col0 / 32;
+          lp.pmax[idx] = mx;
+          lp.parg[idx] = arg;
+          lp.psum[idx] = se;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       if (it.row0 + 16 * m >= it.row_end) continue;  // uniform: a block past the tile's rows
@@ -356,31 +428,33 @@ __device__ __forceinline__ void expert_stream_body(
 
 // Routed tiles: the plan step's tile table holds kTileRows- or kTileRowsTall-row tiles
 // (FLAG_TILE_TALL; never tall for shapes with big tiles); shared-expert tiles: kDenseTileRows
-// rows.  BMAX = the tallest tile the instance handles, which sizes its LDS.
-template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BMAX>
+// rows; LM head (LMHEAD: rows gathered through lp.live_list, lp.n_live of them, the epilogue
+// writing lp's partials): BMAX-row tiles.  BMAX = the tallest tile the instance handles, which
+// sizes its LDS.
+template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BMAX, bool LMHEAD = false>
 __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
   __shared__ __attribute__((aligned(16))) uint16_t As[NB * BMAX * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB * 32 * WAVES * 64];
   if constexpr (ROUTED && BMAX == kTileRowsTall) {
     if (flags[FLAG_TILE_TALL]) {
-      expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRowsTall>(
+      expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRowsTall, false>(
           As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M,
-          Kdim, Ndim);
+          Kdim, Ndim, lp);
       return;
     }
-    expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRows>(
+    expert_stream_body<GATEUP, ROUTED, NB, WAVES, kTileRows, false>(
         As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M, Kdim,
-        Ndim);
+        Ndim, lp);
   } else {
-    expert_stream_body<GATEUP, ROUTED, NB, WAVES, BMAX>(
+    expert_stream_body<GATEUP, ROUTED, NB, WAVES, BMAX, LMHEAD>(
         As, Bs, A, B0, B1, flags, tile_slot, tile_row0, offs, S_list, wl_pos, wl_w, out, M, Kdim,
-        Ndim);
+        Ndim, lp);
   }
 }
 
@@ -433,7 +507,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
     cb = pos % n_cb;
   }
-  // routed big tiles come from their own table, counted in FLAG_NTILES_BIG
+  // routed big tiles come from their own table, counted in FLAG_NTILES_BIG; the LM head is
+  // this kernel's only beyond kLmStreamMaxRows live rows (below, k_expert_stream streams it)
+  if (LMHEAD && *lp.n_live <= kLmStreamMaxRows) return;
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
                                 tile_row0, offs, LMHEAD ? *lp.n_live : M);
   if (!tr.active) return;
@@ -574,41 +650,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   }
   // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
   if (LMHEAD) {
-    // per row: the 64 logits of this wave's token block sit in the 16 lanes with the same g,
-    // four per lane; reduce (max, lower token on ties) and then sum exp(logit - max)
+    // per row: the 64 logits of this wave's token columns sit in the 16 lanes with the same g,
+    // four per lane (token 16 n + r); each 32-token half (n = 0, 1 and n = 2, 3) is reduced
+    // to (max, lower token on ties) and then the sum of exp(logit - max)
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
         const int col0 = cb * 128 + 64 * wn + r;
-        float mx = acc[m][0][q];
-        int arg = col0;
 #pragma unroll
-        for (int n = 1; n < 4; ++n)
-          if (acc[m][n][q] > mx) {
-            mx = acc[m][n][q];
-            arg = col0 + 16 * n;
+        for (int hf = 0; hf < 2; ++hf) {
+          float mx = acc[m][2 * hf][q];
+          int arg = col0 + 32 * hf;
+          if (acc[m][2 * hf + 1][q] > mx) {
+            mx = acc[m][2 * hf + 1][q];
+            arg = col0 + 32 * hf + 16;
           }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float om = __shfl_xor(mx, o, 64);
-          const int oa = __shfl_xor(arg, o, 64);
-          if (om > mx || (om == mx && oa < arg)) {
-            mx = om;
-            arg = oa;
+          for (int o = 1; o < 16; o <<= 1) {
+            const float om = __shfl_xor(mx, o, 64);
+            const int oa = __shfl_xor(arg, o, 64);
+            if (om > mx || (om == mx && oa < arg)) {
+              mx = om;
+              arg = oa;
+            }
           }
-        }
-        float se = 0.0f;
+          float se = expf(acc[m][2 * hf][q] - mx) + expf(acc[m][2 * hf + 1][q] - mx);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) se += expf(acc[m][n][q] - mx);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
-        if (r == 0 && row < tr.row_end) {
-          const size_t idx = (size_t)row * lp.n_p + 2 * cb + wn;
-          lp.pmax[idx] = mx;
-          lp.parg[idx] = arg;
-          lp.psum[idx] = se;
+          for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
+          if (r == 0 && row < tr.row_end) {
+            const size_t idx = (size_t)row * lp.n_p + 4 * cb + 2 * wn + hf;
+            lp.pmax[idx] = mx;
+            lp.parg[idx] = arg;
+            lp.psum[idx] = se;
+          }
         }
       }
     }

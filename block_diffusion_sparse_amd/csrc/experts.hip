@@ -51,7 +51,8 @@ static void launch_gemm_w(int tiles, int per_cu, hipStream_t st, int Kdim, const
   const int items = ((tiles + 7) / 8) * 8 * n_cb;
   launch((k_expert_stream<GATEUP, ROUTED, kStreamBuffers, WAVES, BMAX>),
          dim3(items < slots ? items : slots), dim3(64 * WAVES), 0, st, A, B0, B1, W.flags,
-         W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim);
+         W.tile_slot, W.tile_row0, W.offs, S_list, W.wl_pos, W.wl_w, out, M, Kdim, Ndim,
+         LmPartials{});
 }
 
 // Routed experts run eight waves per workgroup, the shared expert four.  When the compute-bound

@@ -19,16 +19,15 @@ namespace epoch {
 // to fp32.  The contraction index is permuted: in each 64-wide k step, lane group g = l / 16
 // owns k in [16 g, 16 g + 16) and feeds them to 16 successive MFMA steps, for the activation
 // and the weight alike, so every product pairs x[t,k] with W[e,k].  Each lane loads its
-// 16 values of each operand as whole 16-byte vectors, one step ahead of the MFMAs.
+// 16 values of each operand as whole 16-byte vectors, two steps ahead of the MFMAs.
 template <typename T>
 struct RouterRaw;
 template <>
 struct RouterRaw<uint16_t> {
   u32x4 v[2];  // 16 bf16
-  __device__ __forceinline__ void load(const uint16_t* p, bool ok) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    v[0] = ok ? reinterpret_cast<const u32x4*>(p)[0] : z;
-    v[1] = ok ? reinterpret_cast<const u32x4*>(p)[1] : z;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v[0] = reinterpret_cast<const u32x4*>(p)[0];
+    v[1] = reinterpret_cast<const u32x4*>(p)[1];
   }
   __device__ __forceinline__ double get(int m) const {
     const uint32_t w = v[m >> 3][(m >> 1) & 3];
@@ -38,10 +37,9 @@ struct RouterRaw<uint16_t> {
 template <>
 struct RouterRaw<float> {
   u32x4 v[4];  // 16 fp32
-  __device__ __forceinline__ void load(const float* p, bool ok) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+  __device__ __forceinline__ void load(const float* p) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ok ? reinterpret_cast<const u32x4*>(p)[i] : z;
+    for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const u32x4*>(p)[i];
   }
   __device__ __forceinline__ double get(int m) const {
     return (double)__uint_as_float(v[m >> 2][m & 3]);
@@ -390,16 +388,16 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
   const int klen = H / (ksplit * kw), kbeg = (blockIdx.z * ksplit + wave) * klen;
   const int nsteps = klen / 64;
   const int r = lane & 15, g = lane >> 4;
+  // rows past M or E read row 0 (always present): they only feed logits that are never
+  // stored, so every lane loads with no branch around it (a load under a lane mask would make
+  // the compiler wait for the prefetched step too before multiplying the current one)
   const T* xr[NB];
   const float* wr[NB];
-  bool vx[NB], vw[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int t = t0 + 16 * b + r, e = e0 + 16 * b + r;
-    vx[b] = t < M;
-    vw[b] = e < E;
-    xr[b] = x + (size_t)(vx[b] ? t : 0) * H + kbeg + 16 * g;
-    wr[b] = Wg + (size_t)(vw[b] ? e : 0) * H + kbeg + 16 * g;
+    xr[b] = x + (size_t)(t < M ? t : 0) * H + kbeg + 16 * g;
+    wr[b] = Wg + (size_t)(e < E ? e : 0) * H + kbeg + 16 * g;
   }
   f64x4 acc[NB][NB];
 #pragma unroll
@@ -408,12 +406,17 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
     for (int b = 0; b < NB; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
   RouterRaw<T> xa[2][NB];
   RouterRaw<float> wa[2][NB];
+  // a step's loads issue as one group, ahead of the MFMAs of the step before (the scheduling
+  // barriers keep the compiler from sinking them between those MFMAs, where each would be
+  // waited for at once)
   auto load = [&](int step, int buf) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      xa[buf][b].load(xr[b] + 64 * step, vx[b]);
-      wa[buf][b].load(wr[b] + 64 * step, vw[b]);
+      xa[buf][b].load(xr[b] + 64 * step);
+      wa[buf][b].load(wr[b] + 64 * step);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto mma = [&](int buf) {
 #pragma unroll
@@ -431,13 +434,18 @@ __global__ __launch_bounds__(BT == 32 ? 256 : 1024) void k_router(
           acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[a], B[b], acc[a][b], 0, 0, 0);
     }
   };
+  // two steps in flight: a buffer is refilled with the step after next as soon as its MFMAs
+  // are issued.  The refills are unconditional (past the end they re-read the last step): a
+  // load under a branch, even a uniform one, leaves the compiler unable to count it, and it
+  // then waits for every load before the MFMAs of the current step.
   load(0, 0);
+  load(min(1, nsteps - 1), 1);
   for (int st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) load(st + 1, 1);
     mma(0);
+    load(min(st + 2, nsteps - 1), 0);
     if (st + 1 >= nsteps) break;
-    if (st + 2 < nsteps) load(st + 2, 0);
     mma(1);
+    load(min(st + 3, nsteps - 1), 1);
   }
   // f64 16x16x4 output layout: D[i][j] sits in lane (j + 16 * (i % 4)), register i / 4
   double* mine = red + (size_t)wave * BT * BT;

@@ -102,6 +102,35 @@ def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
     assert reported <= int((D == 0).sum()) // 4
 
 
+@pytest.mark.parametrize("batch", [16, 20], ids=["512-live-streamed", "640-live-compute-tiles"])
+def test_lm_head_on_both_sides_of_the_stream_limit(batch):
+    """Every position live: 512 live rows are the most the streamed LM head takes (four
+    128-row passes over each vocabulary slab), 640 go to the compute-bound tiles; both write
+    the same 32-token partials."""
+    block, H, V = 32, 128, 384
+    hs, Wb, _ = synth.decode_inputs(55 + batch, batch, block, H, V)
+    D = np.zeros(batch * block, np.uint8)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
+    assert reported <= batch * block // 4
+
+
+def test_lm_head_wide_vocabulary():
+    """A vocabulary of at least 256 tokens per CU (65536 on 256 CUs) takes the eight-wave
+    streamed LM head (256-token blocks); small hidden size keeps the oracle quick."""
+    batch, block, H, V = 2, 32, 128, 65536
+    hs, Wb, D = synth.decode_inputs(66, batch, block, H, V)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
+    assert reported <= int((D == 0).sum()) // 4
+
+
 def test_all_decoded_and_all_live():
     batch, block, H, V = 2, 32, 128, 256
     hs, Wb, _ = synth.decode_inputs(77, batch, block, H, V)
