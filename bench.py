@@ -394,8 +394,8 @@ def bench_decode(args):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
     live = int((D == 0).sum())
-    row_tiles = (live + 127) // 128
-    lm_bytes = V * H * 2 * row_tiles + live * H * 2 + live * (V // 32) * 12  # 32-token partials
+    # algorithmic bytes: the vocabulary once, the live rows, the 32-token partials
+    lm_bytes = V * H * 2 + live * H * 2 + live * (V // 32) * 12
     flops = 2.0 * live * V * H
     print(json.dumps({
         "metric": "live positions decoded per second (LM head + threshold commit)",

@@ -28,8 +28,11 @@
 namespace epoch {
 
 constexpr int kCompactThreads = 1024;
-constexpr int kLmStreamBuffers = 3;
-constexpr int kLmStreamTileRows = 128;
+// the streamed LM head: 256-row tiles (one pass over the vocabulary for up to 256 live rows),
+// eight waves of 32 tokens with two chunk buffers (2 x 64 KB of LDS), or four waves with three
+// (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
+constexpr int kLmStreamBuffers = 2;
+constexpr int kLmStreamTileRows = 256;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
                                                                   const uint8_t* __restrict__ D,
@@ -256,8 +259,7 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
                      L.live_list, L.live_idx, L.n_live);
   const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
   // few live rows: the streamed LM head, one workgroup per CU walking token blocks
-  // blockIdx.x + j gridDim.x: eight waves (256 tokens a block) when that still gives every CU
-  // a block, else four (128 tokens)
+  // blockIdx.x + j gridDim.x (256 tokens, or 128 when that is needed to give every CU one)
   {
     int dev = 0, n_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -266,15 +268,15 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
       n_cu = 256;
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* wv = static_cast<const uint16_t*>(w_vocab);
-    if (d->vocab / 256 >= n_cu) {
-      const int n_cb = d->vocab / 256;
-      launch((k_expert_stream<false, false, kLmStreamBuffers, 8, kLmStreamTileRows, true>),
-             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(512), 0, st, hb, wv, nullptr, nullptr, nullptr,
+    if (d->vocab / 256 < n_cu) {
+      const int n_cb = d->vocab / 128;
+      launch((k_expert_stream<false, false, kLmStreamBuffers + 1, 4, kLmStreamTileRows, true>),
+             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(256), 0, st, hb, wv, nullptr, nullptr, nullptr,
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     } else {
-      const int n_cb = d->vocab / 128;
-      launch((k_expert_stream<false, false, kLmStreamBuffers, 4, kLmStreamTileRows, true>),
-             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(256), 0, st, hb, wv, nullptr, nullptr, nullptr,
+      const int n_cb = (d->vocab + 255) / 256;  // the last block may be half (vocab % 256 = 128)
+      launch((k_expert_stream<false, false, kLmStreamBuffers, 8, kLmStreamTileRows, true>),
+             dim3(n_cb < n_cu ? n_cb : n_cu), dim3(512), 0, st, hb, wv, nullptr, nullptr, nullptr,
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     }
   }

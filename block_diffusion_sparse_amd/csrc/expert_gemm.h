@@ -114,10 +114,10 @@ __device__ __forceinline__ void expert_stream_body(
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim, const LmPartials& lp) {
-  static_assert(NB >= 3, "a chunk buffer is refilled one step after its fragments were read");
+  static_assert(NB >= 2, "one chunk in flight while another is multiplied");
   static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered product");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
-  static_assert(BM == 64 || BM == 128, "tiles of 64 or 128 rows");
+  static_assert(BM == 64 || BM == 128 || BM == 256, "tiles of 64, 128 or 256 rows");
   constexpr int KC = 64, WR = 32 * WAVES;
   constexpr int CBW = GATEUP ? 16 * WAVES : 32 * WAVES;  // output columns per item
   constexpr int MB = BM / 16;
@@ -257,26 +257,32 @@ __device__ __forceinline__ void expert_stream_body(
   // (weights)
   const int key = (r >> 1) & 7;
   const int off0 = (g ^ key) * 8, off1 = ((4 + g) ^ key) * 8;
-  u32x4 fa[2][MB], fb[2][2];
-  // the fragments of chunk buffer buf for the first mlive row blocks, complete on return
-  auto read_frags = [&](int buf, int mlive) {
-    const uint32_t a0 = (uint32_t)(uintptr_t)&As[buf * ABUF + r * KC + off0];
-    const uint32_t a1 = (uint32_t)(uintptr_t)&As[buf * ABUF + r * KC + off1];
-    const uint32_t b0 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off0];
-    const uint32_t b1 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off1];
+  // activation fragments are read FG row blocks at a time (all of them up to 8 blocks, else in
+  // groups of 4, which keeps a 256-row tile's registers within two waves per SIMD)
+  constexpr int FG = MB <= 8 ? MB : 4;
+  u32x4 fa[2][FG], fb[2][2];
+  // the weight fragments of chunk buffer buf, and the activation fragments of row blocks
+  // g0 .. g0 + FG - 1 below mlive; complete on return
+  auto read_frags = [&](int buf, int g0, int mlive, bool with_b) {
+    const uint32_t a0 = (uint32_t)(uintptr_t)&As[buf * ABUF + (16 * g0 + r) * KC + off0];
+    const uint32_t a1 = (uint32_t)(uintptr_t)&As[buf * ABUF + (16 * g0 + r) * KC + off1];
+    if (with_b) {
+      const uint32_t b0 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off0];
+      const uint32_t b1 = (uint32_t)(uintptr_t)&Bs[buf * BBUF + (32 * wave + r) * KC + off1];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[0][n]) : "v"(b0), "i"(n * 16 * KC * 2));
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[1][n]) : "v"(b1), "i"(n * 16 * KC * 2));
+      for (int n = 0; n < 2; ++n) {
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[0][n]) : "v"(b0), "i"(n * 16 * KC * 2));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[1][n]) : "v"(b1), "i"(n * 16 * KC * 2));
+      }
     }
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      if (m < mlive) {
+    for (int m = 0; m < FG; ++m) {
+      if (g0 + m < mlive) {
         asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[0][m]) : "v"(a0), "i"(m * 16 * KC * 2));
         asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[1][m]) : "v"(a1), "i"(m * 16 * KC * 2));
       }
     }
-    if constexpr (MB == 8)
+    if constexpr (FG == 8)
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]),
                      "+v"(fa[0][4]), "+v"(fa[0][5]), "+v"(fa[0][6]), "+v"(fa[0][7]),
@@ -291,17 +297,17 @@ __device__ __forceinline__ void expert_stream_body(
   };
   // weights as the left operand: lane (r, g) of block m ends up with row 16 m + r and the four
   // consecutive columns 4 g .. 4 g + 3 (one 8-byte store in the epilogue)
-  auto mma = [&](int mlive) {
+  auto mma = [&](int g0, int mlive) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        if (m < mlive) {
+      for (int m = 0; m < FG; ++m) {
+        if (g0 + m < mlive) {
           const bf16x8 f = __builtin_bit_cast(bf16x8, fa[s][m]);
-          c0[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[s][0]),
-                                                           f, c0[m], 0, 0, 0);
-          c1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[s][1]),
-                                                           f, c1[m], 0, 0, 0);
+          c0[g0 + m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fb[s][0]), f, c0[g0 + m], 0, 0, 0);
+          c1[g0 + m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fb[s][1]), f, c1[g0 + m], 0, 0, 0);
         }
       }
   };
@@ -411,8 +417,13 @@ __device__ __forceinline__ void expert_stream_body(
       }
     }
     if (cur.wact) {
-      read_frags(q % NB, mlive);
-      mma(mlive);
+#pragma unroll
+      for (int g0 = 0; g0 < MB; g0 += FG) {
+        if (g0 < mlive) {
+          read_frags(q % NB, g0, mlive, g0 == 0);
+          mma(g0, mlive);
+        }
+      }
     }
     if (++cc == nch) {
       if (cur.wact) epilogue(cur);
