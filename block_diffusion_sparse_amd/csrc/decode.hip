@@ -261,11 +261,7 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   // few live rows: the streamed LM head, one workgroup per CU walking token blocks
   // blockIdx.x + j gridDim.x (256 tokens, or 128 when that is needed to give every CU one)
   {
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu <= 0)
-      n_cu = 256;
+    const int n_cu = device_cu_count();
     const uint16_t* hb = static_cast<const uint16_t*>(h);
     const uint16_t* wv = static_cast<const uint16_t*>(w_vocab);
     if (d->vocab / 256 < n_cu) {

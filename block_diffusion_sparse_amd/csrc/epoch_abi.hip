@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -205,6 +206,22 @@ namespace epoch {
 LaunchEvents& launch_events() {
   thread_local LaunchEvents ev;
   return ev;
+}
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // 0 = not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 }  // namespace epoch
 

@@ -130,6 +130,9 @@ struct Shape {
   int B, c, an, ad, qn, qd, bn, bd;
 };
 
+// Compute units of the current device (read once per device; 256 if the query fails).
+int device_cu_count();
+
 // launchers (stream-ordered, no host sync); each returns hipGetLastError()
 hipError_t launch_init_layer(const Shape& s, const LayerState& L, hipStream_t st);
 hipError_t launch_init_scratch(const Shape& s, const Scratch& W, hipStream_t st);

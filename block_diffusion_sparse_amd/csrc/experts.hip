@@ -29,11 +29,7 @@ constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups
 // Workgroups of k_expert_stream with lds bytes each that fit on the device at once, at most
 // per_cu per CU, as a multiple of 8 (one per XCD lane).
 static int stream_slots(int lds, int per_cu) {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      n_cu <= 0)
-    n_cu = 256;
+  const int n_cu = device_cu_count();
   const int fit = kLdsPerCu / lds;
   return ((n_cu * (fit < per_cu ? fit : per_cu)) / 8) * 8;
 }
