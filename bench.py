@@ -350,7 +350,8 @@ def main():
         "support_paths": {"cold": per_block["cold"], "hot_update": per_block["hot_update"],
                           "hot_skip": per_block["hot_skip"],
                           "restricted": per_block["restricted"],
-                          "coverage_fallback": per_block["coverage_fallback"]},
+                          "coverage_fallback": per_block["coverage_fallback"],
+                          "repair_rounds": per_block["repair_rounds"]},
         "touched_experts_per_forward": round(per_block["touched"] / layer_iters, 2),
         "kernel_us_per_launch": kernels_us,
         "kernel_time_share": kernels_share,
