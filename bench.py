@@ -395,8 +395,10 @@ def bench_decode(args):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
     live = int((D == 0).sum())
-    # algorithmic bytes: the vocabulary once, the live rows, the 32-token partials
-    lm_bytes = V * H * 2 + live * H * 2 + live * (V // 32) * 12
+    # algorithmic bytes: the vocabulary once, the live rows, the partials (32-token blocks
+    # from the streamed LM head, 64-token blocks beyond its live-row limit)
+    blk = 32 if live <= 512 else 64
+    lm_bytes = V * H * 2 + live * H * 2 + live * (V // blk) * 12
     flops = 2.0 * live * V * H
     print(json.dumps({
         "metric": "live positions decoded per second (LM head + threshold commit)",

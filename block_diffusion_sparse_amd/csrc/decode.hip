@@ -13,7 +13,8 @@
 //                   passes in L2), 128 tokens per work item, the epilogue reducing each row's
 //                   32-token blocks to (max, argmax, sum exp);
 //   k_gemm_big      LM-head mode, when more are live: 128 live rows x 128 tokens per
-//                   workgroup on the compute-bound tiles, the same partials;
+//                   workgroup on the compute-bound tiles, the same partials over 64-token
+//                   blocks (one wave's columns);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
 //                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
 //   k_decode_final  one workgroup per sequence: the commits.
@@ -65,8 +66,11 @@ __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
 
 // One workgroup per position: a live position's partials combined in double, the confidence
 // of its top token 1 / sum_v exp(z_v - z_max) and that token (the lowest id among equal
-// maxima); a decoded position gets confidence -1 and token -1.
-__global__ __launch_bounds__(256) void k_decode_rows(int n_p, const int32_t* __restrict__ live_idx,
+// maxima); a decoded position gets confidence -1 and token -1.  The partials are n_p_stream
+// per row when the streamed LM head ran (at most kLmStreamMaxRows live), else n_p_big.
+__global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big,
+                                                     const int32_t* __restrict__ n_live,
+                                                     const int32_t* __restrict__ live_idx,
                                                      const float* __restrict__ pmax,
                                                      const int32_t* __restrict__ parg,
                                                      const float* __restrict__ psum,
@@ -85,6 +89,7 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p, const int32_t* __r
     }
     return;
   }
+  const int n_p = *n_live <= kLmStreamMaxRows ? n_p_stream : n_p_big;
   const size_t row = (size_t)li * n_p;
   float m = -INFINITY;
   int a = 0x7fffffff;
@@ -279,13 +284,14 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
   // at once) x token blocks per XCD
   const int tiles = (M + 127) / 128, n_cb = d->vocab / 128;
+  const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, d->vocab / 64};
   launch((k_gemm_big<false, false, true>), dim3(8 * tiles * ((n_cb + 7) / 8)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp);
+                     nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
-  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, L.live_idx, L.pmax, L.parg, L.psum,
-         L.conf_pos, L.top_pos);
+  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, d->vocab / 64, L.n_live, L.live_idx,
+         L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
   launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, d->tau, decoded,
          L.conf_pos, L.top_pos, decoded_next, tokens, conf);
   return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;

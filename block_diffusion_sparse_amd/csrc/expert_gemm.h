@@ -35,9 +35,9 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
 
 // Output of the LM-head modes (k_gemm_big, k_expert_stream): the rows are live positions
 // (gathered through live_list, n_live of them), the columns vocabulary tokens, and instead of
-// the logits the kernels write, per row and per block of 32 tokens, the largest logit, its
-// token (lower id on ties) and the sum of exp(logit - largest) over the block; n_p = vocab / 32
-// blocks per row.
+// the logits the kernels write, per row and per block of tokens, the largest logit, its token
+// (lower id on ties) and the sum of exp(logit - largest) over the block; n_p blocks per row:
+// vocab / 32 from k_expert_stream (one wave's columns), vocab / 64 from k_gemm_big.
 struct LmPartials {
   const int32_t* live_list;
   const int32_t* n_live;
@@ -662,40 +662,40 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
   if (LMHEAD) {
     // per row: the 64 logits of this wave's token columns sit in the 16 lanes with the same g,
-    // four per lane (token 16 n + r); each 32-token half (n = 0, 1 and n = 2, 3) is reduced
-    // to (max, lower token on ties) and then the sum of exp(logit - max)
+    // four per lane (token 16 n + r), reduced over the wave's 64 tokens to (max, lower token
+    // on ties) and then the sum of exp(logit - max)
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
         const int col0 = cb * 128 + 64 * wn + r;
+        float mx = acc[m][0][q];
+        int arg = col0;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float mx = acc[m][2 * hf][q];
-          int arg = col0 + 32 * hf;
-          if (acc[m][2 * hf + 1][q] > mx) {
-            mx = acc[m][2 * hf + 1][q];
-            arg = col0 + 32 * hf + 16;
+        for (int n = 1; n < 4; ++n)
+          if (acc[m][n][q] > mx) {
+            mx = acc[m][n][q];
+            arg = col0 + 16 * n;
           }
 #pragma unroll
-          for (int o = 1; o < 16; o <<= 1) {
-            const float om = __shfl_xor(mx, o, 64);
-            const int oa = __shfl_xor(arg, o, 64);
-            if (om > mx || (om == mx && oa < arg)) {
-              mx = om;
-              arg = oa;
-            }
+        for (int o = 1; o < 16; o <<= 1) {
+          const float om = __shfl_xor(mx, o, 64);
+          const int oa = __shfl_xor(arg, o, 64);
+          if (om > mx || (om == mx && oa < arg)) {
+            mx = om;
+            arg = oa;
           }
-          float se = expf(acc[m][2 * hf][q] - mx) + expf(acc[m][2 * hf + 1][q] - mx);
+        }
+        float se = (expf(acc[m][0][q] - mx) + expf(acc[m][1][q] - mx)) +
+                   (expf(acc[m][2][q] - mx) + expf(acc[m][3][q] - mx));
 #pragma unroll
-          for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
-          if (r == 0 && row < tr.row_end) {
-            const size_t idx = (size_t)row * lp.n_p + 4 * cb + 2 * wn + hf;
-            lp.pmax[idx] = mx;
-            lp.parg[idx] = arg;
-            lp.psum[idx] = se;
-          }
+        for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (r == 0 && row < tr.row_end) {
+          const size_t idx = (size_t)row * lp.n_p + 2 * cb + wn;
+          lp.pmax[idx] = mx;
+          lp.parg[idx] = arg;
+          lp.psum[idx] = se;
         }
       }
     }
