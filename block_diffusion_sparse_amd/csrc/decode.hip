@@ -34,6 +34,9 @@ constexpr int kCompactThreads = 1024;
 // (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
 constexpr int kLmStreamBuffers = 2;
 constexpr int kLmStreamTileRows = 256;
+// beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 128 tokens (waves
+// of 128 x 64 outputs: a quarter less LDS fragment traffic per MFMA than 128-row tiles)
+constexpr int kLmBigTileRows = 256;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
                                                                   const uint8_t* __restrict__ D,
@@ -283,9 +286,9 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   }
   // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
   // at once) x token blocks per XCD
-  const int tiles = (M + 127) / 128, n_cb = d->vocab / 128;
+  const int tiles = (M + kLmBigTileRows - 1) / kLmBigTileRows, n_cb = d->vocab / 128;
   const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, d->vocab / 64};
-  launch((k_gemm_big<false, false, true>), dim3(8 * tiles * ((n_cb + 7) / 8)),
+  launch((k_gemm_big<false, false, true, kLmBigTileRows>), dim3(8 * tiles * ((n_cb + 7) / 8)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp_big);
