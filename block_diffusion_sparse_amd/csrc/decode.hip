@@ -9,10 +9,10 @@
 //   k_live_compact  one workgroup: the live positions (D = 0) in ascending order, their count,
 //                   and each position's index in that list;
 //   k_expert_stream LM-head mode, when at most kLmStreamMaxRows positions are live: the
-//                   vocabulary streamed through LDS once per 128 live rows (the slab's further
+//                   vocabulary streamed through LDS once per 256 live rows (the slab's further
 //                   passes in L2), 128 tokens per work item, the epilogue reducing each row's
 //                   32-token blocks to (max, argmax, sum exp);
-//   k_gemm_big      LM-head mode, when more are live: 128 live rows x 128 tokens per
+//   k_gemm_big      LM-head mode, when more are live: 256 live rows x 128 tokens per
 //                   workgroup on the compute-bound tiles, the same partials over 64-token
 //                   blocks (one wave's columns);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
