@@ -10,8 +10,8 @@
 //                   and each position's index in that list;
 //   k_expert_stream LM-head mode, when at most kLmStreamMaxRows positions are live: the
 //                   vocabulary streamed through LDS once per 256 live rows (the slab's further
-//                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing each row's
-//                   32-token blocks to (max, argmax, sum exp);
+//                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
+//                   each row's 32-token blocks to (max, argmax, sum exp);
 //   k_gemm_big      LM-head mode, when more are live: 256 live rows x 128 tokens per
 //                   workgroup on the compute-bound tiles, the same partials over 64-token
 //                   blocks (one wave's columns);
