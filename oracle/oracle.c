@@ -143,8 +143,13 @@ void orc_route(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, c
 int orc_support_status(int M, int K, int Kext, const int32_t* ids, const uint8_t* inS,
                        int support_valid) {
   if (!support_valid) return 1;
+#if ORC_MUTATE == 11
+  const int n_checked = Kext;
+#else
+  const int n_checked = K;
+#endif
   for (int t = 0; t < M; ++t)
-    for (int k = 0; k < K; ++k)
+    for (int k = 0; k < n_checked; ++k)
       if (!inS[ids[(size_t)t * Kext + k]]) return 2;
   return 0;
 }
@@ -170,7 +175,11 @@ int64_t orc_under_covered(int M, int K, int Kext, const int32_t* ids, const int6
   coverage(M, K, Kext, ids, q, inS, R, C);
   int64_t n = 0;
   for (int t = 0; t < M; ++t)
+#if ORC_MUTATE == 12
+    if ((int64_t)alpha_den * C[t] <= (int64_t)alpha_num * R[t]) ++n;
+#else
     if ((int64_t)alpha_den * C[t] < (int64_t)alpha_num * R[t]) ++n;
+#endif
   free(R);
   free(C);
   return n;

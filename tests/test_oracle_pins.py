@@ -332,6 +332,71 @@ def pin_atlas_without_closure(orc, lib):
         assert int(st[4]) == len(A)
 
 
+def pin_support_lifecycle(orc, lib):
+    """Teardown, "cold / hot-update / hot-skip": a forward keeps the block's support
+    (hot-skip) while every routed expert has a slot in it, and rebuilds it (hot-update)
+    once one does not.  Only the K routed experts decide this: the planner's extra
+    candidates (ranks K..K_ext-1) are not routed and need no slot.
+
+    Hand-built block: one-hot hidden rows make the logits the router's columns, so every
+    position routes to experts {0, 1} and ranks experts 2..9 as its extra candidates.
+    With B = 0 and alpha = 0 the support is the closure {0, 1} alone, so the extra
+    candidates lie outside it on every iteration."""
+    w = small_workload(n_experts=16, top_k=2, atlas_m=2, atlas_B=0, alpha=(0, 1), iters=5,
+                       n_shared=0, shared_inter=0, liveness="uniform")
+    M, H, E, K, Kext = w.M, w.hidden, w.n_experts, w.top_k, w.k_ext
+    assert Kext == 4 and M <= H
+    G = np.full((M, E), -5.0, np.float32)
+    for t in range(M):
+        G[t, 0], G[t, 1] = 5.0, 4.0
+        G[t, 2 + t % 4], G[t, 6 + t % 4] = 3.0, 2.0
+    Wl = dict(synth.layer_weights(w, 0))
+    Wl["router_w"] = np.zeros((E, H), np.float32)
+    Wl["router_w"][:, :M] = G.T
+    Wl["router_b"] = None
+    x = synth.f32_to_bf16_bits(np.eye(M, H, dtype=np.float32))
+    D = np.zeros(M, np.uint8)
+    L = orc.OracleLayer(w, Wl, lib=lib)
+    paths = []
+    for it in range(w.iters):
+        out = L.forward(x, D)
+        assert set(out["ids"][:, K:].ravel().tolist()) == set(range(2, 10))
+        assert out["S_list"].tolist() == [0, 1]
+        paths.append(out["path"])
+        L.commit()
+    assert paths == [1] + [0] * (w.iters - 1)
+    assert (L.counters["cold"], L.counters["hot_update"], L.counters["hot_skip"]) == (1, 0, w.iters - 1)
+    # a routed expert outside the support: hot-update; no support yet: cold
+    ids = np.ascontiguousarray(out["ids"]).copy()
+    inS = out["inS"]
+    assert orc.support_status(ids, K, inS, True, lib=lib) == 0
+    ids[3, 1] = 12
+    assert orc.support_status(ids, K, inS, True, lib=lib) == 2
+    assert orc.support_status(ids, K, inS, False, lib=lib) == 1
+
+
+def pin_under_covered(orc, lib):
+    """Teardown, Expert Atlas, the U_l equation: a position is under-covered when the
+    support's share of its candidate weight is strictly below alpha times its top-K weight.
+    Hand-worked rows with alpha = 3/4 and S = {0, 2} (C = covered weight, R = top-K weight):
+      row 0  C 150, R 200: 4*150 = 600 = 3*200, on the boundary -> covered
+      row 1  C 120, R 200: 480 < 600                       -> under-covered
+      row 2  C 180, R 180: 720 >= 540                      -> covered
+      row 3  C  60, R 120: 240 < 360                       -> under-covered
+      row 4  C  30, R 120: 120 < 360                       -> under-covered
+      row 5  C  90, R 120: 360 = 360, on the boundary      -> covered"""
+    ids = np.array([[0, 1, 2, 3], [1, 0, 3, 2], [2, 0, 1, 4],
+                    [4, 5, 0, 2], [1, 3, 0, 2], [0, 4, 2, 5]], np.int32)
+    q = np.array([[100, 100, 50, 50], [120, 80, 40, 40], [90, 90, 10, 10],
+                  [60, 60, 30, 30], [80, 40, 20, 10], [60, 60, 30, 30]], np.int64)
+    inS = np.zeros(6, np.uint8)
+    inS[[0, 2]] = 1
+    assert orc.under_covered(ids, q, 2, inS, (3, 4), lib=lib) == 3
+    assert orc.under_covered(ids, q, 2, inS, (0, 1), lib=lib) == 0        # alpha = 0: none
+    assert orc.under_covered(ids, q, 2, np.ones(6, np.uint8), (1, 1), lib=lib) == 0  # C >= R
+    assert orc.under_covered(ids, q, 2, np.zeros(6, np.uint8), (1, 1), lib=lib) == 6
+
+
 def pin_restricted_lifecycle(orc, lib):
     """Support-restricted routing over small blocks:
     - the first forward (cold) and every rebuild route over all experts;
@@ -520,7 +585,8 @@ def pin_live_decode(orc, lib):
 PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
         pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness,
         pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle,
-        pin_group_limited, pin_group_limited_restricted, pin_live_decode]
+        pin_group_limited, pin_group_limited_restricted, pin_live_decode, pin_support_lifecycle,
+        pin_under_covered]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -555,7 +621,9 @@ MUTATIONS = {1: "router bias dropped", 2: "down-projection operand indexed wrong
              5: "refresh-due test dropped", 6: "worklist in position order",
              7: "H_e uses a strict inequality", 8: "restricted top-K ignores the support",
              9: "groups ranked by their first expert, not their best",
-             10: "decoded token ties broken toward the higher id"}
+             10: "decoded token ties broken toward the higher id",
+             11: "support rebuilt when an extra (not routed) candidate lies outside it",
+             12: "boundary rows counted as under-covered (<= instead of <)"}
 
 
 @pytest.mark.parametrize("m", sorted(MUTATIONS), ids=[MUTATIONS[m] for m in sorted(MUTATIONS)])
