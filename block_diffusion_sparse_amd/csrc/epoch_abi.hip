@@ -225,6 +225,21 @@ int device_cu_count() {
 }
 }  // namespace epoch
 
+// The side stream of the current device: one per device for the whole process, created at its
+// first use (default priority, non-blocking) and never destroyed, so that building a plan
+// creates no stream and every plan of a device forks onto the same queue.
+hipStream_t device_side_stream() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
 struct TimedPair {
   int group;
   hipEvent_t a, b;
@@ -265,12 +280,13 @@ struct epoch_plan {
   std::vector<uint8_t> parity;  // which copy of the commit state is current, per layer
   int last_layer = -1;
   uint32_t timing_mask = 0;
-  // Work that does not depend on the rest of the forward runs on a stream of its own, forked
-  // after the caller's earlier work and joined before the combine: the shared expert (it
-  // depends only on x) from the start of the forward, and the compute-bound big-tile routed
+  // Work that does not depend on the rest of the forward runs on the device's side stream,
+  // forked after the caller's earlier work and joined before the combine: the shared expert
+  // (it depends only on x) from the start of the forward, and the compute-bound big-tile routed
   // experts (they depend on the plan step) beside the light tiles' weight stream.  Null when
-  // the layer has neither.
+  // the layer has neither.  The events are the plan's own.
   hipStream_t side = nullptr;
+  bool joined = false;  // `join` has been recorded at least once
   hipEvent_t fork = nullptr, fork_big = nullptr, join = nullptr;
   std::vector<TimedPair> pairs;
   double ms[EPOCH_TIMING_GROUPS] = {};
@@ -369,7 +385,8 @@ int32_t epoch_block_plan_build(const epoch_desc* d, const epoch_layer_weights* w
   p->parity.assign(d->n_layers, 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d->n_shared || s.big_routed) {
-    if (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
+    p->side = device_side_stream();
+    if (!p->side ||
         hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->fork_big, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess) {
@@ -430,7 +447,7 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     tm.done();
   }
   if (e != hipSuccess) return EPOCH_E_HIP;
-  // the big tiles depend on the plan step: forked onto the plan's stream from here
+  // the big tiles depend on the plan step: forked onto the side stream from here
   if (s.big_routed && (hipEventRecord(p->fork_big, st) != hipSuccess ||
                        hipStreamWaitEvent(p->side, p->fork_big, 0) != hipSuccess))
     return EPOCH_E_HIP;
@@ -458,9 +475,12 @@ int32_t epoch_moe_fresh_forward(epoch_plan* p, int32_t layer, const void* x,
     tm.done();
     if (e != hipSuccess) return EPOCH_E_HIP;
   }
-  if (p->side && (hipEventRecord(p->join, p->side) != hipSuccess ||
-                  hipStreamWaitEvent(st, p->join, 0) != hipSuccess))
-    return EPOCH_E_HIP;
+  if (p->side) {
+    if (hipEventRecord(p->join, p->side) != hipSuccess ||
+        hipStreamWaitEvent(st, p->join, 0) != hipSuccess)
+      return EPOCH_E_HIP;
+    p->joined = true;
+  }
   {
     GroupTimer tm(p, st, 6);
     e = launch_combine(s, p->iter[layer], L, W, y, y_routed, st);
@@ -528,10 +548,8 @@ int32_t epoch_block_plan_destroy(epoch_plan* p) {
     pool_release(tp.a);
     pool_release(tp.b);
   }
-  if (p->side) {
-    (void)hipStreamSynchronize(p->side);
-    (void)hipStreamDestroy(p->side);
-  }
+  // the side stream is the device's; the plan's last work on it precedes its join event
+  if (p->joined) (void)hipEventSynchronize(p->join);
   if (p->fork) (void)hipEventDestroy(p->fork);
   if (p->fork_big) (void)hipEventDestroy(p->fork_big);
   if (p->join) (void)hipEventDestroy(p->join);

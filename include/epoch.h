@@ -27,16 +27,18 @@
  *     the descriptor: bf16 (raw 16-bit bfloat16) or fp32.
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (weights, inputs, outputs, workspace); the library never allocates
- *     device memory.  The only allocations are host-side: the plan object and, for
- *     layers with a shared expert, one HIP stream and two events that the plan owns
- *     (created by epoch_block_plan_build on the current device, default priority,
- *     released by epoch_block_plan_destroy).
+ *     device memory.  The only allocations are host-side: the plan object, three
+ *     events per plan for shapes with a shared expert or compute-bound routed tiles
+ *     (created by epoch_block_plan_build, released by epoch_block_plan_destroy), and
+ *     one side stream per device for the whole process (default priority, created at
+ *     the first plan build on that device that needs it, never destroyed).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     only enqueue work on it: no host synchronisation, no host<->device copies.
- *     A forward with a shared expert forks that expert onto the plan's own stream
- *     (an event recorded on `stream`) and joins it back before the combine, so all
- *     of its work is still ordered after earlier work on `stream` and before later
- *     work on it (graph capture of `stream` captures both branches).
+ *     A forward with a shared expert forks that expert onto the device's side
+ *     stream (an event recorded on `stream`) and joins it back before the combine,
+ *     so all of its work is still ordered after earlier work on `stream` and before
+ *     later work on it (graph capture of `stream` captures both branches).  Plans of
+ *     one device share the side stream, so their side work runs in submission order.
  *   - Return value: EPOCH_OK (0) or a negative EPOCH_E_* code; nothing is enqueued
  *     when a call fails its argument checks.  A kernel fault surfaces at the
  *     caller's next synchronisation of the stream.
@@ -132,11 +134,12 @@ typedef struct epoch_desc {
   int32_t routing;      /* EPOCH_ROUTING_EXACT or EPOCH_ROUTING_RESTRICTED */
   int32_t atlas_period; /* restricted mode: rebuild the support after this many iterations
                            (0 = only on the coverage check); must be 0 in exact mode */
-  /* group-limited top-k (teardown, Expert Atlas step three: "the model's group-limited
-     top-k rule"): the experts form n_group contiguous groups of E / n_group ids; each
-     position ranks the groups by their best expert (selection key: logit desc, id asc;
-     in restricted mode among the support's experts) and selects its K_ext candidates and
-     K routed experts among the experts of its topk_group best groups.  n_group <= 1: off.
+  /* group-limited top-k (teardown, Expert Atlas step three, which names the model's own
+     grouped selection rule without defining it): the experts form n_group contiguous
+     groups of E / n_group ids; each position ranks the groups by their best expert
+     (selection key: logit desc, id asc; in restricted mode among the support's experts)
+     and selects its K_ext candidates and K routed experts among the experts of its
+     topk_group best groups.  n_group <= 1: off.
      Otherwise 2 <= n_group <= 64, E % n_group == 0, 1 <= topk_group <= n_group and
      topk_group * E / n_group >= K_ext.  A restricted forward in which some position's
      groups hold fewer than K support experts routes over all experts (full path). */
@@ -250,8 +253,10 @@ int32_t epoch_cache_update(epoch_plan* plan, int32_t layer, void* stream);
    Enqueues nothing; read the buffers after synchronising the stream. */
 int32_t epoch_plan_inspect(const epoch_plan* plan, int32_t layer, epoch_inspect* out);
 
-/* Frees the host-side plan object and its stream and events (the workspace stays the
- * caller's).  Waits for the plan's own stream first.  NULL is a no-op. */
+/* Block end (teardown, Two Clocks: the block plan lives for one diffusion block and is
+ * never carried into the next; a new block starts with a new build).  Frees the host-side
+ * plan object and its events; the workspace stays the caller's.  Waits first for the
+ * plan's latest work on the device's side stream.  NULL is a no-op. */
 int32_t epoch_block_plan_destroy(epoch_plan* plan);
 
 /* Static text for a status code. */
@@ -264,7 +269,7 @@ const char* epoch_status_string(int32_t status);
  * tiles), 5 shared expert, 6 combine, 7 routed gate/up on 256-row compute-bound tiles, 8 routed
  * down on those tiles (7 and 8 only for shapes with big tiles).  While set, the kernels of every
  * selected group of each forward carry a pair of HIP events on the stream the group runs on
- * (the forward's stream, or the plan's own stream for 5, 7 and 8), stamped by the dispatches
+ * (the forward's stream, or the device's side stream for 5, 7 and 8), stamped by the dispatches
  * themselves: the start of the group's first kernel and the end of its last (events come from
  * a process-wide pool, so a measured region reuses events created earlier; a timed dispatch
  * still waits a few microseconds longer for its neighbours, so a measurement that must not

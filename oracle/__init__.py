@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import time
 from typing import Optional
 
 import numpy as np
@@ -60,6 +61,10 @@ def _is_bf16(a: np.ndarray) -> int:
 
 def num_threads(lib=None) -> int:
     return (lib or load()).orc_num_threads()
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    (lib or load()).orc_set_num_threads(_c_int(int(n)))
 
 
 def router_logits(x, Wg, bias=None, lib=None) -> np.ndarray:
@@ -287,6 +292,10 @@ class OracleLayer:
         self.built_iter = 0
 
     def forward(self, x, D, force=None) -> dict:
+        """One forward of the layer.  Wall-clock seconds of its two parts are kept in
+        `last_stage_s` (router, top-k, support, fresh set, worklist over every position) and
+        `last_expert_s` (expert outputs of the evaluated rows, merge of the stable ones)."""
+        t_start = time.perf_counter()
         w, lib = self.w, self.lib
         K, Kext, E = w.top_k, w.k_ext, w.n_experts
         W = self.W
@@ -320,11 +329,14 @@ class OracleLayer:
         R = np.empty((len(rows), H), dtype=np.float64)
         Y = np.empty((len(rows), H), dtype=np.float64)
         x = np.ascontiguousarray(x)
+        t_rows = time.perf_counter()
         lib.orc_moe_rows(_c_int(w.M), _c_int(H), _c_int(I), _c_int(Is), _c_int(E), _c_int(K),
                          _c_int(K), _c_int(_is_bf16(x)), _p(x), _p(rids), _p(rw), _p(fresh),
                          _p(W["w1"]), _p(W["w3"]), _p(W["w2"]), _p(W.get("sw1")),
                          _p(W.get("sw3")), _p(W.get("sw2")), _c_int(len(rows)), _p(rows),
                          _p(self.cache), _p(R), _p(Y))
+        t_end = time.perf_counter()
+        self.last_stage_s, self.last_expert_s = t_rows - t_start, t_end - t_rows
         self._pending = (fresh, np.ascontiguousarray(D, dtype=np.uint8).copy(), anomaly)
         return dict(G=G, ids=ids, s=s, w=wts, q=q, path=path, support_stats=stats,
                     routed_ids=rids, routed_w=rw, inA=self.inA.copy(),

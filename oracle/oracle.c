@@ -44,6 +44,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* threads of the oracle's parallel loops from here on (n >= 1); the baseline timing uses it
+   to time one host core beside all of them */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* element h of a row of bf16 bit patterns (act_bf16) or fp32 values, as double */
 static double ld(const void* base, int act_bf16, size_t idx) {
   if (act_bf16) {

@@ -23,6 +23,7 @@ extern "C" {
 #endif
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 void orc_router_logits(int M, int H, int E, int act_bf16, const void* x, const float* Wg,
                        const float* bias, float* G);
