@@ -291,10 +291,13 @@ class OracleLayer:
         self.inA = np.zeros(E, dtype=np.uint8)
         self.built_iter = 0
 
-    def forward(self, x, D, force=None) -> dict:
-        """One forward of the layer.  Wall-clock seconds of its two parts are kept in
-        `last_stage_s` (router, top-k, support, fresh set, worklist over every position) and
-        `last_expert_s` (expert outputs of the evaluated rows, merge of the stable ones)."""
+    def forward(self, x, D, force=None, rows=None) -> dict:
+        """One forward of the layer.  rows: positions whose outputs this forward evaluates
+        (default: the rows given at construction).  A stable row's output is the oracle's
+        cache row, which holds the row's value only if the row was evaluated at its last fresh
+        iteration.  Wall-clock seconds of the two parts are kept in `last_stage_s` (router,
+        top-k, support, fresh set, worklist over every position) and `last_expert_s` (expert
+        outputs of the evaluated rows, merge of the stable ones)."""
         t_start = time.perf_counter()
         w, lib = self.w, self.lib
         K, Kext, E = w.top_k, w.k_ext, w.n_experts
@@ -325,7 +328,7 @@ class OracleLayer:
         wl = worklist(rids, rw, K, fresh, self.slot_of, len(self.S_list), lib=lib)
         H, I = w.hidden, w.inter
         Is = w.shared_inter if W.get("sw1") is not None else 0
-        rows = self.rows
+        rows = self.rows if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
         R = np.empty((len(rows), H), dtype=np.float64)
         Y = np.empty((len(rows), H), dtype=np.float64)
         x = np.ascontiguousarray(x)

@@ -169,11 +169,28 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
     return True
 
 
+def pick_rows(fresh, known, n, seed):
+    """Rows whose outputs the oracle evaluates in one forward: a seeded sample of n fresh
+    positions (all of them when fewer) and up to n/2 stable positions whose oracle cache row
+    holds a computed value.  `fresh` (the GPU's flags) only chooses the sample; the fresh set
+    itself is compared exactly."""
+    rng = np.random.default_rng(seed)
+    f = np.nonzero(fresh)[0]
+    st = np.nonzero(~fresh & known)[0]
+    pick = set(rng.choice(f, size=min(n, len(f)), replace=False).tolist()) if len(f) else set()
+    if len(st):
+        pick |= set(rng.choice(st, size=min(n // 2, len(st)), replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int32)
+
+
 def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=None, Wdev=None,
               bias_override=None, force_override=None, check=True, verbose=True,
-              D_override=None, hook=None) -> BlockReport:
+              D_override=None, hook=None, fresh_sample=None) -> BlockReport:
     """Replay one block of `iters` iterations over `layers` on GPU and oracle, comparing.
 
+    rows: positions whose outputs the oracle evaluates on every forward (None = all).
+    fresh_sample: instead, a new sample per forward of this many fresh positions plus stable
+    positions whose oracle cache row was computed (pick_rows).
     hook(it, plan, orcs) runs before each iteration (e.g. to rebuild the plan mid-block); it
     may return a replacement (plan, orcs) pair.
     """
@@ -195,6 +212,7 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
     Ddev = to_dev(D)
     Fdev = None if F is None else to_dev(F)
     prev_cache = [None] * len(layers)
+    known = [np.zeros(w.M, dtype=bool) for _ in layers]  # oracle cache rows with a computed value
     for it in range(iters):
         if hook is not None:
             repl = hook(it, plan, orcs)
@@ -209,9 +227,17 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
             plan.forward(li, x, Ddev[it], force, y, yr)
             torch.cuda.synchronize()
             ins = plan.inspect(li)
-            out = orcs[li].forward(X[li][it], D[it], None if F is None else F[it])
+            pick = None
+            if fresh_sample:
+                pick = pick_rows(ins["fresh"].cpu().numpy().astype(bool), known[li], fresh_sample,
+                                 [w.seed, l, it, 99])
+            out = orcs[li].forward(X[li][it], D[it], None if F is None else F[it], rows=pick)
+            ofresh = out["fresh"].astype(bool)
+            evaluated = np.zeros(w.M, dtype=bool)
+            evaluated[out["rows"]] = True
+            known[li] = np.where(ofresh, evaluated, known[li])
             if check:
-                ok = compare_iteration(w, out, ins, y, yr, it, orcs[li].rows, rep, prev_cache[li])
+                ok = compare_iteration(w, out, ins, y, yr, it, out["rows"], rep, prev_cache[li])
                 if not ok:
                     return rep
             prev_cache[li] = ins["cache"].cpu().numpy().copy()
@@ -221,8 +247,9 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
             orcs[li].commit()
         rep.iters += 1
         if verbose:
+            nfr = int(out["fresh"][out["rows"]].sum())
             log(f"  iter {it}: fresh {rep.fresh_counts[-1]}/{w.M} path {rep.paths[-1]} "
-                f"err_y {rep.max_err_y:.2e}")
+                f"rows compared {len(out['rows'])} ({nfr} fresh) err_y {rep.max_err_y:.2e}")
     torch.cuda.synchronize()
     for li, l in enumerate(layers):
         c = plan.counters(li)

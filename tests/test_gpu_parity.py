@@ -69,7 +69,7 @@ def test_workload2_full_size():
     h = H()
     w = synth.workload(2)
     h.log(f"[full] {w.name}")
-    rep = h.run_block(w, rows=sample_rows(w.M, 24, 2))
+    rep = h.run_block(w, fresh_sample=128)
     assert rep.iters == w.iters and rep.stable_rows_checked > 0
 
 
@@ -84,36 +84,50 @@ def test_many_positions_one_expert_per_lane():
 
 
 def test_workload3_full_shape_two_layers():
+    """Layers 0 and 19 of the 20-layer shape in one plan over the whole block of 32
+    iterations (R = 4: refresh-due rows from iteration 4 on)."""
     h = H()
     w = synth.workload(3)
-    h.log(f"[full] {w.name}: layers 0 and 19 of 20, 8 iterations")
-    rep = h.run_block(w, layers=(0, 19), iters=8, rows=sample_rows(w.M, 16, 3))
-    assert rep.iters == 8
+    h.log(f"[full] {w.name}: layers 0 and 19 of 20, 32 iterations, 128 fresh rows a forward")
+    rep = h.run_block(w, layers=(0, 19), fresh_sample=128)
+    assert rep.iters == w.iters
+    assert all(c["due_rows"] > 0 for c in rep.counters)
 
 
-def test_workload4_full_shape_one_layer():
+@pytest.mark.parametrize("layer", [0, 3])
+def test_workload4_full_shape(layer):
+    """One layer of the 4-layer H 4096 shape at a time (host memory) over the whole block of 32
+    iterations; R = 8, so refresh-due rows appear from iteration 8 on."""
     h = H()
     w = synth.workload(4)
-    h.log(f"[full] {w.name}: layer 0 of 4, 5 iterations")
-    rep = h.run_block(w, layers=(0,), iters=5, rows=sample_rows(w.M, 8, 4))
-    assert rep.iters == 5
+    h.log(f"[full] {w.name}: layer {layer} of 4, 32 iterations, 128 fresh rows a forward")
+    rep = h.run_block(w, layers=(layer,), fresh_sample=128)
+    assert rep.iters == w.iters
+    assert rep.counters[0]["due_rows"] > 0
 
 
-@pytest.mark.parametrize("frac,R", [(0.25, 4), (1.0, 1)])
-def test_workload5_sweep_points(frac, R):
+@pytest.mark.parametrize("frac,R,iters", [(0.25, 4, 10), (1.0, 1, 10), (0.5, 4, 32),
+                                          (0.1, 16, 32), (0.05, 16, 32), (0.05, 4, 10)])
+def test_workload5_sweep_points(frac, R, iters):
+    """Forced-fraction sweep points of the 8192-position shape (hidden state redrawn every 8
+    iterations, so the support is rebuilt mid-block)."""
     h = H()
     w = synth.workload(5, forced_fraction=frac, staleness_R=R)
-    h.log(f"[full] {w.name}: f={frac} R={R}, 10 iterations (hidden state redrawn at 8)")
-    rep = h.run_block(w, iters=10, rows=sample_rows(w.M, 8, 5))
-    assert rep.iters == 10
+    h.log(f"[full] {w.name}: f={frac} R={R}, {iters} iterations, 128 fresh rows a forward")
+    rep = h.run_block(w, iters=iters, fresh_sample=128)
+    assert rep.iters == iters
     if R == 1:
         assert all(c == w.M for c in rep.fresh_counts)
+    # the rotating forced window refreshes each position every ~1/f iterations, so rows reach
+    # the age bound R only when that period exceeds it
+    if 1.0 / frac > R + 1 and iters > R + 1:
+        assert rep.counters[0]["due_rows"] > 0
 
 
 @pytest.mark.parametrize("frac,R", [(1.0, 1), (0.5, 4)])
 def test_big_tiles_every_row(frac, R):
     """Shapes whose iterations can hold >= 32768 pairs route experts with >= 768 fresh rows
-    to 128-row compute-bound tiles and run the shared expert (M >= 2048) on them too.  Small
+    to 256-row compute-bound tiles and run the shared expert (M >= 2048) on them too.  Small
     hidden/inter sizes keep the oracle quick, so every row is compared; H = 192 leaves a
     partial 128-column block in the down projection, and the skewed bias gives a mix of
     big-tile experts (ragged last tile) and weight-stream experts in the same iteration."""
@@ -137,7 +151,7 @@ def test_big_tiles_every_row(frac, R):
 
 def test_kernel_timing_on_both_streams():
     """Kernel timing with every group on, at a shape with big tiles and a shared expert: the
-    shared expert and the big tiles run on the plan's own stream and are timed there, and
+    shared expert and the big tiles run on the device's side stream and are timed there, and
     every group reads back one duration per forward."""
     h = H()
     w = synth.workload(5, hidden=192, n_experts=12, top_k=2, inter=128, shared_inter=192,
