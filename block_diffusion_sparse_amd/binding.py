@@ -19,6 +19,8 @@ EPOCH_DTYPE_F32, EPOCH_DTYPE_BF16 = 0, 1
 EPOCH_ROUTING_EXACT, EPOCH_ROUTING_RESTRICTED = 0, 1
 EPOCH_NUM_COUNTERS = 20
 EPOCH_TIMING_GROUPS = 9
+EPOCH_E_SCRATCH = -9
+EPOCH_DECODE_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024
 COUNTERS = ["cold", "hot_update", "hot_skip", "anomaly", "fresh_rows", "pairs", "unmet",
             "forced_rows", "due_rows", "support_size", "u_final", "repair_rounds", "touched",
             "forwards", "reserved14", "restricted", "coverage_fallback", "period_update",
@@ -88,7 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.epoch_decode_workspace_bytes.argtypes = [P(epoch_decode_desc), P(ctypes.c_size_t)]
     lib.epoch_live_decode.argtypes = [P(epoch_decode_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_size_t, _vp]
-    for fn in ("epoch_plan_workspace_bytes", "epoch_block_plan_build", "epoch_moe_fresh_forward",
+    lib.epoch_live_decode_static.argtypes = [P(epoch_decode_desc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp]
+    for fn in ("epoch_live_decode_static", "epoch_plan_workspace_bytes", "epoch_block_plan_build", "epoch_moe_fresh_forward",
                "epoch_cache_update", "epoch_plan_inspect", "epoch_block_plan_destroy",
                "epoch_plan_set_timing", "epoch_plan_timing", "epoch_decode_workspace_bytes",
                "epoch_live_decode"):
@@ -206,3 +210,11 @@ def epoch_live_decode(desc: epoch_decode_desc, h, w_vocab, decoded, decoded_next
                                     _ptr(decoded_next), _ptr(tokens), _ptr(conf),
                                     _ptr(workspace), ctypes.c_size_t(workspace_bytes),
                                     _stream(stream)))
+
+
+def epoch_live_decode_static(desc: epoch_decode_desc, h, w_vocab, decoded, decoded_next, tokens,
+                             conf, stream=None):
+    _check("epoch_live_decode_static",
+           load().epoch_live_decode_static(ctypes.byref(desc), _ptr(h), _ptr(w_vocab),
+                                           _ptr(decoded), _ptr(decoded_next), _ptr(tokens),
+                                           _ptr(conf), _stream(stream)))

@@ -24,6 +24,7 @@
 #include "epoch_internal.h"
 #include "expert_gemm.h"
 
+#include <mutex>
 #include <new>
 
 namespace epoch {
@@ -235,33 +236,24 @@ int32_t check_decode_desc(const epoch_decode_desc* d) {
   return EPOCH_OK;
 }
 
-}  // namespace
-}  // namespace epoch
-
-using namespace epoch;
-
-extern "C" {
-
-int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes) {
-  if (!out_bytes) return EPOCH_E_NULL;
+int32_t check_decode_args(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                          const uint8_t* decoded, const uint8_t* decoded_next,
+                          const int32_t* tokens) {
   const int32_t rc = check_decode_desc(d);
   if (rc) return rc;
-  *out_bytes = decode_carve(d, nullptr).bytes;
+  if (!h || !w_vocab || !decoded || !decoded_next || !tokens) return EPOCH_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(w_vocab)) & 15u)
+    return EPOCH_E_ALIGN;
   return EPOCH_OK;
 }
 
-int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void* w_vocab,
-                          const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
-                          float* conf, void* workspace, size_t workspace_bytes, void* stream) {
-  const int32_t rc = check_decode_desc(d);
-  if (rc) return rc;
-  if (!h || !w_vocab || !decoded || !decoded_next || !tokens || !workspace) return EPOCH_E_NULL;
-  if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(w_vocab)) & 15u)
-    return EPOCH_E_ALIGN;
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EPOCH_E_WORKSPACE;
-  const DecodeLayout L = decode_carve(d, workspace);
-  if (workspace_bytes < L.bytes) return EPOCH_E_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// The launch sequence of one decoding step on the buffers of L.  Every scratch buffer is
+// written before it is read (live list and index for all M positions, partials for the live
+// rows the row kernel reads, confidences and tokens for all positions), so nothing needs to
+// start at zero and a scratch area that holds an earlier call's contents is fine.
+int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                       const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens, float* conf,
+                       const DecodeLayout& L, hipStream_t st) {
   const int M = d->batch * d->block, n_p = d->vocab / 32;
   launch(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
                      L.live_list, L.live_idx, L.n_live);
@@ -298,6 +290,70 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
   launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, d->tau, decoded,
          L.conf_pos, L.top_pos, decoded_next, tokens, conf);
   return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;
+}
+
+// Scratch of epoch_live_decode_static, for callers that cannot allocate device memory: one
+// array per device, kept by the loaded library until the process ends.  Host code never uses
+// the array's name as an address (on the host it names a stand-in, not device memory); it uses
+// the device address looked up below.
+constexpr size_t kDecodeStaticScratchBytes = EPOCH_DECODE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per device (the first
+// static call on it) and kept; null if the lookup fails.
+void* static_scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+}  // namespace epoch
+
+using namespace epoch;
+
+extern "C" {
+
+int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes) {
+  if (!out_bytes) return EPOCH_E_NULL;
+  const int32_t rc = check_decode_desc(d);
+  if (rc) return rc;
+  *out_bytes = decode_carve(d, nullptr).bytes;
+  return EPOCH_OK;
+}
+
+int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                          const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
+                          float* conf, void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t rc = check_decode_args(d, h, w_vocab, decoded, decoded_next, tokens);
+  if (rc) return rc;
+  if (!workspace) return EPOCH_E_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return EPOCH_E_WORKSPACE;
+  const DecodeLayout L = decode_carve(d, workspace);
+  if (workspace_bytes < L.bytes) return EPOCH_E_WORKSPACE;
+  return decode_enqueue(d, h, w_vocab, decoded, decoded_next, tokens, conf, L,
+                        static_cast<hipStream_t>(stream));
+}
+
+int32_t epoch_live_decode_static(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                                 const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
+                                 float* conf, void* stream) {
+  const int32_t rc = check_decode_args(d, h, w_vocab, decoded, decoded_next, tokens);
+  if (rc) return rc;
+  if (decode_carve(d, nullptr).bytes > kDecodeStaticScratchBytes) return EPOCH_E_SCRATCH;
+  void* base = static_scratch_address();
+  if (!base) return EPOCH_E_HIP;
+  return decode_enqueue(d, h, w_vocab, decoded, decoded_next, tokens, conf,
+                        decode_carve(d, base), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -568,6 +568,8 @@ const char* epoch_status_string(int32_t status) {
     case EPOCH_E_STATE: return "commit without a preceding forward of that layer";
     case EPOCH_E_HIP: return "a kernel launch failed";
     case EPOCH_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case EPOCH_E_SCRATCH:
+      return "the shape needs more scratch than the library's static device array holds";
     default: return "unknown status";
   }
 }

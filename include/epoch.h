@@ -27,7 +27,9 @@
  *     the descriptor: bf16 (raw 16-bit bfloat16) or fp32.
  *   - Device pointers must be 16-byte aligned.  The caller owns every device
  *     buffer (weights, inputs, outputs, workspace); the library never allocates
- *     device memory.  The only allocations are host-side: the plan object, three
+ *     device memory (its one device array, the scratch of epoch_live_decode_static,
+ *     is part of the loaded code object).  The only allocations are host-side: the
+ *     plan object, three
  *     events per plan for shapes with a shared expert or compute-bound routed tiles
  *     (created by epoch_block_plan_build, released by epoch_block_plan_destroy), and
  *     one side stream per device for the whole process (default priority, created at
@@ -63,7 +65,8 @@ enum {
   EPOCH_E_LAYER = -5,     /* layer index out of range */
   EPOCH_E_STATE = -6,     /* commit without a preceding forward of that layer */
   EPOCH_E_HIP = -7,       /* a kernel launch failed */
-  EPOCH_E_ALIGN = -8      /* a tensor pointer is not 16-byte aligned */
+  EPOCH_E_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned */
+  EPOCH_E_SCRATCH = -9    /* the call needs more scratch than the library's static array holds */
 };
 
 enum { EPOCH_GATE_SOFTMAX = 0, EPOCH_GATE_SIGMOID = 1 };
@@ -321,6 +324,27 @@ int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_byt
 int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void* w_vocab,
                           const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
                           float* conf, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * epoch_live_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same kernels and outputs as epoch_live_decode, with its scratch (live list,
+ * per-row partial reductions, per-position confidences) in a device array of
+ * EPOCH_DECODE_STATIC_SCRATCH_BYTES that the library holds on each device it runs on until
+ * the process ends; the device address of that array is looked up once per device, at the
+ * first call on it (with that device current).  The call allocates nothing and calls no
+ * allocating routine.  A shape whose epoch_decode_workspace_bytes exceeds
+ * EPOCH_DECODE_STATIC_SCRATCH_BYTES returns EPOCH_E_SCRATCH and enqueues nothing (for example
+ * 512 positions at a 131072-token vocabulary fit, 2048 do not).  Every call on a device uses
+ * the same array: calls whose work overlaps on one device (unordered streams, several host
+ * threads) race and give undefined results; order them on one stream.  The array keeps the
+ * latest call's contents; every buffer in it is written before it is read, so nothing needs
+ * clearing between calls.  Arguments and errors otherwise as for epoch_live_decode.
+ */
+enum { EPOCH_DECODE_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024 };
+int32_t epoch_live_decode_static(const epoch_decode_desc* d, const void* h, const void* w_vocab,
+                                 const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens,
+                                 float* conf, void* stream);
 
 #ifdef __cplusplus
 }

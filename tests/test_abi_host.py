@@ -96,3 +96,24 @@ def test_decode_workspace_query_and_argument_errors():
     with pytest.raises(B.EpochError) as ei:   # NULL tensors: checked before any launch
         B.epoch_live_decode(d, 0, 0, 0, 0, 0, None, 256, n, 0)
     assert ei.value.status == -1
+
+
+def test_static_decode_rejects_shapes_beyond_its_scratch():
+    """The workspace-free decoding call checks its shape against the static scratch array on
+    the host and enqueues nothing for a shape that does not fit (no GPU involved)."""
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libepoch.so not built")
+    cap = B.EPOCH_DECODE_STATIC_SCRATCH_BYTES
+    fits = B.make_decode_desc(16, 32, 2048, 131072)          # 512 positions
+    big = B.make_decode_desc(64, 32, 2048, 131072)           # 2048 positions
+    assert B.epoch_decode_workspace_bytes(fits) <= cap < B.epoch_decode_workspace_bytes(big)
+    with pytest.raises(B.EpochError) as ei:   # aligned stand-in pointers: never dereferenced
+        B.epoch_live_decode_static(big, 256, 256, 256, 256, 256, None, 0)
+    assert ei.value.status == B.EPOCH_E_SCRATCH
+    assert "static" in B.epoch_status_string(B.EPOCH_E_SCRATCH)
+    with pytest.raises(B.EpochError) as ei:
+        B.epoch_live_decode_static(fits, 0, 256, 256, 256, 256, None, 0)
+    assert ei.value.status == -1
+    with pytest.raises(B.EpochError) as ei:
+        B.epoch_live_decode_static(fits, 8, 256, 256, 256, 256, None, 0)
+    assert ei.value.status == -8
