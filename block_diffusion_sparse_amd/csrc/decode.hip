@@ -12,7 +12,7 @@
 //                   vocabulary streamed through LDS once per 256 live rows (the slab's further
 //                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
 //                   each row's 32-token blocks to (max, argmax, sum exp);
-//   k_gemm_big      LM-head mode, when more are live: 256 live rows x 128 tokens per
+//   k_gemm_big      LM-head mode, when more are live: 256 live rows x 256 tokens per
 //                   workgroup on the compute-bound tiles, the same partials over 64-token
 //                   blocks (one wave's columns);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
@@ -35,9 +35,12 @@ constexpr int kCompactThreads = 1024;
 // (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
 constexpr int kLmStreamBuffers = 2;
 constexpr int kLmStreamTileRows = 256;
-// beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 128 tokens (waves
-// of 128 x 64 outputs: a quarter less LDS fragment traffic per MFMA than 128-row tiles)
+// beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 256 tokens, eight
+// waves of 128 x 64 outputs, one workgroup per CU (half the operand bytes per MFMA of
+// 256 x 128 tiles, and a vocabulary gives plenty of token blocks)
 constexpr int kLmBigTileRows = 256;
+constexpr int kLmBigWaves = 8;
+constexpr int kLmBigTileCols = 32 * kLmBigWaves;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
                                                                   const uint8_t* __restrict__ D,
@@ -277,11 +280,14 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
     }
   }
   // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
-  // at once) x token blocks per XCD
-  const int tiles = (M + kLmBigTileRows - 1) / kLmBigTileRows, n_cb = d->vocab / 128;
+  // at once) x token blocks per XCD; blocks of kLmBigTileCols tokens (the last one half when
+  // the vocabulary is an odd multiple of 128)
+  const int tiles = (M + kLmBigTileRows - 1) / kLmBigTileRows;
+  const int n_cb = (d->vocab + kLmBigTileCols - 1) / kLmBigTileCols;
   const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, d->vocab / 64};
-  launch((k_gemm_big<false, false, true, kLmBigTileRows>), dim3(8 * tiles * ((n_cb + 7) / 8)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(h),
+  launch((k_gemm_big<false, false, true, kLmBigTileRows, kLmBigWaves>),
+                     dim3(8 * tiles * ((n_cb + 7) / 8)), dim3(64 * kLmBigWaves), 0, st,
+                     static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));

@@ -83,8 +83,9 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // 16 l) moves eight whole lines.  Every wave copies its own 32 weight rows with the
 // non-temporal policy (whole lines streamed that way sustain a higher HBM rate) and its share
 // of the activation rows with the cached one (the tile's other column blocks read them again).
-// LDS rows of 128 bytes hold k-segment slot ^ ((row >> 1) & 7) in 16-byte slot `slot`, so the
-// 16 rows of an MFMA fragment read fall on distinct banks.
+// LDS rows of 128 bytes hold k-segment slot ^ (row & 7) in 16-byte slot `slot`: ds_read_b128
+// is served eight lanes at a time, 128 bytes a cycle, and the eight rows those lanes read then
+// sit in eight different slots, i.e. on distinct banks (no bank conflicts).
 //
 // Synchronisation (NB chunk buffers): step q waits for its own copies of chunk q (vmcnt; the
 // NB - 2 chunks after it may stay in flight), meets the barrier (every wave's copies of chunk q
@@ -196,7 +197,7 @@ __device__ __forceinline__ void expert_stream_body(
     for (int j = 0; j < NAW; ++j) {
       const int row0 = 8 * (NAW * wave + j);
       const int row = row0 + lrow;
-      const int lslot = pslot ^ ((row >> 1) & 7);
+      const int lslot = pslot ^ (row & 7);
       int src_row;
       if ((ROUTED && GATEUP) || LMHEAD) {
         // the eight gathered rows of this copy (rows past the tile repeat its last row)
@@ -213,8 +214,8 @@ __device__ __forceinline__ void expert_stream_body(
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int row = 8 * j + lrow;  // within the wave's 32 rows; (32 w + row) >> 1 & 7 == row >> 1 & 7
-      const int lslot = pslot ^ ((row >> 1) & 7);
+      const int row = 8 * j + lrow;  // within the wave's 32 rows; (32 w + row) & 7 == row & 7
+      const int lslot = pslot ^ (row & 7);
       int wrow;
       const uint16_t* base;
       if (GATEUP) {
@@ -253,9 +254,9 @@ __device__ __forceinline__ void expert_stream_body(
 
   f32x4 c0[MB], c1[MB];
   // fragments: k-step s of a chunk is k-segment 4 s + g for lane (r, g), held in slot
-  // (4 s + g) ^ ((r >> 1) & 7) of LDS rows 16 m + r (activations) and 32 w + r, 32 w + 16 + r
+  // (4 s + g) ^ (r & 7) of LDS rows 16 m + r (activations) and 32 w + r, 32 w + 16 + r
   // (weights)
-  const int key = (r >> 1) & 7;
+  const int key = r & 7;
   const int off0 = (g ^ key) * 8, off1 = ((4 + g) ^ key) * 8;
   // activation fragments are read FG row blocks at a time (all of them up to 8 blocks, else in
   // groups of 4, which keeps a 256-row tile's registers within two waves per SIMD)
@@ -471,24 +472,30 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
 
 // Compute-bound variant for tiles with many rows (the shared expert over all M positions,
 // routed experts with many fresh pairs, the LM head over the live positions): a BR-row x
-// 128-weight-row output tile per workgroup, four waves in a 2 x 2 arrangement, each
-// accumulating a (BR / 2) x 64 sub-tile with v_mfma_f32_16x16x32_bf16 (BR / 32 x 4 blocks).
+// BC-weight-row output tile per workgroup of WAVES waves, two along the rows and WAVES / 2 along
+// the weight rows, each wave accumulating a (BR / 2) x 64 sub-tile with v_mfma_f32_16x16x32_bf16
+// (BR / 32 x 4 blocks), so BC = 32 WAVES.  Four waves (BC = 128) run two workgroups per CU; eight
+// waves (BR = 256, BC = 256, one workgroup per CU) halve the operand bytes copied per MFMA,
+// which pays on problems with enough tiles to fill the device.
 // K runs in chunks of KC = 32.  Both operands of a chunk go from global memory straight into
 // LDS (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 x lane),
 // NB chunk buffers deep, NB - 2 chunks in flight while a chunk is multiplied.  LDS rows of
-// KC = 32 bf16 (64 bytes, four 16-byte slots) hold k-segment slot ^ ((row >> 2) & 3) in slot
-// `slot`: a lane fetches the segment its slot must hold, so the 16 rows of an MFMA fragment
-// fall on distinct banks.  Rows past the tile (and weight rows past N) load a stand-in row of
-// the same operand: they only feed outputs that are never stored.
+// KC = 32 bf16 (64 bytes, four 16-byte slots) hold k-segment slot ^ ((row >> 1) & 3) in slot
+// `slot`: a lane fetches the segment its slot must hold.  ds_read_b128 is served eight lanes
+// (eight consecutive rows of a fragment, two per 128 bytes) at a time, and with this key those
+// eight rows occupy eight distinct 16-byte bank groups, so fragment reads have no bank
+// conflicts.  Rows past the tile (and weight rows past N) load a stand-in row of the same
+// operand: they only feed outputs that are never stored.
 // Synchronisation is explicit: before each barrier a wave waits for its own copies of the next
 // chunk (vmcnt) and for its LDS reads (lgkmcnt); the fragment reads are inline ds_read_b128,
 // because the compiler, which cannot tell chunk buffers apart, would otherwise wait for every
-// copy in flight before any LDS read.  Gate/up: the 128 staged weight rows are
-// [W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, W3 i0+32..i0+64], so each wave holds g and u of
-// the same 32 columns and the SwiGLU epilogue stays in registers; down: 128 rows of W2.
-// Grid as k_expert_stream (XCD-grouped, 1-D): 64 (gate/up) or 128 (down) columns per block.
-template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128>
-__global__ __launch_bounds__(256, 2) void k_gemm_big(
+// copy in flight before any LDS read.  Gate/up: the BC staged weight rows are groups of 32 rows
+// alternating W1 and W3 ([W1 i0..i0+32, W3 i0..i0+32, W1 i0+32..i0+64, ...]), so each wave
+// holds g and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: BC
+// rows of W2.  Grid as k_expert_stream (XCD-grouped, 1-D): BC / 2 (gate/up) or BC (down)
+// columns per block.
+template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
@@ -497,11 +504,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
   static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
   static_assert(BR == 128 || BR == 256, "row tiles of 128 or 256");
-  constexpr int KC = 32, BC = 128;
-  constexpr int MB = BR / 32;                // 16-row blocks per wave
-  constexpr int NB = BR == 256 ? 3 : 4;      // LDS chunk buffers (2 workgroups per CU)
-  constexpr int NA = BR / 64, NBI = BC / 64; // copies per wave and chunk: A rows, B rows
-  constexpr int CBW = GATEUP ? 64 : 128;
+  static_assert(WAVES == 4 || (WAVES == 8 && BR == 256), "four waves, or eight on 256-row tiles");
+  constexpr int KC = 32, WN = WAVES / 2, BC = 64 * WN;
+  constexpr int MB = BR / 32;                                   // 16-row blocks per wave
+  constexpr int NB = WAVES == 8 ? 4 : (BR == 256 ? 3 : 4);      // LDS chunk buffers
+  constexpr int NA = BR / (16 * WAVES), NBI = BC / (16 * WAVES);  // copies per wave and chunk
+  constexpr int CBW = GATEUP ? BC / 2 : BC;                     // output columns per block
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BC * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
@@ -530,30 +538,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   const int wm = wave & 1, wn = wave >> 1;
   const size_t estride = (size_t)Ndim * Kdim;
   const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
-  // copy sources: copy j of wave w fills LDS rows [64 j + 16 w, +16) of a chunk buffer, lane l
-  // slot l % 4 of row 64 j + 16 w + l / 4
+  // copy sources: copy j of wave w fills LDS rows [16 (WAVES j + w), +16) of a chunk buffer,
+  // lane l slot l % 4 of row 16 (WAVES j + w) + l / 4
   const uint16_t* asrc[NA];
   const uint16_t* bsrc[NBI];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
-    const int row = 64 * j + 16 * wave + (lane >> 2);
-    const int c8 = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = 16 * (WAVES * j + wave) + (lane >> 2);
+    const int c8 = (lane & 3) ^ ((row >> 1) & 3);
     const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
     const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p);
     asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
   }
 #pragma unroll
   for (int j = 0; j < NBI; ++j) {
-    const int row = 64 * j + 16 * wave + (lane >> 2);
-    const int c8 = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = 16 * (WAVES * j + wave) + (lane >> 2);
+    const int c8 = (lane & 3) ^ ((row >> 1) & 3);
     int wrow;
     const uint16_t* base;
     if (GATEUP) {
-      const int q = row >> 5;  // quarter: W1, W3, W1, W3
-      wrow = cb * 64 + (q >> 1) * 32 + (row & 31);
+      const int q = row >> 5;  // groups of 32 staged rows: W1, W3, W1, W3, ...
+      wrow = cb * CBW + (q >> 1) * 32 + (row & 31);
       base = (q & 1) ? B1 : B0;
     } else {
-      wrow = cb * 128 + row;
+      wrow = cb * BC + row;
       base = B0;
     }
     bsrc[j] = base + e * estride + (size_t)(wrow < Ndim ? wrow : 0) * Kdim + c8 * 8;
@@ -561,19 +569,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   auto issue = [&](int c, int buf) {
 #pragma unroll
     for (int j = 0; j < NA; ++j)
-      copy16_to_lds(asrc[j] + (size_t)c * KC, &As[buf][(64 * j + 16 * wave) * KC]);
+      copy16_to_lds(asrc[j] + (size_t)c * KC, &As[buf][16 * (WAVES * j + wave) * KC]);
 #pragma unroll
     for (int j = 0; j < NBI; ++j)
-      copy16_to_lds(bsrc[j] + (size_t)c * KC, &Bs[buf][(64 * j + 16 * wave) * KC]);
+      copy16_to_lds(bsrc[j] + (size_t)c * KC, &Bs[buf][16 * (WAVES * j + wave) * KC]);
   };
   f32x4 acc[MB][4];
 #pragma unroll
   for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
-  // fragments of one chunk: lane (r, g) reads slot g ^ ((r >> 2) & 3) of rows 16 m + r; two
+  // fragments of one chunk: lane (r, g) reads slot g ^ ((r >> 1) & 3) of rows 16 m + r; two
   // register sets, so that chunk c + 1 is read from LDS while c is multiplied
-  const int swz = (g ^ ((r >> 2) & 3)) * 8;
+  const int swz = (g ^ ((r >> 1) & 3)) * 8;
   u32x4 fa[2][MB], fb[2][4];
   auto read_frags = [&](int buf, int set) {
     const uint32_t ab = (uint32_t)(uintptr_t)&As[buf][(BR / 2 * wm + r) * KC + swz];
@@ -663,13 +671,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
   if (LMHEAD) {
     // per row: the 64 logits of this wave's token columns sit in the 16 lanes with the same g,
     // four per lane (token 16 n + r), reduced over the wave's 64 tokens to (max, lower token
-    // on ties) and then the sum of exp(logit - max)
+    // on ties) and then the sum of exp(logit - max); a wave whose columns lie past the
+    // vocabulary (the last block of a vocabulary that is an odd multiple of 128 tokens, with
+    // 256-column blocks) writes nothing
+    if (cb * BC + 64 * wn >= Ndim) return;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
-        const int col0 = cb * 128 + 64 * wn + r;
+        const int col0 = cb * BC + 64 * wn + r;
         float mx = acc[m][0][q];
         int arg = col0;
 #pragma unroll
@@ -692,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
         if (r == 0 && row < tr.row_end) {
-          const size_t idx = (size_t)row * lp.n_p + 2 * cb + wn;
+          const size_t idx = (size_t)row * lp.n_p + WN * cb + wn;
           lp.pmax[idx] = mx;
           lp.parg[idx] = arg;
           lp.psum[idx] = se;
@@ -709,7 +720,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
     if (GATEUP) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const int col = cb * 64 + 32 * wn + 16 * n + 4 * g;
+        const int col = cb * CBW + 32 * wn + 16 * n + 4 * g;
         if (col >= Ndim) continue;
         uint16_t hv[4];
 #pragma unroll
@@ -724,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
       const float sc = ROUTED ? wl_w[row] : 1.0f;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int col = cb * 128 + 64 * wn + 16 * n + 4 * g;
+        const int col = cb * BC + 64 * wn + 16 * n + 4 * g;
         if (col >= Ndim) continue;
         uint16_t yv[4];
 #pragma unroll

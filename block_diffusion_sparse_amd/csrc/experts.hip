@@ -25,6 +25,11 @@ constexpr int kLdsPerCu = 160 * 1024;
 // 128 x 128 kernel; below it the weight-stream kernel has more workgroups to spread
 constexpr int kBigTileMinRows = 2048;
 constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups per CU remain
+// waves of the compute-bound routed tiles (kBigTile rows x 32 kBigWaves weight rows): four, two
+// workgroups per CU.  Eight (256 x 256 tiles, one workgroup per CU) measured no faster at the
+// 8192-position shape, where these tiles run beside the weight-stream kernel and the larger
+// workgroup no longer fits in the LDS it leaves free.
+constexpr int kBigWaves = 4;
 
 // Workgroups of k_expert_stream with lds bytes each that fit on the device at once, at most
 // per_cu per CU, as a multiple of 8 (one per XCD lane).
@@ -146,9 +151,10 @@ hipError_t launch_routed_gateup(const Shape& s, const void* x, const void* w1, c
 hipError_t launch_routed_gateup_big(const Shape& s, const void* x, const void* w1,
                                     const void* w3, const LayerState& L, const Scratch& W,
                                     hipStream_t st) {
-  // experts with many fresh rows: compute-bound kBigTile x 128 tiles
-  launch((k_gemm_big<true, true, false, kBigTile>),
-         dim3(((s.T_big_max + 7) / 8) * 8 * (s.I / 64)), dim3(256), 0, st,
+  // experts with many fresh rows: compute-bound kBigTile-row tiles
+  launch((k_gemm_big<true, true, false, kBigTile, kBigWaves>),
+         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.I + 16 * kBigWaves - 1) / (16 * kBigWaves))),
+         dim3(64 * kBigWaves), 0, st,
          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b, W.offs,
          L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M, s.H, s.I, LmPartials{});
@@ -170,8 +176,9 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
 
 hipError_t launch_routed_down_big(const Shape& s, const void* w2, const LayerState& L,
                                   const Scratch& W, hipStream_t st) {
-  launch((k_gemm_big<false, true, false, kBigTile>),
-         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 127) / 128)), dim3(256), 0, st,
+  launch((k_gemm_big<false, true, false, kBigTile, kBigWaves>),
+         dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 32 * kBigWaves - 1) / (32 * kBigWaves))),
+         dim3(64 * kBigWaves), 0, st,
          static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2), nullptr, W.flags,
          W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list, W.wl_pos, W.wl_w,
          static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H, LmPartials{});
