@@ -41,8 +41,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.orc_route_restricted.restype = _c_int
     lib.orc_group_allowed.restype = None
     lib.orc_live_decode.restype = _c_int
-    for name in ("orc_router_logits", "orc_route", "orc_expert", "orc_moe_rows", "orc_commit",
-                 "orc_dense_moe"):
+    for name in ("orc_router_logits", "orc_route", "orc_score_given", "orc_expert",
+                 "orc_moe_rows", "orc_commit", "orc_dense_moe"):
         getattr(lib, name).restype = None
     _libs[path] = lib
     return lib
@@ -96,6 +96,33 @@ def route(G, K, Kext, gate_sigmoid, norm_topk, allowed=None, lib=None):
     lib.orc_route(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _c_int(int(gate_sigmoid)),
                   _c_int(int(norm_topk)), _p(G), _p(al), _p(ids), _p(s), _p(w), _p(q))
     return ids, s, w, q
+
+
+def score_given(G, ids, K, gate_sigmoid, norm_topk, lib=None):
+    """Scores s, routing weights w and planner weights q of a given ranked selection ids
+    [M x Kext] (the scoring half of route)."""
+    lib = lib or load()
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    M, E = G.shape
+    Kext = ids.shape[1]
+    s = np.empty((M, Kext), dtype=np.float64)
+    w = np.empty((M, K), dtype=np.float64)
+    q = np.empty((M, Kext), dtype=np.int64)
+    lib.orc_score_given(_c_int(M), _c_int(E), _c_int(K), _c_int(Kext), _c_int(int(gate_sigmoid)),
+                        _c_int(int(norm_topk)), _p(G), _p(ids), _p(s), _p(w), _p(q))
+    return s, w, q
+
+
+def tie_order_ok(g_row, ids_row, alt_row, tie):
+    """True if alt_row ranks the same candidates as ids_row up to ties: distinct experts whose
+    logit at every rank is within `tie` of the logit the key order puts there (an order that
+    differs only among logits closer than `tie`)."""
+    g = np.asarray(g_row, dtype=np.float64)
+    alt = np.asarray(alt_row)
+    if len(set(alt.tolist())) != len(alt):
+        return False
+    return bool(np.all(np.abs(g[alt] - g[np.asarray(ids_row)]) < tie))
 
 
 def group_allowed(G, n_group, topk_group, base=None, lib=None):
@@ -266,6 +293,7 @@ class OracleLayer:
     """
 
     NEG_INF_ITER = -(1 << 30)
+    TIE = 1e-6  # logits closer than this are a tie: either order is a correct ranking
 
     def __init__(self, w, weights: dict, lib=None, rows=None):
         self.lib = lib or load()
@@ -291,7 +319,19 @@ class OracleLayer:
         self.inA = np.zeros(E, dtype=np.uint8)
         self.built_iter = 0
 
-    def forward(self, x, D, force=None, rows=None) -> dict:
+    def route(self, x) -> dict:
+        """Router logits and the ranked candidates of every position (no state is touched)."""
+        w, lib, W = self.w, self.lib, self.W
+        G = router_logits(x, W["router_w"], W["router_b"], lib=lib)
+        # group-limited rule: each row selects among the experts of its best groups
+        allowed = (group_allowed(G, w.n_group, w.topk_group, lib=lib) if w.n_group > 1
+                   else None)
+        ids, s, wts, q = route(G, w.top_k, w.k_ext, w.gate == "sigmoid", w.norm_topk,
+                               allowed=allowed, lib=lib)
+        return dict(G=G, ids=ids, s=s, w=wts, q=q)
+
+    def forward(self, x, D, force=None, rows=None, pre=None, tie_ids=None,
+                tie_routed=None) -> dict:
         """One forward of the layer.  rows: positions whose outputs this forward evaluates
         (default: the rows given at construction).  A stable row's output is the oracle's
         cache row, which holds the row's value only if the row was evaluated at its last fresh
@@ -302,15 +342,21 @@ class OracleLayer:
         w, lib = self.w, self.lib
         K, Kext, E = w.top_k, w.k_ext, w.n_experts
         W = self.W
-        G = router_logits(x, W["router_w"], W["router_b"], lib=lib)
-        # group-limited rule: each row selects among the experts of its best groups
-        allowed = (group_allowed(G, w.n_group, w.topk_group, lib=lib) if w.n_group > 1
-                   else None)
-        ids, s, wts, q = route(G, K, Kext, w.gate == "sigmoid", w.norm_topk, allowed=allowed,
-                               lib=lib)
+        r = self.route(x) if pre is None else pre
+        G, ids, s, wts, q = r["G"], r["ids"], r["s"], r["w"], r["q"]
+        if tie_ids:
+            # positions whose ranking is a tie of their logits take the given (equally correct)
+            # order, checked against this forward's own logits; their scores follow from it
+            ids, s, wts, q = ids.copy(), s.copy(), wts.copy(), q.copy()
+            for t, alt in tie_ids.items():
+                assert tie_order_ok(G[t], ids[t], alt, self.TIE), f"row {t}: not a tie order"
+                ids[t] = alt
+            tr = np.array(sorted(tie_ids), dtype=np.int64)
+            s[tr], wts[tr], q[tr] = score_given(G[tr], ids[tr], K, w.gate == "sigmoid",
+                                                w.norm_topk, lib=lib)
         stats = None
         if w.routing == "restricted":
-            path, stats, rids, rw = self._restricted_step(G, ids, q, wts)
+            path, stats, rids, rw = self._restricted_step(G, ids, q, wts, tie_routed)
         else:
             path = support_status(ids, K, self.inS, self.support_valid, lib=lib)
             if path:
@@ -347,7 +393,7 @@ class OracleLayer:
                     fresh=fresh, anomaly=anomaly, worklist=wl, rows=rows, R=R, Y=Y,
                     iter=self.iter)
 
-    def _restricted_step(self, G, ids, q, wts):
+    def _restricted_step(self, G, ids, q, wts, tie_routed=None):
         """Support lifecycle and routing of one forward under support-restricted routing.
 
         Teardown, Expert Atlas (third step) and the block-plan lifecycle: the hot path keeps
@@ -398,6 +444,19 @@ class OracleLayer:
             self.counters["hot_skip"] += 1
             self.counters["restricted"] += 1
             rids, rw = restricted
+            if tie_routed is not None:
+                # rows whose in-support ranking is a tie of their logits take the given order
+                ov = tie_routed(rids)
+                if ov:
+                    rids, rw = rids.copy(), rw.copy()
+                    for t, alt in ov.items():
+                        assert tie_order_ok(G[t], rids[t], alt, self.TIE), f"row {t}: not a tie"
+                        al = allowed[t] if np.ndim(allowed) == 2 else allowed
+                        assert np.asarray(al)[np.asarray(alt)].all(), f"row {t}: outside the support"
+                        rids[t] = alt
+                    tr = np.array(sorted(ov), dtype=np.int64)
+                    _, rw[tr], _ = score_given(G[tr], rids[tr], K, w.gate == "sigmoid",
+                                               w.norm_topk, lib=lib)
             mask = self.inA
         self.inS = np.ascontiguousarray(mask, dtype=np.uint8).copy()
         self.slot_of, self.S_list = slots_of(self.inS)

@@ -101,6 +101,27 @@ static int before(float ga, int ea, float gb, int eb) {
 #endif
 }
 
+/* Scores of one position's ranked candidates ids[0..Kext): s = sigma(G) (softmax over all E
+   experts, or sigmoid), the Atlas integer weight q = floor(s * 2^16 + 1/2), and the routing
+   weights of the first K (s, or s / sum_{j<K} s when norm_topk). */
+static void score_row(int E, int K, int Kext, int gate_sigmoid, int norm_topk, const float* g,
+                      const int32_t* ids, double* s, double* w, int64_t* q) {
+  double zmax = -INFINITY, z = 0.0;
+  if (!gate_sigmoid) {
+    for (int e = 0; e < E; ++e) zmax = fmax(zmax, (double)g[e]);
+    for (int e = 0; e < E; ++e) z += exp((double)g[e] - zmax);
+  }
+  for (int j = 0; j < Kext; ++j) {
+    double ge = (double)g[ids[j]];
+    double sj = gate_sigmoid ? 1.0 / (1.0 + exp(-ge)) : exp(ge - zmax) / z;
+    s[j] = sj;
+    q[j] = (int64_t)floor(sj * (double)ATLAS_Q + 0.5);
+  }
+  double denom = 0.0;
+  for (int k = 0; k < K; ++k) denom += s[k];
+  for (int k = 0; k < K; ++k) w[k] = norm_topk ? s[k] / denom : s[k];
+}
+
 /*
  * Top-k selection and routing weights ([T] MoE bottleneck, y_t = sum over TopK(g(x_t))
  * of w_{t,e} E_e(x_t); [T] Expert Atlas: top-k taken over sigma(G), extended to
@@ -125,24 +146,22 @@ void orc_route(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, c
       ids[(size_t)t * Kext + j] = best;
     }
     free(taken);
-    double zmax = -INFINITY, z = 0.0;
-    if (!gate_sigmoid) {
-      for (int e = 0; e < E; ++e) zmax = fmax(zmax, (double)g[e]);
-      for (int e = 0; e < E; ++e) z += exp((double)g[e] - zmax);
-    }
-    for (int j = 0; j < Kext; ++j) {
-      double ge = (double)g[ids[(size_t)t * Kext + j]];
-      double sj = gate_sigmoid ? 1.0 / (1.0 + exp(-ge)) : exp(ge - zmax) / z;
-      s[(size_t)t * Kext + j] = sj;
-      q[(size_t)t * Kext + j] = (int64_t)floor(sj * (double)ATLAS_Q + 0.5);
-    }
-    double denom = 0.0;
-    for (int k = 0; k < K; ++k) denom += s[(size_t)t * Kext + k];
-    for (int k = 0; k < K; ++k) {
-      double sk = s[(size_t)t * Kext + k];
-      w[(size_t)t * K + k] = norm_topk ? sk / denom : sk;
-    }
+    score_row(E, K, Kext, gate_sigmoid, norm_topk, g, ids + (size_t)t * Kext,
+              s + (size_t)t * Kext, w + (size_t)t * K, q + (size_t)t * Kext);
   }
+}
+
+/*
+ * The scores, weights and planner weights of a given selection (the scoring half of orc_route,
+ * for selections fixed elsewhere): ids [M x Kext] holds each position's candidates in rank
+ * order.  The harness uses it for positions whose order is a tie of their logits (two logits
+ * closer than the near-tie gap), where either order is correct.
+ */
+void orc_score_given(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk,
+                     const float* G, const int32_t* ids, double* s, double* w, int64_t* q) {
+  for (int t = 0; t < M; ++t)
+    score_row(E, K, Kext, gate_sigmoid, norm_topk, G + (size_t)t * E, ids + (size_t)t * Kext,
+              s + (size_t)t * Kext, w + (size_t)t * K, q + (size_t)t * Kext);
 }
 
 /*

@@ -31,6 +31,8 @@ void orc_router_logits(int M, int H, int E, int act_bf16, const void* x, const f
 /* allowed: [M x E] selectable experts per row, or NULL for all */
 void orc_route(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk, const float* G,
                const uint8_t* allowed, int32_t* ids, double* s, double* w, int64_t* q);
+void orc_score_given(int M, int E, int K, int Kext, int gate_sigmoid, int norm_topk,
+                     const float* G, const int32_t* ids, double* s, double* w, int64_t* q);
 
 void orc_group_allowed(int M, int E, int n_group, int topk_group, const float* G,
                        const uint8_t* base, uint8_t* allowed);

@@ -10,11 +10,15 @@ host arrays.  Every stage is compared each iteration:
   row-normwise max_t |a_t - b_t|_inf / |b_t|_inf <= 2e-2 (bf16) or 1e-5 (fp32): outputs.
 Plus the GPU-internal invariant that a stable row's routed output is its cache row,
 bitwise, unchanged since the row's last fresh iteration.
+
+Near ties: a position whose GPU ranking differs from the oracle's only among experts whose
+logits are closer than NEAR_TIE is reported (counted and logged), not failed; the oracle then
+takes the GPU's order for that position (after checking that it is a tie order of its own
+logits) and the block continues, every stage still compared.
 """
 from __future__ import annotations
 
 import sys
-import warnings
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -101,14 +105,8 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
                   out["G"].view(np.int32).astype(np.int64))
     assert ulps.max() <= 1, f"{tag}: router logits differ by {ulps.max()} ulp"
     rep.logits_ulp1 += int((ulps == 1).sum())
-    ids_g = g["ids"]
-    if not np.array_equal(ids_g, out["ids"]):
-        ties, real = _near_tie_rows(out["G"], ids_g, out["ids"])
-        assert not real, f"{tag}: top-k ids differ on rows {real[:8]} (not near-ties)"
-        rep.near_ties += len(ties)
-        warnings.warn(f"{tag}: {len(ties)} near-tie rows (logit gap < {NEAR_TIE}) reported; "
-                      "downstream stages of this iteration not compared")
-        return False
+    # the oracle took the GPU's order on near-tie rows (run_block), so the ids agree in full
+    assert np.array_equal(g["ids"], out["ids"]), f"{tag}: top-k ids differ"
     np.testing.assert_allclose(g["scores"], out["s"], rtol=1e-6, atol=1e-12, err_msg=tag)
     np.testing.assert_allclose(g["weights"], out["w"], rtol=1e-6, atol=1e-12, err_msg=tag)
     assert np.array_equal(g["atlas_q"], out["q"]), f"{tag}: planner weights q differ"
@@ -119,12 +117,7 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
     if w.routing == "restricted":
         assert np.array_equal(g["atlas"], out["inA"]), f"{tag}: Atlas support differs"
     # the routing the worklist used (all-expert top-K, or top-K inside the support)
-    if not np.array_equal(g["routed_ids"], out["routed_ids"]):
-        ties, real = _near_tie_rows(out["G"], g["routed_ids"], out["routed_ids"])
-        assert not real, f"{tag}: routed ids differ on rows {real[:8]} (not near-ties)"
-        rep.near_ties += len(ties)
-        warnings.warn(f"{tag}: {len(ties)} near-tie rows in the routed ids reported")
-        return False
+    assert np.array_equal(g["routed_ids"], out["routed_ids"]), f"{tag}: routed ids differ"
     np.testing.assert_allclose(g["routed_w"], out["routed_w"], rtol=1e-6, atol=1e-12,
                                err_msg=tag)
     fresh = out["fresh"].astype(bool)
@@ -231,15 +224,40 @@ def run_block(w: synth.Workload, layers=(0,), iters=None, rows=None, weights=Non
             if fresh_sample:
                 pick = pick_rows(ins["fresh"].cpu().numpy().astype(bool), known[li], fresh_sample,
                                  [w.seed, l, it, 99])
-            out = orcs[li].forward(X[li][it], D[it], None if F is None else F[it], rows=pick)
+            # ranking first: rows where the GPU's order differs from the oracle's only among
+            # logits closer than NEAR_TIE are ties (both orders correct); they are reported and
+            # the oracle continues on the GPU's order, so every later stage stays comparable
+            pre = orcs[li].route(X[li][it])
+            ids_g = ins["ids"].cpu().numpy()
+            tie_ids = None
+            if not np.array_equal(ids_g, pre["ids"]):
+                ties, real = _near_tie_rows(pre["G"], ids_g, pre["ids"])
+                assert not real, f"iter {it}: top-k ids differ on rows {real[:8]} (not near-ties)"
+                rep.near_ties += len(ties)
+                log(f"  iter {it}: {len(ties)} near-tie rows (logit gap < {NEAR_TIE}) reported; "
+                    "the oracle continues on the GPU's order")
+                tie_ids = {t: ids_g[t].copy() for t in ties}
+            routed_g = ins["routed_ids"].cpu().numpy()
+
+            def tie_routed(rids, it=it):
+                # the same for the ranking inside the support (restricted routing)
+                if np.array_equal(routed_g, rids):
+                    return None
+                ties, real = _near_tie_rows(pre["G"], routed_g, rids)
+                assert not real, f"iter {it}: routed ids differ on rows {real[:8]} (not near-ties)"
+                rep.near_ties += len(ties)
+                log(f"  iter {it}: {len(ties)} near-tie rows in the routing inside the support "
+                    "reported; the oracle continues on the GPU's order")
+                return {t: routed_g[t].copy() for t in ties}
+
+            out = orcs[li].forward(X[li][it], D[it], None if F is None else F[it], rows=pick,
+                                   pre=pre, tie_ids=tie_ids, tie_routed=tie_routed)
             ofresh = out["fresh"].astype(bool)
             evaluated = np.zeros(w.M, dtype=bool)
             evaluated[out["rows"]] = True
             known[li] = np.where(ofresh, evaluated, known[li])
             if check:
-                ok = compare_iteration(w, out, ins, y, yr, it, out["rows"], rep, prev_cache[li])
-                if not ok:
-                    return rep
+                compare_iteration(w, out, ins, y, yr, it, out["rows"], rep, prev_cache[li])
             prev_cache[li] = ins["cache"].cpu().numpy().copy()
             rep.fresh_counts.append(int(out["fresh"].sum()))
             rep.paths.append(out["path"])

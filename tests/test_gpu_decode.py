@@ -1,11 +1,16 @@
 """GPU parity of live-only output decoding (LM head on live positions, threshold commit)
 through the C ABI, against the oracle on the same seeded inputs.
 
-The GPU logits are bf16 products accumulated in fp32 on MFMA, the oracle's in double, so
-decisions taken on them are compared exactly except where the pages' own near-tie rule
-applies: a live row whose top-two logit gap is under 1e-2, or whose confidence lies within
-1e-3 of tau, is reported (counted) instead of compared, and so is the commit outcome of its
-sequence.  Confidences are compared within rtol 2e-3 on every other live row.
+The GPU's logits are exact bf16 x bf16 products accumulated in fp32 on MFMA, the oracle's are
+summed in double.  Every fp32 sum on the GPU is a chain of at most n = H / 32 + 5 roundings
+(H / 32 sequential 32-wide k-steps, each adding a sum of 32 products), so each logit is within
+    B_t = gamma_n * max_v sum_k |h_tk| |w_vk|,   gamma_n = n u / (1 - n u), u = 2^-24
+of the exact value (the standard bound for recursive summation).  Decisions are compared
+exactly wherever this bound makes them unique: a live row whose top-two logit gap is under
+2 B_t, or whose confidence lies within tau (2 B_t + 1e-5) of tau (1e-5 covers expf and the
+fp32 partial sums of the softmax denominator), is reported instead of compared, and so is the
+commit outcome of its sequence.  Confidences of the other live rows agree within a relative
+2 B_t + 1e-5.  Reported rows are logged and capped at 3 % of the live rows (at least one).
 """
 import numpy as np
 import pytest
@@ -16,7 +21,22 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-GAP, NEAR_TAU, CONF_RTOL = 1e-2, 1e-3, 2e-3
+U = 2.0 ** -24
+CONF_EPS = 1e-5
+REPORT_CAP = 0.03
+
+
+def logit_bound(h_bits, W_bits):
+    """Per-row bound B_t on the error of any fp32-accumulated logit of row t."""
+    hf = synth.bf16_bits_to_f32(h_bits).astype(np.float64)
+    Wf = synth.bf16_bits_to_f32(W_bits).astype(np.float64)
+    n = hf.shape[1] // 32 + 5
+    gamma = n * U / (1.0 - n * U)
+    return gamma * (np.abs(hf) @ np.abs(Wf).T).max(axis=1)
+
+
+def report_cap(D):
+    return max(1, int(REPORT_CAP * int((D == 0).sum())))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,12 +72,15 @@ class Decoder:
         return Dn.cpu().numpy(), tok.cpu().numpy(), conf.cpu().numpy()
 
 
-def compare(D, tokens, out, Dn, tok, conf, block, tau):
-    """Compare one step; returns the number of reported (near-tie) rows."""
+def compare(D, tokens, out, Dn, tok, conf, block, tau, B):
+    """Compare one step; B is the per-row logit error bound.  Returns the number of reported
+    (near-tie) rows, after logging it."""
     live = D == 0
-    near = live & ((out["gap"] < GAP) | (np.abs(out["conf"] - tau) < NEAR_TAU))
+    crel = 2.0 * B + CONF_EPS
+    near = live & ((out["gap"] < 2.0 * B) | (np.abs(out["conf"] - tau) < tau * crel))
     ok = live & ~near
-    np.testing.assert_allclose(conf[ok], out["conf"][ok], rtol=CONF_RTOL)
+    assert (np.abs(conf[ok] - out["conf"][ok]) <= crel[ok] * out["conf"][ok]).all(), \
+        "confidence outside the fp32 accumulation bound"
     assert (conf[~live] == 0).all()
     for b in range(D.shape[0] // block):
         sl = slice(b * block, (b + 1) * block)
@@ -65,12 +88,15 @@ def compare(D, tokens, out, Dn, tok, conf, block, tau):
             continue
         c = out["conf"][sl][live[sl]]
         if len(c) and not (c >= tau).any() and len(c) > 1:
-            top2 = np.sort(c)[-2:]
-            if top2[1] - top2[0] < NEAR_TAU * top2[1]:
+            order = np.argsort(-c, kind="stable")
+            if c[order[0]] - c[order[1]] <= c[order[0]] * crel[sl][live[sl]][order[:2]].sum():
                 continue  # the fallback choice is a near tie
         assert np.array_equal(Dn[sl], out["D_next"][sl]), f"sequence {b}: commits differ"
         assert np.array_equal(tok[sl], out["token"][sl]), f"sequence {b}: tokens differ"
-    return int(near.sum())
+    n_near = int(near.sum())
+    print(f"decode parity: {n_near} of {int(live.sum())} live rows reported as near ties "
+          f"(max logit bound {B.max():.2e})", flush=True)
+    return n_near
 
 
 @pytest.mark.parametrize("shape", [(3, 24, 128, 512), (5, 13, 192, 384), (2, 64, 256, 1024)],
@@ -82,31 +108,31 @@ def test_small_decode_step(shape):
     tokens = np.full(batch * block, -1, np.int32)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
-    assert reported <= int((D == 0).sum()) // 4     # most live rows are compared exactly
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95, logit_bound(hs[0], Wb))
+    assert reported <= report_cap(D)
     assert out["commits"] > 0 and (Dn >= D).all()
 
 
 @pytest.mark.parametrize("shape", [(8, 32, 128, 384), (9, 32, 128, 384)],
                          ids=["b8x32-two-row-tiles-v384", "b9x32-three-row-tiles-v384"])
 def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
-    """256 and 288 positions (two and three 128-row LM-head tiles, the last one ragged) with a
-    vocabulary that is not a multiple of 256."""
+    """256 and 288 positions (about 190 and 215 live rows: one 256-row streamed LM-head tile)
+    with a vocabulary that is not a multiple of 256."""
     batch, block, H, V = shape
     hs, Wb, D = synth.decode_inputs(70 + batch, batch, block, H, V)
     dec = Decoder(batch, block, H, V)
     tokens = np.full(batch * block, -1, np.int32)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
-    assert reported <= int((D == 0).sum()) // 4
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95, logit_bound(hs[0], Wb))
+    assert reported <= report_cap(D)
 
 
 @pytest.mark.parametrize("batch", [16, 20], ids=["512-live-streamed", "640-live-compute-tiles"])
 def test_lm_head_on_both_sides_of_the_stream_limit(batch):
-    """Every position live: 512 live rows are the most the streamed LM head takes (four
-    128-row passes over each vocabulary slab), 640 go to the compute-bound tiles; both write
-    the same 32-token partials."""
+    """Every position live: 512 live rows are the most the streamed LM head takes (two
+    256-row passes over each vocabulary slab, 32-token partials); 640 go to the compute-bound
+    tiles (three 256-row tiles, the last ragged; 64-token partials)."""
     block, H, V = 32, 128, 384
     hs, Wb, _ = synth.decode_inputs(55 + batch, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)
@@ -114,8 +140,8 @@ def test_lm_head_on_both_sides_of_the_stream_limit(batch):
     tokens = np.full(batch * block, -1, np.int32)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
-    assert reported <= batch * block // 4
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95, logit_bound(hs[0], Wb))
+    assert reported <= report_cap(D)
 
 
 def test_lm_head_wide_vocabulary():
@@ -127,8 +153,8 @@ def test_lm_head_wide_vocabulary():
     tokens = np.full(batch * block, -1, np.int32)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95)
-    assert reported <= int((D == 0).sum()) // 4
+    reported = compare(D, tokens, out, Dn, tok, conf, block, 0.95, logit_bound(hs[0], Wb))
+    assert reported <= report_cap(D)
 
 
 def test_all_decoded_and_all_live():
@@ -142,7 +168,7 @@ def test_all_decoded_and_all_live():
     D = np.zeros(batch * block, np.uint8)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    compare(D, tokens, out, Dn, tok, conf, block, 0.95)
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95, logit_bound(hs[0], Wb)) <= report_cap(D)
     for b in range(batch):                                          # progress in every sequence
         assert Dn[b * block:(b + 1) * block].sum() >= 1
 
@@ -159,7 +185,8 @@ def test_block_decodes_to_completion():
     for s in range(steps):
         Dn, tok, conf = dec(dev(hs[s]), Wd, D, tokens)
         out = oracle.live_decode(hs[s], Wb, D, block, 0.95, token=tokens)
-        compare(D, tokens, out, Dn, tok, conf, block, 0.95)
+        assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                       logit_bound(hs[s], Wb)) <= report_cap(D)
         assert (Dn >= D).all() and Dn.sum() > D.sum()
         D, tokens = Dn, tok
         if D.all():
@@ -175,4 +202,36 @@ def test_decode_full_vocab_shape():
     tokens = np.full(batch * block, -1, np.int32)
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
-    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95) <= int((D == 0).sum()) // 4
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                   logit_bound(hs[0], Wb)) <= report_cap(D)
+
+
+@pytest.mark.parametrize("n_live", [300, 500], ids=["300-live", "500-live"])
+def test_lm_head_streamed_ragged_second_row_tile(n_live):
+    """The streamed LM head with two 256-row passes, the second one ragged (44 and 244 rows)."""
+    batch, block, H, V = 16, 32, 128, 1024
+    hs, Wb, _ = synth.decode_inputs(300 + n_live, batch, block, H, V)
+    rng = np.random.default_rng(n_live)
+    D = np.ones(batch * block, np.uint8)
+    D[rng.choice(batch * block, size=n_live, replace=False)] = 0
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                   logit_bound(hs[0], Wb)) <= report_cap(D)
+
+
+def test_lm_head_compute_tiles_wide_hidden():
+    """The compute-bound LM head at H = 1024 (32 K chunks) with 640 live rows (three 256-row
+    tiles, the last ragged) over a vocabulary of 9 x 128 tokens (the last 256-token block half
+    past the vocabulary)."""
+    batch, block, H, V = 20, 32, 1024, 1152
+    hs, Wb, _ = synth.decode_inputs(123, batch, block, H, V)
+    D = np.zeros(batch * block, np.uint8)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                   logit_bound(hs[0], Wb)) <= report_cap(D)

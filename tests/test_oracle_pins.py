@@ -132,6 +132,28 @@ def pin_weights(orc, lib):
     np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-13)
 
 
+def pin_score_given(orc, lib):
+    """Scoring a selection the top-k itself produced reproduces its scores bit for bit, and
+    swapping two experts whose logits tie exactly is a valid order with swapped scores."""
+    rng = np.random.default_rng(21)
+    M, E, K, Kext = 30, 16, 4, 8
+    G = rng.standard_normal((M, E)).astype(np.float32)
+    G[:, 9] = G[:, 2]
+    for sigmoid in (True, False):
+        for norm in (True, False):
+            ids, s, w, q = orc.route(G, K, Kext, sigmoid, norm, lib=lib)
+            s2, w2, q2 = orc.score_given(G, ids, K, sigmoid, norm, lib=lib)
+            assert np.array_equal(s, s2) and np.array_equal(w, w2) and np.array_equal(q, q2)
+            t = int(np.nonzero((ids == 2).any(1) & (ids == 9).any(1))[0][0])
+            alt = ids[t].copy()
+            i2, i9 = int(np.nonzero(alt == 2)[0][0]), int(np.nonzero(alt == 9)[0][0])
+            alt[i2], alt[i9] = 9, 2
+            assert orc.tie_order_ok(G[t], ids[t], alt, 1e-6)
+            assert not orc.tie_order_ok(G[t], ids[t], np.roll(ids[t], 1), 1e-6)
+            s3, _, q3 = orc.score_given(G[t:t + 1], alt[None], K, sigmoid, norm, lib=lib)
+            assert np.array_equal(s3[0][[i2, i9]], s[t][[i9, i2]]) and np.array_equal(q3[0][[i2, i9]], q[t][[i9, i2]])
+
+
 def pin_atlas_hand(orc, lib):
     with open(os.path.join(GOLDEN, "atlas_hand_worked.json")) as f:
         g = json.load(f)
@@ -582,7 +604,7 @@ def pin_live_decode(orc, lib):
     assert one["D_next"].all() and np.allclose(one["conf"][live], 1.0)
 
 
-PINS = [pin_router, pin_topk, pin_weights, pin_atlas_hand, pin_atlas_special, pin_fresh,
+PINS = [pin_router, pin_topk, pin_weights, pin_score_given, pin_atlas_hand, pin_atlas_special, pin_fresh,
         pin_worklist, pin_expert, pin_dense, pin_all_fresh_equals_dense, pin_staleness,
         pin_restricted_topk, pin_atlas_without_closure, pin_restricted_lifecycle,
         pin_group_limited, pin_group_limited_restricted, pin_live_decode, pin_support_lifecycle,
@@ -638,3 +660,40 @@ def test_planted_mistakes(orc, m, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake: {MUTATIONS[m]}"
+
+
+def test_tie_order_continuation(orc):
+    """The GPU harness's near-tie rule: where two experts' logits tie exactly, the oracle accepts
+    the other order for a position, scores it from its own logits and routes through it.
+    Experts 3 and 11 get identical router rows (exact ties everywhere); on positions where the
+    tie straddles the top-K boundary, swapping them changes which expert runs."""
+    w = small_workload(n_experts=16, top_k=3, iters=2, n_shared=0, shared_inter=0)
+    Wl = dict(synth.layer_weights(w, 0))
+    Wl["router_w"] = Wl["router_w"].copy()
+    Wl["router_w"][11] = Wl["router_w"][3]
+    Wl["router_w"][3] += 0.3 * np.abs(Wl["router_w"][3])   # rank 3 and 11 high on most rows
+    Wl["router_w"][11] = Wl["router_w"][3]
+    Wl["router_b"] = None
+    D = synth.decoded_masks(w)
+    X = synth.hidden_states(w, 0, D)
+    K = w.top_k
+    La = orc.OracleLayer(w, Wl)
+    Lb = orc.OracleLayer(w, Wl)
+    pre = La.route(X[0])
+    ids = pre["ids"]
+    straddle = [t for t in range(w.M)
+                if 3 in ids[t, :K].tolist() and ids[t, K] == 11]
+    assert straddle, "no position with the tie on the top-K boundary"
+    ties = {}
+    for t in straddle:
+        alt = ids[t].copy()
+        alt[K - 1 if ids[t, K - 1] == 3 else list(alt).index(3)] = 11
+        alt[K] = 3
+        ties[t] = alt
+    oa = La.forward(X[0], D[0], pre=pre)
+    ob = Lb.forward(X[0], D[0], pre=pre, tie_ids=ties)
+    for t in straddle:
+        assert 11 in ob["routed_ids"][t].tolist() and 3 not in ob["routed_ids"][t].tolist()
+        assert np.allclose(ob["w"][t], oa["w"][t])            # tied logits: same weights
+    assert np.array_equal(np.delete(ob["Y"], straddle, 0), np.delete(oa["Y"], straddle, 0))
+    assert ob["worklist"]["P"] == oa["worklist"]["P"]
