@@ -412,8 +412,8 @@ int orc_route_restricted(int M, int E, int K, int gate_sigmoid, int norm_topk, c
 }
 
 /*
- * Group-limited selectable set ([T] Expert Atlas, third step: the routing kernel runs the
- * model's group-limited top-k rule, with the selectable experts limited to the support).
+ * Group-limited selectable set ([T] Expert Atlas, step three: routing there applies the
+ * model's own grouped expert selection, restricted to the experts of the support).
  * Experts form n_group contiguous groups of E / n_group ids.  Among the experts that base
  * allows (base = NULL: all; else a [E] support mask), a group is ranked by its best expert
  * under the selection key (logit desc, id asc), groups without an allowed expert last; the
