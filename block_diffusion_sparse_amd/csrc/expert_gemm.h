@@ -494,6 +494,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
 // holds g and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: BC
 // rows of W2.  Grid as k_expert_stream (XCD-grouped, 1-D): BC / 2 (gate/up) or BC (down)
 // columns per block.
+constexpr float kLog2e = 1.4426950408889634f;
+
 template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128, int WAVES = 4>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
@@ -607,21 +609,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
                    : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
                      "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]));
   };
-  // Expert tiles multiply with the operands swapped (weights as the 16 x 32 left operand), so
+  // The operands go in swapped (weights, or vocabulary rows, as the 16 x 32 left operand), so
   // that a block holds its outputs transposed: lane (r, g) gets four consecutive columns
-  // 4 g .. 4 g + 3 of row r, one 8-byte store.  The LM head keeps rows x tokens, whose
-  // epilogue reduces along a row across lanes.
+  // 4 g .. 4 g + 3 of row r.  Expert tiles store them with one 8-byte store; the LM head finds
+  // 16 of a row's 64 tokens in each lane and reduces them mostly in registers.
   auto mma = [&](int set) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n)
-        acc[m][n] = LMHEAD ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                 __builtin_bit_cast(bf16x8, fa[set][m]),
-                                 __builtin_bit_cast(bf16x8, fb[set][n]), acc[m][n], 0, 0, 0)
-                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                 __builtin_bit_cast(bf16x8, fb[set][n]),
-                                 __builtin_bit_cast(bf16x8, fa[set][m]), acc[m][n], 0, 0, 0);
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, fb[set][n]), __builtin_bit_cast(bf16x8, fa[set][m]),
+            acc[m][n], 0, 0, 0);
   };
   constexpr int kInFlight = (NA + NBI) * (NB - 2);  // copies after chunk c + 1's
   const int nch = Kdim / KC;
@@ -667,47 +666,55 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
       }
     }
   }
-  // D[i][j] of a 16x16 block: lane j + 16 * (i / 4), register i % 4
   if (LMHEAD) {
-    // per row: the 64 logits of this wave's token columns sit in the 16 lanes with the same g,
-    // four per lane (token 16 n + r), reduced over the wave's 64 tokens to (max, lower token
-    // on ties) and then the sum of exp(logit - max); a wave whose columns lie past the
-    // vocabulary (the last block of a vocabulary that is an odd multiple of 128 tokens, with
-    // 256-column blocks) writes nothing
+    // per row: lane (r, g) of row block m holds tokens 16 n + 4 g + i (n, i < 4) of this wave's
+    // 64-token block for row 16 m + r; reduce them in registers (max, lower token on ties:
+    // tokens are visited in increasing order and only a larger logit replaces), then across the
+    // four lanes of the row (lane bits 4 and 5), then the sum of exp(logit - max) likewise; a
+    // wave whose tokens lie past the vocabulary (the last block of a vocabulary that is an odd
+    // multiple of 128 tokens, with 256-token blocks) writes nothing
     if (cb * BC + 64 * wn >= Ndim) return;
+    const int tok0 = cb * BC + 64 * wn + 4 * g;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
+      const int row = tr.row0 + BR / 2 * wm + 16 * m + r;
+      float mx = acc[m][0][0];
+      int arg = tok0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = tr.row0 + BR / 2 * wm + 16 * m + 4 * g + q;
-        const int col0 = cb * BC + 64 * wn + r;
-        float mx = acc[m][0][q];
-        int arg = col0;
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int n = 1; n < 4; ++n)
-          if (acc[m][n][q] > mx) {
-            mx = acc[m][n][q];
-            arg = col0 + 16 * n;
+        for (int i = 0; i < 4; ++i)
+          if ((n | i) && acc[m][n][i] > mx) {
+            mx = acc[m][n][i];
+            arg = tok0 + 16 * n + i;
           }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float om = __shfl_xor(mx, o, 64);
-          const int oa = __shfl_xor(arg, o, 64);
-          if (om > mx || (om == mx && oa < arg)) {
-            mx = om;
-            arg = oa;
-          }
+      for (int o = 16; o < 64; o <<= 1) {
+        const float om = __shfl_xor(mx, o, 64);
+        const int oa = __shfl_xor(arg, o, 64);
+        if (om > mx || (om == mx && oa < arg)) {
+          mx = om;
+          arg = oa;
         }
-        float se = (expf(acc[m][0][q] - mx) + expf(acc[m][1][q] - mx)) +
-                   (expf(acc[m][2][q] - mx) + expf(acc[m][3][q] - mx));
+      }
+      // exp(v - mx) for v <= mx as one v_exp_f32 of v log2(e) - mx log2(e) (a single fma): the
+      // rounding of mx log2(e) makes the relative error about 1e-6 for logits up to 20 in
+      // magnitude; terms below exp(-87) underflow to 0
+      const float nm = -mx * kLog2e;
+      float se = 0.0f;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, 64);
-        if (r == 0 && row < tr.row_end) {
-          const size_t idx = (size_t)row * lp.n_p + WN * cb + wn;
-          lp.pmax[idx] = mx;
-          lp.parg[idx] = arg;
-          lp.psum[idx] = se;
-        }
+      for (int n = 0; n < 4; ++n)
+        se += (__builtin_amdgcn_exp2f(fmaf(acc[m][n][0], kLog2e, nm)) +
+               __builtin_amdgcn_exp2f(fmaf(acc[m][n][1], kLog2e, nm))) +
+              (__builtin_amdgcn_exp2f(fmaf(acc[m][n][2], kLog2e, nm)) +
+               __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
+      if (g == 0 && row < tr.row_end) {
+        const size_t idx = (size_t)row * lp.n_p + WN * cb + wn;
+        lp.pmax[idx] = mx;
+        lp.parg[idx] = arg;
+        lp.psum[idx] = se;
       }
     }
     return;
