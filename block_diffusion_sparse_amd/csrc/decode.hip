@@ -13,8 +13,8 @@
 //                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
 //                   each row's 32-token blocks to (max, argmax, sum exp);
 //   k_gemm_big      LM-head mode, when more are live: 256 live rows x 256 tokens per
-//                   workgroup on the compute-bound tiles, the same partials over 64-token
-//                   blocks (one wave's columns);
+//                   workgroup on the compute-bound tiles, one (max, argmax, sum exp) per row and
+//                   256-token block (the workgroup's four column waves combined in LDS);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
 //                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
 //   k_decode_final  one workgroup per sequence: the commits.
@@ -284,14 +284,14 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
   // the vocabulary is an odd multiple of 128)
   const int tiles = (M + kLmBigTileRows - 1) / kLmBigTileRows;
   const int n_cb = (d->vocab + kLmBigTileCols - 1) / kLmBigTileCols;
-  const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, d->vocab / 64};
+  const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_cb};
   launch((k_gemm_big<false, false, true, kLmBigTileRows, kLmBigWaves>),
                      dim3(8 * tiles * ((n_cb + 7) / 8)), dim3(64 * kLmBigWaves), 0, st,
                      static_cast<const uint16_t*>(h),
                      static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
-  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, d->vocab / 64, L.n_live, L.live_idx,
+  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
          L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
   launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, d->tau, decoded,
          L.conf_pos, L.top_pos, decoded_next, tokens, conf);

@@ -37,7 +37,8 @@ __device__ __forceinline__ TileRows tile_rows(bool routed, int tile, int tile_ro
 // (gathered through live_list, n_live of them), the columns vocabulary tokens, and instead of
 // the logits the kernels write, per row and per block of tokens, the largest logit, its token
 // (lower id on ties) and the sum of exp(logit - largest) over the block; n_p blocks per row:
-// vocab / 32 from k_expert_stream (one wave's columns), vocab / 64 from k_gemm_big.
+// vocab / 32 from k_expert_stream (one wave's columns), vocab / 256 rounded up from k_gemm_big
+// (one workgroup's columns).
 struct LmPartials {
   const int32_t* live_list;
   const int32_t* n_live;
@@ -667,17 +668,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
     }
   }
   if (LMHEAD) {
-    // per row: lane (r, g) of row block m holds tokens 16 n + 4 g + i (n, i < 4) of this wave's
-    // 64-token block for row 16 m + r; reduce them in registers (max, lower token on ties:
-    // tokens are visited in increasing order and only a larger logit replaces), then across the
-    // four lanes of the row (lane bits 4 and 5), then the sum of exp(logit - max) likewise; a
-    // wave whose tokens lie past the vocabulary (the last block of a vocabulary that is an odd
-    // multiple of 128 tokens, with 256-token blocks) writes nothing
-    if (cb * BC + 64 * wn >= Ndim) return;
+    // Per row, over this workgroup's BC tokens: lane (r, g) of row block m holds tokens
+    // 16 n + 4 g + i (n, i < 4) of its wave's 64-token block for row 16 m + r.  Each wave reduces
+    // its 64 tokens in registers (max, lower token on ties: tokens are visited in increasing
+    // order and only a larger logit replaces), then across the four lanes of the row (lane bits
+    // 4 and 5), then the sum of exp(logit - max) likewise; the WN waves of a row half then meet
+    // in LDS, and one (max, argmax, sum) per row and workgroup is written.  A wave whose tokens
+    // lie past the vocabulary (the last block of a vocabulary that is an odd multiple of 128
+    // tokens) contributes (-inf, -, 0).
+    struct Part {
+      float mx;
+      int arg;
+      float se;
+    };
+    static_assert(sizeof(Part) * BR * WN <= sizeof(As), "the partials fit in the operand buffers");
+    Part* part = reinterpret_cast<Part*>(&As[0][0]);  // [BR rows][WN waves]
+    const bool wlive = cb * BC + 64 * wn < Ndim;
     const int tok0 = cb * BC + 64 * wn + 4 * g;
+    __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int row = tr.row0 + BR / 2 * wm + 16 * m + r;
       float mx = acc[m][0][0];
       int arg = tok0;
 #pragma unroll
@@ -710,12 +720,33 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
                __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
 #pragma unroll
       for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
-      if (g == 0 && row < tr.row_end) {
-        const size_t idx = (size_t)row * lp.n_p + WN * cb + wn;
-        lp.pmax[idx] = mx;
-        lp.parg[idx] = arg;
-        lp.psum[idx] = se;
+      if (g == 0)
+        part[(BR / 2 * wm + 16 * m + r) * WN + wn] =
+            wlive ? Part{mx, arg, se} : Part{-INFINITY, 0x7fffffff, 0.0f};
+    }
+    __syncthreads();
+    // the WN partials of a row: wave blocks in token order, so the first maximum holds the lower
+    // token; each earlier sum rescaled to the row maximum
+    for (int rr = tid; rr < BR; rr += 64 * WAVES) {
+      const int row = tr.row0 + rr;
+      if (row >= tr.row_end) continue;
+      Part best = part[rr * WN];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) {
+        const Part q = part[rr * WN + w];
+        if (q.mx > best.mx) best = q;
       }
+      const float nm = -best.mx * kLog2e;
+      float se = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        const Part q = part[rr * WN + w];
+        se += q.se * __builtin_amdgcn_exp2f(fmaf(q.mx, kLog2e, nm));
+      }
+      const size_t idx = (size_t)row * lp.n_p + cb;
+      lp.pmax[idx] = best.mx;
+      lp.parg[idx] = best.arg;
+      lp.psum[idx] = se;
     }
     return;
   }
