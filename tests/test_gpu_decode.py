@@ -132,7 +132,7 @@ def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
 def test_lm_head_on_both_sides_of_the_stream_limit(batch):
     """Every position live: 512 live rows are the most the streamed LM head takes (two
     256-row passes over each vocabulary slab, 32-token partials); 640 go to the compute-bound
-    tiles (three 256-row tiles, the last ragged; 64-token partials)."""
+    tiles (three 256-row tiles, the last ragged; 256-token partials)."""
     block, H, V = 32, 128, 384
     hs, Wb, _ = synth.decode_inputs(55 + batch, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)
@@ -235,3 +235,57 @@ def test_lm_head_compute_tiles_wide_hidden():
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
     assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
                    logit_bound(hs[0], Wb)) <= report_cap(D)
+
+
+# token ids holding one and the same vocabulary row, placed so that the GPU meets their equal
+# logits at every level of its max / argmax reductions: in one lane (5, 6, 21), across the lanes
+# of a row (9), across the waves of a workgroup (69, 197), across token blocks in the row
+# reduction (261) and in the half-width last block (V - 5)
+TIE_IDS = (5, 6, 9, 21, 69, 197, 261)
+
+
+@pytest.mark.parametrize("batch,live_all", [(16, False), (24, True)],
+                         ids=["streamed", "compute-tiles"])
+def test_lm_head_exact_ties_take_the_lowest_token(batch, live_all):
+    """Rows leaning toward a vocabulary row that several token ids share exactly.  A tied top
+    token caps a row's confidence at 1/8, so no such row reaches tau and each sequence commits
+    its most confident live row (one of the leaning rows): the committed tokens show the
+    argmax.  The compute-bound tiles sum every token's logit in the same order, so the shared
+    rows give bit-identical logits and the lowest id must win through every level at which
+    partial maxima merge (lane, row, wave, token block).  The streamed LM head starts each
+    work item's walk over the hidden dimension at a different chunk, so equal rows in
+    different items round differently: there the tie is a near tie (gap 0 < 2 B_t) and any of
+    the shared ids is a correct top token."""
+    block, H, V = 32, 128, 1152
+    hs, Wb, D = synth.decode_inputs(91 + batch, batch, block, H, V, lean_fraction=0.0)
+    ids = TIE_IDS + (V - 5,)
+    Wb = Wb.copy()
+    for t in ids[1:]:
+        Wb[t] = Wb[ids[0]]
+    if live_all:
+        D = np.zeros(batch * block, np.uint8)
+    rng = np.random.default_rng(92 + batch)
+    wf = synth.bf16_bits_to_f32(Wb[ids[0]]).astype(np.float32)
+    h = synth.bf16_bits_to_f32(hs[0]).astype(np.float32)
+    lean = rng.random(h.shape[0]) < 0.6
+    h[lean] = wf * np.float32(8.0 / (0.02 * 0.02 * H)) + 0.5 * h[lean]
+    hb = synth.f32_to_bf16_bits(h)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hb), dev(Wb), D, tokens)
+    out = oracle.live_decode(hb, Wb, D, block, 0.95, token=tokens)
+    live = D == 0
+    assert (live.sum() <= 512) != live_all          # the intended LM-head path
+    assert np.array_equal(Dn, out["D_next"])          # one fallback commit per sequence
+    hot = live & (out["D_next"] == 1) & np.isin(out["token"], ids)
+    assert hot.sum() == batch, int(hot.sum())
+    assert (out["token"][hot] == ids[0]).all()        # the oracle's own tie rule
+    if live_all:
+        assert (tok[hot] == ids[0]).all(), np.unique(tok[hot])
+    else:
+        assert np.isin(tok[hot], ids).all(), np.unique(tok[hot])
+    B = logit_bound(hb, Wb)
+    crel = 2.0 * B + CONF_EPS
+    assert (np.abs(conf[hot] - out["conf"][hot]) <= crel[hot] * out["conf"][hot]).all()
+    print(f"exact ties: {int(hot.sum())} committed rows, tokens {np.unique(tok[hot]).tolist()} "
+          f"({int(live.sum())} live)", flush=True)
