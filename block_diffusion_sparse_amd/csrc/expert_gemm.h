@@ -323,8 +323,7 @@ __device__ __forceinline__ void expert_stream_body(
       }
   };
   auto pack4 = [](const float* v) {
-    return make_uint2(f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+    return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   };
   auto epilogue = [&](const Item& it) {
     if constexpr (LMHEAD) {
@@ -767,14 +766,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
       for (int n = 0; n < 2; ++n) {
         const int col = cb * CBW + 32 * wn + 16 * n + 4 * g;
         if (col >= Ndim) continue;
-        uint16_t hv[4];
+        float hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = acc[m][n][i], uv = acc[m][n + 2][i];
-          hv[i] = f32_to_bf16(silu(gv) * uv);
-        }
+        for (int i = 0; i < 4; ++i) hv[i] = silu(acc[m][n][i]) * acc[m][n + 2][i];
         *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
-            make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
       }
     } else {
       const float sc = ROUTED ? wl_w[row] : 1.0f;
@@ -782,11 +778,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
       for (int n = 0; n < 4; ++n) {
         const int col = cb * BC + 64 * wn + 16 * n + 4 * g;
         if (col >= Ndim) continue;
-        uint16_t yv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yv[i] = f32_to_bf16(sc * acc[m][n][i]);
         *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
-            make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+            make_uint2(pack_bf16x2(sc * acc[m][n][0], sc * acc[m][n][1]),
+                       pack_bf16x2(sc * acc[m][n][2], sc * acc[m][n][3]));
       }
     }
   }
