@@ -356,9 +356,13 @@ __device__ __forceinline__ void expert_stream_body(
             arg = oa;
           }
         }
+        // exp(v - mx) as one v_exp_f32 of v log2(e) - mx log2(e), as in k_gemm_big's LM head
+        const float nm = -mx * kLog2e;
         float se = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) se += expf(c0[m][i] - mx) + expf(c1[m][i] - mx);
+        for (int i = 0; i < 4; ++i)
+          se += __builtin_amdgcn_exp2f(fmaf(c0[m][i], kLog2e, nm)) +
+                __builtin_amdgcn_exp2f(fmaf(c1[m][i], kLog2e, nm));
 #pragma unroll
         for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
         const int li = it.row0 + 16 * m + r;
