@@ -300,7 +300,9 @@ __device__ __forceinline__ void copy8(const T* src, T v[8]) {
   }
 }
 
-template <typename T>
+// KT: the number of pairs per position when fixed at compile time (all K loads of a column
+// block issued before the first add), 0 for any K (one pair at a time)
+template <typename T, int KT>
 __global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_shared, int iter,
                                                  LayerState L, const int32_t* __restrict__ inv,
                                                  const T* __restrict__ y_pair,
@@ -321,12 +323,22 @@ __global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_sh
     T rb[8];
     if (f) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < K; ++k) {
-        const int p = inv[(size_t)t * K + k];
-        float v[8];
-        load8<T>(y_pair + (size_t)p * H + j, v);
+      if constexpr (KT > 0) {
+        float v[KT][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        for (int k = 0; k < KT; ++k) load8<T>(y_pair + (size_t)inv[(size_t)t * KT + k] * H + j, v[k]);
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += v[k][i];
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int p = inv[(size_t)t * K + k];
+          float v[8];
+          load8<T>(y_pair + (size_t)p * H + j, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) rb[i] = from_f32<T>(acc[i]);
@@ -351,13 +363,18 @@ __global__ __launch_bounds__(256) void k_combine(int M, int H, int K, int has_sh
 
 hipError_t launch_combine(const Shape& s, int iter, const LayerState& L, const Scratch& W,
                           void* y, void* y_routed, hipStream_t st) {
-  if (s.bf16)
-    launch(k_combine<uint16_t>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
+  if (s.bf16 && s.K == 8)
+    launch(k_combine<uint16_t, 8>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
+                       s.n_shared, iter, L, W.inv, static_cast<const uint16_t*>(W.y_pair),
+                       static_cast<const uint16_t*>(W.S), static_cast<uint16_t*>(y),
+                       static_cast<uint16_t*>(y_routed));
+  else if (s.bf16)
+    launch(k_combine<uint16_t, 0>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K,
                        s.n_shared, iter, L, W.inv, static_cast<const uint16_t*>(W.y_pair),
                        static_cast<const uint16_t*>(W.S), static_cast<uint16_t*>(y),
                        static_cast<uint16_t*>(y_routed));
   else
-    launch(k_combine<float>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K, s.n_shared,
+    launch(k_combine<float, 0>, dim3(s.M), dim3(256), 0, st, s.M, s.H, s.K, s.n_shared,
                        iter, L, W.inv, static_cast<const float*>(W.y_pair),
                        static_cast<const float*>(W.S), static_cast<float*>(y),
                        static_cast<float*>(y_routed));
