@@ -41,7 +41,11 @@ constexpr int kDenseTileRows = 64;  // rows per shared-expert weight-stream tile
 // (k_expert_stream, 128-row tiles), beyond it the compute-bound tiles take it (k_gemm_big)
 constexpr int kLmStreamMaxRows = 512;
 constexpr int kBigTile = 256;     // rows per compute-bound routed tile
-constexpr int kBigRows = 768;     // experts with at least this many fresh rows use big tiles
+// experts with at least this many fresh rows use the compute-bound tiles (on shapes that enable
+// them): beside those tiles the weight stream keeps 64-row tiles, so an expert with more rows
+// would stream its weights once per 64 rows there, but once per 256 rows here (measured on the
+// 8192-position shape: 64 to 128 best, 768 up to 10% slower)
+constexpr int kBigRows = 128;
 constexpr int kGateUpCols = 64;   // intermediate columns per gate/up workgroup
 constexpr int kDownCols = 64;     // output columns per down workgroup
 

@@ -33,6 +33,12 @@ TOL = {"bf16": 2e-2, "f32": 1e-5}
 NEAR_TIE = 1e-6
 
 
+# the library's rule for compute-bound routed tiles (block_diffusion_sparse_amd/csrc/
+# epoch_internal.h, kBigRows): experts with at least this many fresh pairs, on shapes whose
+# iterations can hold 32768 pairs or more
+BIG_ROWS = 128
+
+
 def log(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -132,12 +138,12 @@ def compare_iteration(w, out, ins, y, y_routed, it, rows, rep: BlockReport, prev
     assert np.array_equal(g["wl_k"][:P], wl["wl_k"]), f"{tag}: worklist k differ"
     np.testing.assert_allclose(g["wl_w"][:P], wl["wl_w"], rtol=1e-6, atol=1e-12, err_msg=tag)
     assert np.array_equal(g["offs"][:nS + 1], wl["offs"]), f"{tag}: offsets differ"
-    # bf16 shapes whose iterations can hold >= 32768 pairs run experts with >= 768 fresh pairs
-    # on the compute-bound tiles
+    # bf16 shapes whose iterations can hold >= 32768 pairs run experts with >= BIG_ROWS fresh
+    # pairs on the compute-bound tiles
     if w.act == "bf16" and w.M * w.top_k >= 32768:
         per_slot = np.diff(wl["offs"])
-        rep.big_experts += int((per_slot >= 768).sum())
-        rep.big_pairs += int(per_slot[per_slot >= 768].sum())
+        rep.big_experts += int((per_slot >= BIG_ROWS).sum())
+        rep.big_pairs += int(per_slot[per_slot >= BIG_ROWS].sum())
     assert np.array_equal(g["inv"], wl["inv"]), f"{tag}: inverse map differs"
     # outputs on the oracle's evaluated rows
     tol = TOL[w.act]

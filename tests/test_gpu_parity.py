@@ -126,24 +126,25 @@ def test_workload5_sweep_points(frac, R, iters):
 
 @pytest.mark.parametrize("frac,R", [(1.0, 1), (0.5, 4)])
 def test_big_tiles_every_row(frac, R):
-    """Shapes whose iterations can hold >= 32768 pairs route experts with >= 768 fresh rows
-    to 256-row compute-bound tiles and run the shared expert (M >= 2048) on them too.  Small
-    hidden/inter sizes keep the oracle quick, so every row is compared; H = 192 leaves a
+    """Shapes whose iterations can hold >= 32768 pairs route experts with >= BIG_ROWS fresh
+    rows to 256-row compute-bound tiles and run the shared expert (M >= 2048) on them too.
+    Small hidden/inter sizes keep the oracle quick, so every row is compared; H = 192 leaves a
     partial 128-column block in the down projection, and the skewed bias gives a mix of
-    big-tile experts (ragged last tile) and weight-stream experts in the same iteration."""
+    big-tile experts (ragged last tiles) and weight-stream experts in the same iteration."""
     h = H()
-    w = synth.workload(5, hidden=192, n_experts=12, top_k=2, inter=128, shared_inter=192,
+    w = synth.workload(5, hidden=192, n_experts=48, top_k=2, inter=128, shared_inter=192,
                        batch=400, block=41, iters=3, staleness_R=R, forced_fraction=frac,
                        zipf=None, redraw_every=0)
     assert w.M * w.top_k >= 32768
-    bias = (-0.3 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
-    # the routed load of the first iteration must put experts on both sides of 768 pairs
+    bias = (-0.2 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
+    # the routed load of the first iteration must put experts on both sides of BIG_ROWS pairs
     W0 = synth.layer_weights(w, 0)
     x0 = synth.bf16_bits_to_f32(synth.hidden_states(w, 0, synth.decoded_masks(w), iters=1)[0])
     G = x0.astype(np.float64) @ W0["router_w"].astype(np.float64).T + bias
     top = np.argsort(-G, axis=1, kind="stable")[:, : w.top_k]
     load = np.bincount(top.ravel(), minlength=w.n_experts)
-    assert load.max() >= 768 and (load[load > 0] < 768).any(), load
+    big = h.BIG_ROWS
+    assert load.max() >= big and (load[load > 0] < big).any(), load
     h.log(f"[big tiles] M={w.M} f={frac} R={R} load={load.tolist()}")
     rep = h.run_block(w, weights=[W0], bias_override=bias)
     assert rep.iters == w.iters
@@ -154,11 +155,11 @@ def test_kernel_timing_on_both_streams():
     shared expert and the big tiles run on the device's side stream and are timed there, and
     every group reads back one duration per forward."""
     h = H()
-    w = synth.workload(5, hidden=192, n_experts=12, top_k=2, inter=128, shared_inter=192,
+    w = synth.workload(5, hidden=192, n_experts=48, top_k=2, inter=128, shared_inter=192,
                        batch=400, block=41, iters=3, staleness_R=1, forced_fraction=1.0,
                        zipf=None, redraw_every=0)
     W0 = synth.layer_weights(w, 0)
-    W0["router_b"] = (-0.3 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
+    W0["router_b"] = (-0.2 * np.log(np.arange(1, w.n_experts + 1))).astype(np.float32)
     plan = h.make_plan(w, [h.upload_weights(W0)], 1)
     D = synth.decoded_masks(w)
     X = h.to_dev(synth.hidden_states(w, 0, D, iters=w.iters))
@@ -176,7 +177,7 @@ def test_kernel_timing_on_both_streams():
     assert list(t) == B.TIMING_GROUPS
     for g, (ms, n) in t.items():
         assert n == w.iters and ms > 0.0, (g, ms, n)
-    assert c["big_experts"] > 0 and c["big_pairs"] >= 768 * c["big_experts"]
+    assert c["big_experts"] > 0 and c["big_pairs"] >= h.BIG_ROWS * c["big_experts"]
 
 
 @pytest.mark.parametrize("frac,R", [(1.0, 1), (0.5, 3)])
