@@ -299,7 +299,8 @@ typedef struct epoch_decode_desc {
 } epoch_decode_desc;
 
 /* Bytes of device workspace epoch_live_decode needs for `d` (live list, per-position
-   live index, per-row partial reductions of M x V/64 entries). */
+   live index, per-row partial reductions of up to M x V/32 entries, per-position confidence
+   and top token). */
 int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes);
 
 /*
