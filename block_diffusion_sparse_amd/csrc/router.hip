@@ -151,7 +151,9 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
   for (int j = 0; j < NPER; ++j) key[j] = (lane + 64 * j < E) ? sel_key(gv[j], lane + 64 * j) : 0ull;
   // the n largest of the keys kk (0 = excluded): membership masks and ranks
   auto select = [&](const uint64_t* kk, int n, uint64_t* selm, int* rank) {
-    // largest threshold T with #{key >= T} >= n: the n-th largest key
+    // largest threshold T with #{key >= T} >= n: the n-th largest key.  Keys are unique (the
+    // expert id is in the low bits), so once exactly n keys lie at or above a candidate they
+    // are the n largest and the lower bits cannot change the set: stop there.
     uint64_t T = 0;
     for (int b = 41; b >= 0; --b) {
       const uint64_t cand = T | (1ull << b);
@@ -159,6 +161,7 @@ __device__ __forceinline__ void route_row(int t, const float* __restrict__ G, co
 #pragma unroll
       for (int j = 0; j < NPER; ++j) cnt += __popcll(ballot64(kk[j] >= cand));
       if (cnt >= n) T = cand;
+      if (cnt == n) break;
     }
     // rank of each selected key among the selected ones
 #pragma unroll
