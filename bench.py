@@ -10,8 +10,9 @@ resident in HBM before the timed region starts.
 
 Prints one JSON line: fresh token-expert pairs/s over the timed steps, the
 per-layer-iteration time, the roofline of the dominant kernel (measured live with
-HIP events on the stream the kernels run on) and the CPU oracle timed on a
-bounded sample of the same workload as a baseline.
+HIP events on the stream the kernels run on), the rooflines of the combine, the
+router and the compaction steps (from the untimed per-kernel breakdown), and the
+CPU oracle timed on a bounded sample of the same workload as a baseline.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 """
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 TIMED_EVERY = 4            # the timed region times the dominant kernel on every 4th forward
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
+MFMA_FP64_PEAK_TFS = 78.6    # dense fp64 MFMA, TFLOP/s (the router's contraction)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -200,7 +202,8 @@ def main():
         block)."""
         plan = B.epoch_block_plan_build(desc, lw, ws, nbytes, sp)
         prev = [layer_counters(plan, l) for l in range(n_layers)]
-        idx = [B.COUNTERS.index(n) for n in ("touched", "pairs", "big_experts", "big_pairs")]
+        idx = [B.COUNTERS.index(n)
+               for n in ("touched", "pairs", "big_experts", "big_pairs", "fresh_rows")]
         fwd = []
         for it in range(iters):
             for l in range(n_layers):
@@ -299,6 +302,48 @@ def main():
                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     kernels_us = {g: round(1e3 * brk_ms[g] / max(brk_n[g], 1), 2) for g in B.TIMING_GROUPS
                   if brk_n[g]}
+
+    # ------------------------------------------------- rooflines of the other kernel groups
+    # per launch, averaged over every forward of a block, against the breakdown pass's event
+    # times (every group timed, so each carries a few us of event gap):
+    #   combine: y_pair rows of the fresh pairs and cached rows of the stable positions read,
+    #            y and the committed copy written, the shared expert's output read -> HBM;
+    #   logits + top-k: 2 M E H flop in fp64 -> the fp64 MFMA peak (the top-k kernel is
+    #            latency-bound and inside the same group);
+    #   compaction (plan step + placement): ids and scores of the K_ext candidates read,
+    #            the worklist (12 bytes a pair) and the inverse map written: latency-bound.
+    n_fwd = max(len(per_fwd), 1)
+    Pavg = sum(f[1] for f in per_fwd) / n_fwd
+    Favg = sum(f[4] for f in per_fwd) / n_fwd
+    Kx = w.k_ext
+    other = {}
+    if brk_n["combine"]:
+        t = brk_ms["combine"] / brk_n["combine"] * 1e-3
+        nb = (Pavg + (M - Favg) + 2 * M + (M if w.n_shared else 0)) * H * act
+        other["combine"] = {"bound": "hbm", "achieved": round(nb / t / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes_per_launch": int(nb),
+                            "avg_launch_us": round(t * 1e6, 2)}
+    if brk_n["router"]:
+        t = brk_ms["router"] / brk_n["router"] * 1e-3
+        fl = 2.0 * M * E * H
+        other["router"] = {"bound": "mfma_fp64", "achieved": round(fl / t / 1e12, 2),
+                           "peak": MFMA_FP64_PEAK_TFS, "unit": "TFLOP/s",
+                           "frac": round(fl / t / 1e12 / MFMA_FP64_PEAK_TFS, 4),
+                           "algorithmic_flop_per_launch": int(fl),
+                           "algorithmic_bytes_per_launch": int(M * H * act + 4 * E * H),
+                           "avg_launch_us": round(t * 1e6, 2),
+                           "groups": "logits + top-k"}
+    t = sum(brk_ms[g] for g in ("plan", "place")) / max(brk_n["plan"], 1) * 1e-3
+    if brk_n["plan"]:
+        nb = M * Kx * 12 + Pavg * 12 + M * K * 4
+        other["compaction"] = {"bound": "latency", "achieved": round(nb / t / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes_per_launch": int(nb),
+                               "avg_launch_us": round(t * 1e6, 2),
+                               "groups": "plan step + placement"}
     kernels_share = {g: round(brk_ms[g] / max(sum(brk_ms.values()), 1e-9), 4)
                      for g in B.TIMING_GROUPS if brk_n[g]}
 
@@ -338,6 +383,7 @@ def main():
         "kernel_us_per_launch": kernels_us,
         "kernel_time_share": kernels_share,
         "roofline": roofline,
+        "other_rooflines": other,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
