@@ -12,9 +12,9 @@
 //                   vocabulary streamed through LDS once per 256 live rows (the slab's further
 //                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
 //                   each row's 32-token blocks to (max, argmax, sum exp);
-//   k_gemm_big      LM-head mode, when more are live: 256 live rows x 256 tokens per
+//   k_gemm_w4       LM-head mode, when more are live: 256 live rows x 256 tokens per
 //                   workgroup on the compute-bound tiles, one (max, argmax, sum exp) per row and
-//                   256-token block (the workgroup's four column waves combined in LDS);
+//                   256-token block (the workgroup's two column waves combined in LDS);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
 //                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
 //   k_decode_final  one workgroup per sequence: the commits.
@@ -35,12 +35,10 @@ constexpr int kCompactThreads = 1024;
 // (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
 constexpr int kLmStreamBuffers = 2;
 constexpr int kLmStreamTileRows = 256;
-// beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 256 tokens, eight
-// waves of 128 x 64 outputs, one workgroup per CU (half the operand bytes per MFMA of
-// 256 x 128 tiles, and a vocabulary gives plenty of token blocks)
-constexpr int kLmBigTileRows = 256;
-constexpr int kLmBigWaves = 8;
-constexpr int kLmBigTileCols = 32 * kLmBigWaves;
+// beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 256 tokens
+// (k_gemm_w4: four waves of 128 x 128 outputs, one workgroup per CU; a vocabulary gives plenty
+// of token blocks)
+constexpr int kLmBigTileCols = 256;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
                                                                   const uint8_t* __restrict__ D,
@@ -279,17 +277,15 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     }
   }
-  // grid: 8 XCDs x row tiles (sized for all M positions live; tiles past the live count exit
-  // at once) x token blocks per XCD; blocks of kLmBigTileCols tokens (the last one half when
-  // the vocabulary is an odd multiple of 128)
-  const int tiles = (M + kLmBigTileRows - 1) / kLmBigTileRows;
+  // grid: XCD supertiles of 4 row tiles x 8 token blocks (sized for all M positions live;
+  // tiles past the live count exit at once); blocks of kLmBigTileCols tokens (the last one
+  // half when the vocabulary is an odd multiple of 128)
   const int n_cb = (d->vocab + kLmBigTileCols - 1) / kLmBigTileCols;
   const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_cb};
-  launch((k_gemm_big<false, false, true, kLmBigTileRows, kLmBigWaves>),
-                     dim3(8 * tiles * ((n_cb + 7) / 8)), dim3(64 * kLmBigWaves), 0, st,
-                     static_cast<const uint16_t*>(h),
-                     static_cast<const uint16_t*>(w_vocab), nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden, d->vocab, lp_big);
+  launch((k_gemm_w4<false, false, true>), dim3(gemm_w4_dense_grid(M, n_cb)), dim3(256), 0, st,
+         static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), nullptr,
+         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden,
+         d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
   launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
          L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);

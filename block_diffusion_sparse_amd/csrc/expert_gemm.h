@@ -42,11 +42,11 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
 }
 
-// Output of the LM-head modes (k_gemm_big, k_expert_stream): the rows are live positions
+// Output of the LM-head modes (k_gemm_w4, k_expert_stream): the rows are live positions
 // (gathered through live_list, n_live of them), the columns vocabulary tokens, and instead of
 // the logits the kernels write, per row and per block of tokens, the largest logit, its token
 // (lower id on ties) and the sum of exp(logit - largest) over the block; n_p blocks per row:
-// vocab / 32 from k_expert_stream (one wave's columns), vocab / 256 rounded up from k_gemm_big
+// vocab / 32 from k_expert_stream (one wave's columns), vocab / 256 rounded up from k_gemm_w4
 // (one workgroup's columns).
 struct LmPartials {
   const int32_t* live_list;
@@ -356,7 +356,7 @@ __device__ __forceinline__ void expert_stream_body(
             arg = oa;
           }
         }
-        // exp(v - mx) as one v_exp_f32 of v log2(e) - mx log2(e), as in k_gemm_big's LM head
+        // exp(v - mx) as one v_exp_f32 of v log2(e) - mx log2(e), as in k_gemm_w4's LM head
         const float nm = -mx * kLog2e;
         float se = 0.0f;
 #pragma unroll
@@ -483,13 +483,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
   }
 }
 
-// Compute-bound variant for tiles with many rows (the shared expert over all M positions,
-// routed experts with many fresh pairs, the LM head over the live positions): a BR-row x
-// BC-weight-row output tile per workgroup of WAVES waves, two along the rows and WAVES / 2 along
-// the weight rows, each wave accumulating a (BR / 2) x 64 sub-tile with v_mfma_f32_16x16x32_bf16
-// (BR / 32 x 4 blocks), so BC = 32 WAVES.  Four waves (BC = 128) run two workgroups per CU; eight
-// waves (BR = 256, BC = 256, one workgroup per CU) halve the operand bytes copied per MFMA,
-// which pays on problems with enough tiles to fill the device.
+// Compute-bound variant for tiles with many rows on two waves per SIMD (routed experts with
+// many fresh pairs, which run beside the weight-stream kernel, and shared-expert layers with
+// too few 256 x 256 tiles for k_gemm_w4): a BR-row x 128-weight-row output tile per workgroup
+// of four waves, two along the rows and two along the weight rows, each wave accumulating a
+// (BR / 2) x 64 sub-tile with v_mfma_f32_16x16x32_bf16 (BR / 32 x 4 blocks); two workgroups
+// per CU.
 // K runs in chunks of KC = 32.  Both operands of a chunk go from global memory straight into
 // LDS (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base + 16 x lane),
 // NB chunk buffers deep, NB - 2 chunks in flight while a chunk is multiplied.  LDS rows of
@@ -507,43 +506,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_expert_stream(
 // holds g and u of the same 32 columns and the SwiGLU epilogue stays in registers; down: BC
 // rows of W2.  Grid as k_expert_stream (XCD-grouped, 1-D): BC / 2 (gate/up) or BC (down)
 // columns per block.
-template <bool GATEUP, bool ROUTED, bool LMHEAD = false, int BR = 128, int WAVES = 4>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
+template <bool GATEUP, bool ROUTED, int BR = 128>
+__global__ __launch_bounds__(256, 2) void k_gemm_big(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
-  static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
   static_assert(BR == 128 || BR == 256, "row tiles of 128 or 256");
-  static_assert(WAVES == 4 || (WAVES == 8 && BR == 256), "four waves, or eight on 256-row tiles");
-  constexpr int KC = 32, WN = WAVES / 2, BC = 64 * WN;
+  constexpr int WAVES = 4, KC = 32, WN = WAVES / 2, BC = 64 * WN;
   constexpr int MB = BR / 32;                                   // 16-row blocks per wave
-  constexpr int NB = WAVES == 8 ? 4 : (BR == 256 ? 3 : 4);      // LDS chunk buffers
+  constexpr int NB = BR == 256 ? 3 : 4;                         // LDS chunk buffers
   constexpr int NA = BR / (16 * WAVES), NBI = BC / (16 * WAVES);  // copies per wave and chunk
   constexpr int CBW = GATEUP ? BC / 2 : BC;                     // output columns per block
   __shared__ __attribute__((aligned(16))) uint16_t As[NB][BR * KC];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BC * KC];
   const int n_cb = (Ndim + CBW - 1) / CBW;
-  int tile, cb;
-  if (LMHEAD) {
-    // few row tiles, many token blocks: token blocks go round the 8 XCDs and every row tile
-    // of a block runs on the block's XCD (its W_v rows enter one L2); M bounds the row tiles
-    const int T = (M + BR - 1) / BR, within = blockIdx.x >> 3;
-    cb = 8 * (within / T) + (blockIdx.x & 7);
-    tile = within % T;
-    if (cb >= n_cb) return;
-  } else {
-    const int pos = blockIdx.x >> 3;
-    tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
-    cb = pos % n_cb;
-  }
-  // routed big tiles come from their own table, counted in FLAG_NTILES_BIG; the LM head is
-  // this kernel's only beyond kLmStreamMaxRows live rows (below, k_expert_stream streams it)
-  if (LMHEAD && *lp.n_live <= kLmStreamMaxRows) return;
+  const int pos = blockIdx.x >> 3;
+  const int tile = ((pos / n_cb) << 3) + (blockIdx.x & 7), cb = pos % n_cb;
+  // routed big tiles come from their own table, counted in FLAG_NTILES_BIG
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
-                                tile_row0, offs, LMHEAD ? *lp.n_live : M);
+                                tile_row0, offs, M);
   if (!tr.active) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -560,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
     const int row = 16 * (WAVES * j + wave) + (lane >> 2);
     const int c8 = (lane & 3) ^ ((row >> 1) & 3);
     const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
-    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p);
+    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : p;
     asrc[j] = A + (size_t)src_row * Kdim + c8 * 8;
   }
 #pragma unroll
@@ -620,10 +604,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
                    : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
                      "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]));
   };
-  // The operands go in swapped (weights, or vocabulary rows, as the 16 x 32 left operand), so
-  // that a block holds its outputs transposed: lane (r, g) gets four consecutive columns
-  // 4 g .. 4 g + 3 of row r.  Expert tiles store them with one 8-byte store; the LM head finds
-  // 16 of a row's 64 tokens in each lane and reduces them mostly in registers.
+  // The operands go in swapped (weights as the 16 x 32 left operand), so that a block holds its
+  // outputs transposed: lane (r, g) gets four consecutive columns 4 g .. 4 g + 3 of row r,
+  // stored with one 8-byte store.
   auto mma = [&](int set) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -677,89 +660,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
       }
     }
   }
-  if (LMHEAD) {
-    // Per row, over this workgroup's BC tokens: lane (r, g) of row block m holds tokens
-    // 16 n + 4 g + i (n, i < 4) of its wave's 64-token block for row 16 m + r.  Each wave reduces
-    // its 64 tokens in registers (max, lower token on ties: tokens are visited in increasing
-    // order and only a larger logit replaces), then across the four lanes of the row (lane bits
-    // 4 and 5), then the sum of exp(logit - max) likewise; the WN waves of a row half then meet
-    // in LDS, and one (max, argmax, sum) per row and workgroup is written.  A wave whose tokens
-    // lie past the vocabulary (the last block of a vocabulary that is an odd multiple of 128
-    // tokens) contributes (-inf, -, 0).
-    struct Part {
-      float mx;
-      int arg;
-      float se;
-    };
-    static_assert(sizeof(Part) * BR * WN <= sizeof(As), "the partials fit in the operand buffers");
-    Part* part = reinterpret_cast<Part*>(&As[0][0]);  // [BR rows][WN waves]
-    const bool wlive = cb * BC + 64 * wn < Ndim;
-    const int tok0 = cb * BC + 64 * wn + 4 * g;
-    __syncthreads();  // every wave is done with the operand buffers
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      float mx = acc[m][0][0];
-      int arg = tok0;
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((n | i) && acc[m][n][i] > mx) {
-            mx = acc[m][n][i];
-            arg = tok0 + 16 * n + i;
-          }
-#pragma unroll
-      for (int o = 16; o < 64; o <<= 1) {
-        const float om = __shfl_xor(mx, o, 64);
-        const int oa = __shfl_xor(arg, o, 64);
-        if (om > mx || (om == mx && oa < arg)) {
-          mx = om;
-          arg = oa;
-        }
-      }
-      // exp(v - mx) for v <= mx as one v_exp_f32 of v log2(e) - mx log2(e) (a single fma): the
-      // rounding of mx log2(e) makes the relative error about 1e-6 for logits up to 20 in
-      // magnitude; terms below exp(-87) underflow to 0
-      const float nm = -mx * kLog2e;
-      float se = 0.0f;
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        se += (__builtin_amdgcn_exp2f(fmaf(acc[m][n][0], kLog2e, nm)) +
-               __builtin_amdgcn_exp2f(fmaf(acc[m][n][1], kLog2e, nm))) +
-              (__builtin_amdgcn_exp2f(fmaf(acc[m][n][2], kLog2e, nm)) +
-               __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
-#pragma unroll
-      for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
-      if (g == 0)
-        part[(BR / 2 * wm + 16 * m + r) * WN + wn] =
-            wlive ? Part{mx, arg, se} : Part{-INFINITY, 0x7fffffff, 0.0f};
-    }
-    __syncthreads();
-    // the WN partials of a row: wave blocks in token order, so the first maximum holds the lower
-    // token; each earlier sum rescaled to the row maximum
-    for (int rr = tid; rr < BR; rr += 64 * WAVES) {
-      const int row = tr.row0 + rr;
-      if (row >= tr.row_end) continue;
-      Part best = part[rr * WN];
-#pragma unroll
-      for (int w = 1; w < WN; ++w) {
-        const Part q = part[rr * WN + w];
-        if (q.mx > best.mx) best = q;
-      }
-      const float nm = -best.mx * kLog2e;
-      float se = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WN; ++w) {
-        const Part q = part[rr * WN + w];
-        se += q.se * __builtin_amdgcn_exp2f(fmaf(q.mx, kLog2e, nm));
-      }
-      const size_t idx = (size_t)row * lp.n_p + cb;
-      lp.pmax[idx] = best.mx;
-      lp.parg[idx] = best.arg;
-      lp.psum[idx] = se;
-    }
-    return;
-  }
   // transposed blocks: lane (r, g) holds row 16 m + r, columns 16 n + 4 g .. + 3
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -788,6 +688,307 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void k_gemm_big(
       }
     }
   }
+}
+
+// Compute-bound tiles on one wave per SIMD: a 256 x 256 output tile per workgroup of four
+// waves, each wave accumulating 128 x 128 (8 x 8 blocks of v_mfma_f32_16x16x32_bf16, 256 fp32
+// accumulators per lane held in AGPRs), so that a wave reads a third fewer operand bytes from
+// LDS per MFMA than the two-waves-per-SIMD tiles of k_gemm_big.  Same operand roles, staged row
+// layouts (gate/up: groups of 64 rows alternating W1 and W3, so a wave holds g and u of the same
+// 64 columns) and epilogues as k_gemm_big, plus the LM head's (max, argmax, sum exp) epilogue;
+// used where the grid has at least one tile per CU.
+// K runs in chunks of 64 bf16: a chunk row is one 128-byte line, and one copy instruction
+// (global_load_lds_dwordx4) moves eight whole lines straight into LDS, half the cache-line
+// requests of 64-byte rows.  Two chunk buffers of 64 KB: chunk c + 2 is copied into chunk c's
+// buffer while chunk c + 1 is multiplied.  LDS rows hold k-segment slot ^ (row & 7) in 16-byte
+// slot `slot`, so that the eight lanes a ds_read_b128 serves at once hit distinct banks.
+// Each chunk is multiplied as two halves of K = 32 with fragment register sets 0 and 1: the
+// fragments of the next half are read from LDS (one ds_read_b128 per four MFMAs) while the
+// current half is multiplied.  One barrier per chunk, before the second half: every wave's
+// copies of chunk c + 1 have landed and every wave has read all of chunk c, whose buffer the
+// second half refills.  Every step issues the same copies and reads (past the last chunk they
+// repeat the last one into a buffer nobody reads again), so the loop has no tail.
+// The MFMAs are inline asm with AGPR accumulators ("+a"): the compiler, which otherwise keeps
+// MFMA results in VGPRs and spills them to AGPRs around every use, cannot insert the wait
+// states an MFMA result needs before a VALU reads it, so the epilogue starts after 48 idle
+// cycles.
+// Grid: LMHEAD and dense tiles in XCD supertiles (MAP): workgroup 8 i + x runs on XCD x, and the
+// 32 workgroups an XCD holds at once cover 4 row tiles x 8 column blocks, so each XCD's L2
+// serves a 4 x 8 block of tiles; routed tiles as k_gemm_big (the big-tile table).
+template <bool GATEUP, bool ROUTED, bool LMHEAD = false>
+__global__ __launch_bounds__(256, 1) void k_gemm_w4(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
+    const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
+    const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
+  static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
+  constexpr int BR = 256, BC = 256, KC = 64, WAVES = 4, WN = 2, MB = 8, NBK = 8;
+  constexpr int NA = BR / (8 * WAVES), NBI = BC / (8 * WAVES);  // copies per wave and chunk
+  constexpr int CPC = NA + NBI;
+  constexpr int CBW = GATEUP ? BC / 2 : BC;  // output columns per block
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BR * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BC * KC];
+  const int n_cb = (Ndim + CBW - 1) / CBW;
+  int tile, cb;
+  if (!ROUTED) {
+    const int T = (M + BR - 1) / BR, nsc = (n_cb + 7) / 8;
+    const int within = blockIdx.x >> 3, s = (within >> 5) * 8 + (blockIdx.x & 7);
+    tile = (s / nsc) * 4 + ((within & 31) >> 3);
+    cb = (s % nsc) * 8 + (within & 7);
+    if (tile >= T || cb >= n_cb) return;
+  } else {
+    const int pos = blockIdx.x >> 3;
+    tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
+    cb = pos % n_cb;
+  }
+  if (LMHEAD && *lp.n_live <= kLmStreamMaxRows) return;
+  const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
+                                tile_row0, offs, LMHEAD ? *lp.n_live : M);
+  if (!tr.active) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const size_t estride = (size_t)Ndim * Kdim;
+  const size_t e = ROUTED ? (size_t)S_list[tr.slot] : 0;
+  // copy j of wave w fills LDS rows [8 (WAVES j + w), +8) of a chunk buffer: lane l slot l % 8
+  // of row 8 (WAVES j + w) + l / 8, i.e. k-segment (l % 8) ^ (row & 7) of that row.  Activation
+  // rows by pointer, weight rows by 32-bit byte offset from their column block's first row (at
+  // most 256 rows of at most 16384 elements); rows past the tile or past N load a stand-in row
+  // of the operand: they only feed outputs that are never stored
+  const char* asrc[NA];
+  uint32_t boff[NBI];
+  const uint16_t* bbase[NBI];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int row = 8 * (WAVES * j + wave) + (lane >> 3);
+    const int seg = (lane & 7) ^ (row & 7);
+    const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
+    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p);
+    asrc[j] = reinterpret_cast<const char*>(A + (size_t)src_row * Kdim + seg * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < NBI; ++j) {
+    const int row = 8 * (WAVES * j + wave) + (lane >> 3);
+    const int seg = (lane & 7) ^ (row & 7);
+    int first, wrow;  // the column block's first row of this operand, the staged row's row
+    const uint16_t* base;
+    if (GATEUP) {
+      // groups of 64 staged rows: W1, W3, W1, W3; copy j's rows 32 j + [0, 32) lie in group j / 2
+      const int q = j >> 1;
+      first = cb * CBW;
+      wrow = first + (q >> 1) * 64 + (row & 63);
+      base = (q & 1) ? B1 : B0;
+    } else {
+      first = cb * BC;
+      wrow = first + row;
+      base = B0;
+    }
+    bbase[j] = base + e * estride + (size_t)first * Kdim;
+    const int lrow = wrow < Ndim ? wrow - first : 0;
+    boff[j] = ((uint32_t)lrow * (uint32_t)Kdim + seg * 8) * 2u;
+  }
+  auto issue = [&](int j, int c, int buf) {
+    if (j < NA)
+      copy16_to_lds(asrc[j] + (size_t)c * (KC * 2), &As[buf][8 * (WAVES * j + wave) * KC]);
+    else
+      copy16_to_lds(reinterpret_cast<const char*>(bbase[j - NA]) + (size_t)c * (KC * 2) +
+                        boff[j - NA],
+                    &Bs[buf][8 * (WAVES * (j - NA) + wave) * KC]);
+  };
+  f32x4 acc[MB][NBK];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+  // fragments of half h: lane (r, g) reads row 16 i + r, k-segment 4 h + g, which sits in slot
+  // (4 h + g) ^ (r & 7)
+  u32x4 fa[2][MB], fb[2][NBK];
+  const uint32_t a_l = (uint32_t)(uintptr_t)&As[0][(128 * wm + r) * KC];
+  const uint32_t b_l = (uint32_t)(uintptr_t)&Bs[0][(128 * wn + r) * KC];
+  const uint32_t sw0 = (g ^ (r & 7)) * 16, sw1 = ((4 + g) ^ (r & 7)) * 16;
+  auto read = [&](int buf, int half, int set, int i) {
+    const uint32_t sw = half ? sw1 : sw0;
+    if (i < MB)
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(fa[set][i]) : "v"(a_l + buf * (BR * KC * 2) + sw), "i"(i * 16 * KC * 2));
+    else
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(fb[set][i - MB])
+                   : "v"(b_l + buf * (BC * KC * 2) + sw), "i"((i - MB) * 16 * KC * 2));
+  };
+  // a set's fragments are complete once this wave's LDS reads are; the wait names them as
+  // operands, so no MFMA using them is placed before it
+  auto frags_ready = [&](int set) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]),
+                   "+v"(fa[set][4]), "+v"(fa[set][5]), "+v"(fa[set][6]), "+v"(fa[set][7]),
+                   "+v"(fb[set][0]), "+v"(fb[set][1]), "+v"(fb[set][2]), "+v"(fb[set][3]),
+                   "+v"(fb[set][4]), "+v"(fb[set][5]), "+v"(fb[set][6]), "+v"(fb[set][7]));
+  };
+  // operands swapped as in k_gemm_big: lane (r, g) of block (m, n) gets columns 16 n + 4 g ..
+  // + 3 of row 16 m + r
+  auto mma = [&](int set, int idx) {
+    const int m = idx / NBK, n = idx % NBK;
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+        : "+a"(acc[m][n]) : "v"(fb[set][n]), "v"(fa[set][m]));
+  };
+  // one half: 64 MFMAs on `set`; the 16 fragment reads of (rbuf, rhalf) into the other set;
+  // when `copy`, the CPC copies of chunk cp into buffer cbuf
+  auto half_step = [&](int set, int rbuf, int rhalf, bool copy, int cp, int cbuf) {
+#pragma unroll
+    for (int grp = 0; grp < 16; ++grp) {
+      read(rbuf, rhalf, set ^ 1, grp);
+      mma(set, 4 * grp + 0);
+      mma(set, 4 * grp + 1);
+      if (copy) issue(grp, cp, cbuf);
+      mma(set, 4 * grp + 2);
+      mma(set, 4 * grp + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int nch = Kdim / KC;
+  auto src_chunk = [&](int c) { return c < nch ? c : nch - 1; };
+#pragma unroll
+  for (int j = 0; j < CPC; ++j) issue(j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < CPC; ++j) issue(j, src_chunk(1), 1);
+  wait_vm_lds<CPC>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) read(0, 0, 0, i);
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    frags_ready(0);
+    half_step(0, buf, 1, false, 0, 0);
+    wait_vm_lds<0>();
+    frags_ready(1);
+    __builtin_amdgcn_s_barrier();
+    half_step(1, buf ^ 1, 0, true, src_chunk(c + 2), buf);
+  }
+  // the last step's surplus copies and reads land before anything else uses LDS or those
+  // registers; then the wait states before the accumulators are read
+  wait_vm_lds<0>();
+  frags_ready(0);
+  frags_ready(1);
+  asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+  if (LMHEAD) {
+    // Per row, over this workgroup's 256 tokens: lane (r, g) of row block m holds tokens
+    // 16 n + 4 g + i (n < 8, i < 4) of its wave's 128-token block for row 16 m + r.  Each wave
+    // reduces its tokens in registers (max, lower token on ties: tokens are visited in
+    // increasing order and only a larger logit replaces), then across the four lanes of the row
+    // (lane bits 4 and 5), then the sum of exp(logit - max) likewise; the two waves of a row
+    // half then meet in LDS, and one (max, argmax, sum) per row and workgroup is written.  A
+    // wave whose tokens lie past the vocabulary (the last block of a vocabulary that is an odd
+    // multiple of 128 tokens) contributes (-inf, -, 0).  exp(v - mx) for v <= mx is one
+    // v_exp_f32 of v log2(e) - mx log2(e) (a single fma): the rounding of mx log2(e) makes the
+    // relative error about 1e-6 for logits up to 20 in magnitude; terms below exp(-87)
+    // underflow to 0
+    struct Part {
+      float mx;
+      int arg;
+      float se;
+    };
+    static_assert(sizeof(Part) * BR * WN <= sizeof(As), "the partials fit in the operand buffers");
+    Part* part = reinterpret_cast<Part*>(&As[0][0]);  // [BR rows][WN waves]
+    const bool wlive = cb * BC + 128 * wn < Ndim;
+    const int tok0 = cb * BC + 128 * wn + 4 * g;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float mx = acc[m][0][0];
+      int arg = tok0;
+#pragma unroll
+      for (int n = 0; n < NBK; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((n | i) && acc[m][n][i] > mx) {
+            mx = acc[m][n][i];
+            arg = tok0 + 16 * n + i;
+          }
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const float om = __shfl_xor(mx, o, 64);
+        const int oa = __shfl_xor(arg, o, 64);
+        if (om > mx || (om == mx && oa < arg)) {
+          mx = om;
+          arg = oa;
+        }
+      }
+      const float nm = -mx * kLog2e;
+      float se = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NBK; ++n)
+        se += (__builtin_amdgcn_exp2f(fmaf(acc[m][n][0], kLog2e, nm)) +
+               __builtin_amdgcn_exp2f(fmaf(acc[m][n][1], kLog2e, nm))) +
+              (__builtin_amdgcn_exp2f(fmaf(acc[m][n][2], kLog2e, nm)) +
+               __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
+      if (g == 0)
+        part[(128 * wm + 16 * m + r) * WN + wn] =
+            wlive ? Part{mx, arg, se} : Part{-INFINITY, 0x7fffffff, 0.0f};
+    }
+    __syncthreads();
+    for (int rr = tid; rr < BR; rr += 64 * WAVES) {
+      const int row = tr.row0 + rr;
+      if (row >= tr.row_end) continue;
+      Part best = part[rr * WN];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) {
+        const Part q = part[rr * WN + w];
+        if (q.mx > best.mx) best = q;
+      }
+      const float nm = -best.mx * kLog2e;
+      float se = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        const Part q = part[rr * WN + w];
+        se += q.se * __builtin_amdgcn_exp2f(fmaf(q.mx, kLog2e, nm));
+      }
+      const size_t idx = (size_t)row * lp.n_p + cb;
+      lp.pmax[idx] = best.mx;
+      lp.parg[idx] = best.arg;
+      lp.psum[idx] = se;
+    }
+    return;
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = tr.row0 + 128 * wm + 16 * m + r;
+    if (row >= tr.row_end) continue;
+    if (GATEUP) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = cb * CBW + 64 * wn + 16 * n + 4 * g;
+        if (col >= Ndim) continue;
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = silu(acc[m][n][i]) * acc[m][n + 4][i];
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
+            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      }
+    } else {
+      const float sc = ROUTED ? wl_w[row] : 1.0f;
+#pragma unroll
+      for (int n = 0; n < NBK; ++n) {
+        const int col = cb * BC + 128 * wn + 16 * n + 4 * g;
+        if (col >= Ndim) continue;
+        *reinterpret_cast<uint2*>(out + (size_t)row * Ndim + col) =
+            make_uint2(pack_bf16x2(sc * acc[m][n][0], sc * acc[m][n][1]),
+                       pack_bf16x2(sc * acc[m][n][2], sc * acc[m][n][3]));
+      }
+    }
+  }
+}
+
+// Grid of k_gemm_w4 for a dense or LM-head GEMM of `rows` rows and n_cb column blocks: whole
+// XCD supertiles of 4 x 8 tiles, 32 workgroups each, supertiles dealt to the 8 XCDs in turn.
+inline int gemm_w4_dense_grid(int rows, int n_cb) {
+  const int supertiles = ((rows + 255) / 256 + 3) / 4 * ((n_cb + 7) / 8);
+  return (supertiles + 7) / 8 * 8 * 32;
 }
 
 }  // namespace epoch

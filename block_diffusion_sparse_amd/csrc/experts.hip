@@ -28,7 +28,9 @@ constexpr int kBig256MinBlocks = 512;  // 256-row tiles only when two workgroups
 // waves of the compute-bound routed tiles (kBigTile rows x 32 kBigWaves weight rows): four, two
 // workgroups per CU.  Eight (256 x 256 tiles, one workgroup per CU) measured no faster at the
 // 8192-position shape, where these tiles run beside the weight-stream kernel and the larger
-// workgroup no longer fits in the LDS it leaves free.
+// workgroup no longer fits in the LDS it leaves free; nor did k_gemm_w4's one wave per SIMD,
+// which takes whole CUs from that kernel (1038 -> 1006 us per layer-iteration at full
+// freshness, 755 -> 768 us at half).
 constexpr int kBigWaves = 4;
 
 // Workgroups of k_expert_stream with lds bytes each that fit on the device at once, at most
@@ -152,12 +154,12 @@ hipError_t launch_routed_gateup_big(const Shape& s, const void* x, const void* w
                                     const void* w3, const LayerState& L, const Scratch& W,
                                     hipStream_t st) {
   // experts with many fresh rows: compute-bound kBigTile-row tiles
-  launch((k_gemm_big<true, true, false, kBigTile, kBigWaves>),
+  launch((k_gemm_big<true, true, kBigTile>),
          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.I + 16 * kBigWaves - 1) / (16 * kBigWaves))),
          dim3(64 * kBigWaves), 0, st,
          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w1),
          static_cast<const uint16_t*>(w3), W.flags, W.tile_slot_b, W.tile_row0_b, W.offs,
-         L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M, s.H, s.I, LmPartials{});
+         L.S_list, W.wl_pos, W.wl_w, static_cast<uint16_t*>(W.h), s.M, s.H, s.I);
   return hipGetLastError();
 }
 
@@ -176,12 +178,12 @@ hipError_t launch_routed_down(const Shape& s, const void* w2, const LayerState& 
 
 hipError_t launch_routed_down_big(const Shape& s, const void* w2, const LayerState& L,
                                   const Scratch& W, hipStream_t st) {
-  launch((k_gemm_big<false, true, false, kBigTile, kBigWaves>),
+  launch((k_gemm_big<false, true, kBigTile>),
          dim3(((s.T_big_max + 7) / 8) * 8 * ((s.H + 32 * kBigWaves - 1) / (32 * kBigWaves))),
          dim3(64 * kBigWaves), 0, st,
          static_cast<const uint16_t*>(W.h), static_cast<const uint16_t*>(w2), nullptr, W.flags,
          W.tile_slot_b, W.tile_row0_b, W.offs, L.S_list, W.wl_pos, W.wl_w,
-         static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H, LmPartials{});
+         static_cast<uint16_t*>(W.y_pair), s.M, s.I, s.H);
   return hipGetLastError();
 }
 
@@ -202,22 +204,31 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
     const uint16_t* w1b = static_cast<const uint16_t*>(sw1);
     const uint16_t* w3b = static_cast<const uint16_t*>(sw3);
     const uint16_t* w2b = static_cast<const uint16_t*>(sw2);
-    if (t256 * ncu >= kBig256MinBlocks)
-      launch((k_gemm_big<true, false, false, 256>), grid(t256, ncu), dim3(256), 0, st, xb, w1b,
+    // one-wave-per-SIMD 256 x 256 tiles once they give every CU a tile
+    const int n_cu = device_cu_count();
+    const int w4u = (s.Is + 127) / 128, w4d = (s.H + 255) / 256;
+    if (t256 * w4u >= n_cu)
+      launch((k_gemm_w4<true, false>), dim3(gemm_w4_dense_grid(s.M, w4u)), dim3(256), 0, st, xb,
+             w1b, w3b, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M,
+             s.H, s.Is, LmPartials{});
+    else if (t256 * ncu >= kBig256MinBlocks)
+      launch((k_gemm_big<true, false, 256>), grid(t256, ncu), dim3(256), 0, st, xb, w1b,
              w3b, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H,
-             s.Is, LmPartials{});
+             s.Is);
     else
       launch((k_gemm_big<true, false>), grid(t128, ncu), dim3(256), 0, st, xb, w1b, w3b, W.flags,
-             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H, s.Is,
-             LmPartials{});
-    if (t256 * ncd >= kBig256MinBlocks)
-      launch((k_gemm_big<false, false, false, 256>), grid(t256, ncd), dim3(256), 0, st, hs, w2b,
+             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H, s.Is);
+    if (t256 * w4d >= n_cu)
+      launch((k_gemm_w4<false, false>), dim3(gemm_w4_dense_grid(s.M, w4d)), dim3(256), 0, st, hs,
+             w2b, nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out,
+             s.M, s.Is, s.H, LmPartials{});
+    else if (t256 * ncd >= kBig256MinBlocks)
+      launch((k_gemm_big<false, false, 256>), grid(t256, ncd), dim3(256), 0, st, hs, w2b,
              nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M,
-             s.Is, s.H, LmPartials{});
+             s.Is, s.H);
     else
       launch((k_gemm_big<false, false>), grid(t128, ncd), dim3(256), 0, st, hs, w2b, nullptr,
-             W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M, s.Is, s.H,
-             LmPartials{});
+             W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M, s.Is, s.H);
   } else if (s.bf16) {
     launch_gemm<true, false>(s.T_dense, st, s.H, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(sw1), static_cast<const uint16_t*>(sw3),
