@@ -150,6 +150,25 @@ def test_big_tiles_every_row(frac, R):
     assert rep.iters == w.iters
 
 
+def test_wide_shared_expert_tiles_every_row():
+    """Shared-expert layers whose 256 x 256 tiles are at least as many as the device's CUs run
+    both projections on the one-wave-per-SIMD tiles: M = 32800 positions (129 row tiles, the
+    last one of 32 rows), I_s = 192 and H = 320 (each projection's second column block only
+    partly inside the matrix).  The routed experts take the big tiles too (M K >= 32768).
+    Small hidden/inter sizes keep the oracle quick, so every row is compared."""
+    h = H()
+    w = synth.workload(5, hidden=320, n_experts=16, top_k=1, inter=64, shared_inter=192,
+                       batch=800, block=41, iters=2, staleness_R=1, forced_fraction=1.0,
+                       zipf=None, redraw_every=0)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    t256 = -(-w.M // 256)
+    assert t256 * -(-w.shared_inter // 128) >= n_cu and t256 * -(-w.hidden // 256) >= n_cu
+    assert w.M * w.top_k >= 32768
+    h.log(f"[wide shared tiles] M={w.M} H={w.hidden} Is={w.shared_inter} n_cu={n_cu}")
+    rep = h.run_block(w)
+    assert rep.iters == w.iters
+
+
 def test_kernel_timing_on_both_streams():
     """Kernel timing with every group on, at a shape with big tiles and a shared expert: the
     shared expert and the big tiles run on the device's side stream and are timed there, and
