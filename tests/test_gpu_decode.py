@@ -238,9 +238,10 @@ def test_lm_head_compute_tiles_wide_hidden():
 
 
 # token ids holding one and the same vocabulary row, placed so that the GPU meets their equal
-# logits at every level of its max / argmax reductions: in one lane (5, 6, 21), across the lanes
-# of a row (9), across the waves of a workgroup (69, 197), across token blocks in the row
-# reduction (261) and in the half-width last block (V - 5)
+# logits at every level of its max / argmax reductions: in one lane (5, 6, 21; on the
+# compute-bound tiles, whose waves hold 128 tokens, also 69), across the lanes of a row (9),
+# across the waves of a workgroup (197; on the streamed head, whose waves hold 32 tokens, also
+# 69), across token blocks in the row reduction (261) and in the half-width last block (V - 5)
 TIE_IDS = (5, 6, 9, 21, 69, 197, 261)
 
 
