@@ -699,8 +699,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 // used where the grid has at least one tile per CU.
 // K runs in chunks of 64 bf16: a chunk row is one 128-byte line, and one copy instruction
 // (global_load_lds_dwordx4) moves eight whole lines straight into LDS, half the cache-line
-// requests of 64-byte rows.  Two chunk buffers of 64 KB: chunk c + 2 is copied into chunk c's
-// buffer while chunk c + 1 is multiplied.  LDS rows hold k-segment slot ^ (row & 7) in 16-byte
+// requests of 64-byte rows.  Two chunk buffers of 64 KB: while the second half of chunk c is
+// multiplied, chunk c + 2 is copied into chunk c's buffer (whose fragments have all been read)
+// and chunk c + 1, which has landed, is read.  LDS rows hold k-segment slot ^ (row & 7) in 16-byte
 // slot `slot`, so that the eight lanes a ds_read_b128 serves at once hit distinct banks.
 // Each chunk is multiplied as two halves of K = 32 with fragment register sets 0 and 1: the
 // fragments of the next half are read from LDS (one ds_read_b128 per four MFMAs) while the
@@ -712,9 +713,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 // MFMA results in VGPRs and spills them to AGPRs around every use, cannot insert the wait
 // states an MFMA result needs before a VALU reads it, so the epilogue starts after 48 idle
 // cycles.
-// Grid: LMHEAD and dense tiles in XCD supertiles (MAP): workgroup 8 i + x runs on XCD x, and the
-// 32 workgroups an XCD holds at once cover 4 row tiles x 8 column blocks, so each XCD's L2
-// serves a 4 x 8 block of tiles; routed tiles as k_gemm_big (the big-tile table).
+// Grid: LM-head and dense tiles in XCD supertiles: workgroup 8 i + x runs on XCD x, and the 32
+// workgroups an XCD holds at once cover 4 row tiles x 8 column blocks, so each XCD's L2 serves
+// a 4 x 8 block of tiles; routed tiles as in k_gemm_big (the big-tile table).
 template <bool GATEUP, bool ROUTED, bool LMHEAD = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
