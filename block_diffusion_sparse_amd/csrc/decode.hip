@@ -12,9 +12,11 @@
 //                   vocabulary streamed through LDS once per 256 live rows (the slab's further
 //                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
 //                   each row's 32-token blocks to (max, argmax, sum exp);
-//   k_gemm_w4       LM-head mode, when more are live: 256 live rows x 256 tokens per
-//                   workgroup on the compute-bound tiles, one (max, argmax, sum exp) per row and
-//                   256-token block (the workgroup's two column waves combined in LDS);
+//   k_lm_head_w4    when more are live: tiles of 256 live rows x 256 tokens on the compute-bound
+//                   MFMA tiles, one workgroup per CU walking its tiles with the next tile's
+//                   first chunks copied during the current one's last chunks and epilogue, one
+//                   (max, argmax, sum exp) per row and 256-token block (the tile's two column
+//                   waves combined in LDS);
 //   k_decode_rows   one workgroup per position: the partials of each live row combined in double
 //                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
 //   k_decode_final  one workgroup per sequence: the commits.
@@ -23,6 +25,7 @@
 #include "device_common.h"
 #include "epoch_internal.h"
 #include "expert_gemm.h"
+#include "lm_head.h"
 
 #include <mutex>
 #include <new>
@@ -36,8 +39,7 @@ constexpr int kCompactThreads = 1024;
 constexpr int kLmStreamBuffers = 2;
 constexpr int kLmStreamTileRows = 256;
 // beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 256 tokens
-// (k_gemm_w4: four waves of 128 x 128 outputs, one workgroup per CU; a vocabulary gives plenty
-// of token blocks)
+// (k_lm_head_w4: four waves of 128 x 128 outputs, one workgroup per CU)
 constexpr int kLmBigTileCols = 256;
 
 __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
@@ -277,14 +279,12 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     }
   }
-  // grid: XCD supertiles of 4 row tiles x 8 token blocks (sized for all M positions live;
-  // tiles past the live count exit at once); blocks of kLmBigTileCols tokens (the last one
-  // half when the vocabulary is an odd multiple of 128)
+  // one workgroup per CU, eight per XCD group (a walk per XCD); blocks of kLmBigTileCols tokens
+  // (the last one half when the vocabulary is an odd multiple of 128)
   const int n_cb = (d->vocab + kLmBigTileCols - 1) / kLmBigTileCols;
   const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_cb};
-  launch((k_gemm_w4<false, false, true>), dim3(gemm_w4_dense_grid(M, n_cb)), dim3(256), 0, st,
-         static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), nullptr,
-         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, d->hidden,
+  launch(k_lm_head_w4, dim3(lm_head_grid(device_cu_count())), dim3(256), 0, st,
+         static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), d->hidden,
          d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
   launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,

@@ -38,7 +38,7 @@ constexpr int kTileRows = 64;
 constexpr int kTileRowsTall = 128;
 constexpr int kDenseTileRows = 64;  // rows per shared-expert weight-stream tile
 // live-only decoding: up to this many live rows the LM head streams the vocabulary
-// (k_expert_stream, 128-row tiles), beyond it the compute-bound tiles take it (k_gemm_w4)
+// (k_expert_stream, 128-row tiles), beyond it the compute-bound tiles take it (k_lm_head_w4)
 constexpr int kLmStreamMaxRows = 512;
 constexpr int kBigTile = 256;     // rows per compute-bound routed tile
 // experts with at least this many fresh rows use the compute-bound tiles (on shapes that enable

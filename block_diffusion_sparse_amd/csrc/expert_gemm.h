@@ -42,12 +42,12 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
 }
 
-// Output of the LM-head modes (k_gemm_w4, k_expert_stream): the rows are live positions
-// (gathered through live_list, n_live of them), the columns vocabulary tokens, and instead of
-// the logits the kernels write, per row and per block of tokens, the largest logit, its token
-// (lower id on ties) and the sum of exp(logit - largest) over the block; n_p blocks per row:
-// vocab / 32 from k_expert_stream (one wave's columns), vocab / 256 rounded up from k_gemm_w4
-// (one workgroup's columns).
+// Output of the LM-head kernels (k_expert_stream's LM mode, k_lm_head_w4): the rows are live
+// positions (gathered through live_list, n_live of them), the columns vocabulary tokens, and
+// instead of the logits the kernels write, per row and per block of tokens, the largest logit,
+// its token (lower id on ties) and the sum of exp(logit - largest) over the block; n_p per row:
+// vocab / 32 from k_expert_stream (one wave's columns), vocab / 256 rounded up from k_lm_head_w4
+// (one tile's columns).
 struct LmPartials {
   const int32_t* live_list;
   const int32_t* n_live;
@@ -356,7 +356,7 @@ __device__ __forceinline__ void expert_stream_body(
             arg = oa;
           }
         }
-        // exp(v - mx) as one v_exp_f32 of v log2(e) - mx log2(e), as in k_gemm_w4's LM head
+        // exp(v - mx) as one v_exp_f32 of v log2(e) - mx log2(e), as in k_lm_head_w4
         const float nm = -mx * kLog2e;
         float se = 0.0f;
 #pragma unroll
@@ -695,8 +695,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 // accumulators per lane held in AGPRs), so that a wave reads a third fewer operand bytes from
 // LDS per MFMA than the two-waves-per-SIMD tiles of k_gemm_big.  Same operand roles, staged row
 // layouts (gate/up: groups of 64 rows alternating W1 and W3, so a wave holds g and u of the same
-// 64 columns) and epilogues as k_gemm_big, plus the LM head's (max, argmax, sum exp) epilogue;
-// used where the grid has at least one tile per CU.
+// 64 columns) and epilogues as k_gemm_big; used where the grid has at least one tile per CU
+// (the LM head's persistent variant is k_lm_head_w4).
 // K runs in chunks of 64 bf16: a chunk row is one 128-byte line, and one copy instruction
 // (global_load_lds_dwordx4) moves eight whole lines straight into LDS, half the cache-line
 // requests of 64-byte rows.  Two chunk buffers of 64 KB: while the second half of chunk c is
@@ -713,19 +713,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 // MFMA results in VGPRs and spills them to AGPRs around every use, cannot insert the wait
 // states an MFMA result needs before a VALU reads it, so the epilogue starts after 48 idle
 // cycles.
-// Grid: LM-head and dense tiles in XCD supertiles: workgroup 8 i + x runs on XCD x, and the 32
+// Grid: dense tiles in XCD supertiles: workgroup 8 i + x runs on XCD x, and the 32
 // workgroups an XCD holds at once cover 4 row tiles x 8 column blocks, so each XCD's L2 serves
 // a 4 x 8 block of tiles; routed tiles as in k_gemm_big (the big-tile table).
-template <bool GATEUP, bool ROUTED, bool LMHEAD = false>
+template <bool GATEUP, bool ROUTED>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const int32_t* __restrict__ flags,
     const int32_t* __restrict__ tile_slot, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ offs, const int32_t* __restrict__ S_list,
     const int32_t* __restrict__ wl_pos, const float* __restrict__ wl_w,
-    uint16_t* __restrict__ out, int M, int Kdim, int Ndim, LmPartials lp) {
-  static_assert(!LMHEAD || (!GATEUP && !ROUTED), "the LM head is a plain gathered GEMM");
-  constexpr int BR = 256, BC = 256, KC = 64, WAVES = 4, WN = 2, MB = 8, NBK = 8;
+    uint16_t* __restrict__ out, int M, int Kdim, int Ndim) {
+  constexpr int BR = 256, BC = 256, KC = 64, WAVES = 4, MB = 8, NBK = 8;
   constexpr int NA = BR / (8 * WAVES), NBI = BC / (8 * WAVES);  // copies per wave and chunk
   constexpr int CPC = NA + NBI;
   constexpr int CBW = GATEUP ? BC / 2 : BC;  // output columns per block
@@ -744,9 +743,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     tile = ((pos / n_cb) << 3) + (blockIdx.x & 7);
     cb = pos % n_cb;
   }
-  if (LMHEAD && *lp.n_live <= kLmStreamMaxRows) return;
   const TileRows tr = tile_rows(ROUTED, tile, BR, ROUTED ? flags[FLAG_NTILES_BIG] : 0, tile_slot,
-                                tile_row0, offs, LMHEAD ? *lp.n_live : M);
+                                tile_row0, offs, M);
   if (!tr.active) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -767,7 +765,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     const int row = 8 * (WAVES * j + wave) + (lane >> 3);
     const int seg = (lane & 7) ^ (row & 7);
     const int p = tr.row0 + row < tr.row_end ? tr.row0 + row : tr.row0;
-    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : (LMHEAD ? lp.live_list[p] : p);
+    const int src_row = (ROUTED && GATEUP) ? wl_pos[p] : p;
     asrc[j] = reinterpret_cast<const char*>(A + (size_t)src_row * Kdim + seg * 8);
   }
 #pragma unroll
@@ -868,94 +866,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     frags_ready(1);
     __builtin_amdgcn_s_barrier();
     half_step(1, buf ^ 1, 0, true, src_chunk(c + 2), buf);
+    // the wait states before the accumulators are read, inside the loop: the compiler, which
+    // does not know that the asm MFMAs' results arrive late, places the copies and spills of
+    // the accumulators that the epilogue needs where the loop exits
+    if (c == nch - 1) asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
   }
   // the last step's surplus copies and reads land before anything else uses LDS or those
-  // registers; then the wait states before the accumulators are read
+  // registers
   wait_vm_lds<0>();
   frags_ready(0);
   frags_ready(1);
-  asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
-  if (LMHEAD) {
-    // Per row, over this workgroup's 256 tokens: lane (r, g) of row block m holds tokens
-    // 16 n + 4 g + i (n < 8, i < 4) of its wave's 128-token block for row 16 m + r.  Each wave
-    // reduces its tokens in registers (max, lower token on ties: tokens are visited in
-    // increasing order and only a larger logit replaces), then across the four lanes of the row
-    // (lane bits 4 and 5), then the sum of exp(logit - max) likewise; the two waves of a row
-    // half then meet in LDS, and one (max, argmax, sum) per row and workgroup is written.  A
-    // wave whose tokens lie past the vocabulary (the last block of a vocabulary that is an odd
-    // multiple of 128 tokens) contributes (-inf, -, 0).  exp(v - mx) for v <= mx is one
-    // v_exp_f32 of v log2(e) - mx log2(e) (a single fma): the rounding of mx log2(e) makes the
-    // relative error about 1e-6 for logits up to 20 in magnitude; terms below exp(-87)
-    // underflow to 0
-    struct Part {
-      float mx;
-      int arg;
-      float se;
-    };
-    static_assert(sizeof(Part) * BR * WN <= sizeof(As), "the partials fit in the operand buffers");
-    Part* part = reinterpret_cast<Part*>(&As[0][0]);  // [BR rows][WN waves]
-    const bool wlive = cb * BC + 128 * wn < Ndim;
-    const int tok0 = cb * BC + 128 * wn + 4 * g;
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      float mx = acc[m][0][0];
-      int arg = tok0;
-#pragma unroll
-      for (int n = 0; n < NBK; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((n | i) && acc[m][n][i] > mx) {
-            mx = acc[m][n][i];
-            arg = tok0 + 16 * n + i;
-          }
-#pragma unroll
-      for (int o = 16; o < 64; o <<= 1) {
-        const float om = __shfl_xor(mx, o, 64);
-        const int oa = __shfl_xor(arg, o, 64);
-        if (om > mx || (om == mx && oa < arg)) {
-          mx = om;
-          arg = oa;
-        }
-      }
-      const float nm = -mx * kLog2e;
-      float se = 0.0f;
-#pragma unroll
-      for (int n = 0; n < NBK; ++n)
-        se += (__builtin_amdgcn_exp2f(fmaf(acc[m][n][0], kLog2e, nm)) +
-               __builtin_amdgcn_exp2f(fmaf(acc[m][n][1], kLog2e, nm))) +
-              (__builtin_amdgcn_exp2f(fmaf(acc[m][n][2], kLog2e, nm)) +
-               __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
-#pragma unroll
-      for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
-      if (g == 0)
-        part[(128 * wm + 16 * m + r) * WN + wn] =
-            wlive ? Part{mx, arg, se} : Part{-INFINITY, 0x7fffffff, 0.0f};
-    }
-    __syncthreads();
-    for (int rr = tid; rr < BR; rr += 64 * WAVES) {
-      const int row = tr.row0 + rr;
-      if (row >= tr.row_end) continue;
-      Part best = part[rr * WN];
-#pragma unroll
-      for (int w = 1; w < WN; ++w) {
-        const Part q = part[rr * WN + w];
-        if (q.mx > best.mx) best = q;
-      }
-      const float nm = -best.mx * kLog2e;
-      float se = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WN; ++w) {
-        const Part q = part[rr * WN + w];
-        se += q.se * __builtin_amdgcn_exp2f(fmaf(q.mx, kLog2e, nm));
-      }
-      const size_t idx = (size_t)row * lp.n_p + cb;
-      lp.pmax[idx] = best.mx;
-      lp.parg[idx] = best.arg;
-      lp.psum[idx] = se;
-    }
-    return;
-  }
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int row = tr.row0 + 128 * wm + 16 * m + r;
@@ -985,7 +905,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
   }
 }
 
-// Grid of k_gemm_w4 for a dense or LM-head GEMM of `rows` rows and n_cb column blocks: whole
+// Grid of k_gemm_w4 for a dense GEMM of `rows` rows and n_cb column blocks: whole
 // XCD supertiles of 4 x 8 tiles, 32 workgroups each, supertiles dealt to the 8 XCDs in turn.
 inline int gemm_w4_dense_grid(int rows, int n_cb) {
   const int supertiles = ((rows + 255) / 256 + 3) / 4 * ((n_cb + 7) / 8);

@@ -210,7 +210,7 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
     if (t256 * w4u >= n_cu)
       launch((k_gemm_w4<true, false>), dim3(gemm_w4_dense_grid(s.M, w4u)), dim3(256), 0, st, xb,
              w1b, w3b, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M,
-             s.H, s.Is, LmPartials{});
+             s.H, s.Is);
     else if (t256 * ncu >= kBig256MinBlocks)
       launch((k_gemm_big<true, false, 256>), grid(t256, ncu), dim3(256), 0, st, xb, w1b,
              w3b, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hs_out, s.M, s.H,
@@ -221,7 +221,7 @@ hipError_t launch_shared(const Shape& s, const void* x, const void* sw1, const v
     if (t256 * w4d >= n_cu)
       launch((k_gemm_w4<false, false>), dim3(gemm_w4_dense_grid(s.M, w4d)), dim3(256), 0, st, hs,
              w2b, nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out,
-             s.M, s.Is, s.H, LmPartials{});
+             s.M, s.Is, s.H);
     else if (t256 * ncd >= kBig256MinBlocks)
       launch((k_gemm_big<false, false, 256>), grid(t256, ncd), dim3(256), 0, st, hs, w2b,
              nullptr, W.flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S_out, s.M,
