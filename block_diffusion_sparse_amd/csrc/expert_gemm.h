@@ -704,8 +704,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(
 // and chunk c + 1, which has landed, is read.  LDS rows hold k-segment slot ^ (row & 7) in 16-byte
 // slot `slot`, so that the eight lanes a ds_read_b128 serves at once hit distinct banks.
 // Each chunk is multiplied as two halves of K = 32 with fragment register sets 0 and 1: the
-// fragments of the next half are read from LDS (one ds_read_b128 per four MFMAs) while the
-// current half is multiplied.  One barrier per chunk, before the second half: every wave's
+// fragments of the next half are read from LDS (two ds_read_b128 per four MFMAs in the first
+// half of the half) while the current half is multiplied, and have landed by its end.  One barrier per chunk, before the second half: every wave's
 // copies of chunk c + 1 have landed and every wave has read all of chunk c, whose buffer the
 // second half refills.  Every step issues the same copies and reads (past the last chunk they
 // repeat the last one into a buffer nobody reads again), so the loop has no tail.
@@ -834,12 +834,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
         : "+a"(acc[m][n]) : "v"(fb[set][n]), "v"(fa[set][m]));
   };
-  // one half: 64 MFMAs on `set`; the 16 fragment reads of (rbuf, rhalf) into the other set;
-  // when `copy`, the CPC copies of chunk cp into buffer cbuf
+  // one half: 64 MFMAs on `set`; the 16 fragment reads of (rbuf, rhalf) into the other set,
+  // two per group of four MFMAs in the first eight groups, so that they have landed by the
+  // half's end; when `copy`, the CPC copies of chunk cp into buffer cbuf, one per group
   auto half_step = [&](int set, int rbuf, int rhalf, bool copy, int cp, int cbuf) {
 #pragma unroll
     for (int grp = 0; grp < 16; ++grp) {
-      read(rbuf, rhalf, set ^ 1, grp);
+      if (grp < 8) {
+        read(rbuf, rhalf, set ^ 1, 2 * grp);
+        read(rbuf, rhalf, set ^ 1, 2 * grp + 1);
+      }
       mma(set, 4 * grp + 0);
       mma(set, 4 * grp + 1);
       if (copy) issue(grp, cp, cbuf);
@@ -858,24 +862,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4(
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 16; ++i) read(0, 0, 0, i);
+  frags_ready(0);
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
-    frags_ready(0);
     half_step(0, buf, 1, false, 0, 0);
     wait_vm_lds<0>();
     frags_ready(1);
     __builtin_amdgcn_s_barrier();
     half_step(1, buf ^ 1, 0, true, src_chunk(c + 2), buf);
+    // the next chunk's first-half fragments have landed before the loop's back edge, where the
+    // compiler may copy registers
+    frags_ready(0);
     // the wait states before the accumulators are read, inside the loop: the compiler, which
     // does not know that the asm MFMAs' results arrive late, places the copies and spills of
     // the accumulators that the epilogue needs where the loop exits
     if (c == nch - 1) asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
   }
-  // the last step's surplus copies and reads land before anything else uses LDS or those
-  // registers
+  // the last step's surplus copies land before anything else uses LDS
   wait_vm_lds<0>();
-  frags_ready(0);
-  frags_ready(1);
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int row = tr.row0 + 128 * wm + 16 * m + r;

@@ -183,6 +183,29 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
     if (!last) frags_ready(0);
     advance();
   };
+  // The row's four lanes (lane bits 4 and 5) combine in two rounds of pairs (lanes 16, then 32
+  // apart) on the VALU: v_permlane16_swap / v_permlane32_swap with both operands one register
+  // leave the two lanes of every pair holding both pair values, one in each result, so a
+  // symmetric combine of the two results is the pair's combine in both of its lanes.  The
+  // best of two is the larger logit, the lower token on ties; sums add the two values, which
+  // gives both lanes the same bits
+  auto swap_pair = [](uint32_t v, bool far) __attribute__((always_inline)) {
+    return far ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+               : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  };
+  auto pair_best = [&](float& mx, int& arg, bool far) __attribute__((always_inline)) {
+    const auto pm = swap_pair(__float_as_uint(mx), far);
+    const auto pa = swap_pair((uint32_t)arg, far);
+    const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+    const int a0 = (int)pa[0], a1 = (int)pa[1];
+    const bool one = (m1 > m0) | ((m1 == m0) & (a1 < a0));
+    mx = one ? m1 : m0;
+    arg = one ? a1 : a0;
+  };
+  auto pair_sum = [&](float& v, bool far) __attribute__((always_inline)) {
+    const auto p = swap_pair(__float_as_uint(v), far);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  };
   set_rows(cu_tile);
   set_cols(cu_cb);
 #pragma unroll
@@ -237,22 +260,14 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
         // first equal logit, from two independent scans over halves of the lane's tokens
         int k0 = 4 * NBK, k1 = 0;
 #pragma unroll
-        for (int k = 2 * NBK - 1; k >= 0; --k)
-          if (acc[m][k >> 2][k & 3] == mx) k0 = k;
-#pragma unroll
-        for (int k = 4 * NBK - 1; k >= 2 * NBK; --k)
-          if (acc[m][k >> 2][k & 3] == mx) k1 = k;
+        for (int k = 2 * NBK - 1; k >= 0; --k) {
+          k0 = acc[m][k >> 2][k & 3] == mx ? k : k0;
+          k1 = acc[m][(k + 2 * NBK) >> 2][k & 3] == mx ? k + 2 * NBK : k1;
+        }
         const int k = k0 < 4 * NBK ? k0 : k1;
         int arg = tok0 + 16 * (k >> 2) + (k & 3);
-#pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-          const float om = __shfl_xor(mx, o, 64);
-          const int oa = __shfl_xor(arg, o, 64);
-          if (om > mx || (om == mx && oa < arg)) {
-            mx = om;
-            arg = oa;
-          }
-        }
+        pair_best(mx, arg, false);
+        pair_best(mx, arg, true);
         const float nm = -mx * kLog2e;
         float se = 0.0f;
 #pragma unroll
@@ -261,8 +276,8 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
                  __builtin_amdgcn_exp2f(fmaf(acc[m][n][1], kLog2e, nm))) +
                 (__builtin_amdgcn_exp2f(fmaf(acc[m][n][2], kLog2e, nm)) +
                  __builtin_amdgcn_exp2f(fmaf(acc[m][n][3], kLog2e, nm)));
-#pragma unroll
-        for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
+        pair_sum(se, false);
+        pair_sum(se, true);
         if (g == 0)
           part[(128 * wm + 16 * m + r) * WN + wn] =
               wlive ? Part{mx, arg, se} : Part{-INFINITY, 0x7fffffff, 0.0f};

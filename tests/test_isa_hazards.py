@@ -149,8 +149,9 @@ def test_lm_head_kernel_has_no_fragment_or_accumulator_hazards(tmp_path_factory)
 def test_dense_tile_kernel_has_no_fragment_or_accumulator_hazards(tmp_path_factory, gateup):
     asm = _assembly("experts.hip", tmp_path_factory)
     lines = _kernel_body(asm, "_ZN5epoch9k_gemm_w4ILb%dELb0EE" % int(gateup))
-    touched, early, _, _ = scan(lines)
-    # the loop carries the next half's fragment reads over its back edge to the wait at its
-    # top; along the layout order nothing may touch them before that wait
+    touched, early, labels, scratch = scan(lines)
     assert not touched, touched[:5]
     assert not early, early[:5]
+    # every chunk step waits for its fragment reads before the loop's back edge
+    assert not labels, labels[:5]
+    assert scratch == 0
