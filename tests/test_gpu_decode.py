@@ -237,6 +237,25 @@ def test_lm_head_compute_tiles_wide_hidden():
                    logit_bound(hs[0], Wb)) <= report_cap(D)
 
 
+@pytest.mark.parametrize("H", [64, 192], ids=["one-chunk", "three-chunks"])
+def test_lm_head_compute_tiles_walk_several_tiles_per_workgroup(H):
+    """Enough compute-bound tiles that every workgroup of the fixed grid walks several: 1312
+    live rows (six 256-row tiles, the last with 32 rows, so two row supertiles of four with
+    two tiles missing from the second) over 257 x 128 tokens (129 token blocks, the last half
+    past the vocabulary; 17 token supertiles, the last with one block).  A workgroup's copy
+    cursor then crosses tile boundaries, row-tile changes and skipped tiles, with K in one
+    chunk (the first chunk of a tile is also its last) and in three."""
+    batch, block, V = 41, 32, 257 * 128
+    hs, Wb, _ = synth.decode_inputs(130 + H, batch, block, H, V)
+    D = np.zeros(batch * block, np.uint8)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                   logit_bound(hs[0], Wb)) <= report_cap(D)
+
+
 # token ids holding one and the same vocabulary row, placed so that the GPU meets their equal
 # logits at every level of its max / argmax reductions: in one lane (5, 6, 21; on the
 # compute-bound tiles, whose waves hold 128 tokens, also 69), across the lanes of a row (9),
