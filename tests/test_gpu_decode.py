@@ -256,6 +256,22 @@ def test_lm_head_compute_tiles_walk_several_tiles_per_workgroup(H):
                    logit_bound(hs[0], Wb)) <= report_cap(D)
 
 
+@pytest.mark.parametrize("batch", [10, 20], ids=["320-live-streamed", "640-live-compute-tiles"])
+def test_lm_head_largest_hidden_size(batch):
+    """H = 16384, the largest hidden size the decoding call accepts (256 K chunks; the widest
+    byte offsets of both LM heads' copies), on the streamed head and on the compute-bound tiles,
+    over a ragged vocabulary of 3 x 128 tokens."""
+    block, H, V = 32, 16384, 384
+    hs, Wb, _ = synth.decode_inputs(160 + batch, batch, block, H, V)
+    D = np.zeros(batch * block, np.uint8)
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
+    assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
+                   logit_bound(hs[0], Wb)) <= report_cap(D)
+
+
 # token ids holding one and the same vocabulary row, placed so that the GPU meets their equal
 # logits at every level of its max / argmax reductions: in one lane (5, 6, 21; on the
 # compute-bound tiles, whose waves hold 128 tokens, also 69), across the lanes of a row (9),
