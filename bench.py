@@ -490,8 +490,9 @@ def bench_decode(args):
     dt = (time.perf_counter() - t0) / reps
     live = int((D == 0).sum())
     # algorithmic bytes: the vocabulary once, the live rows, the partials (32-token blocks
-    # from the streamed LM head, 64-token blocks beyond its live-row limit)
-    blk = 32 if live <= 512 else 64
+    # from the streamed LM head, which takes up to 128 live rows; 256-token blocks from the
+    # compute-bound tiles beyond that)
+    blk = 32 if live <= 128 else 256
     lm_bytes = V * H * 2 + live * H * 2 + live * (V // blk) * 12
     flops = 2.0 * live * V * H
     print(json.dumps({

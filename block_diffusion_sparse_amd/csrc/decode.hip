@@ -33,7 +33,7 @@
 namespace epoch {
 
 constexpr int kCompactThreads = 1024;
-// the streamed LM head: 256-row tiles (one pass over the vocabulary for up to 256 live rows),
+// the streamed LM head: 256-row tiles (one pass over the vocabulary for its live rows),
 // eight waves of 32 tokens with two chunk buffers (2 x 64 KB of LDS), or four waves with three
 // (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
 constexpr int kLmStreamBuffers = 2;

@@ -38,8 +38,11 @@ constexpr int kTileRows = 64;
 constexpr int kTileRowsTall = 128;
 constexpr int kDenseTileRows = 64;  // rows per shared-expert weight-stream tile
 // live-only decoding: up to this many live rows the LM head streams the vocabulary
-// (k_expert_stream, 128-row tiles), beyond it the compute-bound tiles take it (k_lm_head_w4)
-constexpr int kLmStreamMaxRows = 512;
+// (k_expert_stream, one 256-row tile per token block), beyond it the compute-bound tiles of
+// k_lm_head_w4 take it: from about this many rows up they are faster even with most of a
+// 256-row tile empty, since every wave of the streamed head reads every live row's
+// fragments from LDS
+constexpr int kLmStreamMaxRows = 128;
 constexpr int kBigTile = 256;     // rows per compute-bound routed tile
 // experts with at least this many fresh rows use the compute-bound tiles (on shapes that enable
 // them): beside those tiles the weight stream keeps 64-row tiles, so an expert with more rows

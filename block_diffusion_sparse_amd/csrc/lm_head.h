@@ -14,13 +14,13 @@ namespace epoch {
 // the next one, which land while the epilogue reduces the tile.  The start of a tile
 // (activation row lookups, the first two chunks' latency, a workgroup launch) is thus paid
 // once per workgroup instead of once per tile.
-// Walk: workgroup 8 i + x (on XCD x) of a grid of 8 P takes the u-th tiles of XCD x's walk for
-// u = i, i + P, i + 2 P, ...; XCD x's walk covers supertiles s = x, x + 8, x + 16, ... (4 row
-// tiles x 8 token blocks each, row supertile s / nsc, token supertile s % nsc) 32 tiles apiece,
-// tile u & 31 of a supertile being row tile (u & 31) / 8 and token block u & 7 in it; tiles past
-// the live rows or the vocabulary are skipped.  With P = 32 workgroup i keeps one slot of the
-// supertile: its row tile changes only when the walk reaches the next row supertile, and the
-// 32 workgroups of an XCD share 4 row tiles and 8 token blocks in its L2.
+// Walk: the tiles in supertile order (row supertiles of 4 row tiles; in each, supertiles of
+// 4 row tiles x 8 token blocks, row-major; the last row or token supertile narrower when the
+// counts are not multiples of 4 and 8), dealt in rounds of G = 8 P tiles: in round k workgroup
+// 8 i + x (on XCD x) takes tile k G + P x + i.  So every workgroup gets the same number of
+// tiles, give or take one, whatever the row and token counts; each XCD takes P consecutive
+// tiles per round, with P = 32 one whole supertile, of which workgroup i keeps slot i (row
+// tile i / 8, token block i % 8), so that its row tile changes only at a new row supertile.
 // Accumulators start from zero through the first half-chunk's MFMAs (inline constant C = 0).
 // Epilogue per row: the lane's largest logit is a max tree and its token the first equal
 // logit (so the lowest token on ties), then the row's four lanes and two waves combine with
@@ -41,20 +41,48 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
   __shared__ Part part[BR * WN];  // [row][wave column half]
   const int rows = *lp.n_live;
   if (rows <= kLmStreamMaxRows) return;  // the streamed LM head covered them
-  const int T = (rows + BR - 1) / BR, n_cb = (V + BC - 1) / BC, nsc = (n_cb + 7) / 8;
-  const int nsup = (T + 3) / 4 * nsc, P = gridDim.x >> 3, x = blockIdx.x & 7;
+  const int T = (rows + BR - 1) / BR, n_cb = (V + BC - 1) / BC, NV = T * n_cb;
+  const int G = gridDim.x, P = G >> 3;
   const int nch = Kdim / KC;
-  // the first valid tile of the walk at or after u (u advanced to it), or false at its end
-  auto locate = [&](int& u, int& tile, int& cb) __attribute__((always_inline)) -> bool {
-    for (;; u += P) {
-      const int s = 8 * (u >> 5) + x;
-      if (s >= nsup) return false;
-      tile = (s / nsc) * 4 + ((u & 31) >> 3);
-      cb = (s % nsc) * 8 + (u & 7);
-      if (tile < T && cb < n_cb) return true;
+  // tile v of the walk order: row supertiles of four row tiles (the last one R < 4 when T is
+  // not a multiple of 4), each in supertiles of R row tiles x 8 token blocks (the last one
+  // C < 8 blocks wide), each supertile row-major
+  auto tile_of = [&](int v, int& tile, int& cb) __attribute__((always_inline)) {
+    const int full_rs = T >> 2, per_rs = 4 * n_cb;
+    int rs, w, R;
+    if (v < full_rs * per_rs) {
+      rs = v / per_rs;
+      w = v - rs * per_rs;
+      R = 4;
+    } else {
+      rs = full_rs;
+      w = v - full_rs * per_rs;
+      R = T - 4 * full_rs;
     }
+    const int ncs = n_cb >> 3, full = 8 * R * ncs;
+    int cs, o, C;
+    if (w < full) {
+      cs = w / (8 * R);
+      o = w - cs * 8 * R;
+      C = 8;
+    } else {
+      cs = ncs;
+      o = w - full;
+      C = n_cb - 8 * ncs;
+    }
+    tile = 4 * rs + o / C;
+    cb = 8 * cs + o % C;
   };
-  int cu_u = blockIdx.x >> 3, cu_tile = 0, cu_cb = 0, cu_c = 0;  // copy cursor
+  // walk position u of this workgroup: tile u G + P (blockIdx.x % 8) + blockIdx.x / 8, so that
+  // each round of G tiles gives every XCD P consecutive tiles of the order; false at the end
+  const int wg_off = P * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3);
+  auto locate = [&](int u, int& tile, int& cb) __attribute__((always_inline)) -> bool {
+    const int v = u * G + wg_off;
+    if (v >= NV) return false;
+    tile_of(v, tile, cb);
+    return true;
+  };
+  int cu_u = 0, cu_tile = 0, cu_cb = 0, cu_c = 0;  // copy cursor
   if (!locate(cu_u, cu_tile, cu_cb)) return;
   int co_u = cu_u, co_tile = cu_tile, co_cb = cu_cb;  // the tile being multiplied
   const int tid = threadIdx.x, lane = tid & 63;
@@ -89,7 +117,8 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
   // tile; past the walk's end it stays on the last chunk (copies nobody reads)
   auto advance = [&]() __attribute__((always_inline)) {
     if (++cu_c < nch) return;
-    int u = cu_u + P, t = 0, cb = 0;
+    const int u = cu_u + 1;
+    int t = 0, cb = 0;
     if (!locate(u, t, cb)) {
       cu_c = nch - 1;
       return;
@@ -308,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_w4(const uint16_t* __restric
         lp.psum[idx] = se;
       }
     }
-    co_u += P;
+    ++co_u;
     if (!locate(co_u, co_tile, co_cb)) break;
   }
   // the surplus copies land before the workgroup's LDS is released

@@ -22,6 +22,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -24
+# the most live rows the streamed LM head takes; more go to the compute-bound tiles
+STREAM_MAX_ROWS = 128
 CONF_EPS = 1e-5
 REPORT_CAP = 0.03
 
@@ -114,10 +116,10 @@ def test_small_decode_step(shape):
 
 
 @pytest.mark.parametrize("shape", [(8, 32, 128, 384), (9, 32, 128, 384)],
-                         ids=["b8x32-two-row-tiles-v384", "b9x32-three-row-tiles-v384"])
+                         ids=["b8x32-v384", "b9x32-v384"])
 def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
-    """256 and 288 positions (about 190 and 215 live rows: one 256-row streamed LM-head tile)
-    with a vocabulary that is not a multiple of 256."""
+    """256 and 288 positions (about 190 and 215 live rows: one ragged 256-row tile of the
+    compute-bound LM head) with a vocabulary that is not a multiple of 256."""
     batch, block, H, V = shape
     hs, Wb, D = synth.decode_inputs(70 + batch, batch, block, H, V)
     dec = Decoder(batch, block, H, V)
@@ -128,11 +130,11 @@ def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
     assert reported <= report_cap(D)
 
 
-@pytest.mark.parametrize("batch", [16, 20], ids=["512-live-streamed", "640-live-compute-tiles"])
+@pytest.mark.parametrize("batch", [4, 5], ids=["128-live-streamed", "160-live-compute-tiles"])
 def test_lm_head_on_both_sides_of_the_stream_limit(batch):
-    """Every position live: 512 live rows are the most the streamed LM head takes (two
-    256-row passes over each vocabulary slab, 32-token partials); 640 go to the compute-bound
-    tiles (three 256-row tiles, the last ragged; 256-token partials)."""
+    """Every position live: 128 live rows are the most the streamed LM head takes (one
+    256-row pass over each vocabulary slab, 32-token partials); 160 go to the compute-bound
+    tiles (one ragged 256-row tile; 256-token partials)."""
     block, H, V = 32, 128, 384
     hs, Wb, _ = synth.decode_inputs(55 + batch, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)
@@ -207,8 +209,9 @@ def test_decode_full_vocab_shape():
 
 
 @pytest.mark.parametrize("n_live", [300, 500], ids=["300-live", "500-live"])
-def test_lm_head_streamed_ragged_second_row_tile(n_live):
-    """The streamed LM head with two 256-row passes, the second one ragged (44 and 244 rows)."""
+def test_lm_head_compute_tiles_ragged_second_row_tile(n_live):
+    """The compute-bound LM head with two 256-row tiles, the second one ragged (44 and 244
+    rows): fewer than four row tiles, so its walk's row supertile is two tiles tall."""
     batch, block, H, V = 16, 32, 128, 1024
     hs, Wb, _ = synth.decode_inputs(300 + n_live, batch, block, H, V)
     rng = np.random.default_rng(n_live)
@@ -237,15 +240,19 @@ def test_lm_head_compute_tiles_wide_hidden():
                    logit_bound(hs[0], Wb)) <= report_cap(D)
 
 
-@pytest.mark.parametrize("H", [64, 192], ids=["one-chunk", "three-chunks"])
-def test_lm_head_compute_tiles_walk_several_tiles_per_workgroup(H):
-    """Enough compute-bound tiles that every workgroup of the fixed grid walks several: 1312
-    live rows (six 256-row tiles, the last with 32 rows, so two row supertiles of four with
-    two tiles missing from the second) over 257 x 128 tokens (129 token blocks, the last half
-    past the vocabulary; 17 token supertiles, the last with one block).  A workgroup's copy
-    cursor then crosses tile boundaries, row-tile changes and skipped tiles, with K in one
-    chunk (the first chunk of a tile is also its last) and in three."""
-    batch, block, V = 41, 32, 257 * 128
+@pytest.mark.parametrize("batch,H,V", [(41, 64, 257 * 128), (41, 192, 257 * 128),
+                                       (7, 64, 513 * 128)],
+                         ids=["six-row-tiles-one-chunk", "six-row-tiles-three-chunks",
+                              "one-row-tile-257-blocks"])
+def test_lm_head_compute_tiles_walk_several_tiles_per_workgroup(batch, H, V):
+    """Enough compute-bound tiles that workgroups of the fixed grid walk several: 1312 live
+    rows (six 256-row tiles, the last with 32 rows: a full row supertile of four and one of
+    two) over 257 x 128 tokens (129 token blocks, the last half past the vocabulary; the last
+    token supertile one block wide), and 224 live rows (one row tile) over 513 x 128 tokens
+    (257 blocks: one more tile than a 256-CU grid).  A workgroup's copy cursor then crosses
+    tile boundaries and row-tile changes, with K in one chunk (the first chunk of a tile is
+    also its last) and in three."""
+    block = 32
     hs, Wb, _ = synth.decode_inputs(130 + H, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)
     dec = Decoder(batch, block, H, V)
@@ -256,11 +263,15 @@ def test_lm_head_compute_tiles_walk_several_tiles_per_workgroup(H):
                    logit_bound(hs[0], Wb)) <= report_cap(D)
 
 
-@pytest.mark.parametrize("batch", [10, 20], ids=["320-live-streamed", "640-live-compute-tiles"])
+@pytest.mark.parametrize("batch", [4, 20], ids=["128-live-streamed", "640-live-compute-tiles"])
 def test_lm_head_largest_hidden_size(batch):
     """H = 16384, the largest hidden size the decoding call accepts (256 K chunks; the widest
     byte offsets of both LM heads' copies), on the streamed head and on the compute-bound tiles,
-    over a ragged vocabulary of 3 x 128 tokens."""
+    over a ragged vocabulary of 3 x 128 tokens.  The fp32 accumulation bound is widest here
+    (B_t near 7e-3, far above its value at H = 1024), and so is the band of rows whose
+    decision it leaves open (a top-two gap under 2 B_t, a confidence within tau (2 B_t + 1e-5)
+    of tau): about 3 % of the rows of these inputs, judged on the oracle's values alone; up to
+    5 % may be reported here."""
     block, H, V = 32, 16384, 384
     hs, Wb, _ = synth.decode_inputs(160 + batch, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)
@@ -269,7 +280,7 @@ def test_lm_head_largest_hidden_size(batch):
     Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
     out = oracle.live_decode(hs[0], Wb, D, block, 0.95, token=tokens)
     assert compare(D, tokens, out, Dn, tok, conf, block, 0.95,
-                   logit_bound(hs[0], Wb)) <= report_cap(D)
+                   logit_bound(hs[0], Wb)) <= max(report_cap(D), -(-5 * batch * block // 100))
 
 
 # token ids holding one and the same vocabulary row, placed so that the GPU meets their equal
@@ -280,7 +291,7 @@ def test_lm_head_largest_hidden_size(batch):
 TIE_IDS = (5, 6, 9, 21, 69, 197, 261)
 
 
-@pytest.mark.parametrize("batch,live_all", [(16, False), (24, True)],
+@pytest.mark.parametrize("batch,live_all", [(4, False), (24, True)],
                          ids=["streamed", "compute-tiles"])
 def test_lm_head_exact_ties_take_the_lowest_token(batch, live_all):
     """Rows leaning toward a vocabulary row that several token ids share exactly.  A tied top
@@ -311,7 +322,7 @@ def test_lm_head_exact_ties_take_the_lowest_token(batch, live_all):
     Dn, tok, conf = dec(dev(hb), dev(Wb), D, tokens)
     out = oracle.live_decode(hb, Wb, D, block, 0.95, token=tokens)
     live = D == 0
-    assert (live.sum() <= 512) != live_all          # the intended LM-head path
+    assert (live.sum() <= STREAM_MAX_ROWS) != live_all   # the intended LM-head path
     assert np.array_equal(Dn, out["D_next"])          # one fallback commit per sequence
     hot = live & (out["D_next"] == 1) & np.isin(out["token"], ids)
     assert hot.sum() == batch, int(hot.sum())
