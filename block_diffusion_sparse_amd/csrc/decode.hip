@@ -9,9 +9,8 @@
 //   k_live_compact  one workgroup: the live positions (D = 0) in ascending order, their count,
 //                   and each position's index in that list;
 //   k_expert_stream LM-head mode, when at most kLmStreamMaxRows positions are live: the
-//                   vocabulary streamed through LDS once per 256 live rows (the slab's further
-//                   passes in L2), 256 or 128 tokens per work item, the epilogue reducing
-//                   each row's 32-token blocks to (max, argmax, sum exp);
+//                   vocabulary streamed through LDS once, 256 or 128 tokens per work item,
+//                   the epilogue reducing each row's 32-token blocks to (max, argmax, sum exp);
 //   k_lm_head_w4    when more are live: tiles of 256 live rows x 256 tokens on the compute-bound
 //                   MFMA tiles, one workgroup per CU walking its tiles with the next tile's
 //                   first chunks copied during the current one's last chunks and epilogue, one
@@ -33,11 +32,14 @@
 namespace epoch {
 
 constexpr int kCompactThreads = 1024;
-// the streamed LM head: 256-row tiles (one pass over the vocabulary for its live rows),
-// eight waves of 32 tokens with two chunk buffers (2 x 64 KB of LDS), or four waves with three
-// (3 x 48 KB) when the vocabulary has fewer 256-token blocks than the device has CUs
-constexpr int kLmStreamBuffers = 2;
-constexpr int kLmStreamTileRows = 256;
+// the streamed LM head: one 128-row tile (a single pass over the vocabulary, its rows streamed
+// with the non-temporal policy), eight waves of 32 tokens with three chunk buffers (3 x 48 KB
+// of LDS, two chunks in flight), or four waves with four (4 x 32 KB) when the vocabulary has
+// fewer 256-token blocks than the device has CUs
+constexpr int kLmStreamBuffers = 3;
+constexpr int kLmStreamBuffers4 = 4;
+constexpr int kLmStreamTileRows = 128;
+static_assert(kLmStreamTileRows >= kLmStreamMaxRows, "one pass over the vocabulary");
 // beyond kLmStreamMaxRows live rows: compute-bound tiles of 256 live rows x 256 tokens
 // (k_lm_head_w4: four waves of 128 x 128 outputs, one workgroup per CU)
 constexpr int kLmBigTileCols = 256;
@@ -269,7 +271,7 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
     const uint16_t* wv = static_cast<const uint16_t*>(w_vocab);
     if (d->vocab / 256 < n_cu) {
       const int n_cb = d->vocab / 128;
-      launch((k_expert_stream<false, false, kLmStreamBuffers + 1, 4, kLmStreamTileRows, true>),
+      launch((k_expert_stream<false, false, kLmStreamBuffers4, 4, kLmStreamTileRows, true>),
              dim3(n_cb < n_cu ? n_cb : n_cu), dim3(256), 0, st, hb, wv, nullptr, nullptr, nullptr,
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     } else {

@@ -38,7 +38,7 @@ constexpr int kTileRows = 64;
 constexpr int kTileRowsTall = 128;
 constexpr int kDenseTileRows = 64;  // rows per shared-expert weight-stream tile
 // live-only decoding: up to this many live rows the LM head streams the vocabulary
-// (k_expert_stream, one 256-row tile per token block), beyond it the compute-bound tiles of
+// (k_expert_stream, one 128-row tile per token block), beyond it the compute-bound tiles of
 // k_lm_head_w4 take it: from about this many rows up they are faster even with most of a
 // 256-row tile empty, since every wave of the streamed head reads every live row's
 // fragments from LDS

@@ -145,7 +145,8 @@ __device__ __forceinline__ void expert_stream_body(
   // this workgroup's items: position (blockIdx.x / 8) + k G8 along the tile-major order of
   // its XCD lane, active while the tile 8 (position / n_cb) + lane8 exists.  LM head: the
   // column blocks blockIdx.x + j gridDim.x, each with all its row tiles back to back (the
-  // vocabulary slab is read from memory once and its next passes find it in L2).
+  // decoding call gives it no more live rows than one tile holds, so each vocabulary slab is
+  // read once).
   const int lane8 = blockIdx.x & 7, pos0 = blockIdx.x >> 3, G8 = gridDim.x >> 3;
   int nitems;
   if (LMHEAD) {
@@ -253,12 +254,8 @@ __device__ __forceinline__ void expert_stream_body(
     for (int j = 0; j < NAW; ++j)
       copy16_to_lds(asrc[j] + (size_t)cc * KC, &As[buf * ABUF + 8 * (NAW * wave + j) * KC]);
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      if (LMHEAD)  // the slab's next row tile reads it again: keep it in L2
-        copy16_to_lds(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
-      else
-        copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
-    }
+    for (int j = 0; j < NBW; ++j)
+      copy16_to_lds_stream(bsrc[j] + (size_t)cc * KC, &Bs[buf * BBUF + (32 * wave + 8 * j) * KC]);
     ++ic;
   };
 
