@@ -53,6 +53,9 @@ def parse():
                     help="measure live-only output decoding (LM head on live rows + threshold "
                          "commit) instead of the MoE layer")
     ap.add_argument("--vocab", type=int, default=32768, help="--decode: vocabulary size")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="--decode: sequences of the workload's block length (default: the "
+                         "workload's batch)")
     ap.add_argument("--n-group", type=int, default=0,
                     help="group-limited top-k: number of contiguous expert groups (0: off)")
     ap.add_argument("--topk-group", type=int, default=0,
@@ -464,8 +467,9 @@ def bench_decode(args):
     import synth
     from block_diffusion_sparse_amd import binding as B
     w = synth.workload(args.workload)
-    M, H, V = w.M, w.hidden, args.vocab
-    hs, Wb, D = synth.decode_inputs(w.seed, w.batch, w.block, H, V)
+    batch = args.decode_batch or w.batch
+    M, H, V = batch * w.block, w.hidden, args.vocab
+    hs, Wb, D = synth.decode_inputs(w.seed, batch, w.block, H, V)
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -473,7 +477,7 @@ def bench_decode(args):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     h, Wv, Dd = dev(hs[0]), dev(Wb), dev(D)
-    d = B.make_decode_desc(w.batch, w.block, H, V)
+    d = B.make_decode_desc(batch, w.block, H, V)
     n = B.epoch_decode_workspace_bytes(d)
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     Dn = torch.empty(M, dtype=torch.uint8, device="cuda")
@@ -501,7 +505,7 @@ def bench_decode(args):
         "steps": reps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"live-decode {w.batch}x{w.block} h{H} v{V}", "live": live,
+        "config": {"workload": f"live-decode {batch}x{w.block} h{H} v{V}", "live": live,
                    "tau": 0.95},
         "us_per_step": round(dt * 1e6, 2),
         "lm_head_gbs": round(lm_bytes / dt / 1e9, 1),
