@@ -206,8 +206,14 @@ struct DecodeLayout {
   size_t bytes;
 };
 
+// The partials hold the streamed LM head's (at most kLmStreamMaxRows rows of vocab / 32
+// blocks) or the compute-bound tiles' (all M rows of vocab / 256 blocks, rounded up).
 DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
-  const size_t M = (size_t)d->batch * d->block, n_p = (size_t)d->vocab / 32;
+  const size_t M = (size_t)d->batch * d->block;
+  const size_t n_stream = (M < (size_t)kLmStreamMaxRows ? M : (size_t)kLmStreamMaxRows) *
+                          ((size_t)d->vocab / 32);
+  const size_t n_big = M * (((size_t)d->vocab + kLmBigTileCols - 1) / kLmBigTileCols);
+  const size_t n_part = n_stream > n_big ? n_stream : n_big;
   size_t off = 0;
   char* b = static_cast<char*>(base);
   auto take = [&](size_t n) {
@@ -220,9 +226,9 @@ DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
   L.live_list = static_cast<int32_t*>(take(M * 4));
   L.live_idx = static_cast<int32_t*>(take(M * 4));
   L.n_live = static_cast<int32_t*>(take(4));
-  L.pmax = static_cast<float*>(take(M * n_p * 4));
-  L.parg = static_cast<int32_t*>(take(M * n_p * 4));
-  L.psum = static_cast<float*>(take(M * n_p * 4));
+  L.pmax = static_cast<float*>(take(n_part * 4));
+  L.parg = static_cast<int32_t*>(take(n_part * 4));
+  L.psum = static_cast<float*>(take(n_part * 4));
   L.conf_pos = static_cast<double*>(take(M * 8));
   L.top_pos = static_cast<int32_t*>(take(M * 4));
   L.bytes = (off + 255) / 256 * 256;

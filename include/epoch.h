@@ -299,8 +299,8 @@ typedef struct epoch_decode_desc {
 } epoch_decode_desc;
 
 /* Bytes of device workspace epoch_live_decode needs for `d` (live list, per-position
-   live index, per-row partial reductions of up to M x V/32 entries, per-position confidence
-   and top token). */
+   live index, per-row partial reductions of max(min(M, 128) x V/32, M x ceil(V/256)) entries,
+   per-position confidence and top token). */
 int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes);
 
 /*
@@ -336,7 +336,7 @@ int32_t epoch_live_decode(const epoch_decode_desc* d, const void* h, const void*
  * first call on it (with that device current).  The call allocates nothing and calls no
  * allocating routine.  A shape whose epoch_decode_workspace_bytes exceeds
  * EPOCH_DECODE_STATIC_SCRATCH_BYTES returns EPOCH_E_SCRATCH and enqueues nothing (for example
- * 512 positions at a 131072-token vocabulary fit, 2048 do not).  Every call on a device uses
+ * 2048 positions at a 131072-token vocabulary fit, 8192 do not).  Every call on a device uses
  * the same array: calls whose work overlaps on one device (unordered streams, several host
  * threads) race and give undefined results; order them on one stream.  The array keeps the
  * latest call's contents; every buffer in it is written before it is read, so nothing needs

@@ -92,7 +92,7 @@ int main(void) {
                           (void*)256, n, NULL) == EPOCH_E_ALIGN);
   CHECK(epoch_live_decode(&dd, (void*)256, (void*)256, (uint8_t*)256, (uint8_t*)256, (int32_t*)256, NULL,
                           (void*)256, 16, NULL) == EPOCH_E_WORKSPACE);
-  epoch_decode_desc big = {64, 32, 2048, 131072, EPOCH_DTYPE_BF16, 0, 0.95};
+  epoch_decode_desc big = {256, 32, 2048, 131072, EPOCH_DTYPE_BF16, 0, 0.95};
   CHECK(epoch_live_decode_static(&big, (void*)256, (void*)256, (uint8_t*)256, (uint8_t*)256,
                                  (int32_t*)256, NULL, NULL) == EPOCH_E_SCRATCH);
   for (int code = 1; code >= -10; --code) CHECK(epoch_status_string(code) != NULL);

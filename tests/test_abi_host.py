@@ -104,8 +104,8 @@ def test_static_decode_rejects_shapes_beyond_its_scratch():
     if not os.path.exists(B.LIB_PATH):
         pytest.skip("libepoch.so not built")
     cap = B.EPOCH_DECODE_STATIC_SCRATCH_BYTES
-    fits = B.make_decode_desc(16, 32, 2048, 131072)          # 512 positions
-    big = B.make_decode_desc(64, 32, 2048, 131072)           # 2048 positions
+    fits = B.make_decode_desc(64, 32, 2048, 131072)          # 2048 positions
+    big = B.make_decode_desc(256, 32, 2048, 131072)          # 8192 positions
     assert B.epoch_decode_workspace_bytes(fits) <= cap < B.epoch_decode_workspace_bytes(big)
     with pytest.raises(B.EpochError) as ei:   # aligned stand-in pointers: never dereferenced
         B.epoch_live_decode_static(big, 256, 256, 256, 256, 256, None, 0)
