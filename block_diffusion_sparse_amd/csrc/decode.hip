@@ -100,14 +100,37 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big
   }
   const int n_p = *n_live <= kLmStreamMaxRows ? n_p_stream : n_p_big;
   const size_t row = (size_t)li * n_p;
+  // up to kRowCache partials per thread stay in registers between the two passes (every
+  // vocabulary up to 131072 tokens), so the row is read from memory once
+  constexpr int kRowCache = 16;
+  const bool cached = n_p <= 256 * kRowCache;
+  float cm[kRowCache], cs[kRowCache];
   float m = -INFINITY;
   int a = 0x7fffffff;
-  for (int j = threadIdx.x; j < n_p; j += 256) {
-    const float pm = pmax[row + j];
-    const int pa = parg[row + j];
-    if (pm > m || (pm == m && pa < a)) {
-      m = pm;
-      a = pa;
+  if (cached) {
+#pragma unroll
+    for (int k = 0; k < kRowCache; ++k) {
+      const int j = threadIdx.x + 256 * k;
+      cm[k] = -INFINITY;
+      cs[k] = 0.0f;
+      if (j < n_p) {
+        cm[k] = pmax[row + j];
+        cs[k] = psum[row + j];
+        const int pa = parg[row + j];
+        if (cm[k] > m || (cm[k] == m && pa < a)) {
+          m = cm[k];
+          a = pa;
+        }
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < n_p; j += 256) {
+      const float pm = pmax[row + j];
+      const int pa = parg[row + j];
+      if (pm > m || (pm == m && pa < a)) {
+        m = pm;
+        a = pa;
+      }
     }
   }
 #pragma unroll
@@ -133,8 +156,14 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big
       a = sa[w];
     }
   double z = 0.0;
-  for (int j = threadIdx.x; j < n_p; j += 256)
-    z += (double)psum[row + j] * exp((double)pmax[row + j] - (double)m);
+  if (cached) {
+#pragma unroll
+    for (int k = 0; k < kRowCache; ++k)
+      if (threadIdx.x + 256 * k < n_p) z += (double)cs[k] * exp((double)cm[k] - (double)m);
+  } else {
+    for (int j = threadIdx.x; j < n_p; j += 256)
+      z += (double)psum[row + j] * exp((double)pmax[row + j] - (double)m);
+  }
   z = wave_sum(z);
   if (lane == 0) sz[wave] = z;
   __syncthreads();
