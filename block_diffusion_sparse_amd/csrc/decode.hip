@@ -20,7 +20,8 @@
 //                   (confidence = 1 / sum_v exp(z_v - z_max)) with its top token;
 //   k_decode_final  one workgroup per sequence: the commits.
 // The live count is known on the device only, so both LM-head kernels are launched and the one
-// that does not own it exits at once.
+// that does not own it exits at once (the compute-bound one is not launched for batches of at
+// most kLmStreamMaxRows positions).
 #include "device_common.h"
 #include "epoch_internal.h"
 #include "expert_gemm.h"
@@ -318,11 +319,13 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
   }
   // one workgroup per CU, eight per XCD group (a walk per XCD); blocks of kLmBigTileCols tokens
   // (the last one half when the vocabulary is an odd multiple of 128)
+  // (not launched when the batch has no more positions than the streamed head takes)
   const int n_cb = (d->vocab + kLmBigTileCols - 1) / kLmBigTileCols;
   const LmPartials lp_big{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_cb};
-  launch(k_lm_head_w4, dim3(lm_head_grid(device_cu_count())), dim3(256), 0, st,
-         static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), d->hidden,
-         d->vocab, lp_big);
+  if (M > kLmStreamMaxRows)
+    launch(k_lm_head_w4, dim3(lm_head_grid(device_cu_count())), dim3(256), 0, st,
+           static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), d->hidden,
+           d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
   launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
          L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
