@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_live_compact(int M,
 // of its top token 1 / sum_v exp(z_v - z_max) and that token (the lowest id among equal
 // maxima); a decoded position gets confidence -1 and token -1.  The partials are n_p_stream
 // per row when the streamed LM head ran (at most kLmStreamMaxRows live), else n_p_big.
+template <bool CACHED>
 __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big,
                                                      const int32_t* __restrict__ n_live,
                                                      const int32_t* __restrict__ live_idx,
@@ -101,10 +102,13 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big
   }
   const int n_p = *n_live <= kLmStreamMaxRows ? n_p_stream : n_p_big;
   const size_t row = (size_t)li * n_p;
-  // up to kRowCache partials per thread stay in registers between the two passes (every
-  // vocabulary up to 131072 tokens), so the row is read from memory once
+  // CACHED (launched for batches of at most kLmStreamMaxRows positions, whose partials the
+  // streamed head wrote, 32-token blocks): up to kRowCache partials per thread stay in
+  // registers between the two passes (every vocabulary up to 131072 tokens), so the row is
+  // read from memory once.  The registers this takes would halve the workgroups per CU of a
+  // large batch's launch, so other batches read their (fewer, 256-token) partials twice.
   constexpr int kRowCache = 16;
-  const bool cached = n_p <= 256 * kRowCache;
+  const bool cached = CACHED && n_p <= 256 * kRowCache;
   float cm[kRowCache], cs[kRowCache];
   float m = -INFINITY;
   int a = 0x7fffffff;
@@ -327,8 +331,12 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_vocab), d->hidden,
            d->vocab, lp_big);
   const size_t lds = (size_t)d->block * (sizeof(double) + sizeof(int32_t));
-  launch(k_decode_rows, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
-         L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
+  if (M <= kLmStreamMaxRows)
+    launch(k_decode_rows<true>, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
+           L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
+  else
+    launch(k_decode_rows<false>, dim3(M), dim3(256), 0, st, n_p, n_cb, L.n_live, L.live_idx,
+           L.pmax, L.parg, L.psum, L.conf_pos, L.top_pos);
   launch(k_decode_final, dim3(d->batch), dim3(256), lds, st, d->block, d->tau, decoded,
          L.conf_pos, L.top_pos, decoded_next, tokens, conf);
   return hipGetLastError() == hipSuccess ? EPOCH_OK : EPOCH_E_HIP;
