@@ -10,7 +10,8 @@
 //                   and each position's index in that list;
 //   k_expert_stream LM-head mode, when at most kLmStreamMaxRows positions are live: the
 //                   vocabulary streamed through LDS once, 256 or 128 tokens per work item,
-//                   the epilogue reducing each row's 32-token blocks to (max, argmax, sum exp);
+//                   the epilogue reducing each row's logits of a work item to (max, argmax,
+//                   sum exp), the item's waves combined in LDS;
 //   k_lm_head_w4    when more are live: tiles of 256 live rows x 256 tokens on the compute-bound
 //                   MFMA tiles, one workgroup per CU walking its tiles with the next tile's
 //                   first chunks copied during the current one's last chunks and epilogue, one
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big
   const int n_p = *n_live <= kLmStreamMaxRows ? n_p_stream : n_p_big;
   const size_t row = (size_t)li * n_p;
   // CACHED (launched for batches of at most kLmStreamMaxRows positions, whose partials the
-  // streamed head wrote, 32-token blocks): up to kRowCache partials per thread stay in
-  // registers between the two passes (every vocabulary up to 131072 tokens), so the row is
+  // streamed head wrote, 128- or 256-token blocks): up to kRowCache partials per thread stay
+  // in registers between the two passes (every vocabulary up to 524288 tokens), so the row is
   // read from memory once.  The registers this takes would halve the workgroups per CU of a
   // large batch's launch, so other batches read their (fewer, 256-token) partials twice.
   constexpr int kRowCache = 16;
@@ -240,12 +241,12 @@ struct DecodeLayout {
   size_t bytes;
 };
 
-// The partials hold the streamed LM head's (at most kLmStreamMaxRows rows of vocab / 32
-// blocks) or the compute-bound tiles' (all M rows of vocab / 256 blocks, rounded up).
+// The partials hold the streamed LM head's (at most kLmStreamMaxRows rows of vocab / 128
+// blocks at most) or the compute-bound tiles' (all M rows of vocab / 256 blocks, rounded up).
 DecodeLayout decode_carve(const epoch_decode_desc* d, void* base) {
   const size_t M = (size_t)d->batch * d->block;
   const size_t n_stream = (M < (size_t)kLmStreamMaxRows ? M : (size_t)kLmStreamMaxRows) *
-                          ((size_t)d->vocab / 32);
+                          ((size_t)d->vocab / 128);
   const size_t n_big = M * (((size_t)d->vocab + kLmBigTileCols - 1) / kLmBigTileCols);
   const size_t n_part = n_stream > n_big ? n_stream : n_big;
   size_t off = 0;
@@ -299,10 +300,11 @@ int32_t check_decode_args(const epoch_decode_desc* d, const void* h, const void*
 int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_vocab,
                        const uint8_t* decoded, uint8_t* decoded_next, int32_t* tokens, float* conf,
                        const DecodeLayout& L, hipStream_t st) {
-  const int M = d->batch * d->block, n_p = d->vocab / 32;
+  const int M = d->batch * d->block;
   launch(k_live_compact, dim3(1), dim3(kCompactThreads), 0, st, M, decoded,
                      L.live_list, L.live_idx, L.n_live);
-  const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
+  // the streamed head's partials: one per row and work item (256 or 128 tokens)
+  int n_p = 0;
   // few live rows: the streamed LM head, one workgroup per CU walking token blocks
   // blockIdx.x + j gridDim.x (256 tokens, or 128 when that is needed to give every CU one)
   {
@@ -311,11 +313,15 @@ int32_t decode_enqueue(const epoch_decode_desc* d, const void* h, const void* w_
     const uint16_t* wv = static_cast<const uint16_t*>(w_vocab);
     if (d->vocab / 256 < n_cu) {
       const int n_cb = d->vocab / 128;
+      n_p = n_cb;
+      const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
       launch((k_expert_stream<false, false, kLmStreamBuffers4, 4, kLmStreamTileRows, true>),
              dim3(n_cb < n_cu ? n_cb : n_cu), dim3(256), 0, st, hb, wv, nullptr, nullptr, nullptr,
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);
     } else {
       const int n_cb = (d->vocab + 255) / 256;  // the last block may be half (vocab % 256 = 128)
+      n_p = n_cb;
+      const LmPartials lp{L.live_list, L.n_live, L.pmax, L.parg, L.psum, n_p};
       launch((k_expert_stream<false, false, kLmStreamBuffers, 8, kLmStreamTileRows, true>),
              dim3(n_cb < n_cu ? n_cb : n_cu), dim3(512), 0, st, hb, wv, nullptr, nullptr, nullptr,
              nullptr, nullptr, nullptr, L.live_list, nullptr, nullptr, M, d->hidden, d->vocab, lp);

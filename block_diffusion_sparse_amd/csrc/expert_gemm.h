@@ -117,6 +117,19 @@ __device__ __forceinline__ void copy16_to_lds_stream(const void* src, void* lds_
 // would make the wait for it also wait for every copy in flight.
 // The kernel body for tiles of BM rows; As / Bs: NB chunk buffers of BM x 64 and 32 WAVES x 64
 // bf16 in LDS.
+// The LM-head mode's per-row, per-wave partials of one work item, for the combine of the
+// item's waves (an LDS array only in the kernels that use it).
+struct LmPart {
+  float mx;
+  int arg;
+  float se;
+};
+template <int N>
+__device__ __forceinline__ LmPart* lm_part_lds() {
+  __shared__ LmPart part[N];
+  return part;
+}
+
 template <bool GATEUP, bool ROUTED, int NB, int WAVES, int BM, bool LMHEAD>
 __device__ __forceinline__ void expert_stream_body(
     uint16_t* As, uint16_t* Bs, const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
@@ -326,7 +339,10 @@ __device__ __forceinline__ void expert_stream_body(
     if constexpr (LMHEAD) {
       // per row: the 32 logits of this wave's token block sit in the 4 lanes with the same r
       // (tokens 4 g .. 4 g + 3 and 16 + 4 g .. + 3); reduce (max, lower token on ties), then
-      // the sum of exp(logit - max)
+      // the sum of exp(logit - max); the item's WAVES waves then meet in LDS and one
+      // (max, token, sum) per row and item (CBW tokens) is written.  Every wave runs this
+      // (a wave past the vocabulary contributes (-inf, -, 0)), so its barrier is uniform.
+      LmPart* part = lm_part_lds<BM * WAVES>();  // [row][wave]
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (it.row0 + 16 * m >= it.row_end) continue;
@@ -362,13 +378,34 @@ __device__ __forceinline__ void expert_stream_body(
                 __builtin_amdgcn_exp2f(fmaf(c1[m][i], kLog2e, nm));
 #pragma unroll
         for (int o = 16; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
-        const int li = it.row0 + 16 * m + r;
-        if (g == 0 && li < it.row_end) {
-          const size_t idx = (size_t)li * lp.n_p + it.col0 / 32;
-          lp.pmax[idx] = mx;
-          lp.parg[idx] = arg;
-          lp.psum[idx] = se;
+        if (g == 0)
+          part[(16 * m + r) * WAVES + wave] =
+              it.wact ? LmPart{mx, arg, se} : LmPart{-INFINITY, 0x7fffffff, 0.0f};
+      }
+      // the partials of every wave are in LDS (the next item's writes follow at least one
+      // more barrier of the chunk loop, after these reads)
+      asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+      const int blk = it.col0 / CBW;  // col0 = CBW blk + 32 wave
+      for (int rr = tid; rr < BM; rr += 64 * WAVES) {
+        const int li = it.row0 + rr;
+        if (li >= it.row_end) continue;
+        LmPart best = part[rr * WAVES];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+          const LmPart q = part[rr * WAVES + w];
+          if (q.mx > best.mx) best = q;
         }
+        const float nm = -best.mx * kLog2e;
+        float se = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+          const LmPart q = part[rr * WAVES + w];
+          se += q.se * __builtin_amdgcn_exp2f(fmaf(q.mx, kLog2e, nm));
+        }
+        const size_t idx = (size_t)li * lp.n_p + blk;
+        lp.pmax[idx] = best.mx;
+        lp.parg[idx] = best.arg;
+        lp.psum[idx] = se;
       }
       return;
     }
@@ -437,7 +474,7 @@ __device__ __forceinline__ void expert_stream_body(
       }
     }
     if (++cc == nch) {
-      if (cur.wact) epilogue(cur);
+      if (LMHEAD || cur.wact) epilogue(cur);
       ++ck;
       cc = 0;
       if (ck < nitems) {

@@ -299,7 +299,7 @@ typedef struct epoch_decode_desc {
 } epoch_decode_desc;
 
 /* Bytes of device workspace epoch_live_decode needs for `d` (live list, per-position
-   live index, per-row partial reductions of max(min(M, 128) x V/32, M x ceil(V/256)) entries,
+   live index, per-row partial reductions of max(min(M, 128) x V/128, M x ceil(V/256)) entries,
    per-position confidence and top token). */
 int32_t epoch_decode_workspace_bytes(const epoch_decode_desc* d, size_t* out_bytes);
 

@@ -146,10 +146,12 @@ def test_lm_head_on_both_sides_of_the_stream_limit(batch):
     assert reported <= report_cap(D)
 
 
-def test_lm_head_wide_vocabulary():
+@pytest.mark.parametrize("V", [65536, 65536 + 128], ids=["v65536", "v65664-half-last-block"])
+def test_lm_head_wide_vocabulary(V):
     """A vocabulary of at least 256 tokens per CU (65536 on 256 CUs) takes the eight-wave
-    streamed LM head (256-token blocks); small hidden size keeps the oracle quick."""
-    batch, block, H, V = 2, 32, 128, 65536
+    streamed LM head (256-token blocks; with 65664 tokens the last block is half, its upper
+    four waves past the vocabulary); small hidden size keeps the oracle quick."""
+    batch, block, H = 2, 32, 128
     hs, Wb, D = synth.decode_inputs(66, batch, block, H, V)
     dec = Decoder(batch, block, H, V)
     tokens = np.full(batch * block, -1, np.int32)
