@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_decode_rows(int n_p_stream, int n_p_big
   const size_t row = (size_t)li * n_p;
   // CACHED (launched for batches of at most kLmStreamMaxRows positions, whose partials the
   // streamed head wrote, 128- or 256-token blocks): up to kRowCache partials per thread stay
-  // in registers between the two passes (every vocabulary up to 524288 tokens), so the row is
+  // in registers between the two passes (every vocabulary the call accepts), so the row is
   // read from memory once.  The registers this takes would halve the workgroups per CU of a
   // large batch's launch, so other batches read their (fewer, 256-token) partials twice.
   constexpr int kRowCache = 16;
