@@ -493,10 +493,11 @@ def bench_decode(args):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
     live = int((D == 0).sum())
-    # algorithmic bytes: the vocabulary once, the live rows, the partials (32-token blocks
-    # from the streamed LM head, which takes up to 128 live rows; 256-token blocks from the
-    # compute-bound tiles beyond that)
-    blk = 32 if live <= 128 else 256
+    # algorithmic bytes: the vocabulary once, the live rows, the partials (one per live row
+    # and 256-token block; 128-token blocks from the streamed LM head, which takes up to 128
+    # live rows, when the vocabulary has fewer 256-token blocks than the chip has CUs)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blk = 128 if (live <= 128 and V // 256 < n_cu) else 256
     lm_bytes = V * H * 2 + live * H * 2 + live * (V // blk) * 12
     flops = 2.0 * live * V * H
     print(json.dumps({
