@@ -133,8 +133,9 @@ def test_lm_head_row_tiles_and_ragged_vocabulary(shape):
 @pytest.mark.parametrize("batch", [4, 5], ids=["128-live-streamed", "160-live-compute-tiles"])
 def test_lm_head_on_both_sides_of_the_stream_limit(batch):
     """Every position live: 128 live rows are the most the streamed LM head takes (one
-    256-row pass over each vocabulary slab, 32-token partials); 160 go to the compute-bound
-    tiles (one ragged 256-row tile; 256-token partials)."""
+    128-row pass over each vocabulary slab; at this vocabulary four-wave work items of 128
+    tokens, one partial each); 160 go to the compute-bound tiles (one ragged 256-row tile;
+    256-token partials)."""
     block, H, V = 32, 128, 384
     hs, Wb, _ = synth.decode_inputs(55 + batch, batch, block, H, V)
     D = np.zeros(batch * block, np.uint8)

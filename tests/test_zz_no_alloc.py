@@ -37,7 +37,7 @@ def test_static_scratch_decode_matches_workspace_decode():
     from block_diffusion_sparse_amd import binding as B
     B.load()
     # first call: 768 positions, all live (the compute-bound LM head, 256-token partials);
-    # second call: 96 positions with a quarter decoded (the streamed LM head, 32-token partials)
+    # second call: 96 positions with a quarter decoded (the streamed LM head, 128-token partials)
     shapes = [(24, 32, 256, 4096, True), (3, 32, 192, 2048, False)]
     for batch, block, H, V, all_live in shapes:
         hs, Wb, D = synth.decode_inputs(900 + batch, batch, block, H, V)
