@@ -211,6 +211,33 @@ def test_decode_full_vocab_shape():
                    logit_bound(hs[0], Wb)) <= report_cap(D)
 
 
+def test_decode_bench_shape_sampled_sequences():
+    """The largest decoding shape the benchmark times: 128 sequences of 64 positions from the
+    8192-position sweep workload's seed (about 6080 live), H 2048, V 131072 (a 512 MiB bf16 LM
+    head).  The GPU decodes every position, in the same launch configuration as the benchmark
+    (the compute-bound LM-head tiles, a fixed grid walking 24 row tiles x 512 token blocks);
+    the oracle decodes the first, a middle and the last sequence whole.  That is exact for
+    them: a sequence's commits depend only on its own positions' logits."""
+    w = synth.workload(5)
+    batch, block, H, V = w.batch, w.block, w.hidden, 131072
+    hs, Wb, D = synth.decode_inputs(w.seed, batch, block, H, V)
+    assert int((D == 0).sum()) > 2 * 1024  # several row tiles of 256 live rows
+    dec = Decoder(batch, block, H, V)
+    tokens = np.full(batch * block, -1, np.int32)
+    Dn, tok, conf = dec(dev(hs[0]), dev(Wb), D, tokens)
+    rows = np.concatenate([np.arange(b * block, (b + 1) * block)
+                           for b in (0, batch // 2, batch - 1)])
+    h_s, D_s, t_s = hs[0][rows], D[rows], tokens[rows]
+    out = oracle.live_decode(h_s, Wb, D_s, block, 0.95, token=t_s)
+    assert compare(D_s, t_s, out, Dn[rows], tok[rows], conf[rows], block, 0.95,
+                   logit_bound(h_s, Wb)) <= report_cap(D_s)
+    # every position: a decoded one stays decoded with its token untouched; a live one commits
+    # exactly when it gets a token, which is a vocabulary id
+    live = D == 0
+    assert (Dn[~live] == 1).all() and (tok[~live] == -1).all()
+    assert ((tok[live] >= 0) == (Dn[live] == 1)).all() and (tok < V).all()
+
+
 @pytest.mark.parametrize("n_live", [300, 500], ids=["300-live", "500-live"])
 def test_lm_head_compute_tiles_ragged_second_row_tile(n_live):
     """The compute-bound LM head with two 256-row tiles, the second one ragged (44 and 244
